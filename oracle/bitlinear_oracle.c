@@ -1,0 +1,271 @@
+/*
+ * CPU oracle for the BitNet b1.58 BitLinear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls
+ * this file: only the tests, the smoke check and the benchmark's CPU-baseline leg
+ * do.  It shares no code, header, table or constant with the HIP library.
+ *
+ * Every function is the plain definition of one step, written as slow scalar
+ * loops so that it can be checked against the sources by eye:
+ *
+ *   [CS]    "1-bit LLM era: Microsoft introduces BitNet b1.58" (cheatsheet.md),
+ *           section "What is BitNet b1.58?": BitLinear replaces nn.Linear; the
+ *           weight quantiser scales by the mean absolute value, rounds to the
+ *           nearest integer and constrains to {-1,0,1}; activations are scaled
+ *           per token; no bias.
+ *   [ASI]   asi.tokyo article on BitNet b1.58 2B4T (2025-04-27), the paragraphs
+ *           on the absmean quantiser, the 8-bit messages between layers and the
+ *           custom GPU software that packs four weights into one byte.
+ *   [LUMEN] lumen-it.ai article on BitNet (original 1-bit BitNet): absmax
+ *           quantisation of activations.
+ *   [HADA]  news.hada.io topic 20406 (vi and pt editions), comment on ternary
+ *           packing: five ternary digits in one byte, log2(3) = 1.58 bits.
+ *
+ * Readings taken where the sources are silent (each is listed with its reason
+ * in the design notes):
+ *   - gamma is one scalar per weight matrix, accumulated in double precision in
+ *     a fixed order (row by row, k ascending inside a row), then divided by N*K
+ *     and rounded once to float.
+ *   - "round to the nearest integer" is round-half-to-even on the exact
+ *     quotient w/gamma; the result is clipped to [-1, 1].
+ *   - activation quantisation is symmetric 8-bit: s = 127 / max|x| per token,
+ *     q = clamp(rint(x * s), -127, 127), computed in float (the precision of
+ *     the GPU kernel, since this decides an integer); an all-zero token gets
+ *     s = 1 and q = 0.
+ *   - accumulation is exact integer arithmetic; the output is acc * gamma / s,
+ *     evaluated here in double precision.
+ *   - packed layouts are the ones the library header documents (2-bit codes
+ *     t+1 in 32-bit words of 16 trits; base-3 bytes of 5 trits).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ---- input element types --------------------------------------------- */
+
+enum { ORC_F32 = 0, ORC_BF16 = 1 };
+
+/* bfloat16 is the upper half of a binary32: widening is a 16-bit shift. */
+float orc_bf16_to_f32(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static float load_elem(const void *p, int dtype, int64_t i)
+{
+    if (dtype == ORC_BF16)
+        return orc_bf16_to_f32(((const uint16_t *)p)[i]);
+    return ((const float *)p)[i];
+}
+
+/* ---- weights: absmean quantiser [CS "What is BitNet b1.58?", first bullet;
+ *      ASI, absmean-quantiser paragraph] --------------------------------- */
+
+/* gamma = mean |W| over the whole N x K matrix. */
+float orc_absmean_gamma(const void *w, int dtype, int64_t n_rows, int64_t k_cols)
+{
+    double total = 0.0;
+    for (int64_t n = 0; n < n_rows; ++n) {
+        double row = 0.0;
+        for (int64_t k = 0; k < k_cols; ++k)
+            row += fabs((double)load_elem(w, dtype, n * k_cols + k));
+        total += row;
+    }
+    return (float)(total / ((double)n_rows * (double)k_cols));
+}
+
+/* t = clip(round(w / gamma), -1, 1), round half to even. */
+void orc_absmean_trits(const void *w, int dtype, int64_t n_rows, int64_t k_cols,
+                       float gamma, int8_t *t)
+{
+    for (int64_t i = 0; i < n_rows * k_cols; ++i) {
+        double v = (double)load_elem(w, dtype, i);
+        if (v == 0.0) {           /* zero scales to zero, whatever gamma is */
+            t[i] = 0;
+            continue;
+        }
+        double r = rint(v / (double)gamma);  /* gamma == 0 gives +-inf */
+        if (r > 1.0) r = 1.0;
+        if (r < -1.0) r = -1.0;
+        t[i] = (int8_t)r;
+    }
+}
+
+/* ---- 2-bit packing, four trits per byte [ASI, custom-software paragraph] --
+ * Row n occupies pitch2(K) bytes, a whole number of 16-byte groups of 64 trits.
+ * Inside a row, 32-bit little-endian word g holds trits k = 16g .. 16g+15: the
+ * trit k = 16g + 4i + j sits in byte j of the word, bits 2i..2i+1, as the code
+ * t + 1 in {0,1,2}.  Positions past K hold code 1 (trit 0). */
+
+int64_t orc_pack2_pitch(int64_t k_cols)
+{
+    return ((k_cols + 63) / 64) * 16;
+}
+
+void orc_pack2(const int8_t *t, int64_t n_rows, int64_t k_cols, uint8_t *packed)
+{
+    int64_t pitch = orc_pack2_pitch(k_cols);
+    for (int64_t n = 0; n < n_rows; ++n) {
+        for (int64_t b = 0; b < pitch; ++b) {
+            /* byte b of the row is byte j of word g */
+            int64_t g = b / 4, j = b % 4;
+            unsigned byte = 0;
+            for (int i = 0; i < 4; ++i) {
+                int64_t k = 16 * g + 4 * i + j;
+                int code = 1;
+                if (k < k_cols)
+                    code = t[n * k_cols + k] + 1;
+                byte |= (unsigned)code << (2 * i);
+            }
+            packed[n * pitch + b] = (uint8_t)byte;
+        }
+    }
+}
+
+void orc_unpack2(const uint8_t *packed, int64_t n_rows, int64_t k_cols, int8_t *t)
+{
+    int64_t pitch = orc_pack2_pitch(k_cols);
+    for (int64_t n = 0; n < n_rows; ++n) {
+        for (int64_t k = 0; k < k_cols; ++k) {
+            int64_t g = k / 16, i = (k % 16) / 4, j = k % 4;
+            unsigned byte = packed[n * pitch + 4 * g + j];
+            int code = (int)((byte >> (2 * i)) & 3u);
+            t[n * k_cols + k] = (int8_t)(code - 1);
+        }
+    }
+}
+
+/* ---- base-3 packing, five trits per byte [HADA, ternary-packing comment] --
+ * Byte j of row n is sum_{i=0..4} (t[n][5j+i] + 1) * 3^i, so the lowest k is
+ * the least significant digit.  Trits past K are 0 (digit 1); the row pitch is
+ * ceil(K/5) rounded up to 16 bytes and the filler bytes are 121 (= 11111 in
+ * base 3, five zero trits). */
+
+int64_t orc_pack3_pitch(int64_t k_cols)
+{
+    int64_t nbytes = (k_cols + 4) / 5;
+    return ((nbytes + 15) / 16) * 16;
+}
+
+void orc_pack3(const int8_t *t, int64_t n_rows, int64_t k_cols, uint8_t *packed)
+{
+    int64_t pitch = orc_pack3_pitch(k_cols);
+    for (int64_t n = 0; n < n_rows; ++n) {
+        for (int64_t b = 0; b < pitch; ++b) {
+            unsigned value = 0, weight = 1;
+            for (int i = 0; i < 5; ++i) {
+                int64_t k = 5 * b + i;
+                int digit = 1;
+                if (k < k_cols)
+                    digit = t[n * k_cols + k] + 1;
+                value += (unsigned)digit * weight;
+                weight *= 3;
+            }
+            packed[n * pitch + b] = (uint8_t)value;
+        }
+    }
+}
+
+void orc_unpack3(const uint8_t *packed, int64_t n_rows, int64_t k_cols, int8_t *t)
+{
+    int64_t pitch = orc_pack3_pitch(k_cols);
+    for (int64_t n = 0; n < n_rows; ++n) {
+        for (int64_t k = 0; k < k_cols; ++k) {
+            unsigned value = packed[n * pitch + k / 5];
+            for (int64_t i = 0; i < k % 5; ++i)
+                value /= 3;
+            t[n * k_cols + k] = (int8_t)((int)(value % 3) - 1);
+        }
+    }
+}
+
+/* ---- activations: per-token absmax to 8 bits [CS "What is BitNet b1.58?",
+ *      activation bullet; ASI, 8-bit messages; LUMEN, absmax] ------------- */
+
+void orc_quantize_act(const void *x, int dtype, int64_t m_rows, int64_t k_cols,
+                      int8_t *q, float *scale, int32_t *rowsum)
+{
+    for (int64_t m = 0; m < m_rows; ++m) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < k_cols; ++k) {
+            float a = fabsf(load_elem(x, dtype, m * k_cols + k));
+            if (a > amax)
+                amax = a;
+        }
+        int32_t sum = 0;
+        if (amax == 0.0f) {
+            scale[m] = 1.0f;
+            for (int64_t k = 0; k < k_cols; ++k)
+                q[m * k_cols + k] = 0;
+        } else {
+            float s = 127.0f / amax;
+            scale[m] = s;
+            for (int64_t k = 0; k < k_cols; ++k) {
+                float v = load_elem(x, dtype, m * k_cols + k) * s;
+                float r = rintf(v);
+                if (r > 127.0f) r = 127.0f;
+                if (r < -127.0f) r = -127.0f;
+                q[m * k_cols + k] = (int8_t)r;
+                sum += (int32_t)r;
+            }
+        }
+        if (rowsum)
+            rowsum[m] = sum;
+    }
+}
+
+/* ---- integer contraction and rescale [ASI, custom-software paragraph: the
+ *      trits are multiplied with the 8-bit activations] ------------------- */
+
+/* acc[m][n] = sum_k t[n][k] * q[m][k], exact. */
+void orc_matmul_i32(const int8_t *q, int64_t m_rows, const int8_t *t, int64_t n_rows,
+                    int64_t k_cols, int32_t *acc)
+{
+    for (int64_t m = 0; m < m_rows; ++m) {
+        for (int64_t n = 0; n < n_rows; ++n) {
+            int64_t sum = 0;
+            for (int64_t k = 0; k < k_cols; ++k)
+                sum += (int64_t)t[n * k_cols + k] * (int64_t)q[m * k_cols + k];
+            acc[m * n_rows + n] = (int32_t)sum;
+        }
+    }
+}
+
+/* y[m][n] = acc[m][n] * gamma / s[m]: undoes both quantiser scalings. */
+void orc_rescale(const int32_t *acc, const float *scale, float gamma, int64_t m_rows,
+                 int64_t n_rows, double *y)
+{
+    for (int64_t m = 0; m < m_rows; ++m)
+        for (int64_t n = 0; n < n_rows; ++n)
+            y[m * n_rows + n] =
+                (double)acc[m * n_rows + n] * (double)gamma / (double)scale[m];
+}
+
+/* ---- 2B-class decoder block glue, used only by the layer-stack workload ----
+ * [ASI, stabiliser paragraph: a sub-layer norm and squared ReLU; CS "What is
+ * BitNet b1.58?", third bullet: RMSNorm, no bias].  Double precision. */
+
+/* out = x / sqrt(mean(x^2) + eps), unit gain, one row of length K at a time. */
+void orc_rmsnorm(const double *x, int64_t m_rows, int64_t k_cols, double eps, double *out)
+{
+    for (int64_t m = 0; m < m_rows; ++m) {
+        double ss = 0.0;
+        for (int64_t k = 0; k < k_cols; ++k)
+            ss += x[m * k_cols + k] * x[m * k_cols + k];
+        double inv = 1.0 / sqrt(ss / (double)k_cols + eps);
+        for (int64_t k = 0; k < k_cols; ++k)
+            out[m * k_cols + k] = x[m * k_cols + k] * inv;
+    }
+}
+
+/* out = relu(gate)^2 * up, elementwise. */
+void orc_relu2_mul(const double *gate, const double *up, int64_t count, double *out)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        double g = gate[i] > 0.0 ? gate[i] : 0.0;
+        out[i] = g * g * up[i];
+    }
+}

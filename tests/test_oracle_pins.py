@@ -1,0 +1,413 @@
+"""Pins of the CPU oracle against what the sources and mathematics fix.
+
+Nothing here compares the oracle with itself: every expectation comes from a
+closed form, a hand-derived fixture (tests/golden), a library routine
+(numpy, scipy, Python integers), brute force on tiny inputs, or an invariant
+of the method.  The cases are chosen so that a plausible slip in the oracle
+(a dropped row or column, a wrong sign, a swapped operand, truncation instead
+of rounding, a tie rule, a per-tensor vs per-token mix-up) fails one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import scipy.special
+
+import oracle
+from ternary_weight_linear_absmax_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_cases(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            rows.append([part.split() for part in line.split("|")])
+    return rows
+
+
+# ---- bfloat16 widening ----------------------------------------------------------
+
+def _bf16_by_definition(bits: int) -> float:
+    """Value of a bfloat16 from the format: 1 sign, 8 exponent, 7 fraction bits."""
+    sign = -1.0 if bits & 0x8000 else 1.0
+    exp = (bits >> 7) & 0xFF
+    frac = bits & 0x7F
+    if exp == 0:
+        return sign * math.ldexp(frac / 128.0, -126)
+    return sign * math.ldexp(1.0 + frac / 128.0, exp - 127)
+
+
+def test_bf16_widening_matches_format_definition():
+    rng = np.random.default_rng(7)
+    bits = np.concatenate([
+        np.array([0x0000, 0x8000, 0x3F80, 0xBF80, 0x4049, 0x0080, 0x0001, 0x7F7F, 0x3E80, 0xC2F7],
+                 dtype=np.uint16),
+        rng.integers(0, 0x7F80, size=200, dtype=np.uint16),          # finite positives
+        rng.integers(0x8000, 0xFF80, size=200, dtype=np.uint16),     # finite negatives
+    ])
+    got = oracle.bf16_to_f32(bits)
+    want = np.array([_bf16_by_definition(int(b)) for b in bits])
+    np.testing.assert_array_equal(got.astype(np.float64), want)
+
+
+# ---- gamma ------------------------------------------------------------------------
+
+def test_gamma_matches_numpy_mean_within_one_ulp():
+    w, _ = inputs.tiny()
+    g = oracle.absmean_gamma(w)
+    ref = np.float32(np.mean(np.abs(w.astype(np.float64))))
+    assert abs(float(g) - float(ref)) <= float(np.spacing(ref))
+
+
+def test_gamma_bf16_input_equals_widened_f32_input():
+    w = inputs.normal_bf16(np.random.default_rng(3), (64, 320), 0.02)
+    assert oracle.absmean_gamma(w) == oracle.absmean_gamma(inputs.bf16_bits_to_f32(w))
+
+
+def test_gamma_constant_magnitude_is_exact():
+    rng = np.random.default_rng(11)
+    c = np.float32(0.0375)
+    w = np.where(rng.random((37, 129)) < 0.5, -c, c).astype(np.float32)
+    assert oracle.absmean_gamma(w) == c
+
+
+def test_gamma_zero_matrix():
+    assert oracle.absmean_gamma(np.zeros((5, 7), np.float32)) == 0.0
+
+
+@pytest.mark.parametrize("pos", [(0, 0), (0, 6), (4, 0), (4, 6), (2, 3)])
+def test_gamma_single_entry_every_position(pos):
+    # A loop that skips the first or last row or column fails one of these.
+    w = np.zeros((5, 7), np.float32)
+    w[pos] = -3.0
+    assert oracle.absmean_gamma(w) == np.float32(3.0 / 35.0)
+
+
+def test_gamma_power_of_two_scaling_is_exact():
+    w, _ = inputs.tiny()
+    assert oracle.absmean_gamma(w * np.float32(8.0)) == oracle.absmean_gamma(w) * np.float32(8.0)
+
+
+def test_gamma_gaussian_expectation():
+    # E|w| = sigma * sqrt(2/pi); sd of the sample mean = sigma*sqrt(1-2/pi)/sqrt(n)
+    rng = np.random.default_rng(5)
+    sigma = 0.02
+    w = rng.standard_normal((1024, 1024), dtype=np.float32) * np.float32(sigma)
+    g = float(oracle.absmean_gamma(w))
+    mean = sigma * math.sqrt(2 / math.pi)
+    sd = sigma * math.sqrt(1 - 2 / math.pi) / math.sqrt(w.size)
+    assert abs(g - mean) < 5 * sd
+
+
+# ---- trits ------------------------------------------------------------------------
+
+def test_trit_golden_cases():
+    for wv, gv, tv in _read_cases("absmean_cases.txt"):
+        w = np.array([float(v) for v in wv], np.float32)[None, :]
+        t, g = oracle.quantize_weights(w)
+        assert g == np.float32(float(gv[0])), (wv, g)
+        assert t[0].tolist() == [int(v) for v in tv], (wv, t)
+
+
+def test_trits_match_numpy_round_half_even_in_fp64():
+    for seed in range(3):
+        w = inputs.random_case(100 + seed, 1, 96, 200, bf16=False)[0]
+        t, g = oracle.quantize_weights(w)
+        ref = np.clip(np.round(w.astype(np.float64) / np.float64(g)), -1, 1).astype(np.int8)
+        np.testing.assert_array_equal(t, ref)
+
+
+def test_trits_exact_threshold_ties():
+    # w = gamma/2 exactly must give 0; one ulp above must give sign(w)
+    g = np.float32(0.02)
+    half = np.float32(0.01)
+    above = np.nextafter(half, np.float32(1))
+    w = np.array([[half, -half, above, -above, 0.0, 3 * g]], np.float32)
+    t = oracle.absmean_trits(w, g)
+    assert t[0].tolist() == [0, 0, 1, -1, 0, 1]
+
+
+def test_trits_values_sign_symmetry_and_scale_invariance():
+    w, _ = inputs.tiny()
+    t, g = oracle.quantize_weights(w)
+    assert set(np.unique(t).tolist()) <= {-1, 0, 1}
+    tn, _ = oracle.quantize_weights(-w)
+    np.testing.assert_array_equal(tn, -t)
+    t4, _ = oracle.quantize_weights(w * np.float32(4.0))
+    np.testing.assert_array_equal(t4, t)
+
+
+def test_trit_zero_fraction_gaussian():
+    # P(|z| <= sqrt(2/pi)/2) = erf(sqrt(2/pi) / (2 sqrt 2)) = 0.31006
+    rng = np.random.default_rng(9)
+    w = rng.standard_normal((512, 512), dtype=np.float32) * np.float32(0.02)
+    t, _ = oracle.quantize_weights(w)
+    p0 = scipy.special.erf(math.sqrt(2 / math.pi) / (2 * math.sqrt(2)))
+    assert abs(p0 - 0.31006) < 1e-5
+    frac = float(np.mean(t == 0))
+    sd = math.sqrt(p0 * (1 - p0) / t.size)
+    assert abs(frac - p0) < 5 * sd
+    assert abs(float(np.mean(t == 1)) - (1 - p0) / 2) < 5 * sd
+
+
+def test_trits_gamma_zero_underflow_reading():
+    # gamma == 0 with a non-zero entry: w/0 is infinite and clips to sign(w)
+    w = np.array([[0.0, 1e-45, -1e-45, 0.0]], np.float32)
+    t = oracle.absmean_trits(w, np.float32(0.0))
+    assert t[0].tolist() == [0, 1, -1, 0]
+
+
+# ---- 2-bit packing -------------------------------------------------------------------
+
+def test_pack2_all_81_byte_states_distinct_and_round_trip():
+    # Byte j of word g holds trits k = 16g + 4i + j (i = 0..3).
+    combos = np.array(np.meshgrid(*[[-1, 0, 1]] * 4, indexing="ij")).reshape(4, -1).T
+    seen = set()
+    for c in combos:
+        t = np.zeros((1, 64), np.int8)
+        for i in range(4):
+            t[0, 4 * i + 1] = c[i]          # word 0, byte 1
+        p = oracle.pack2(t)
+        byte = int(p[0, 1])
+        assert all(((byte >> (2 * i)) & 3) != 3 for i in range(4))
+        seen.add(byte)
+        np.testing.assert_array_equal(oracle.unpack2(p, 64), t)
+    assert len(seen) == 81
+
+
+def test_pack2_word_layout_matches_header_contract():
+    # Reading a word as little-endian uint32, (word >> 2i) & 0x03030303 holds
+    # codes t+1 of k = 16g+4i .. 16g+4i+3 in its four bytes.
+    rng = np.random.default_rng(2)
+    t = rng.integers(-1, 2, size=(3, 128)).astype(np.int8)
+    words = oracle.pack2(t).view("<u4")
+    for n in range(3):
+        for g in range(8):
+            for i in range(4):
+                v = (int(words[n, g]) >> (2 * i)) & 0x03030303
+                got = [(v >> (8 * j)) & 0xFF for j in range(4)]
+                want = (t[n, 16 * g + 4 * i: 16 * g + 4 * i + 4] + 1).tolist()
+                assert got == want
+
+
+@pytest.mark.parametrize("k", [1, 3, 15, 16, 17, 63, 64, 65, 100, 256, 2560])
+def test_pack2_round_trip_and_padding(k):
+    rng = np.random.default_rng(k)
+    t = rng.integers(-1, 2, size=(5, k)).astype(np.int8)
+    p = oracle.pack2(t)
+    assert p.shape == (5, 16 * ((k + 63) // 64))
+    np.testing.assert_array_equal(oracle.unpack2(p, k), t)
+    # every position past K decodes as trit 0: unpacking at the padded width
+    kp = p.shape[1] * 4
+    tp = oracle.unpack2(p, kp)
+    assert np.all(tp[:, k:] == 0)
+    np.testing.assert_array_equal(tp[:, :k], t)
+
+
+def test_pack2_sizes():
+    assert oracle.pack2_pitch(8192) * 28672 == 58_720_256       # 70B-class matrix, ~58 MB
+    assert oracle.pack2_pitch(28672) * 8192 == 58_720_256
+    for k in (256, 2560, 3200, 6912, 8640):
+        assert oracle.pack2_pitch(k) * 4 == k                     # 0.25 byte per weight
+    zero = oracle.pack2(np.zeros((2, 64), np.int8))
+    assert np.all(zero == 0x55)                                  # code 1 in every field
+
+
+# ---- base-3 packing ------------------------------------------------------------------
+
+def test_pack3_golden_bytes():
+    for tv, bv in _read_cases("base3_bytes.txt"):
+        t = np.array([[int(v) for v in tv]], np.int8)
+        p = oracle.pack3(t)
+        assert int(p[0, 0]) == int(bv[0])
+        # the same byte from Python's base-3 integer parser (most significant first)
+        digits = "".join(str(int(v) + 1) for v in reversed(tv))
+        assert int(digits, 3) == int(bv[0])
+
+
+def test_pack3_all_243_states_distinct_round_trip():
+    combos = np.array(np.meshgrid(*[[-1, 0, 1]] * 5, indexing="ij")).reshape(5, -1).T
+    t = combos.astype(np.int8)                     # 243 rows of 5 trits
+    p = oracle.pack3(t)
+    assert p.shape == (243, 16)
+    assert sorted(p[:, 0].tolist()) == list(range(243))
+    assert np.all(p[:, 1:] == 121)
+    np.testing.assert_array_equal(oracle.unpack3(p, 5), t)
+
+
+def test_pack3_density_bounds():
+    # 3^5 = 243 <= 256 < 729 = 3^6: five trits is the most a byte can hold
+    assert 3 ** 5 <= 256 < 3 ** 6
+    assert 8 / 5 >= math.log2(3) > 1.58
+    assert abs(math.log(3) / math.log(2) - 1.5849625) < 1e-7
+
+
+@pytest.mark.parametrize("k", [1, 4, 5, 6, 79, 80, 81, 256, 8192])
+def test_pack3_round_trip_equals_pack2(k):
+    rng = np.random.default_rng(1000 + k)
+    t = rng.integers(-1, 2, size=(4, k)).astype(np.int8)
+    p3 = oracle.pack3(t)
+    assert p3.shape[1] % 16 == 0 and p3.shape[1] >= (k + 4) // 5
+    np.testing.assert_array_equal(oracle.unpack3(p3, k), t)
+    np.testing.assert_array_equal(oracle.unpack3(p3, k), oracle.unpack2(oracle.pack2(t), k))
+
+
+# ---- activation quantiser ---------------------------------------------------------------
+
+def test_act_golden_cases():
+    for xv, sv, qv in _read_cases("absmax_cases.txt"):
+        x = np.array([[float(v) for v in xv]], np.float32)
+        q, s, r = oracle.quantize_act(x)
+        assert s[0] == np.float32(float(sv[0])), (xv, s)
+        assert q[0].tolist() == [int(v) for v in qv], (xv, q)
+        assert r[0] == sum(int(v) for v in qv)
+
+
+def test_act_invariants_on_decode_inputs():
+    _, _, x = inputs.decode(0, m=3)
+    xf = inputs.bf16_bits_to_f32(x).astype(np.float64)
+    q, s, r = oracle.quantize_act(x)
+    for m in range(3):
+        amax = np.max(np.abs(xf[m]))
+        am = int(np.argmax(np.abs(xf[m])))
+        assert abs(int(q[m, am])) == 127 and np.sign(q[m, am]) == np.sign(xf[m, am])
+        assert np.max(np.abs(q[m])) == 127
+        # half a quantisation step bounds the error (catches truncation)
+        err = np.abs(q[m] / np.float64(s[m]) - xf[m])
+        assert np.all(err <= 0.5 / np.float64(s[m]) * (1 + 2.0 ** -20))
+        assert abs(np.float64(s[m]) - 127.0 / amax) <= 127.0 / amax * 2.0 ** -23
+        assert np.all((q[m] == 0) | (np.sign(q[m]) == np.sign(xf[m])))
+    np.testing.assert_array_equal(r, q.astype(np.int64).sum(axis=1))
+
+
+def test_act_matches_numpy_float32_rint():
+    _, x = inputs.tiny()
+    q, s, _ = oracle.quantize_act(x)
+    amax = np.max(np.abs(x), axis=1)
+    s_ref = (np.float32(127.0) / amax).astype(np.float32)
+    q_ref = np.clip(np.rint(x * s_ref[:, None]), -127, 127).astype(np.int8)
+    np.testing.assert_array_equal(s, s_ref)
+    np.testing.assert_array_equal(q, q_ref)
+
+
+def test_act_is_per_token():
+    # scaling one token by 2^j changes only that token's scale
+    _, x = inputs.tiny()
+    x2 = x.copy()
+    x2[1] *= np.float32(64.0)
+    x2[3] *= np.float32(0.25)
+    q, s, _ = oracle.quantize_act(x)
+    q2, s2, _ = oracle.quantize_act(x2)
+    np.testing.assert_array_equal(q2, q)
+    assert s2[0] == s[0] and s2[2] == s[2]
+    assert s2[1] == s[1] / np.float32(64.0) and s2[3] == s[3] * np.float32(4.0)
+
+
+def test_act_zero_token_and_bf16_equivalence():
+    x = inputs.f32_to_bf16_bits(np.array([[0, 0, 0, 0], [1, -2, 3, 0.5]], np.float32))
+    q, s, r = oracle.quantize_act(x)
+    assert q[0].tolist() == [0, 0, 0, 0] and s[0] == 1.0 and r[0] == 0
+    qf, sf, rf = oracle.quantize_act(inputs.bf16_bits_to_f32(x))
+    np.testing.assert_array_equal(q, qf)
+    np.testing.assert_array_equal(s, sf)
+
+
+# ---- integer contraction -----------------------------------------------------------------
+
+def test_matmul_matches_numpy_int64():
+    rng = np.random.default_rng(21)
+    q = rng.integers(-127, 128, size=(5, 300)).astype(np.int8)
+    t = rng.integers(-1, 2, size=(70, 300)).astype(np.int8)
+    acc = oracle.matmul_i32(q, t)
+    np.testing.assert_array_equal(acc, q.astype(np.int64) @ t.astype(np.int64).T)
+
+
+def test_matmul_identity_permutation_and_ones():
+    rng = np.random.default_rng(22)
+    q = rng.integers(-127, 128, size=(3, 64)).astype(np.int8)
+    eye = np.eye(64, dtype=np.float32) * np.float32(0.7)       # W = c*I -> t = I
+    t, g = oracle.quantize_weights(eye)
+    np.testing.assert_array_equal(t, np.eye(64, dtype=np.int8))
+    np.testing.assert_array_equal(oracle.matmul_i32(q, t), q.astype(np.int32))
+    perm = rng.permutation(64)
+    tp = np.eye(64, dtype=np.int8)[perm]                        # row n picks column perm[n]
+    np.testing.assert_array_equal(oracle.matmul_i32(q, tp), q[:, perm].astype(np.int32))
+    ones = np.ones((4, 64), np.int8)
+    acc = oracle.matmul_i32(q, ones)
+    assert np.all(acc == q.astype(np.int32).sum(axis=1, keepdims=True))
+
+
+@pytest.mark.parametrize("n", [256, 512])
+def test_hadamard_weights_give_walsh_hadamard_transform(n):
+    h = scipy.linalg.hadamard(n).astype(np.float32)             # +-1 entries: gamma = 1, t = H
+    t, g = oracle.quantize_weights(h)
+    assert g == 1.0
+    np.testing.assert_array_equal(t, h.astype(np.int8))
+    rng = np.random.default_rng(n)
+    q = rng.integers(-127, 128, size=(4, n)).astype(np.int8)
+    acc = oracle.matmul_i32(q, t)
+    # Walsh-Hadamard transform by the fast butterfly (natural / Sylvester order)
+    v = q.astype(np.int64).copy()
+    hlen = 1
+    while hlen < n:
+        v = v.reshape(4, -1, 2 * hlen)
+        a, b = v[:, :, :hlen].copy(), v[:, :, hlen:].copy()
+        v[:, :, :hlen], v[:, :, hlen:] = a + b, a - b
+        v = v.reshape(4, n)
+        hlen *= 2
+    np.testing.assert_array_equal(acc, v)
+
+
+# ---- rescale and whole forward --------------------------------------------------------------
+
+def test_forward_equals_float_brute_force_of_dequantised_operands():
+    w, x = inputs.tiny()
+    t, g = oracle.quantize_weights(w)
+    q, s, r, acc, y = oracle.forward(x, t, g)
+    xd = q.astype(np.float64) / s.astype(np.float64)[:, None]
+    wd = np.float64(g) * t.astype(np.float64)
+    ref = np.zeros((x.shape[0], w.shape[0]))
+    for m in range(x.shape[0]):               # explicit loops: brute force
+        for n in range(w.shape[0]):
+            ref[m, n] = float(np.dot(xd[m], wd[n]))
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=0)
+    assert np.all((y == 0) == (acc == 0))
+
+
+def test_forward_tracks_unquantised_matmul():
+    # information about quantisation error, with a loose floor: the method's
+    # error, not a bug, separates y from x @ W^T
+    w, x = inputs.tiny()
+    t, g = oracle.quantize_weights(w)
+    y = oracle.forward(x, t, g)[4]
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    cos = np.sum(y * ref) / np.sqrt(np.sum(y * y) * np.sum(ref * ref))
+    assert cos > 0.8
+
+
+def test_packed_forward_chain_matches_unpacked():
+    w, x = inputs.random_case(77, 3, 40, 200)
+    t, g = oracle.quantize_weights(w)
+    for pack, unpack in ((oracle.pack2, oracle.unpack2), (oracle.pack3, oracle.unpack3)):
+        t2 = unpack(pack(t), 200)
+        np.testing.assert_array_equal(oracle.forward(x, t2, g)[3], oracle.forward(x, t, g)[3])
+
+
+# ---- decoder glue -------------------------------------------------------------------------
+
+def test_rmsnorm_and_relu2():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((3, 2560)) * 3.0
+    y = oracle.rmsnorm(x, eps=0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=1)), 1.0, rtol=1e-12)
+    np.testing.assert_allclose(y / x, (y / x)[:, :1] * np.ones_like(x), rtol=1e-12)
+    g = np.array([-2.0, -0.0, 0.5, 3.0])
+    u = np.array([5.0, 7.0, 2.0, -1.0])
+    np.testing.assert_array_equal(oracle.relu2_mul(g, u), np.array([0.0, 0.0, 0.5, -9.0]))
