@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Throughput of the BitLinear hot path on one MI355X.
+
+Headline workload (``value``): decode at M = 1 over the four 2B-class BitLinear
+shapes (fused QKV 2560->3840, O 2560->2560, fused up/gate 2560->13824, down
+6912->2560), for 30 layers whose packed weights sit at 30 distinct HBM
+addresses (521 MB per step, twice the 256 MB Infinity Cache, so every step
+streams its weights from HBM).  One step = for every layer and matrix:
+per-token absmax quantisation of that matrix's input, then the ternary
+product with rescale.  Weights are quantised and packed once, before timing
+(the method packs them offline).  Metric: packed-weight bytes per second.
+
+Also measured on the same line (``extra``): the 70B-class layer at M = 1
+(2-bit and base-3 layouts) and M = 16 / 128, and the 3B-class prefill GEMM at
+M = 512 in TOPS; plus the roofline of the dominant kernel and the CPU oracle
+timed on a bounded sample on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+I8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, TOP/s
+METRIC = "BitLinear weight GB/s (% HBM peak) at M=1; TOPS (% int8 MFMA peak) at M=512"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=30)
+    ap.add_argument("--no-extra", action="store_true", help="skip the 70B / prefill lines")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def to_dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def time_loop(fn, iters, warmup):
+    """Average ms per call of fn() over `iters` calls, HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(iters):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def decode_workload(layers):
+    """Quantise the four decode matrices once; replicate the packed weights to
+    `layers` distinct buffers; inputs resident in HBM."""
+    import torch
+    from ternary_weight_linear_absmax_amd import bitlinear as bl
+    from ternary_weight_linear_absmax_amd import inputs
+    mats = []
+    for i in range(len(inputs.DECODE_SHAPES)):
+        name, w, x = inputs.decode(i, m=1)
+        n, k = w.shape
+        packed, gamma = bl.quantize_weights(to_dev(w))
+        xd = to_dev(x)
+        copies = [packed] + [packed.clone() for _ in range(layers - 1)]
+        xq, scale, rowsum = bl.quantize_act(xd)
+        y = torch.empty((1, n), dtype=torch.float32, device="cuda")
+        mats.append(dict(name=name, n=n, k=k, x=xd, copies=copies, gamma=gamma, xq=xq,
+                         scale=scale, rowsum=rowsum, y=y, bytes=packed.numel()))
+    torch.cuda.synchronize()
+    return mats
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1 "
+                          "(multi-GPU sharding is a design note, not built)"}))
+        sys.exit(2)
+
+    import torch
+    from ternary_weight_linear_absmax_amd import bitlinear as bl
+    from ternary_weight_linear_absmax_amd import inputs
+
+    bl.load()
+    dev_name = torch.cuda.get_device_name(0)
+    log(f"device {dev_name}")
+
+    # ---------------- headline: decode M=1, 30 layers -----------------------
+    mats = decode_workload(args.layers)
+    step_bytes = sum(m["bytes"] for m in mats) * args.layers
+    log(f"decode workload ready: {step_bytes / 1e6:.1f} MB packed per step")
+
+    lib = bl.load()
+    stream_ptr = torch.cuda.current_stream().cuda_stream
+
+    def quant_act_into(m):
+        # writes into the matrix's resident xq / scale / rowsum buffers
+        st = lib.bitlinear_quantize_act(ctypes.c_void_p(m["x"].data_ptr()), bl.BL_BF16, 1, m["k"],
+                                        ctypes.c_void_p(m["xq"].data_ptr()),
+                                        ctypes.c_void_p(m["scale"].data_ptr()),
+                                        ctypes.c_void_p(m["rowsum"].data_ptr()),
+                                        ctypes.c_void_p(stream_ptr))
+        assert st == 0, st
+
+    def step():
+        for layer in range(args.layers):
+            for m in mats:
+                quant_act_into(m)
+                bl.forward(m["xq"], m["scale"], m["rowsum"], m["copies"][layer], m["gamma"],
+                           m["n"], m["k"], y=m["y"])
+
+    ms_step = time_loop(step, args.steps, args.warmup)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"decode step {ms_step * 1e3:.1f} us -> {value:.1f} GB/s")
+
+    # dominant kernel: the M=1 GEMV, timed alone over the same rotation
+    def gemv_only():
+        for layer in range(args.layers):
+            for m in mats:
+                bl.forward(m["xq"], m["scale"], m["rowsum"], m["copies"][layer], m["gamma"],
+                           m["n"], m["k"], y=m["y"])
+    launches = args.layers * len(mats)
+    ms_gemv = time_loop(gemv_only, args.steps, args.warmup)
+    us_per_launch = ms_gemv * 1e3 / launches
+    bytes_per_launch = step_bytes / launches
+    achieved = bytes_per_launch / (us_per_launch * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "gemv2_kernel (decode, M=1)",
+                "avg_launch_us": round(us_per_launch, 3),
+                "algorithmic_bytes_per_launch": int(bytes_per_launch)}
+    log(f"decode GEMV alone: {us_per_launch:.2f} us/launch, {achieved:.1f} GB/s")
+
+    # ---------------- extra: 70B-class layer and prefill ------------------------
+    extra = {}
+    if not args.no_extra:
+        extra = measure_extra(args)
+
+    # ---------------- CPU oracle baseline ----------------------------------------
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode M=1, 2B-class BitLinear shapes (QKV 2560x3840, O 2560x2560, "
+                        "up/gate 2560x13824, down 6912x2560), %d layers of distinct packed "
+                        "weights; per matrix: absmax int8 quantisation + ternary GEMV + rescale"
+                        % args.layers,
+            "M": 1,
+            "layers": args.layers,
+            "packed_bytes_per_step": step_bytes,
+            "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+            "device": dev_name,
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def measure_extra(args):
+    import torch
+    from ternary_weight_linear_absmax_amd import bitlinear as bl
+    from ternary_weight_linear_absmax_amd import inputs
+    extra = {}
+    # 70B-class: rotate 10 copies (587 MB > Infinity Cache)
+    copies_n = 10
+    for si, (name, k, n) in enumerate(inputs.XL_SHAPES):
+        _, w, x = inputs.xl(si, m=128)
+        wd = to_dev(w)
+        p2, g2 = bl.quantize_weights(wd)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        p3, g3 = bl.quantize_weights(wd, bl.BL_PACK3)
+        torch.cuda.synchronize()
+        quant_ms = (time.perf_counter() - t0) * 1e3
+        del wd
+        c2 = [p2] + [p2.clone() for _ in range(copies_n - 1)]
+        c3 = [p3] + [p3.clone() for _ in range(copies_n - 1)]
+        xq, scale, rowsum = bl.quantize_act(to_dev(x))
+        for m in inputs.XL_MS:
+            y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            it = [0]
+
+            def fwd2():
+                bl.forward(xq[:m], scale[:m], rowsum[:m], c2[it[0] % copies_n], g2, n, k, y=y)
+                it[0] += 1
+            ms = time_loop(fwd2, 100, 10)
+            gbs = p2.numel() / (ms * 1e-3) / 1e9
+            tops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+            extra[f"xl_{name}_M{m}_pack2"] = {
+                "K": k, "N": n, "M": m, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "TOPS": round(tops, 2),
+                "i8_frac": round(tops / I8_PEAK_TOPS, 4),
+                "path": bl.forward_path(m, n, k)}
+            log(f"xl {name} M={m} pack2: {ms * 1e3:.1f} us {gbs:.0f} GB/s {tops:.1f} TOPS")
+            if m == 1:
+                def fwd3():
+                    bl.forward(xq[:1], scale[:1], rowsum[:1], c3[it[0] % copies_n], g3, n, k,
+                               layout=bl.BL_PACK3, y=y)
+                    it[0] += 1
+                ms3 = time_loop(fwd3, 50, 5)
+                gbs3 = p3.numel() / (ms3 * 1e-3) / 1e9
+                extra[f"xl_{name}_M1_pack3"] = {
+                    "K": k, "N": n, "M": 1, "us": round(ms3 * 1e3, 2), "GB/s": round(gbs3, 1),
+                    "hbm_frac": round(gbs3 / HBM_PEAK_GBS, 4),
+                    "trits_per_s": round(n * k / (ms3 * 1e-3), 1)}
+                log(f"xl {name} M=1 pack3: {ms3 * 1e3:.1f} us {gbs3:.0f} GB/s")
+        extra[f"xl_{name}_quantize_weights_pack3_ms"] = round(quant_ms, 2)
+        del c2, c3
+        torch.cuda.empty_cache()
+    # prefill M=512
+    for si, (name, k, n) in enumerate(inputs.PREFILL_SHAPES):
+        _, w, x = inputs.prefill(si)
+        packed, gamma = bl.quantize_weights(to_dev(w))
+        xd = to_dev(x)
+        xq, scale, rowsum = bl.quantize_act(xd)
+        m = x.shape[0]
+        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+
+        def fwd():
+            bl.forward(xq, scale, rowsum, packed, gamma, n, k, y=y)
+        ms = time_loop(fwd, 100, 10)
+        tops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+
+        def full():
+            bl.quantize_act(xd)
+            bl.forward(xq, scale, rowsum, packed, gamma, n, k, y=y)
+        ms_full = time_loop(full, 50, 5)
+        extra[f"prefill_{name}_M512"] = {
+            "K": k, "N": n, "M": m, "us": round(ms * 1e3, 2), "TOPS": round(tops, 2),
+            "i8_frac": round(tops / I8_PEAK_TOPS, 4),
+            "us_with_act_quant": round(ms_full * 1e3, 2),
+            "TOPS_with_act_quant": round(2.0 * m * n * k / (ms_full * 1e-3) / 1e12, 2)}
+        log(f"prefill {name}: {ms * 1e3:.1f} us {tops:.1f} TOPS")
+    return extra
+
+
+def cpu_baseline(seconds):
+    """The oracle, untuned, on this host: the decode workload's per-matrix chain
+    (absmax quantisation, exact int32 product, rescale) at M = 1, repeated over
+    the four shapes until `seconds` have passed."""
+    import oracle
+    from ternary_weight_linear_absmax_amd import inputs
+    prepared = []
+    for i in range(len(inputs.DECODE_SHAPES)):
+        _, w, x = inputs.decode(i, m=1)
+        t, g = oracle.quantize_weights(w)
+        prepared.append((x, t, g, oracle.pack2_pitch(w.shape[1]) * w.shape[0]))
+    done_bytes, passes = 0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for x, t, g, nbytes in prepared:
+            q, s, r = oracle.quantize_act(x)
+            acc = oracle.matmul_i32(q, t)
+            oracle.rescale(acc, s, g)
+            done_bytes += nbytes
+        passes += 1
+    el = time.perf_counter() - t0
+    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{passes} passes over the 4 decode matrices (one layer, M=1) in "
+                      f"{el:.1f} s; single-threaded scalar C"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+/*
+ * bitlinear.h - C ABI of the BitNet b1.58 BitLinear layer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The layer replaces a linear layer y = x W^T (no bias) with
+ *   - weights quantised by their absolute mean gamma = mean|W| to ternary
+ *     values t = clip(round(W / gamma), -1, 1);
+ *   - activations quantised per token to 8 bits by their absolute maximum,
+ *     q = round(x * s) with s = 127 / max|x|;
+ *   - an exact integer product acc = q t^T, rescaled to y = acc * gamma / s.
+ * Sources: "1-bit LLM era: Microsoft introduces BitNet b1.58" (cheatsheet.md),
+ * section "What is BitNet b1.58?" (absmean weights, per-token activation
+ * scaling, BitLinear in place of nn.Linear, no bias); the asi.tokyo article on
+ * BitNet b1.58 2B4T (8-bit activations; four trits packed per byte, unpacked
+ * next to the arithmetic units and multiplied with the 8-bit values); the
+ * news.hada.io topic 20406 comment on ternary packing (five trits per byte).
+ *
+ * Conventions shared by every call
+ *   - Shapes follow nn.Linear: x is [M, K] (M tokens), W is [N, K] (N output
+ *     features), y is [M, N]; all row-major and dense.
+ *   - Pointers marked "device" are HIP device pointers (or host-coherent memory
+ *     a kernel may read); the caller owns every buffer.  The library never
+ *     allocates, frees or keeps a pointer after the call returns.
+ *   - Calls are asynchronous on `stream` (0 = the null stream).  Arguments are
+ *     checked on the host before anything is launched; a failed check returns
+ *     a negative bl_status and launches nothing.  A failed launch returns
+ *     BL_ERR_HIP.  No host synchronisation happens inside any call.
+ *   - Device pointers must be 16-byte aligned.  Sizes are element counts.
+ *   - Inputs must be finite; NaN or infinite inputs give unspecified results.
+ *   - M == 0 or N == 0 is an empty product and returns BL_OK without a
+ *     launch; K must be in [1, BITLINEAR_MAX_K].
+ *   - Every call is stateless and re-entrant; calls on different streams may
+ *     overlap if their buffers do not.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BL_OK = 0,
+    BL_ERR_NULL = -1,        /* a required pointer is NULL */
+    BL_ERR_SHAPE = -2,       /* a size is negative, zero where it may not be, or too large */
+    BL_ERR_ALIGN = -3,       /* a device pointer is not 16-byte aligned */
+    BL_ERR_DTYPE = -4,       /* unknown bl_dtype */
+    BL_ERR_LAYOUT = -5,      /* unknown bl_layout */
+    BL_ERR_WORKSPACE = -6,   /* workspace smaller than the size query returned */
+    BL_ERR_HIP = -7,         /* a HIP launch or runtime call failed */
+    BL_ERR_PATH = -8         /* the requested kernel path cannot run this shape */
+} bl_status;
+
+typedef enum {
+    BL_F32 = 0,              /* IEEE binary32 */
+    BL_BF16 = 1              /* bfloat16, stored as 16-bit words */
+} bl_dtype;
+
+typedef enum {
+    /* Four trits per byte.  Row n of an [N, K] matrix occupies
+     * bitlinear_packed_row_bytes(K, BL_PACK2) = 16 * ceil(K / 64) bytes.  Read
+     * as little-endian 32-bit words, word g of a row holds k = 16g .. 16g+15:
+     * trit k = 16g + 4i + j is stored in byte j of the word at bits 2i..2i+1
+     * as the code t + 1 (0 for -1, 1 for 0, 2 for +1; code 3 never occurs).
+     * So (word >> 2i) & 0x03030303 yields the codes of four consecutive k in
+     * its four bytes.  Positions k >= K hold code 1 (trit 0). */
+    BL_PACK2 = 0,
+    /* Five trits per byte (base 3).  Byte j of a row is
+     * sum_{i=0..4} (t[5j+i] + 1) * 3^i, the lowest k being the least
+     * significant digit; positions k >= K are trit 0, and the row is padded to
+     * bitlinear_packed_row_bytes(K, BL_PACK3) = 16 * ceil(ceil(K / 5) / 16)
+     * bytes with the byte 121 (five zero trits). */
+    BL_PACK3 = 1
+} bl_layout;
+
+typedef enum {
+    BL_PATH_AUTO = 0,        /* choose by M and layout (the default) */
+    BL_PATH_GEMV = 1,        /* vector dot-product kernel, M <= 8 per pass */
+    BL_PATH_MFMA = 2         /* int8 matrix-core kernel, any M (PACK2 only) */
+} bl_path;
+
+#define BITLINEAR_MAX_K (1 << 20)
+
+/* ---- host-only size queries (pure; no HIP calls) ---------------------------- */
+
+/* Bytes of one packed row; 0 for an unknown layout or K < 1. */
+int64_t bitlinear_packed_row_bytes(int64_t K, int layout);
+
+/* Bytes of a packed [N, K] matrix: N * bitlinear_packed_row_bytes(K, layout). */
+int64_t bitlinear_packed_bytes(int64_t N, int64_t K, int layout);
+
+/* Workspace that bitlinear_quantize_weights needs: 8 * N bytes (one double per
+ * row for the fixed-order absolute sums). */
+int64_t bitlinear_quantize_weights_workspace_bytes(int64_t N, int64_t K);
+
+/* Workspace that bitlinear_forward / bitlinear_matmul_i32 need for this shape
+ * (0 when none; then workspace may be NULL). */
+int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int layout);
+
+/* Kernel path that BL_PATH_AUTO selects for this shape (a bl_path value). */
+int bitlinear_forward_path(int64_t M, int64_t N, int64_t K, int layout);
+
+/* Static description of a status code. */
+const char *bitlinear_status_string(int status);
+
+/* ---- weights: absmean quantiser and packing (offline, once per matrix) ------
+ * [cheatsheet.md BitNet b1.58 summary, "What is BitNet b1.58?", weight bullet;
+ *  asi.tokyo 2B4T article, packing paragraph; news.hada.io 20406, packing
+ *  comment]
+ *
+ * W       device, [N, K] of `dtype`.
+ * packed  device, bitlinear_packed_bytes(N, K, layout) bytes, written.
+ * gamma   device, one float, written: gamma = mean|W|, summed in double
+ *         precision row by row (k ascending within a row, rows in order), then
+ *         divided by N*K and rounded once to float.
+ * t       t = sign(w) when 2|w| > gamma, else 0: round-half-to-even of the
+ *         exact quotient w / gamma, clipped to [-1, 1].
+ * workspace  device, >= bitlinear_quantize_weights_workspace_bytes(N, K).
+ * Requires N >= 1 (the mean of an empty matrix is undefined). */
+int bitlinear_quantize_weights(const void *W, int dtype, int64_t N, int64_t K, int layout,
+                               uint8_t *packed, float *gamma, void *workspace,
+                               int64_t workspace_bytes, hipStream_t stream);
+
+/* ---- activations: per-token absmax to int8 -----------------------------------
+ * [cheatsheet.md BitNet b1.58 summary, "What is BitNet b1.58?", activation
+ *  bullet; asi.tokyo 2B4T article, 8-bit messages; lumen-it.ai BitNet, absmax]
+ *
+ * x       device, [M, K] of `dtype`.
+ * xq      device, [M, K] int8, written: clamp(rint(x * s), -127, 127) with
+ *         float multiply and round-half-to-even.
+ * scale   device, [M] float, written: s = 127 / max_k |x[m, k]| (IEEE float
+ *         division), or 1 for an all-zero token (then xq is 0).
+ * rowsum  device, [M] int32, written if not NULL: sum_k xq[m, k].
+ */
+int bitlinear_quantize_act(const void *x, int dtype, int64_t M, int64_t K, int8_t *xq,
+                           float *scale, int32_t *rowsum, hipStream_t stream);
+
+/* ---- forward: exact integer product and rescale ---------------------------------
+ * [asi.tokyo 2B4T article, packing paragraph: unpack next to the arithmetic
+ *  units and multiply with the 8-bit activations; cheatsheet.md summary:
+ *  both quantiser scalings are undone at the output]
+ *
+ * xq, scale, rowsum  device, as written by bitlinear_quantize_act (rowsum is
+ *         required and must equal sum_k xq[m, k]).
+ * packed, gamma      device, as written by bitlinear_quantize_weights.
+ * y       device, [M, N] float, written:
+ *         y[m, n] = float(acc[m, n]) * (gamma / scale[m]),
+ *         acc[m, n] = sum_k t[n, k] * xq[m, k] computed exactly in int32.
+ * workspace  device, >= bitlinear_forward_workspace_bytes(M, N, K, layout).
+ */
+int bitlinear_forward(const int8_t *xq, const float *scale, const int32_t *rowsum, int64_t M,
+                      const uint8_t *packed, int layout, const float *gamma, int64_t N,
+                      int64_t K, float *y, void *workspace, int64_t workspace_bytes,
+                      hipStream_t stream);
+
+/* bitlinear_forward with an explicit kernel path (bl_path); BL_ERR_PATH if that
+ * path cannot run the shape or layout. */
+int bitlinear_forward_ex(const int8_t *xq, const float *scale, const int32_t *rowsum,
+                         int64_t M, const uint8_t *packed, int layout, const float *gamma,
+                         int64_t N, int64_t K, float *y, void *workspace,
+                         int64_t workspace_bytes, int path, hipStream_t stream);
+
+/* The same kernels without the rescale: acc[m, n] = sum_k t[n, k] * xq[m, k]
+ * as int32 (device, [M, N]).  path as in bitlinear_forward_ex. */
+int bitlinear_matmul_i32(const int8_t *xq, const int32_t *rowsum, int64_t M,
+                         const uint8_t *packed, int layout, int64_t N, int64_t K,
+                         int32_t *acc, void *workspace, int64_t workspace_bytes, int path,
+                         hipStream_t stream);
+
+/* Decode packed weights to int8 trits in {-1, 0, 1} (device, [N, K]). */
+int bitlinear_unpack_weights(const uint8_t *packed, int layout, int64_t N, int64_t K,
+                             int8_t *trits, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

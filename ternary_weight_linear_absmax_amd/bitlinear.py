@@ -1,0 +1,205 @@
+"""Python binding of libbitlinear (ctypes).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the computation runs in the library's HIP kernels.
+The names mirror the C ABI in include/bitlinear.h.  If the library has not
+been built this module raises at first use: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbitlinear.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "bitlinear.h")
+
+# enums of bitlinear.h
+BL_OK = 0
+BL_F32, BL_BF16 = 0, 1
+BL_PACK2, BL_PACK3 = 0, 1
+BL_PATH_AUTO, BL_PATH_GEMV, BL_PATH_MFMA = 0, 1, 2
+MAX_K = 1 << 20
+
+_lib = None
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+def header_functions() -> list[str]:
+    """Names of the functions that include/bitlinear.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(bitlinear_\w+)\s*\(", text)))
+
+
+def load():
+    """Load libbitlinear.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sig = {
+        "bitlinear_packed_row_bytes": (i64, [i64, i32]),
+        "bitlinear_packed_bytes": (i64, [i64, i64, i32]),
+        "bitlinear_quantize_weights_workspace_bytes": (i64, [i64, i64]),
+        "bitlinear_forward_workspace_bytes": (i64, [i64, i64, i64, i32]),
+        "bitlinear_forward_path": (i32, [i64, i64, i64, i32]),
+        "bitlinear_status_string": (ctypes.c_char_p, [i32]),
+        "bitlinear_quantize_weights": (i32, [p, i32, i64, i64, i32, p, p, p, i64, p]),
+        "bitlinear_quantize_act": (i32, [p, i32, i64, i64, p, p, p, p]),
+        "bitlinear_forward": (i32, [p, p, p, i64, p, i32, p, i64, i64, p, p, i64, p]),
+        "bitlinear_forward_ex": (i32, [p, p, p, i64, p, i32, p, i64, i64, p, p, i64, i32, p]),
+        "bitlinear_matmul_i32": (i32, [p, p, i64, p, i32, i64, i64, p, p, i64, i32, p]),
+        "bitlinear_unpack_weights": (i32, [p, i32, i64, i64, p, p]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != BL_OK:
+        raise BitLinearError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BL_BF16
+    if t.dtype == torch.float32:
+        return BL_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+
+
+# ---- host queries ----------------------------------------------------------------
+
+def status_string(status: int) -> str:
+    return load().bitlinear_status_string(status).decode()
+
+
+def packed_row_bytes(k: int, layout: int = BL_PACK2) -> int:
+    return int(load().bitlinear_packed_row_bytes(k, layout))
+
+
+def packed_bytes(n: int, k: int, layout: int = BL_PACK2) -> int:
+    return int(load().bitlinear_packed_bytes(n, k, layout))
+
+
+def quantize_weights_workspace_bytes(n: int, k: int) -> int:
+    return int(load().bitlinear_quantize_weights_workspace_bytes(n, k))
+
+
+def forward_workspace_bytes(m: int, n: int, k: int, layout: int = BL_PACK2) -> int:
+    return int(load().bitlinear_forward_workspace_bytes(m, n, k, layout))
+
+
+def forward_path(m: int, n: int, k: int, layout: int = BL_PACK2) -> int:
+    return int(load().bitlinear_forward_path(m, n, k, layout))
+
+
+# ---- device calls -------------------------------------------------------------------
+
+def quantize_weights(w: torch.Tensor, layout: int = BL_PACK2, stream=None):
+    """w [N, K] (float32/bfloat16, on the GPU) -> (packed uint8 [N, row_bytes], gamma float32 [1])."""
+    lib = load()
+    assert w.dim() == 2 and w.is_contiguous()
+    n, k = w.shape
+    packed = torch.empty((n, packed_row_bytes(k, layout)), dtype=torch.uint8, device=w.device)
+    gamma = torch.empty((1,), dtype=torch.float32, device=w.device)
+    ws_bytes = quantize_weights_workspace_bytes(n, k)
+    ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=w.device)
+    _check(lib.bitlinear_quantize_weights(_ptr(w), _dtype_code(w), n, k, layout, _ptr(packed),
+                                          _ptr(gamma), _ptr(ws), ws.numel(), _stream(stream)),
+           "bitlinear_quantize_weights")
+    return packed, gamma
+
+
+def quantize_act(x: torch.Tensor, stream=None):
+    """x [M, K] -> (xq int8 [M, K], scale float32 [M], rowsum int32 [M])."""
+    lib = load()
+    assert x.dim() == 2 and x.is_contiguous()
+    m, k = x.shape
+    xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    scale = torch.empty((m,), dtype=torch.float32, device=x.device)
+    rowsum = torch.empty((m,), dtype=torch.int32, device=x.device)
+    _check(lib.bitlinear_quantize_act(_ptr(x), _dtype_code(x), m, k, _ptr(xq), _ptr(scale),
+                                      _ptr(rowsum), _stream(stream)),
+           "bitlinear_quantize_act")
+    return xq, scale, rowsum
+
+
+def forward(xq, scale, rowsum, packed, gamma, n: int, k: int, layout: int = BL_PACK2,
+            path: int = BL_PATH_AUTO, y=None, workspace=None, stream=None):
+    """y [M, N] float32 = (xq . t^T) * gamma / scale."""
+    lib = load()
+    m = xq.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
+    ws_bytes = forward_workspace_bytes(m, n, k, layout)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=xq.device)
+    _check(lib.bitlinear_forward_ex(_ptr(xq), _ptr(scale), _ptr(rowsum), m, _ptr(packed), layout,
+                                    _ptr(gamma), n, k, _ptr(y), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel(), path,
+                                    _stream(stream)),
+           "bitlinear_forward_ex")
+    return y
+
+
+def matmul_i32(xq, rowsum, packed, n: int, k: int, layout: int = BL_PACK2,
+               path: int = BL_PATH_AUTO, acc=None, workspace=None, stream=None):
+    """acc [M, N] int32 = xq . t^T exactly."""
+    lib = load()
+    m = xq.shape[0]
+    if acc is None:
+        acc = torch.empty((m, n), dtype=torch.int32, device=xq.device)
+    ws_bytes = forward_workspace_bytes(m, n, k, layout)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=xq.device)
+    _check(lib.bitlinear_matmul_i32(_ptr(xq), _ptr(rowsum), m, _ptr(packed), layout, n, k,
+                                    _ptr(acc), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel(), path,
+                                    _stream(stream)),
+           "bitlinear_matmul_i32")
+    return acc
+
+
+def unpack_weights(packed, n: int, k: int, layout: int = BL_PACK2, stream=None):
+    lib = load()
+    trits = torch.empty((n, k), dtype=torch.int8, device=packed.device)
+    _check(lib.bitlinear_unpack_weights(_ptr(packed), layout, n, k, _ptr(trits), _stream(stream)),
+           "bitlinear_unpack_weights")
+    return trits
+
+
+# names of the C ABI
+bitlinear_quantize_weights = quantize_weights
+bitlinear_quantize_act = quantize_act
+bitlinear_forward = forward
+bitlinear_matmul_i32 = matmul_i32
+bitlinear_unpack_weights = unpack_weights
+bitlinear_packed_bytes = packed_bytes
+bitlinear_packed_row_bytes = packed_row_bytes
+bitlinear_status_string = status_string

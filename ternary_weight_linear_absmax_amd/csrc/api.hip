@@ -1,0 +1,178 @@
+// C ABI of libbitlinear: host-side argument checks, kernel-path dispatch and
+// launches.  Nothing here allocates, frees or synchronises.
+#include "../../include/bitlinear.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;   // bound on N*K and M*K (grid sizes)
+
+inline bool al16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool al4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+inline bool good_dtype(int d) { return d == BL_F32 || d == BL_BF16; }
+inline bool good_layout(int l) { return l == BL_PACK2 || l == BL_PACK3; }
+inline bool good_k(int64_t k) { return k >= 1 && k <= BITLINEAR_MAX_K; }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
+
+int choose_path(int64_t m, int layout)
+{
+    if (layout == BL_PACK3) return BL_PATH_GEMV;
+    return m <= 4 ? BL_PATH_GEMV : BL_PATH_MFMA;
+}
+
+// Shared body of bitlinear_forward_ex and bitlinear_matmul_i32.
+int run_product(const int8_t *xq, const float *scale, const int32_t *rowsum, int64_t m,
+                const uint8_t *packed, int layout, const float *gamma, int64_t n, int64_t k,
+                float *y, int32_t *acc, void *workspace, int64_t workspace_bytes, int path,
+                hipStream_t stream)
+{
+    (void)workspace;
+    if (!xq || !rowsum || !packed || (!y && !acc)) return BL_ERR_NULL;
+    if (y && (!scale || !gamma)) return BL_ERR_NULL;
+    if (!good_layout(layout)) return BL_ERR_LAYOUT;
+    if (path != BL_PATH_AUTO && path != BL_PATH_GEMV && path != BL_PATH_MFMA) return BL_ERR_PATH;
+    if (m < 0 || n < 0 || !good_k(k)) return BL_ERR_SHAPE;
+    if (m > 0 && k > kMaxElems / m) return BL_ERR_SHAPE;
+    if (n > 0 && k > kMaxElems / n) return BL_ERR_SHAPE;
+    if (m > 0 && n > kMaxElems / m) return BL_ERR_SHAPE;
+    if (!al16(xq) || !al16(packed) || !al4(rowsum)) return BL_ERR_ALIGN;
+    if (y && (!al4(y) || !al4(scale) || !al4(gamma))) return BL_ERR_ALIGN;
+    if (acc && !al4(acc)) return BL_ERR_ALIGN;
+    if (workspace_bytes < bitlinear_forward_workspace_bytes(m, n, k, layout))
+        return BL_ERR_WORKSPACE;
+    if (path == BL_PATH_AUTO) path = choose_path(m, layout);
+    if (layout == BL_PACK3 && path == BL_PATH_MFMA) return BL_ERR_PATH;
+    if (m == 0 || n == 0) return BL_OK;
+
+    bl::Out out{scale, gamma, y, acc};
+    hipError_t e;
+    if (layout == BL_PACK3)
+        e = bl::launch_gemv_pack3(xq, rowsum, m, packed, n, k, out, stream);
+    else if (path == BL_PATH_GEMV)
+        e = bl::launch_gemv_pack2(xq, rowsum, m, packed, n, k, out, stream);
+    else
+        e = bl::launch_gemm_pack2(xq, rowsum, m, packed, n, k, out, stream);
+    return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t bitlinear_packed_row_bytes(int64_t K, int layout)
+{
+    if (K < 1 || !good_layout(layout)) return 0;
+    return layout == BL_PACK2 ? bl::pack2_pitch(K) : bl::pack3_pitch(K);
+}
+
+int64_t bitlinear_packed_bytes(int64_t N, int64_t K, int layout)
+{
+    if (N < 0) return 0;
+    return N * bitlinear_packed_row_bytes(K, layout);
+}
+
+int64_t bitlinear_quantize_weights_workspace_bytes(int64_t N, int64_t K)
+{
+    (void)K;
+    return N > 0 ? 8 * N : 0;
+}
+
+int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int layout)
+{
+    (void)M; (void)N; (void)K; (void)layout;
+    return 0;
+}
+
+int bitlinear_forward_path(int64_t M, int64_t N, int64_t K, int layout)
+{
+    (void)N; (void)K;
+    return choose_path(M, layout);
+}
+
+const char *bitlinear_status_string(int status)
+{
+    switch (status) {
+    case BL_OK: return "ok";
+    case BL_ERR_NULL: return "a required pointer is NULL";
+    case BL_ERR_SHAPE: return "invalid size (negative, zero where not allowed, or too large)";
+    case BL_ERR_ALIGN: return "a device pointer is not suitably aligned (16 bytes for data)";
+    case BL_ERR_DTYPE: return "unknown element type";
+    case BL_ERR_LAYOUT: return "unknown packed layout";
+    case BL_ERR_WORKSPACE: return "workspace smaller than the size query returned";
+    case BL_ERR_HIP: return "a HIP launch or runtime call failed";
+    case BL_ERR_PATH: return "the requested kernel path cannot run this shape or layout";
+    default: return "unknown status";
+    }
+}
+
+int bitlinear_quantize_weights(const void *W, int dtype, int64_t N, int64_t K, int layout,
+                               uint8_t *packed, float *gamma, void *workspace,
+                               int64_t workspace_bytes, hipStream_t stream)
+{
+    if (!W || !packed || !gamma || !workspace) return BL_ERR_NULL;
+    if (!good_dtype(dtype)) return BL_ERR_DTYPE;
+    if (!good_layout(layout)) return BL_ERR_LAYOUT;
+    if (N < 1 || !good_k(K) || K > kMaxElems / N) return BL_ERR_SHAPE;
+    if (!al16(W) || !al16(packed) || !al16(workspace) || !al4(gamma)) return BL_ERR_ALIGN;
+    if (workspace_bytes < bitlinear_quantize_weights_workspace_bytes(N, K)) return BL_ERR_WORKSPACE;
+    double *rowsums = (double *)workspace;
+    hipError_t e = bl::launch_gamma_rows(W, dtype, N, K, rowsums, stream);
+    if (e == hipSuccess) e = bl::launch_gamma_final(rowsums, N, K, gamma, stream);
+    if (e == hipSuccess) e = bl::launch_pack(W, dtype, N, K, layout, gamma, packed, stream);
+    return hip_status(e);
+}
+
+int bitlinear_quantize_act(const void *x, int dtype, int64_t M, int64_t K, int8_t *xq,
+                           float *scale, int32_t *rowsum, hipStream_t stream)
+{
+    if (!x || !xq || !scale) return BL_ERR_NULL;
+    if (!good_dtype(dtype)) return BL_ERR_DTYPE;
+    if (M < 0 || !good_k(K) || (M > 0 && K > kMaxElems / M) || M > 0x7FFFFFFF)
+        return BL_ERR_SHAPE;
+    if (!al16(x) || !al16(xq) || !al4(scale) || (rowsum && !al4(rowsum))) return BL_ERR_ALIGN;
+    if (M == 0) return BL_OK;
+    return hip_status(bl::launch_quant_act(x, dtype, M, K, xq, scale, rowsum, stream));
+}
+
+int bitlinear_forward(const int8_t *xq, const float *scale, const int32_t *rowsum, int64_t M,
+                      const uint8_t *packed, int layout, const float *gamma, int64_t N,
+                      int64_t K, float *y, void *workspace, int64_t workspace_bytes,
+                      hipStream_t stream)
+{
+    if (!y) return BL_ERR_NULL;
+    return run_product(xq, scale, rowsum, M, packed, layout, gamma, N, K, y, nullptr, workspace,
+                       workspace_bytes, BL_PATH_AUTO, stream);
+}
+
+int bitlinear_forward_ex(const int8_t *xq, const float *scale, const int32_t *rowsum,
+                         int64_t M, const uint8_t *packed, int layout, const float *gamma,
+                         int64_t N, int64_t K, float *y, void *workspace,
+                         int64_t workspace_bytes, int path, hipStream_t stream)
+{
+    if (!y) return BL_ERR_NULL;
+    return run_product(xq, scale, rowsum, M, packed, layout, gamma, N, K, y, nullptr, workspace,
+                       workspace_bytes, path, stream);
+}
+
+int bitlinear_matmul_i32(const int8_t *xq, const int32_t *rowsum, int64_t M,
+                         const uint8_t *packed, int layout, int64_t N, int64_t K, int32_t *acc,
+                         void *workspace, int64_t workspace_bytes, int path, hipStream_t stream)
+{
+    if (!acc) return BL_ERR_NULL;
+    return run_product(xq, nullptr, rowsum, M, packed, layout, nullptr, N, K, nullptr, acc,
+                       workspace, workspace_bytes, path, stream);
+}
+
+int bitlinear_unpack_weights(const uint8_t *packed, int layout, int64_t N, int64_t K,
+                             int8_t *trits, hipStream_t stream)
+{
+    if (!packed || !trits) return BL_ERR_NULL;
+    if (!good_layout(layout)) return BL_ERR_LAYOUT;
+    if (N < 0 || !good_k(K) || (N > 0 && K > kMaxElems / N)) return BL_ERR_SHAPE;
+    if (!al16(packed)) return BL_ERR_ALIGN;
+    if (N == 0) return BL_OK;
+    return hip_status(bl::launch_unpack(packed, layout, N, K, trits, stream));
+}
+
+}  // extern "C"

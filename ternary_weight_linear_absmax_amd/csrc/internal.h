@@ -1,0 +1,77 @@
+// Internal declarations shared by the HIP translation units of libbitlinear.
+// Every launcher returns the hipError_t of its launch; shapes are validated by
+// the C-ABI layer before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+enum : int { DT_F32 = 0, DT_BF16 = 1 };
+enum : int { LAYOUT_PACK2 = 0, LAYOUT_PACK3 = 1 };
+
+// Row pitch of the packed layouts (bytes); both are multiples of 16.
+__host__ __device__ inline int64_t pack2_pitch(int64_t k) { return ((k + 63) / 64) * 16; }
+__host__ __device__ inline int64_t pack3_pitch(int64_t k) { return (((k + 4) / 5 + 15) / 16) * 16; }
+
+// Output of a forward kernel: either the rescaled float y or the raw int32
+// accumulator (acc != nullptr selects the raw form).
+struct Out {
+    const float *scale;   // [M] per-token quantiser multiplier s
+    const float *gamma;   // one float, absmean of the weights
+    float *y;             // [M, N]
+    int32_t *acc;         // [M, N] or nullptr
+};
+
+// ---- weights (quant_weights.hip) ----
+hipError_t launch_gamma_rows(const void *w, int dtype, int64_t n, int64_t k, double *rowsums,
+                             hipStream_t s);
+hipError_t launch_gamma_final(const double *rowsums, int64_t n, int64_t k, float *gamma,
+                              hipStream_t s);
+hipError_t launch_pack(const void *w, int dtype, int64_t n, int64_t k, int layout,
+                       const float *gamma, uint8_t *packed, hipStream_t s);
+hipError_t launch_unpack(const uint8_t *packed, int layout, int64_t n, int64_t k,
+                         int8_t *trits, hipStream_t s);
+
+// ---- activations (quant_act.hip) ----
+hipError_t launch_quant_act(const void *x, int dtype, int64_t m, int64_t k, int8_t *xq,
+                            float *scale, int32_t *rowsum, hipStream_t s);
+
+// ---- products ----
+// 2-bit layout, vector dot-product kernel; tokens handled in groups of up to 4.
+hipError_t launch_gemv_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
+                             const uint8_t *packed, int64_t n, int64_t k, Out out,
+                             hipStream_t s);
+// base-3 layout, vector kernel.
+hipError_t launch_gemv_pack3(const int8_t *xq, const int32_t *rowsum, int64_t m,
+                             const uint8_t *packed, int64_t n, int64_t k, Out out,
+                             hipStream_t s);
+// 2-bit layout, int8 matrix-core kernel.
+hipError_t launch_gemm_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
+                             const uint8_t *packed, int64_t n, int64_t k, Out out,
+                             hipStream_t s);
+
+// 128-bit streaming load (the packed weights are read once per call).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline uint4 load_nt16(const void *p)
+{
+    u32x4 v = __builtin_nontemporal_load((const u32x4 *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Writes the output element (m, n) from the code-weighted sum sum_k (t+1) q
+// and the token's rowsum: acc = codesum - rowsum.
+__device__ inline void store_out(const Out &o, int64_t ldy, int64_t m, int64_t n,
+                                 int32_t codesum, int32_t rowsum)
+{
+    int32_t acc = codesum - rowsum;
+    if (o.acc) {
+        o.acc[m * ldy + n] = acc;
+    } else {
+        float gs = o.gamma[0] / o.scale[m];
+        o.y[m * ldy + n] = (float)acc * gs;
+    }
+}
+
+}  // namespace bl

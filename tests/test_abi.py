@@ -1,0 +1,116 @@
+"""The C-ABI library loads, exports every declared function, and rejects bad
+arguments on the host before any launch (no GPU needed: every call below
+fails validation or is an empty product, so nothing reaches the HIP runtime).
+"""
+import ctypes
+import os
+
+import pytest
+
+import oracle
+from ternary_weight_linear_absmax_amd import bitlinear as bl
+from ternary_weight_linear_absmax_amd import build_lib
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bl.LIB_PATH):
+        build_lib.build()
+    return bl.load()
+
+
+def test_every_header_function_is_exported(lib):
+    names = bl.header_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_size_queries_match_the_layout_definitions(lib):
+    for k in (1, 15, 16, 64, 65, 256, 2560, 6912, 8192, 28672):
+        assert bl.packed_row_bytes(k, bl.BL_PACK2) == oracle.pack2_pitch(k)
+        assert bl.packed_row_bytes(k, bl.BL_PACK3) == oracle.pack3_pitch(k)
+    assert bl.packed_bytes(28672, 8192) == 58_720_256
+    assert bl.packed_bytes(7, 0) == 0 and bl.packed_row_bytes(64, 9) == 0
+    assert bl.quantize_weights_workspace_bytes(100, 64) == 800
+    assert bl.forward_workspace_bytes(512, 8640, 3200) >= 0
+
+
+def test_path_selection(lib):
+    assert bl.forward_path(1, 28672, 8192) == bl.BL_PATH_GEMV
+    assert bl.forward_path(512, 8640, 3200) == bl.BL_PATH_MFMA
+    assert bl.forward_path(1, 28672, 8192, bl.BL_PACK3) == bl.BL_PATH_GEMV
+
+
+def test_status_strings(lib):
+    for code in range(-8, 1):
+        assert bl.status_string(code) and bl.status_string(code) != "unknown status"
+    assert bl.status_string(-99) == "unknown status"
+
+
+P = ctypes.c_void_p(0x10000)        # fake, 16-byte aligned, never dereferenced
+ODD = ctypes.c_void_p(0x10001)
+NULL = None
+
+
+def test_quantize_weights_argument_checks(lib):
+    f = lib.bitlinear_quantize_weights
+    ok = dict(W=P, dt=bl.BL_BF16, N=8, K=64, lay=bl.BL_PACK2, packed=P, gamma=P, ws=P, wsb=64)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["W"], a["dt"], a["N"], a["K"], a["lay"], a["packed"], a["gamma"], a["ws"],
+                 a["wsb"], None)
+
+    assert call(W=NULL) == -1
+    assert call(gamma=NULL) == -1
+    assert call(dt=3) == -4
+    assert call(lay=2) == -5
+    assert call(N=0) == -2
+    assert call(K=0) == -2
+    assert call(K=bl.MAX_K + 1) == -2
+    assert call(W=ODD) == -3
+    assert call(packed=ODD) == -3
+    assert call(wsb=63) == -6
+
+
+def test_quantize_act_argument_checks(lib):
+    f = lib.bitlinear_quantize_act
+    assert f(NULL, 1, 4, 64, P, P, P, None) == -1
+    assert f(P, 2, 4, 64, P, P, P, None) == -4
+    assert f(P, 1, -1, 64, P, P, P, None) == -2
+    assert f(P, 1, 4, 0, P, P, P, None) == -2
+    assert f(ODD, 1, 4, 64, P, P, P, None) == -3
+    assert f(P, 1, 0, 64, P, P, P, None) == 0            # empty batch: no launch
+
+
+def test_forward_argument_checks(lib):
+    f = lib.bitlinear_forward_ex
+
+    def call(xq=P, s=P, r=P, m=4, pk=P, lay=0, g=P, n=8, k=64, y=P, ws=NULL, wsb=0, path=0):
+        return f(xq, s, r, m, pk, lay, g, n, k, y, ws, wsb, path, None)
+
+    assert call(xq=NULL) == -1
+    assert call(r=NULL) == -1
+    assert call(y=NULL) == -1
+    assert call(g=NULL) == -1
+    assert call(lay=7) == -5
+    assert call(path=9) == -8
+    assert call(lay=bl.BL_PACK3, path=bl.BL_PATH_MFMA) == -8
+    assert call(k=0) == -2
+    assert call(m=-1) == -2
+    assert call(pk=ODD) == -3
+    assert call(xq=ODD) == -3
+    assert call(m=0) == 0 and call(n=0) == 0             # empty products: no launch
+    g = lib.bitlinear_matmul_i32
+    assert g(P, P, 4, P, 0, 8, 64, NULL, NULL, 0, 0, None) == -1
+    assert g(P, P, 0, P, 0, 8, 64, P, NULL, 0, 0, None) == 0
+
+
+def test_unpack_argument_checks(lib):
+    f = lib.bitlinear_unpack_weights
+    assert f(NULL, 0, 4, 64, P, None) == -1
+    assert f(P, 3, 4, 64, P, None) == -5
+    assert f(P, 0, 4, 0, P, None) == -2
+    assert f(ODD, 0, 4, 64, P, None) == -3
+    assert f(P, 0, 0, 64, P, None) == 0

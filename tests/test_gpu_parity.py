@@ -1,0 +1,189 @@
+"""GPU parity: every HIP kernel against the CPU oracle on the same seeded
+inputs, through the C ABI.
+
+Bar: bit-exact for gamma, packed bytes, int8 activations, scales, row sums and
+int32 accumulators; fp32 outputs within 1e-5 relative error of the oracle's
+double-precision rescale (exact zeros where the accumulator is zero).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ternary_weight_linear_absmax_amd import bitlinear as bl
+from ternary_weight_linear_absmax_amd import inputs
+
+from gpu_helpers import assert_y_close, dev, host, oracle_weights
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = [bl.BL_PACK2, bl.BL_PACK3]
+
+
+def run_case(w: np.ndarray, x: np.ndarray, layout: int, paths=(bl.BL_PATH_AUTO,)):
+    """Full chain on both sides; returns nothing, asserts parity at every step."""
+    n, k = w.shape
+    t, g, packed_ref = oracle_weights(w, layout)
+    q_ref, s_ref, r_ref = oracle.quantize_act(x)
+    acc_ref = oracle.matmul_i32(q_ref, t)
+    y_ref = oracle.rescale(acc_ref, s_ref, g)
+
+    packed, gamma = bl.quantize_weights(dev(w), layout)
+    xq, scale, rowsum = bl.quantize_act(dev(x))
+    assert host(gamma)[0] == g
+    np.testing.assert_array_equal(host(packed), packed_ref)
+    np.testing.assert_array_equal(host(xq), q_ref)
+    np.testing.assert_array_equal(host(scale), s_ref)
+    np.testing.assert_array_equal(host(rowsum), r_ref)
+    np.testing.assert_array_equal(host(bl.unpack_weights(packed, n, k, layout)), t)
+    for path in paths:
+        acc = bl.matmul_i32(xq, rowsum, packed, n, k, layout, path=path)
+        np.testing.assert_array_equal(host(acc), acc_ref, err_msg=f"path {path}")
+        y = bl.forward(xq, scale, rowsum, packed, gamma, n, k, layout, path=path)
+        assert_y_close(host(y), y_ref, acc_ref)
+
+
+def all_paths(layout):
+    if layout == bl.BL_PACK2:
+        return (bl.BL_PATH_AUTO, bl.BL_PATH_GEMV, bl.BL_PATH_MFMA)
+    return (bl.BL_PATH_AUTO, bl.BL_PATH_GEMV)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_tiny_layer_fp32(layout):
+    w, x = inputs.tiny()
+    run_case(w, x, layout, all_paths(layout))
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("m,n,k", [
+    (1, 1, 1), (1, 7, 15), (3, 77, 100), (2, 33, 64), (4, 129, 65), (5, 130, 320),
+    (1, 300, 2560), (9, 64, 1000), (130, 257, 200), (17, 300, 384), (64, 128, 256),
+    (129, 129, 129), (200, 513, 1040),
+])
+def test_ragged_shapes_bf16(layout, m, n, k):
+    w, x = inputs.random_case(10_000 + m * 7 + n * 13 + k, m, n, k, bf16=True)
+    run_case(w, x, layout, all_paths(layout))
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_ragged_shapes_fp32_unaligned_k(layout):
+    w, x = inputs.random_case(555, 6, 150, 201, bf16=False)
+    run_case(w, x, layout, all_paths(layout))
+
+
+def test_zero_token_and_zero_weight_rows():
+    w, x = inputs.random_case(31, 4, 96, 320, bf16=True)
+    x[2] = 0
+    w[5] = 0
+    for layout in LAYOUTS:
+        run_case(w, x, layout, all_paths(layout))
+
+
+def test_hadamard_weights_give_integer_walsh_hadamard():
+    import scipy.linalg
+    h = scipy.linalg.hadamard(512).astype(np.float32)
+    _, x = inputs.random_case(32, 8, 1, 512, bf16=False)
+    for layout in LAYOUTS:
+        run_case(h, x, layout, all_paths(layout))
+
+
+def test_max_k():
+    k = bl.MAX_K
+    w, x = inputs.random_case(33, 2, 3, k, bf16=True)
+    run_case(w, x, bl.BL_PACK2, all_paths(bl.BL_PACK2))
+    run_case(w, x, bl.BL_PACK3, all_paths(bl.BL_PACK3))
+
+
+def test_empty_products_are_noops():
+    w, x = inputs.random_case(34, 2, 16, 64, bf16=True)
+    packed, gamma = bl.quantize_weights(dev(w))
+    xq, scale, rowsum = bl.quantize_act(dev(x))
+    y = bl.forward(xq[:0], scale[:0], rowsum[:0], packed, gamma, 16, 64)
+    assert y.shape == (0, 16)
+    y = bl.forward(xq, scale, rowsum, packed[:0], gamma, 0, 64)
+    assert y.shape == (2, 0)
+    torch.cuda.synchronize()
+
+
+def test_repeated_calls_are_bit_identical():
+    _, w, x = inputs.decode(3, m=3)
+    packed, gamma = bl.quantize_weights(dev(w))
+    xq, scale, rowsum = bl.quantize_act(dev(x))
+    n, k = w.shape
+    for path in (bl.BL_PATH_GEMV, bl.BL_PATH_MFMA):
+        ys = [host(bl.forward(xq, scale, rowsum, packed, gamma, n, k, path=path)) for _ in range(3)]
+        assert all(np.array_equal(ys[0].view(np.uint32), v.view(np.uint32)) for v in ys[1:])
+
+
+# ---- decode shapes of the 2B-class model, M = 1 (full parity) ---------------------------
+
+@pytest.mark.parametrize("shape", range(len(inputs.DECODE_SHAPES)))
+def test_decode_shapes_m1(shape):
+    _, w, x = inputs.decode(shape, m=1)
+    run_case(w, x, bl.BL_PACK2, all_paths(bl.BL_PACK2))
+
+
+@pytest.mark.parametrize("shape", range(len(inputs.DECODE_SHAPES)))
+def test_decode_shapes_m1_base3(shape):
+    _, w, x = inputs.decode(shape, m=1)
+    run_case(w, x, bl.BL_PACK3)
+
+
+# ---- prefill shapes of the 3B-class model, M = 512 (sampled tokens) ------------------------
+
+@pytest.mark.parametrize("shape", range(len(inputs.PREFILL_SHAPES)))
+def test_prefill_shapes_m512_sampled(shape):
+    _, w, x = inputs.prefill(shape)
+    n, k = w.shape
+    t, g, packed_ref = oracle_weights(w, bl.BL_PACK2)
+    q_ref, s_ref, r_ref = oracle.quantize_act(x)
+    packed, gamma = bl.quantize_weights(dev(w))
+    xq, scale, rowsum = bl.quantize_act(dev(x))
+    assert host(gamma)[0] == g
+    np.testing.assert_array_equal(host(packed), packed_ref)
+    np.testing.assert_array_equal(host(xq), q_ref)
+    np.testing.assert_array_equal(host(scale), s_ref)
+    np.testing.assert_array_equal(host(rowsum), r_ref)
+    acc = host(bl.matmul_i32(xq, rowsum, packed, n, k))
+    y = host(bl.forward(xq, scale, rowsum, packed, gamma, n, k))
+    rng = np.random.default_rng(99)
+    rows = np.sort(rng.choice(512, size=12, replace=False))
+    rows[0], rows[-1] = 0, 511
+    acc_ref = oracle.matmul_i32(q_ref[rows], t)
+    np.testing.assert_array_equal(acc[rows], acc_ref)
+    assert_y_close(y[rows], oracle.rescale(acc_ref, s_ref[rows], g), acc_ref)
+    # the zero fraction the generator produces (30% forced near zero)
+    zero_frac = float(np.mean(t == 0))
+    assert 0.40 < zero_frac < 0.50
+
+
+# ---- 70B-class layer (single GPU), M in {1, 16, 128}; base-3 at M = 1 -------------------------
+
+@pytest.mark.parametrize("shape", range(len(inputs.XL_SHAPES)))
+def test_xl_layer(shape):
+    _, w, x = inputs.xl(shape, m=128)
+    n, k = w.shape
+    t, g = oracle.quantize_weights(w)
+    p2_ref = oracle.pack2(t)
+    wd = dev(w)
+    packed, gamma = bl.quantize_weights(wd)
+    packed3, gamma3 = bl.quantize_weights(wd, bl.BL_PACK3)
+    del wd
+    assert host(gamma)[0] == g and host(gamma3)[0] == g
+    np.testing.assert_array_equal(host(packed), p2_ref)
+    del p2_ref
+    np.testing.assert_array_equal(host(packed3), oracle.pack3(t))
+    q_ref, s_ref, r_ref = oracle.quantize_act(x)
+    xq, scale, rowsum = bl.quantize_act(dev(x))
+    np.testing.assert_array_equal(host(xq), q_ref)
+    for m in inputs.XL_MS:
+        acc = host(bl.matmul_i32(xq[:m], rowsum[:m], packed, n, k))
+        rows = np.arange(m) if m <= 16 else np.array([0, 1, 37, 64, 100, 127])
+        acc_ref = oracle.matmul_i32(q_ref[rows], t)
+        np.testing.assert_array_equal(acc[rows], acc_ref, err_msg=f"M={m}")
+        y = host(bl.forward(xq[:m], scale[:m], rowsum[:m], packed, gamma, n, k))
+        assert_y_close(y[rows], oracle.rescale(acc_ref, s_ref[rows], g), acc_ref)
+        if m == 1:
+            acc3 = host(bl.matmul_i32(xq[:1], rowsum[:1], packed3, n, k, bl.BL_PACK3))
+            np.testing.assert_array_equal(acc3, acc)      # base-3 == 2-bit, bit for bit
