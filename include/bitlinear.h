@@ -28,7 +28,8 @@
  *   - Device pointers must be 16-byte aligned.  Sizes are element counts.
  *   - Inputs must be finite; NaN or infinite inputs give unspecified results.
  *   - M == 0 or N == 0 is an empty product and returns BL_OK without a
- *     launch; K must be in [1, BITLINEAR_MAX_K].
+ *     launch (the buffers of an empty product may be NULL); K must be in
+ *     [1, BITLINEAR_MAX_K].  Other size and layout checks come first.
  *   - Every call is stateless and re-entrant; calls on different streams may
  *     overlap if their buffers do not.
  */

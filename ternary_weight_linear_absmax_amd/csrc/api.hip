@@ -28,22 +28,22 @@ int run_product(const int8_t *xq, const float *scale, const int32_t *rowsum, int
                 hipStream_t stream)
 {
     (void)workspace;
-    if (!xq || !rowsum || !packed || (!y && !acc)) return BL_ERR_NULL;
-    if (y && (!scale || !gamma)) return BL_ERR_NULL;
     if (!good_layout(layout)) return BL_ERR_LAYOUT;
     if (path != BL_PATH_AUTO && path != BL_PATH_GEMV && path != BL_PATH_MFMA) return BL_ERR_PATH;
     if (m < 0 || n < 0 || !good_k(k)) return BL_ERR_SHAPE;
     if (m > 0 && k > kMaxElems / m) return BL_ERR_SHAPE;
     if (n > 0 && k > kMaxElems / n) return BL_ERR_SHAPE;
     if (m > 0 && n > kMaxElems / m) return BL_ERR_SHAPE;
+    if (path == BL_PATH_AUTO) path = choose_path(m, layout);
+    if (layout == BL_PACK3 && path == BL_PATH_MFMA) return BL_ERR_PATH;
+    if (m == 0 || n == 0) return BL_OK;    // empty product: buffers may be NULL
+    if (!xq || !rowsum || !packed || (!y && !acc)) return BL_ERR_NULL;
+    if (y && (!scale || !gamma)) return BL_ERR_NULL;
     if (!al16(xq) || !al16(packed) || !al4(rowsum)) return BL_ERR_ALIGN;
     if (y && (!al4(y) || !al4(scale) || !al4(gamma))) return BL_ERR_ALIGN;
     if (acc && !al4(acc)) return BL_ERR_ALIGN;
     if (workspace_bytes < bitlinear_forward_workspace_bytes(m, n, k, layout))
         return BL_ERR_WORKSPACE;
-    if (path == BL_PATH_AUTO) path = choose_path(m, layout);
-    if (layout == BL_PACK3 && path == BL_PATH_MFMA) return BL_ERR_PATH;
-    if (m == 0 || n == 0) return BL_OK;
 
     bl::Out out{scale, gamma, y, acc};
     hipError_t e;
@@ -126,12 +126,12 @@ int bitlinear_quantize_weights(const void *W, int dtype, int64_t N, int64_t K, i
 int bitlinear_quantize_act(const void *x, int dtype, int64_t M, int64_t K, int8_t *xq,
                            float *scale, int32_t *rowsum, hipStream_t stream)
 {
-    if (!x || !xq || !scale) return BL_ERR_NULL;
     if (!good_dtype(dtype)) return BL_ERR_DTYPE;
     if (M < 0 || !good_k(K) || (M > 0 && K > kMaxElems / M) || M > 0x7FFFFFFF)
         return BL_ERR_SHAPE;
+    if (M == 0) return BL_OK;              // empty batch: buffers may be NULL
+    if (!x || !xq || !scale) return BL_ERR_NULL;
     if (!al16(x) || !al16(xq) || !al4(scale) || (rowsum && !al4(rowsum))) return BL_ERR_ALIGN;
-    if (M == 0) return BL_OK;
     return hip_status(bl::launch_quant_act(x, dtype, M, K, xq, scale, rowsum, stream));
 }
 
@@ -140,7 +140,6 @@ int bitlinear_forward(const int8_t *xq, const float *scale, const int32_t *rowsu
                       int64_t K, float *y, void *workspace, int64_t workspace_bytes,
                       hipStream_t stream)
 {
-    if (!y) return BL_ERR_NULL;
     return run_product(xq, scale, rowsum, M, packed, layout, gamma, N, K, y, nullptr, workspace,
                        workspace_bytes, BL_PATH_AUTO, stream);
 }
@@ -150,7 +149,6 @@ int bitlinear_forward_ex(const int8_t *xq, const float *scale, const int32_t *ro
                          int64_t N, int64_t K, float *y, void *workspace,
                          int64_t workspace_bytes, int path, hipStream_t stream)
 {
-    if (!y) return BL_ERR_NULL;
     return run_product(xq, scale, rowsum, M, packed, layout, gamma, N, K, y, nullptr, workspace,
                        workspace_bytes, path, stream);
 }
@@ -159,7 +157,6 @@ int bitlinear_matmul_i32(const int8_t *xq, const int32_t *rowsum, int64_t M,
                          const uint8_t *packed, int layout, int64_t N, int64_t K, int32_t *acc,
                          void *workspace, int64_t workspace_bytes, int path, hipStream_t stream)
 {
-    if (!acc) return BL_ERR_NULL;
     return run_product(xq, nullptr, rowsum, M, packed, layout, nullptr, N, K, nullptr, acc,
                        workspace, workspace_bytes, path, stream);
 }
@@ -167,11 +164,11 @@ int bitlinear_matmul_i32(const int8_t *xq, const int32_t *rowsum, int64_t M,
 int bitlinear_unpack_weights(const uint8_t *packed, int layout, int64_t N, int64_t K,
                              int8_t *trits, hipStream_t stream)
 {
-    if (!packed || !trits) return BL_ERR_NULL;
     if (!good_layout(layout)) return BL_ERR_LAYOUT;
     if (N < 0 || !good_k(K) || (N > 0 && K > kMaxElems / N)) return BL_ERR_SHAPE;
-    if (!al16(packed)) return BL_ERR_ALIGN;
     if (N == 0) return BL_OK;
+    if (!packed || !trits) return BL_ERR_NULL;
+    if (!al16(packed)) return BL_ERR_ALIGN;
     return hip_status(bl::launch_unpack(packed, layout, N, K, trits, stream));
 }
 

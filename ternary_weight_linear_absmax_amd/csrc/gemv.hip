@@ -4,7 +4,7 @@
 // Source: asi.tokyo BitNet b1.58 2B4T article, packing paragraph: the trits
 // travel packed (four per byte) and are unpacked right next to the arithmetic
 // units, where they are multiplied with the 8-bit activations.  On gfx950 the
-// "arithmetic unit" is v_dot4_i32_i8: the 2-bit layout is chosen so that
+// arithmetic unit is v_dot4_i32_i8: the 2-bit layout is chosen so that
 // (word >> 2i) & 0x03030303 gives four consecutive k as int8 codes t + 1, which
 // dot4 multiplies with four consecutive int8 activations in one instruction.
 // The codes are offset by one, so sum_k (t+1) q = acc + rowsum(q); the row sum
@@ -12,13 +12,8 @@
 //
 // Two masks avoid two of the four shifts: word & 0x0C0C0C0C is 4x the codes of
 // the second quarter, whose dot products are collected in a separate
-// accumulator and divided by 4 (exactly) at the end.
-//
-// Work split: lanes run along k in groups of LG lanes (one packed row per
-// group); each lane loads 16 bytes (64 trits) per step with a 128-bit load and
-// the matching 64 activation bytes per token; a lane group owns R consecutive
-// rows, so every activation load is reused R times.  Partial sums are reduced
-// across the LG lanes with xor shuffles.
+// accumulator and divided by 4 (exactly) at the end: 9 ALU operations per 16
+// trits.
 #include "internal.h"
 
 namespace bl {
@@ -26,7 +21,43 @@ namespace {
 
 __device__ inline uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
-// 64 activation bytes k = 64c .. 64c+63 of one token, zero past K.
+// One packed word (16 trits) against the 16 matching activation bytes.
+__device__ inline void dot_word(uint32_t w, uint4 x, int &lo, int &hi)
+{
+    const int u0 = (int)(w & 0x03030303u);
+    const int u1 = (int)(w & 0x0C0C0C0Cu);
+    const uint32_t w4 = w >> 4;
+    const int u2 = (int)(w4 & 0x03030303u);
+    const int u3 = (int)(w4 & 0x0C0C0C0Cu);
+    lo = __builtin_amdgcn_sdot4(u0, (int)x.x, lo, false);
+    hi = __builtin_amdgcn_sdot4(u1, (int)x.y, hi, false);
+    lo = __builtin_amdgcn_sdot4(u2, (int)x.z, lo, false);
+    hi = __builtin_amdgcn_sdot4(u3, (int)x.w, hi, false);
+}
+
+template <int LG>
+__device__ inline int group_sum(int v)
+{
+#pragma unroll
+    for (int off = LG / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Sum over the 64 lanes of a wave with DPP row operations; lane 63 holds the
+// result.
+__device__ inline int wave_sum_dpp(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return v;
+}
+
+// 64 activation bytes k = 64c .. 64c+63 of one token; zero past K.  AL: K is a
+// multiple of 16, so every 16-byte piece is wholly inside or outside the row.
 template <bool AL>
 __device__ inline void load_x64(const int8_t *__restrict__ xrow, int64_t k, int64_t c, uint4 xv[4])
 {
@@ -54,75 +85,121 @@ __device__ inline void load_x64(const int8_t *__restrict__ xrow, int64_t k, int6
     }
 }
 
-// One packed word (16 trits) against the 16 matching activation bytes.
-__device__ inline void dot_word(uint32_t w, uint4 x, int &lo, int &hi)
-{
-    const int u0 = (int)(w & 0x03030303u);
-    const int u1 = (int)(w & 0x0C0C0C0Cu);
-    const uint32_t w4 = w >> 4;
-    const int u2 = (int)(w4 & 0x03030303u);
-    const int u3 = (int)(w4 & 0x0C0C0C0Cu);
-    lo = __builtin_amdgcn_sdot4(u0, (int)x.x, lo, false);
-    hi = __builtin_amdgcn_sdot4(u1, (int)x.y, hi, false);
-    lo = __builtin_amdgcn_sdot4(u2, (int)x.z, lo, false);
-    hi = __builtin_amdgcn_sdot4(u3, (int)x.w, hi, false);
-}
+// ---- 2-bit layout ------------------------------------------------------------
+// A block is KS waves.  It owns RB = R * ST consecutive weight rows; wave w
+// takes the w-th share of every row's 16-byte chunks, and lane l of the wave
+// takes chunks l and l + 64 of that share (CPL <= 2), so a lane holds at most
+// 2 x 64 activation bytes per token in registers.  The block walks its rows in
+// ST steps of R rows; the weights of step s+1 are issued before the arithmetic
+// of step s (a scheduling barrier keeps them there), so every wave always has
+// loads in flight.  Row indices past N are clamped: the loads stay in bounds and
+// those rows are not stored.  Per-wave partial sums go through LDS and are
+// combined once at the end.
+constexpr int GEMV_R = 2;
+constexpr int GEMV_KS_MAX = 8;
 
-template <int LG>
-__device__ inline int group_sum(int v)
+template <int MT, int CPL, int ST, bool AL>
+__global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
+    const int8_t *__restrict__ xq, const int32_t *__restrict__ rowsum, int64_t k,
+    const uint4 *__restrict__ packed, int64_t n, int64_t chunks, int64_t share, Out out,
+    int64_t ldy, int64_t m0)
 {
-#pragma unroll
-    for (int off = LG / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
-
-template <int MT, int LG, int R, bool AL>
-__global__ __launch_bounds__(256) void gemv2_kernel(const int8_t *__restrict__ xq,
-                                                    const int32_t *__restrict__ rowsum,
-                                                    int64_t k, const uint4 *__restrict__ packed,
-                                                    int64_t n, int64_t chunks, Out out,
-                                                    int64_t ldy, int64_t m0)
-{
-    constexpr int RPW = 64 / LG;
+    constexpr int R = GEMV_R, RB = GEMV_R * ST;
+    __shared__ int part[GEMV_KS_MAX][RB][MT];
+    const int ks = blockDim.x >> 6;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int grp = lane / LG, li = lane % LG;
-    const int64_t row0 = (((int64_t)blockIdx.x * 4 + wave) * RPW + grp) * R;
-    if (row0 >= n) return;
+    const int64_t row0 = (int64_t)blockIdx.x * RB;
 
-    int lo[R][MT], hi[R][MT];
+    int64_t coff[CPL];
+    bool ok[CPL];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int t = 0; t < MT; ++t) lo[r][t] = hi[r][t] = 0;
+    for (int j = 0; j < CPL; ++j) {
+        const int64_t c = wave * share + lane + 64 * j;
+        ok[j] = (lane + 64 * j < share) && c < chunks;
+        coff[j] = ok[j] ? c : 0;
+    }
 
-    for (int64_t c = li; c < chunks; c += LG) {
-        uint4 w[R];
+    uint4 w[2][R][CPL];
+    auto load = [&](uint4(&wb)[R][CPL], int s) {
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-            w[r] = (row0 + r < n) ? load_nt16(packed + (row0 + r) * chunks + c)
-                                  : zero4();
+        for (int r = 0; r < R; ++r) {
+            int64_t row = row0 + s * R + r;
+            row = row < n ? row : n - 1;
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            uint4 xv[4];
-            load_x64<AL>(xq + (m0 + t) * k, k, c, xv);
+            for (int j = 0; j < CPL; ++j) wb[r][j] = load_nt16(packed + row * chunks + coff[j]);
+        }
+    };
+    load(w[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    uint4 xv[MT][CPL][4];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                dot_word(w[r].x, xv[0], lo[r][t], hi[r][t]);
-                dot_word(w[r].y, xv[1], lo[r][t], hi[r][t]);
-                dot_word(w[r].z, xv[2], lo[r][t], hi[r][t]);
-                dot_word(w[r].w, xv[3], lo[r][t], hi[r][t]);
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            load_x64<AL>(xq + (m0 + t) * k, k, coff[j], xv[t][j]);
+            if (!ok[j])
+#pragma unroll
+                for (int d = 0; d < 4; ++d) xv[t][j][d] = zero4();
+        }
+
+#pragma unroll
+    for (int s = 0; s < ST; ++s) {
+        if (s + 1 < ST) load(w[(s + 1) & 1], s + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int b = s & 1;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                int lo = 0, hi = 0;
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) {
+                    dot_word(w[b][r][j].x, xv[t][j][0], lo, hi);
+                    dot_word(w[b][r][j].y, xv[t][j][1], lo, hi);
+                    dot_word(w[b][r][j].z, xv[t][j][2], lo, hi);
+                    dot_word(w[b][r][j].w, xv[t][j][3], lo, hi);
+                }
+                const int v = wave_sum_dpp(lo + (hi >> 2));
+                if (lane == 63) part[wave][s * R + r][t] = v;
             }
         }
     }
+    __syncthreads();
+    for (int e = threadIdx.x; e < RB * MT; e += blockDim.x) {
+        const int rr = e / MT, t = e % MT;
+        int sum = 0;
+        for (int q = 0; q < ks; ++q) sum += part[q][rr][t];
+        if (row0 + rr < n) store_out(out, ldy, m0 + t, row0 + rr, sum, rowsum[m0 + t]);
+    }
+}
 
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            int v = lo[r][t] + (hi[r][t] >> 2);
-            v = group_sum<LG>(v);
-            if (li == 0 && row0 + r < n) store_out(out, ldy, m0 + t, row0 + r, v, rowsum[m0 + t]);
+// Rows longer than GEMV_KS_MAX * 128 chunks (K > 65536): one wave per row,
+// lanes stride over the chunks, activations loaded with each chunk.
+template <bool AL>
+__global__ __launch_bounds__(256) void gemv2_long_kernel(const int8_t *__restrict__ xq,
+                                                         const int32_t *__restrict__ rowsum,
+                                                         int64_t k, const uint4 *__restrict__ packed,
+                                                         int64_t n, int64_t chunks, Out out,
+                                                         int64_t ldy, int64_t m)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= n) return;
+    for (int64_t t = 0; t < m; ++t) {
+        int lo = 0, hi = 0;
+        for (int64_t c = lane; c < chunks; c += 64) {
+            const uint4 w = load_nt16(packed + row * chunks + c);
+            uint4 xv[4];
+            load_x64<AL>(xq + t * k, k, c, xv);
+            dot_word(w.x, xv[0], lo, hi);
+            dot_word(w.y, xv[1], lo, hi);
+            dot_word(w.z, xv[2], lo, hi);
+            dot_word(w.w, xv[3], lo, hi);
         }
+        const int v = wave_sum_dpp(lo + (hi >> 2));
+        if (lane == 63) store_out(out, ldy, t, row, v, rowsum[t]);
+    }
 }
 
 // ---- base-3 layout --------------------------------------------------------------
@@ -199,46 +276,61 @@ __global__ __launch_bounds__(256) void gemv3_kernel(const int8_t *__restrict__ x
     }
 }
 
-// Lanes per row: the largest group whose last step wastes at most 1/8 of the
-// row's 16-byte chunks (all lanes of a group step together).
-int pick_lanes(int64_t chunks)
+// Launch shape of the 2-bit GEMV for (N, K): waves per block KS (so that each
+// lane holds at most 2 chunks of activations per token), chunks per lane CPL,
+// and steps per block ST (a power of two, about 1792 waves in total).
+struct Gemv2Shape { int ks, cpl, st; int64_t share; };
+
+Gemv2Shape gemv2_shape(int64_t n, int64_t chunks, int mt)
 {
-    const int cands[4] = {64, 32, 16, 8};
-    for (int i = 0; i < 4; ++i) {
-        int lg = cands[i];
-        int64_t waste = ((chunks + lg - 1) / lg) * lg - chunks;
-        if (waste * 8 <= chunks) return lg;
-    }
-    return 8;
+    const int cpl_max = mt <= 2 ? 2 : 1;
+    int ks = (int)((chunks + 64 * cpl_max - 1) / (64 * cpl_max));
+    if (ks > GEMV_KS_MAX) ks = GEMV_KS_MAX;
+    const int64_t share = (chunks + ks - 1) / ks;
+    const int cpl = (int)((share + 63) / 64);
+    int64_t per = n * ks / (GEMV_R * 1792);
+    int st = 1;
+    while (st < 8 && 2 * st <= per) st *= 2;
+    return {ks, cpl, st, share};
 }
 
-template <int MT, int LG, int R>
-hipError_t launch2(bool al, const int8_t *xq, const int32_t *rowsum, int64_t n, int64_t k,
-                   const uint8_t *packed, Out out, int64_t m0, hipStream_t s)
+template <int MT, int CPL, int ST>
+hipError_t launch2_st(bool al, const int8_t *xq, const int32_t *rowsum, int64_t n, int64_t k,
+                      const uint8_t *packed, Out out, int64_t m0, const Gemv2Shape &sh,
+                      hipStream_t s)
 {
     const int64_t chunks = pack2_pitch(k) / 16;
-    const int64_t tasks = (n + R - 1) / R;
-    const int64_t waves = (tasks + (64 / LG) - 1) / (64 / LG);
-    const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+    const int64_t rb = (int64_t)GEMV_R * ST;
+    const dim3 grid((unsigned)((n + rb - 1) / rb)), block((unsigned)(64 * sh.ks));
     if (al)
-        hipLaunchKernelGGL((gemv2_kernel<MT, LG, R, true>), grid, block, 0, s, xq, rowsum, k,
-                           (const uint4 *)packed, n, chunks, out, n, m0);
+        hipLaunchKernelGGL((gemv2_kernel<MT, CPL, ST, true>), grid, block, 0, s, xq, rowsum, k,
+                           (const uint4 *)packed, n, chunks, sh.share, out, n, m0);
     else
-        hipLaunchKernelGGL((gemv2_kernel<MT, LG, R, false>), grid, block, 0, s, xq, rowsum, k,
-                           (const uint4 *)packed, n, chunks, out, n, m0);
+        hipLaunchKernelGGL((gemv2_kernel<MT, CPL, ST, false>), grid, block, 0, s, xq, rowsum, k,
+                           (const uint4 *)packed, n, chunks, sh.share, out, n, m0);
     return hipGetLastError();
 }
 
-template <int MT, int R>
-hipError_t launch2_lg(int lg, bool al, const int8_t *xq, const int32_t *rowsum, int64_t n,
-                      int64_t k, const uint8_t *packed, Out out, int64_t m0, hipStream_t s)
+template <int MT, int CPL>
+hipError_t launch2_cpl(bool al, const int8_t *xq, const int32_t *rowsum, int64_t n, int64_t k,
+                       const uint8_t *packed, Out out, int64_t m0, const Gemv2Shape &sh,
+                       hipStream_t s)
 {
-    switch (lg) {
-    case 64: return launch2<MT, 64, R>(al, xq, rowsum, n, k, packed, out, m0, s);
-    case 32: return launch2<MT, 32, R>(al, xq, rowsum, n, k, packed, out, m0, s);
-    case 16: return launch2<MT, 16, R>(al, xq, rowsum, n, k, packed, out, m0, s);
-    default: return launch2<MT, 8, R>(al, xq, rowsum, n, k, packed, out, m0, s);
+    switch (sh.st) {
+    case 1: return launch2_st<MT, CPL, 1>(al, xq, rowsum, n, k, packed, out, m0, sh, s);
+    case 2: return launch2_st<MT, CPL, 2>(al, xq, rowsum, n, k, packed, out, m0, sh, s);
+    case 4: return launch2_st<MT, CPL, 4>(al, xq, rowsum, n, k, packed, out, m0, sh, s);
+    default: return launch2_st<MT, CPL, 8>(al, xq, rowsum, n, k, packed, out, m0, sh, s);
     }
+}
+
+template <int MT>
+hipError_t launch2(bool al, const int8_t *xq, const int32_t *rowsum, int64_t n, int64_t k,
+                   const uint8_t *packed, Out out, int64_t m0, hipStream_t s)
+{
+    const Gemv2Shape sh = gemv2_shape(n, pack2_pitch(k) / 16, MT);
+    if (sh.cpl == 1) return launch2_cpl<MT, 1>(al, xq, rowsum, n, k, packed, out, m0, sh, s);
+    return launch2_cpl<MT, 2>(al, xq, rowsum, n, k, packed, out, m0, sh, s);
 }
 
 template <int MT>
@@ -262,15 +354,25 @@ hipError_t launch_gemv_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
                              const uint8_t *packed, int64_t n, int64_t k, Out out, hipStream_t s)
 {
     const bool al = (k % 16) == 0;
-    const int lg = pick_lanes(pack2_pitch(k) / 16);
+    const int64_t chunks = pack2_pitch(k) / 16;
+    if (chunks > (int64_t)GEMV_KS_MAX * 128) {
+        const dim3 grid((unsigned)((n + 3) / 4)), block(256);
+        if (al)
+            hipLaunchKernelGGL((gemv2_long_kernel<true>), grid, block, 0, s, xq, rowsum, k,
+                               (const uint4 *)packed, n, chunks, out, n, m);
+        else
+            hipLaunchKernelGGL((gemv2_long_kernel<false>), grid, block, 0, s, xq, rowsum, k,
+                               (const uint4 *)packed, n, chunks, out, n, m);
+        return hipGetLastError();
+    }
     for (int64_t m0 = 0; m0 < m; m0 += 4) {
         const int64_t mt = (m - m0) < 4 ? (m - m0) : 4;
         hipError_t e;
         switch (mt) {
-        case 1: e = launch2_lg<1, 4>(lg, al, xq, rowsum, n, k, packed, out, m0, s); break;
-        case 2: e = launch2_lg<2, 4>(lg, al, xq, rowsum, n, k, packed, out, m0, s); break;
-        case 3: e = launch2_lg<3, 2>(lg, al, xq, rowsum, n, k, packed, out, m0, s); break;
-        default: e = launch2_lg<4, 2>(lg, al, xq, rowsum, n, k, packed, out, m0, s); break;
+        case 1: e = launch2<1>(al, xq, rowsum, n, k, packed, out, m0, s); break;
+        case 2: e = launch2<2>(al, xq, rowsum, n, k, packed, out, m0, s); break;
+        case 3: e = launch2<3>(al, xq, rowsum, n, k, packed, out, m0, s); break;
+        default: e = launch2<4>(al, xq, rowsum, n, k, packed, out, m0, s); break;
         }
         if (e != hipSuccess) return e;
     }

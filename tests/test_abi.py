@@ -77,6 +77,7 @@ def test_quantize_weights_argument_checks(lib):
 def test_quantize_act_argument_checks(lib):
     f = lib.bitlinear_quantize_act
     assert f(NULL, 1, 4, 64, P, P, P, None) == -1
+    assert f(NULL, 1, 0, 64, NULL, NULL, NULL, None) == 0    # empty batch may pass NULL
     assert f(P, 2, 4, 64, P, P, P, None) == -4
     assert f(P, 1, -1, 64, P, P, P, None) == -2
     assert f(P, 1, 4, 0, P, P, P, None) == -2
@@ -102,6 +103,7 @@ def test_forward_argument_checks(lib):
     assert call(pk=ODD) == -3
     assert call(xq=ODD) == -3
     assert call(m=0) == 0 and call(n=0) == 0             # empty products: no launch
+    assert call(m=0, xq=NULL, s=NULL, r=NULL, y=NULL) == 0   # ... and may pass NULL
     g = lib.bitlinear_matmul_i32
     assert g(P, P, 4, P, 0, 8, 64, NULL, NULL, 0, 0, None) == -1
     assert g(P, P, 0, P, 0, 8, 64, P, NULL, 0, 0, None) == 0
