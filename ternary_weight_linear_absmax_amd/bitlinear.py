@@ -121,6 +121,21 @@ def forward_path(m: int, n: int, k: int, layout: int = BL_PACK2) -> int:
 
 # ---- device calls -------------------------------------------------------------------
 
+_workspaces = {}
+
+
+def _zero_workspace(nbytes: int, device):
+    """A per-device zero-initialised workspace, grown on demand and reused (the
+    library leaves it all-zero after every call).  Calls on different streams
+    that share it must not overlap; pass your own workspace for that."""
+    key = torch.device(device)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros((nbytes,), dtype=torch.uint8, device=key)
+        _workspaces[key] = ws
+    return ws
+
+
 def quantize_weights(w: torch.Tensor, layout: int = BL_PACK2, stream=None):
     """w [N, K] (float32/bfloat16, on the GPU) -> (packed uint8 [N, row_bytes], gamma float32 [1])."""
     lib = load()
@@ -159,7 +174,7 @@ def forward(xq, scale, rowsum, packed, gamma, n: int, k: int, layout: int = BL_P
         y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
     ws_bytes = forward_workspace_bytes(m, n, k, layout)
     if workspace is None and ws_bytes > 0:
-        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=xq.device)
+        workspace = _zero_workspace(ws_bytes, xq.device)
     _check(lib.bitlinear_forward_ex(_ptr(xq), _ptr(scale), _ptr(rowsum), m, _ptr(packed), layout,
                                     _ptr(gamma), n, k, _ptr(y), _ptr(workspace),
                                     0 if workspace is None else workspace.numel(), path,
@@ -177,7 +192,7 @@ def matmul_i32(xq, rowsum, packed, n: int, k: int, layout: int = BL_PACK2,
         acc = torch.empty((m, n), dtype=torch.int32, device=xq.device)
     ws_bytes = forward_workspace_bytes(m, n, k, layout)
     if workspace is None and ws_bytes > 0:
-        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=xq.device)
+        workspace = _zero_workspace(ws_bytes, xq.device)
     _check(lib.bitlinear_matmul_i32(_ptr(xq), _ptr(rowsum), m, _ptr(packed), layout, n, k,
                                     _ptr(acc), _ptr(workspace),
                                     0 if workspace is None else workspace.numel(), path,

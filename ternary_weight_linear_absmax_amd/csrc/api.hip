@@ -27,7 +27,6 @@ int run_product(const int8_t *xq, const float *scale, const int32_t *rowsum, int
                 float *y, int32_t *acc, void *workspace, int64_t workspace_bytes, int path,
                 hipStream_t stream)
 {
-    (void)workspace;
     if (!good_layout(layout)) return BL_ERR_LAYOUT;
     if (path != BL_PATH_AUTO && path != BL_PATH_GEMV && path != BL_PATH_MFMA) return BL_ERR_PATH;
     if (m < 0 || n < 0 || !good_k(k)) return BL_ERR_SHAPE;
@@ -42,8 +41,9 @@ int run_product(const int8_t *xq, const float *scale, const int32_t *rowsum, int
     if (!al16(xq) || !al16(packed) || !al4(rowsum)) return BL_ERR_ALIGN;
     if (y && (!al4(y) || !al4(scale) || !al4(gamma))) return BL_ERR_ALIGN;
     if (acc && !al4(acc)) return BL_ERR_ALIGN;
-    if (workspace_bytes < bitlinear_forward_workspace_bytes(m, n, k, layout))
-        return BL_ERR_WORKSPACE;
+    const int64_t need = path == BL_PATH_MFMA ? bl::gemm_workspace_bytes(m, n, k) : 0;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return BL_ERR_WORKSPACE;
+    if (need > 0 && !al16(workspace)) return BL_ERR_ALIGN;
 
     bl::Out out{scale, gamma, y, acc};
     hipError_t e;
@@ -52,7 +52,7 @@ int run_product(const int8_t *xq, const float *scale, const int32_t *rowsum, int
     else if (path == BL_PATH_GEMV)
         e = bl::launch_gemv_pack2(xq, rowsum, m, packed, n, k, out, stream);
     else
-        e = bl::launch_gemm_pack2(xq, rowsum, m, packed, n, k, out, stream);
+        e = bl::launch_gemm_pack2(xq, rowsum, m, packed, n, k, out, workspace, stream);
     return hip_status(e);
 }
 
@@ -80,8 +80,10 @@ int64_t bitlinear_quantize_weights_workspace_bytes(int64_t N, int64_t K)
 
 int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int layout)
 {
-    (void)M; (void)N; (void)K; (void)layout;
-    return 0;
+    if (M < 1 || N < 1 || !good_k(K) || !good_layout(layout)) return 0;
+    if (layout == BL_PACK3) return 0;
+    // the largest need over the paths the caller may force
+    return bl::gemm_workspace_bytes(M, N, K);
 }
 
 int bitlinear_forward_path(int64_t M, int64_t N, int64_t K, int layout)

@@ -20,10 +20,21 @@
 // The B operand carries the codes t + 1; the epilogue subtracts the token's
 // row sum of q (exact integer arithmetic), then rescales by gamma / s.
 //
-// Block tile: 128 tokens x 128 weight rows, k in steps of 128; four waves in a
-// 2 x 2 arrangement, each owning a 64 x 64 output tile (2 x 2 MFMA tiles).
-// The k loop is double-buffered: the next stage's global loads are issued
-// before the current stage's MFMAs.
+// Block: four waves in a 2 x 2 arrangement, each owning a (32 WM) x (32 WN)
+// output tile, so the block tile is (64 WM) x (64 WN); k advances in stages of
+// 128.  Activations go through a two-slot register ring (loads issued two
+// stages ahead) into a double-buffered, padded LDS tile; packed weights go
+// into a four-slot register ring (loads issued three stages ahead).  Within
+// the loop every address is a per-lane offset fixed at the start plus a
+// uniform stage offset, so the stage costs no address arithmetic.  Blocks are numbered so that consecutive tiles (which share weight
+// columns) land on the same XCD and its L2.
+//
+// Split-K (S > 1 slices of the k range) adds int32 partial tiles into a
+// workspace with device-scope atomics; a second kernel applies the epilogue
+// and clears the workspace again, so it stays all-zero between calls.  Integer
+// addition makes the result independent of the order of the slices.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace bl {
@@ -32,27 +43,34 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 128;
+constexpr int BK = 128;
 constexpr int LDA = BK + 16;            // padded LDS row (bytes)
+constexpr int NXCD = 8;
 
 __device__ inline uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
-// Global -> register load of this thread's four 16-byte pieces of the A tile.
-template <bool AL>
+// Global -> register load of this thread's pieces of the [BM x BK] A tile.
+// AL (K a multiple of 16): every load is issued unconditionally from a clamped,
+// in-bounds address; pieces past K are zeroed later, when the tile is written
+// to LDS, so no wait is forced here.  Rows past M carry duplicate data whose
+// outputs are never stored.  !AL: byte-wise loads with bounds checks.
+template <int BM, bool AL>
 __device__ inline void load_a(const int8_t *__restrict__ xq, int64_t m, int64_t k, int64_t m0,
-                              int64_t k0, uint4 regs[4])
+                              int64_t k0, uint4 (&regs)[BM / 32], int tid)
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = threadIdx.x + 256 * i;
+    for (int i = 0; i < BM / 32; ++i) {
+        const int e = tid + 256 * i;
         const int row = e >> 3, col = (e & 7) * 16;
-        const int64_t gm = m0 + row, gk = k0 + col;
-        uint4 v = zero4();
-        if (gm < m) {
-            const int8_t *p = xq + gm * k + gk;
-            if (AL) {
-                if (gk < k) v = *(const uint4 *)p;
-            } else {
+        int64_t gm = m0 + row, gk = k0 + col;
+        if (AL) {
+            gm = gm < m ? gm : m - 1;
+            gk = gk < k ? gk : k - 16;
+            regs[i] = load16(xq + gm * k + gk);
+        } else {
+            uint4 v = zero4();
+            if (gm < m) {
+                const int8_t *p = xq + gm * k + gk;
                 uint32_t wds[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -64,28 +82,38 @@ __device__ inline void load_a(const int8_t *__restrict__ xq, int64_t m, int64_t 
                 }
                 v = make_uint4(wds[0], wds[1], wds[2], wds[3]);
             }
+            regs[i] = v;
         }
-        regs[i] = v;
     }
 }
 
-__device__ inline void store_a(uint8_t *lds, const uint4 regs[4])
+// Register -> LDS store of the A tile for the stage at k0 (pieces past K
+// zeroed).
+template <int BM, bool AL>
+__device__ inline void store_a(uint8_t *lds, const uint4 (&regs)[BM / 32], int64_t k0, int64_t k,
+                               int tid)
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = threadIdx.x + 256 * i;
+    for (int i = 0; i < BM / 32; ++i) {
+        const int e = tid + 256 * i;
         const int row = e >> 3, col = (e & 7) * 16;
-        *(uint4 *)(lds + row * LDA + col) = regs[i];
+        uint4 v = regs[i];
+        if (AL && k0 + col >= k) v = zero4();
+        *(uint4 *)(lds + row * LDA + col) = v;
     }
 }
 
-// This lane's 16 packed bytes (64 trits) of weight row n for the stage at k0.
+// This lane's 16 packed bytes (64 trits) of weight row nrow for the stage at
+// k0: bytes k0/4 + 16h .. +15.  The address is clamped into the matrix, so the
+// load is unconditional: rows past N only feed outputs that are not stored,
+// and bytes past the row meet activations that are zero there.
 __device__ inline uint4 load_b(const uint8_t *__restrict__ packed, int64_t pitch, int64_t n,
                                int64_t nrow, int64_t k0, int h)
 {
-    const int64_t byte = (k0 / 4) + 16 * h;   // 4 trits per byte
-    if (nrow >= n || byte >= pitch) return zero4();
-    return load_nt16(packed + nrow * pitch + byte);
+    int64_t byte = (k0 / 4) + 16 * h;
+    byte = byte < pitch ? byte : pitch - 16;
+    const int64_t row = nrow < n ? nrow : n - 1;
+    return load_nt16(packed + row * pitch + byte);
 }
 
 __device__ inline v4i unpack_word(uint32_t w)
@@ -103,107 +131,365 @@ __device__ inline uint32_t word_of(const uint4 &v, int p)
     return p == 0 ? v.x : p == 1 ? v.y : p == 2 ? v.z : v.w;
 }
 
-template <bool AL>
+// Fast-path stage loads: a per-lane offset fixed for the whole k loop plus a
+// uniform stage offset (stage index clamped to the last full stage).
+template <int BM>
+__device__ __forceinline__ void ld_a(uint4 (&r)[BM / 32], const int8_t *abase,
+                                     const uint32_t (&aoff)[BM / 32], int kt, int nfull)
+{
+    const int8_t *p = abase + (int64_t)(kt < nfull ? kt : nfull - 1) * BK;
+#pragma unroll
+    for (int i = 0; i < BM / 32; ++i) r[i] = load16(p + aoff[i]);
+}
+
+template <int WN>
+__device__ __forceinline__ void ld_b(uint4 (&r)[WN], const uint8_t *bbase,
+                                     const uint32_t (&boff)[WN], int kt, int nfull)
+{
+    const uint8_t *p = bbase + (int64_t)(kt < nfull ? kt : nfull - 1) * (BK / 4);
+#pragma unroll
+    for (int s = 0; s < WN; ++s) r[s] = load_nt16(p + boff[s]);
+}
+
+template <int BM>
+__device__ __forceinline__ void st_a(uint8_t *lds_buf, const uint4 (&r)[BM / 32], int tid)
+{
+#pragma unroll
+    for (int i = 0; i < BM / 32; ++i) {
+        const int e = tid + 256 * i;
+        *(uint4 *)(lds_buf + (e >> 3) * LDA + (e & 7) * 16) = r[i];
+    }
+}
+
+// Tile of block b: consecutive tile ids on one XCD (blocks b, b+8, ... share an
+// XCD); tiles are numbered m-fastest so neighbours share weight columns.
+__device__ inline int64_t tile_of_block(int64_t b, int64_t q)
+{
+    return (b % NXCD) * q + b / NXCD;
+}
+
+template <int WM, int WN, bool AL>
 __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ xq,
                                                     const int32_t *__restrict__ rowsum,
                                                     int64_t m, int64_t k,
                                                     const uint8_t *__restrict__ packed, int64_t n,
-                                                    int64_t pitch, int tiles_m, Out out)
+                                                    int64_t pitch, int tiles_m, int64_t tiles,
+                                                    int64_t per_xcd, int splits, int stages_per,
+                                                    Out out, int64_t ldy, int32_t *__restrict__ ws)
 {
+    constexpr int BM = 64 * WM, BN = 64 * WN;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM * LDA];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t t = tile_of_block(blockIdx.x, per_xcd);
+    if (t >= tiles * splits) return;
+    const int64_t tile = t / splits;
+    const int split = (int)(t % splits);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
     const int h = lane >> 5, l32 = lane & 31;
-    const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-    const int nk = (int)((k + BK - 1) / BK);
+    const int tm = (int)(tile % tiles_m);
+    const int64_t tn = tile / tiles_m;
+    const int64_t m0 = (int64_t)tm * BM, n0 = tn * BN;
+    const int nk_total = (int)((k + BK - 1) / BK);
+    const int kt0 = split * stages_per;
+    const int kt1 = kt0 + stages_per < nk_total ? kt0 + stages_per : nk_total;
+    const int nk = kt1 - kt0;
 
-    v16i acc[2][2];
+    v16i acc[WM][WN];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < WM; ++a)
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < WN; ++s)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][s][r] = 0;
 
-    const int64_t nrow[2] = {n0 + wn * 64 + l32, n0 + wn * 64 + 32 + l32};
+    int64_t nrow[WN];
+#pragma unroll
+    for (int s = 0; s < WN; ++s) nrow[s] = n0 + wn * 32 * WN + 32 * s + l32;
 
-    uint4 areg[4];
-    uint4 breg[2], bnext[2];
-    load_a<AL>(xq, m, k, m0, 0, areg);
-    store_a(lds[0], areg);
-    breg[0] = load_b(packed, pitch, n, nrow[0], 0, h);
-    breg[1] = load_b(packed, pitch, n, nrow[1], 0, h);
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            const int64_t k1 = (int64_t)(kt + 1) * BK;
-            load_a<AL>(xq, m, k, m0, k1, areg);
-            bnext[0] = load_b(packed, pitch, n, nrow[0], k1, h);
-            bnext[1] = load_b(packed, pitch, n, nrow[1], k1, h);
-        }
-        const uint8_t *la = lds[cur];
+    // This wave's A fragments of one stage: 4 k-steps x WM row blocks.
+    auto read_frags = [&](v4i (&af)[4][WM], const uint8_t *la) __attribute__((always_inline)) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int a = 0; a < WM; ++a) {
+                const int row = wm * 32 * WM + 32 * a + l32;
+                const uint4 v = load16(la + row * LDA + 64 * h + 16 * p);
+                af[p][a] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+            }
+    };
+    // The MFMAs of one stage: A fragments from registers, B unpacked from
+    // this lane's packed weight words.
+    auto mma = [&](const v4i (&af)[4][WM], const uint4 (&bw)[WN]) __attribute__((always_inline)) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            v4i af[2], bf[2];
+            v4i bf[WN];
 #pragma unroll
-            for (int a = 0; a < 2; ++a) {
-                const int row = wm * 64 + 32 * a + l32;
-                uint4 v = *(const uint4 *)(la + row * LDA + 64 * h + 16 * p);
-                af[a] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-            }
+            for (int s = 0; s < WN; ++s) bf[s] = unpack_word(word_of(bw[s], p));
 #pragma unroll
-            for (int s = 0; s < 2; ++s) bf[s] = unpack_word(word_of(breg[s], p));
+            for (int a = 0; a < WM; ++a)
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    acc[a][s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bf[s], acc[a][s], 0,
-                                                                      0, 0);
+                for (int s = 0; s < WN; ++s)
+                    acc[a][s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[p][a], bf[s], acc[a][s],
+                                                                      0, 0, 0);
         }
-        if (more) store_a(lds[cur ^ 1], areg);
+    };
+
+    // Full stages (k0 + 128 <= K) of this slice run through the pipelined
+    // loop; a final partial stage, and every stage when K is not a multiple
+    // of 16, take the bounds-checked path below.
+    int nfull = 0;
+    if (AL) {
+        const int64_t full_total = k / BK;
+        nfull = (int)(kt1 <= full_total ? nk : (full_total > kt0 ? full_total - kt0 : 0));
+    }
+    if (nfull > 0) {
+        // Per-lane byte offsets, fixed for the whole k loop (rows clamped into
+        // the matrix); a stage only adds a uniform offset.
+        uint32_t aoff[BM / 32];
+#pragma unroll
+        for (int i = 0; i < BM / 32; ++i) {
+            const int e = tid + 256 * i;
+            int64_t gm = m0 + (e >> 3);
+            gm = gm < m ? gm : m - 1;
+            aoff[i] = (uint32_t)(gm * k + (e & 7) * 16);
+        }
+        uint32_t boff[WN];
+#pragma unroll
+        for (int s = 0; s < WN; ++s) {
+            const int64_t row = nrow[s] < n ? nrow[s] : n - 1;
+            boff[s] = (uint32_t)(row * pitch + 16 * h);
+        }
+        const int8_t *abase = xq + (int64_t)kt0 * BK;
+        const uint8_t *bbase = packed + (int64_t)kt0 * (BK / 4);
+        // Pipeline of stage j (all rings indexed by j mod ring size, fixed at
+        // compile time by the unrolled stage index J):
+        //   packed weights: loaded at stage j - 3 into a 4-slot register ring;
+        //   activations:    loaded at stage j - 4 into a 2-slot register ring,
+        //                   written to LDS buffer j mod 2 at stage j - 2;
+        //   A fragments:    read from LDS at stage j - 1 into a 2-slot ring.
+        // So a stage issues its loads, reads the next stage's fragments, runs
+        // its MFMAs from registers, writes a later stage's activations, and
+        // ends with one barrier; no LDS latency sits in front of the MFMAs.
+        // Loads are unconditional (stage index clamped to the last full
+        // stage), so the control flow is straight and the compiler counts
+        // outstanding loads exactly.
+        constexpr int NB = 4;
+        uint4 areg[2][BM / 32];
+        uint4 breg[NB][WN];
+        v4i af[2][4][WM];
+#pragma unroll
+        for (int j = 0; j < NB - 1; ++j) ld_b<WN>(breg[j], bbase, boff, j, nfull);
+        ld_a<BM>(areg[0], abase, aoff, 0, nfull);
+        ld_a<BM>(areg[1], abase, aoff, 1, nfull);
+        st_a<BM>(lds[0], areg[0], tid);
+        st_a<BM>(lds[1], areg[1], tid);
+        ld_a<BM>(areg[0], abase, aoff, 2, nfull);
+        ld_a<BM>(areg[1], abase, aoff, 3, nfull);
         __syncthreads();
-        if (more) {
-            breg[0] = bnext[0];
-            breg[1] = bnext[1];
+        read_frags(af[0], lds[0]);
+        __syncthreads();   // buffer 0 is rewritten in stage 0
+
+        auto stage = [&](auto jc, int j) __attribute__((always_inline)) {
+            constexpr int J = decltype(jc)::value;
+            constexpr int C = J & 1;
+            // sched_barrier keeps the compiler from moving MFMAs across the
+            // phases (and the barrier), which would put LDS waits back in
+            // front of them.
+            ld_b<WN>(breg[(J + NB - 1) % NB], bbase, boff, j + NB - 1, nfull);
+            read_frags(af[C ^ 1], lds[C ^ 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(af[C], breg[J % NB]);
+            __builtin_amdgcn_sched_barrier(0);
+            st_a<BM>(lds[C], areg[C], tid);
+            ld_a<BM>(areg[C], abase, aoff, j + 4, nfull);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        const int n4 = nfull & ~3;
+        for (int j = 0; j < n4; j += 4) {
+            stage(std::integral_constant<int, 0>{}, j);
+            stage(std::integral_constant<int, 1>{}, j + 1);
+            stage(std::integral_constant<int, 2>{}, j + 2);
+            stage(std::integral_constant<int, 3>{}, j + 3);
         }
+        if (n4 < nfull) stage(std::integral_constant<int, 0>{}, n4);
+        if (n4 + 1 < nfull) stage(std::integral_constant<int, 1>{}, n4 + 1);
+        if (n4 + 2 < nfull) stage(std::integral_constant<int, 2>{}, n4 + 2);
+    }
+    // Bounds-checked stages: the partial last stage, or all stages when K is
+    // not a multiple of 16.  Loads are masked per piece; not pipelined.
+    for (int kt = nfull; kt < nk; ++kt) {
+        const int64_t k0 = (int64_t)(kt0 + kt) * BK;
+        uint4 r[BM / 32];
+        uint4 bw[WN];
+        load_a<BM, AL>(xq, m, k, m0, k0, r, tid);
+#pragma unroll
+        for (int s = 0; s < WN; ++s) bw[s] = load_b(packed, pitch, n, nrow[s], k0, h);
+        __syncthreads();
+        store_a<BM, AL>(lds[0], r, k0, k, tid);
+        __syncthreads();
+        v4i af[4][WM];
+        read_frags(af, lds[0]);
+        mma(af, bw);
     }
 
+    // Epilogue.  Per-row operands are loaded for all of this lane's rows first
+    // (clamped indices, unconditional), then the stores are predicated.
+    if (splits > 1) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+        for (int a = 0; a < WM; ++a)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t gm = m0 + wm * 32 * WM + 32 * a + 8 * (r / 4) + 4 * h + (r % 4);
+#pragma unroll
+                for (int s = 0; s < WN; ++s)
+                    if (gm < m && nrow[s] < n) atomicAdd(ws + gm * n + nrow[s], acc[a][s][r]);
+            }
+        return;
+    }
+    const float gamma = out.acc ? 0.0f : out.gamma[0];
+#pragma unroll
+    for (int a = 0; a < WM; ++a) {
+        int32_t rs[16];
+        float gs[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int64_t gm = m0 + wm * 64 + 32 * a + 8 * (r / 4) + 4 * h + (r % 4);
-            if (gm >= m) continue;
-            const int32_t rs = rowsum[gm];
+            int64_t gm = m0 + wm * 32 * WM + 32 * a + 8 * (r / 4) + 4 * h + (r % 4);
+            gm = gm < m ? gm : m - 1;
+            rs[r] = rowsum[gm];
+            gs[r] = out.acc ? 0.0f : gamma / out.scale[gm];
+        }
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int64_t gn = nrow[s];
-                if (gn < n) store_out(out, n, gm, gn, acc[a][s][r], rs);
+        for (int r = 0; r < 16; ++r) {
+            const int64_t gm = m0 + wm * 32 * WM + 32 * a + 8 * (r / 4) + 4 * h + (r % 4);
+#pragma unroll
+            for (int s = 0; s < WN; ++s) {
+                if (gm >= m || nrow[s] >= n) continue;
+                const int32_t v = acc[a][s][r] - rs[r];
+                if (out.acc)
+                    out.acc[gm * ldy + nrow[s]] = v;
+                else
+                    out.y[gm * ldy + nrow[s]] = (float)v * gs[r];
             }
         }
     }
 }
 
+// Split-K epilogue: y (or acc) from the summed codes in the workspace, which
+// is cleared again for the next call.
+__global__ __launch_bounds__(256) void splitk_finish_kernel(int32_t *__restrict__ ws,
+                                                            const int32_t *__restrict__ rowsum,
+                                                            int64_t m, int64_t n, Out out,
+                                                            int64_t ldy)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= m * n) return;
+    const int64_t gm = i / n, gn = i % n;
+    const int32_t v = ws[i];
+    ws[i] = 0;
+    store_out(out, ldy, gm, gn, v, rowsum[gm]);
+}
+
 }  // namespace
 
-hipError_t launch_gemm_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
-                             const uint8_t *packed, int64_t n, int64_t k, Out out, hipStream_t s)
+// Kernel configuration of the GEMM for (M, N, K).
+struct GemmCfg { int wm, wn, splits; };
+
+GemmCfg gemm_config(int64_t m, int64_t n, int64_t k)
 {
+    // Prefer the largest block tile that still gives every CU a tile; split
+    // the k range when even the smallest tiles leave CUs idle.
+    const int64_t cus = 256;
+    const int cand[4][2] = {{2, 2}, {1, 2}, {2, 1}, {1, 1}};
+    for (int i = 0; i < 4; ++i) {
+        const int64_t bm = 64 * cand[i][0], bn = 64 * cand[i][1];
+        const int64_t tiles = ((m + bm - 1) / bm) * ((n + bn - 1) / bn);
+        if (tiles >= cus * 3 / 4) return {cand[i][0], cand[i][1], 1};
+    }
+    const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
+    const int64_t nk = (k + BK - 1) / BK;
+    int64_t s = (cus + tiles - 1) / tiles;
+    if (s > nk) s = nk;
+    if (s > 8) s = 8;
+    return {2, 2, (int)(s < 1 ? 1 : s)};
+}
+
+int64_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k)
+{
+    const GemmCfg c = gemm_config(m, n, k);
+    return c.splits > 1 ? 4 * m * n : 0;
+}
+
+template <int WM, int WN>
+hipError_t launch_gemm_cfg(const int8_t *xq, const int32_t *rowsum, int64_t m,
+                           const uint8_t *packed, int64_t n, int64_t k, Out out, int splits,
+                           int32_t *ws, hipStream_t s, int64_t ldy = -1)
+{
+    constexpr int BM = 64 * WM, BN = 64 * WN;
     const int tiles_m = (int)((m + BM - 1) / BM);
-    const int64_t tiles_n = (n + BN - 1) / BN;
-    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(256);
+    const int64_t tiles = (int64_t)tiles_m * ((n + BN - 1) / BN);
+    const int64_t nk = (k + BK - 1) / BK;
+    const int stages_per = (int)((nk + splits - 1) / splits);
+    const int64_t units = tiles * splits;
+    const int64_t per_xcd = (units + NXCD - 1) / NXCD;
+    const dim3 grid((unsigned)(per_xcd * NXCD)), block(256);
     const int64_t pitch = pack2_pitch(k);
+    if (ldy < 0) ldy = n;
     if (k % 16 == 0)
-        hipLaunchKernelGGL((gemm2_kernel<true>), grid, block, 0, s, xq, rowsum, m, k, packed, n,
-                           pitch, tiles_m, out);
+        hipLaunchKernelGGL((gemm2_kernel<WM, WN, true>), grid, block, 0, s, xq, rowsum, m, k,
+                           packed, n, pitch, tiles_m, tiles, per_xcd, splits, stages_per, out, ldy,
+                           ws);
     else
-        hipLaunchKernelGGL((gemm2_kernel<false>), grid, block, 0, s, xq, rowsum, m, k, packed, n,
-                           pitch, tiles_m, out);
+        hipLaunchKernelGGL((gemm2_kernel<WM, WN, false>), grid, block, 0, s, xq, rowsum, m, k,
+                           packed, n, pitch, tiles_m, tiles, per_xcd, splits, stages_per, out, ldy,
+                           ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    const int64_t total = m * n;
+    hipLaunchKernelGGL(splitk_finish_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                       s, ws, rowsum, m, n, out, ldy);
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
+                             const uint8_t *packed, int64_t n, int64_t k, Out out, void *ws,
+                             hipStream_t s)
+{
+    // The kernel addresses each operand with 32-bit per-lane offsets: larger
+    // operands are processed in blocks of rows of x and of weight rows.
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t pitch = pack2_pitch(k);
+    int64_t mc = m, nc = n;
+    if (mc * k >= lim) mc = ((lim - 1) / k) / 128 * 128;
+    if (nc * pitch >= lim) nc = ((lim - 1) / pitch) / 128 * 128;
+    if (mc < 1) mc = 1;
+    if (nc < 1) nc = 1;
+    for (int64_t m0 = 0; m0 < m; m0 += mc) {
+        for (int64_t n0 = 0; n0 < n; n0 += nc) {
+            const int64_t mb = m - m0 < mc ? m - m0 : mc;
+            const int64_t nb = n - n0 < nc ? n - n0 : nc;
+            Out o = out;
+            if (o.scale) o.scale += m0;
+            if (o.y) o.y += m0 * n + n0;
+            if (o.acc) o.acc += m0 * n + n0;
+            const GemmCfg c = gemm_config(mb, nb, k);
+            int32_t *w = (int32_t *)ws;
+            const int8_t *x = xq + m0 * k;
+            const int32_t *rs = rowsum + m0;
+            const uint8_t *pk = packed + n0 * pitch;
+            hipError_t e;
+            if (c.wm == 2 && c.wn == 2)
+                e = launch_gemm_cfg<2, 2>(x, rs, mb, pk, nb, k, o, c.splits, w, s, n);
+            else if (c.wm == 1 && c.wn == 2)
+                e = launch_gemm_cfg<1, 2>(x, rs, mb, pk, nb, k, o, c.splits, w, s, n);
+            else if (c.wm == 2 && c.wn == 1)
+                e = launch_gemm_cfg<2, 1>(x, rs, mb, pk, nb, k, o, c.splits, w, s, n);
+            else
+                e = launch_gemm_cfg<1, 1>(x, rs, mb, pk, nb, k, o, c.splits, w, s, n);
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
 }
 
 }  // namespace bl

@@ -47,16 +47,26 @@ hipError_t launch_gemv_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
 hipError_t launch_gemv_pack3(const int8_t *xq, const int32_t *rowsum, int64_t m,
                              const uint8_t *packed, int64_t n, int64_t k, Out out,
                              hipStream_t s);
-// 2-bit layout, int8 matrix-core kernel.
+// 2-bit layout, int8 matrix-core kernel.  ws: gemm_workspace_bytes(m, n, k)
+// bytes, all-zero on entry and left all-zero (used only when k is split).
 hipError_t launch_gemm_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
-                             const uint8_t *packed, int64_t n, int64_t k, Out out,
+                             const uint8_t *packed, int64_t n, int64_t k, Out out, void *ws,
                              hipStream_t s);
+int64_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 // 128-bit streaming load (the packed weights are read once per call).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ inline uint4 load_nt16(const void *p)
 {
     u32x4 v = __builtin_nontemporal_load((const u32x4 *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Plain 128-bit load through a native vector type (assigning a uint4 struct
+// straight from memory can become a memcpy that keeps arrays out of registers).
+__device__ inline uint4 load16(const void *p)
+{
+    const u32x4 v = *(const u32x4 *)p;
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
