@@ -21,7 +21,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "bitlinear.h")
 BL_OK = 0
 BL_F32, BL_BF16 = 0, 1
 BL_PACK2, BL_PACK3 = 0, 1
-BL_PATH_AUTO, BL_PATH_GEMV, BL_PATH_MFMA = 0, 1, 2
+BL_PATH_AUTO, BL_PATH_GEMV, BL_PATH_MFMA, BL_PATH_SKINNY = 0, 1, 2, 3
 MAX_K = 1 << 20
 
 _lib = None

@@ -15,9 +15,13 @@ inline bool good_k(int64_t k) { return k >= 1 && k <= BITLINEAR_MAX_K; }
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
 
-int choose_path(int64_t m, int layout)
+// M = 1, 2: the vector kernel reads each weight word once per pass of up to
+// four tokens and is the fastest; 3..16 tokens: the weight-streaming matrix-core
+// kernel (one pass over the weights for all tokens); more: the tiled GEMM.
+int choose_path(int64_t m, int64_t n, int64_t k, int layout)
 {
-    if (layout == BL_PACK3) return BL_PATH_GEMV;
+    if (layout == BL_PACK3 || m <= 2) return BL_PATH_GEMV;
+    if (bl::skinny_supported(m, n, k)) return BL_PATH_SKINNY;
     return m <= 4 ? BL_PATH_GEMV : BL_PATH_MFMA;
 }
 
@@ -28,13 +32,17 @@ int run_product(const int8_t *xq, const float *scale, const int32_t *rowsum, int
                 hipStream_t stream)
 {
     if (!good_layout(layout)) return BL_ERR_LAYOUT;
-    if (path != BL_PATH_AUTO && path != BL_PATH_GEMV && path != BL_PATH_MFMA) return BL_ERR_PATH;
+    if (path != BL_PATH_AUTO && path != BL_PATH_GEMV && path != BL_PATH_MFMA &&
+        path != BL_PATH_SKINNY)
+        return BL_ERR_PATH;
     if (m < 0 || n < 0 || !good_k(k)) return BL_ERR_SHAPE;
     if (m > 0 && k > kMaxElems / m) return BL_ERR_SHAPE;
     if (n > 0 && k > kMaxElems / n) return BL_ERR_SHAPE;
     if (m > 0 && n > kMaxElems / m) return BL_ERR_SHAPE;
-    if (path == BL_PATH_AUTO) path = choose_path(m, layout);
-    if (layout == BL_PACK3 && path == BL_PATH_MFMA) return BL_ERR_PATH;
+    if (path == BL_PATH_AUTO) path = choose_path(m, n, k, layout);
+    if (layout == BL_PACK3 && path != BL_PATH_GEMV) return BL_ERR_PATH;
+    if (path == BL_PATH_SKINNY && m > 0 && n > 0 && !bl::skinny_supported(m, n, k))
+        return BL_ERR_PATH;
     if (m == 0 || n == 0) return BL_OK;    // empty product: buffers may be NULL
     if (!xq || !rowsum || !packed || (!y && !acc)) return BL_ERR_NULL;
     if (y && (!scale || !gamma)) return BL_ERR_NULL;
@@ -51,6 +59,8 @@ int run_product(const int8_t *xq, const float *scale, const int32_t *rowsum, int
         e = bl::launch_gemv_pack3(xq, rowsum, m, packed, n, k, out, stream);
     else if (path == BL_PATH_GEMV)
         e = bl::launch_gemv_pack2(xq, rowsum, m, packed, n, k, out, stream);
+    else if (path == BL_PATH_SKINNY)
+        e = bl::launch_skinny_pack2(xq, rowsum, m, packed, n, k, out, stream);
     else
         e = bl::launch_gemm_pack2(xq, rowsum, m, packed, n, k, out, workspace, stream);
     return hip_status(e);
@@ -88,8 +98,7 @@ int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int l
 
 int bitlinear_forward_path(int64_t M, int64_t N, int64_t K, int layout)
 {
-    (void)N; (void)K;
-    return choose_path(M, layout);
+    return choose_path(M, N, K, layout);
 }
 
 const char *bitlinear_status_string(int status)

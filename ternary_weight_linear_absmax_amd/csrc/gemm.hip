@@ -34,6 +34,7 @@
 // and clears the workspace again, so it stays all-zero between calls.  Integer
 // addition makes the result independent of the order of the slices.
 #include <type_traits>
+#include <utility>
 
 #include "internal.h"
 
@@ -161,6 +162,33 @@ __device__ __forceinline__ void st_a(uint8_t *lds_buf, const uint4 (&r)[BM / 32]
     }
 }
 
+#ifndef GEMM_NA
+#define GEMM_NA 2
+#endif
+#ifndef GEMM_NB
+#define GEMM_NB 4
+#endif
+
+constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
+// Stages after which every register/LDS ring is back at slot 0.
+constexpr int ring_period(int na, int nb)
+{
+    const int l = 2 * na / gcd_int(2, na);
+    return l * nb / gcd_int(l, nb);
+}
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), unrolled.
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Tile of block b: consecutive tile ids on one XCD (blocks b, b+8, ... share an
 // XCD); tiles are numbered m-fastest so neighbours share weight columns.
 __device__ inline int64_t tile_of_block(int64_t b, int64_t q)
@@ -168,7 +196,7 @@ __device__ inline int64_t tile_of_block(int64_t b, int64_t q)
     return (b % NXCD) * q + b / NXCD;
 }
 
-template <int WM, int WN, bool AL>
+template <int WM, int WN, bool AL, int NA = GEMM_NA, int NB = GEMM_NB>
 __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ xq,
                                                     const int32_t *__restrict__ rowsum,
                                                     int64_t m, int64_t k,
@@ -263,9 +291,10 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
         const uint8_t *bbase = packed + (int64_t)kt0 * (BK / 4);
         // Pipeline of stage j (all rings indexed by j mod ring size, fixed at
         // compile time by the unrolled stage index J):
-        //   packed weights: loaded at stage j - 3 into a 4-slot register ring;
-        //   activations:    loaded at stage j - 4 into a 2-slot register ring,
-        //                   written to LDS buffer j mod 2 at stage j - 2;
+        //   packed weights: loaded at stage j - (NB - 1) into an NB-slot
+        //                   register ring;
+        //   activations:    loaded at stage j - 2 - NA into an NA-slot register
+        //                   ring, written to LDS buffer j mod 2 at stage j - 2;
         //   A fragments:    read from LDS at stage j - 1 into a 2-slot ring.
         // So a stage issues its loads, reads the next stage's fragments, runs
         // its MFMAs from registers, writes a later stage's activations, and
@@ -273,8 +302,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
         // Loads are unconditional (stage index clamped to the last full
         // stage), so the control flow is straight and the compiler counts
         // outstanding loads exactly.
-        constexpr int NB = 4;
-        uint4 areg[2][BM / 32];
+        uint4 areg[NA][BM / 32];
         uint4 breg[NB][WN];
         v4i af[2][4][WM];
 #pragma unroll
@@ -283,8 +311,8 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
         ld_a<BM>(areg[1], abase, aoff, 1, nfull);
         st_a<BM>(lds[0], areg[0], tid);
         st_a<BM>(lds[1], areg[1], tid);
-        ld_a<BM>(areg[0], abase, aoff, 2, nfull);
-        ld_a<BM>(areg[1], abase, aoff, 3, nfull);
+#pragma unroll
+        for (int j = 0; j < NA; ++j) ld_a<BM>(areg[j], abase, aoff, 2 + j, nfull);
         __syncthreads();
         read_frags(af[0], lds[0]);
         __syncthreads();   // buffer 0 is rewritten in stage 0
@@ -300,21 +328,18 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
             __builtin_amdgcn_sched_barrier(0);
             mma(af[C], breg[J % NB]);
             __builtin_amdgcn_sched_barrier(0);
-            st_a<BM>(lds[C], areg[C], tid);
-            ld_a<BM>(areg[C], abase, aoff, j + 4, nfull);
+            st_a<BM>(lds[C], areg[J % NA], tid);
+            ld_a<BM>(areg[J % NA], abase, aoff, j + 2 + NA, nfull);
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
         };
-        const int n4 = nfull & ~3;
-        for (int j = 0; j < n4; j += 4) {
-            stage(std::integral_constant<int, 0>{}, j);
-            stage(std::integral_constant<int, 1>{}, j + 1);
-            stage(std::integral_constant<int, 2>{}, j + 2);
-            stage(std::integral_constant<int, 3>{}, j + 3);
-        }
-        if (n4 < nfull) stage(std::integral_constant<int, 0>{}, n4);
-        if (n4 + 1 < nfull) stage(std::integral_constant<int, 1>{}, n4 + 1);
-        if (n4 + 2 < nfull) stage(std::integral_constant<int, 2>{}, n4 + 2);
+        constexpr int U = ring_period(NA, NB);
+        const int nu = nfull - nfull % U;
+        for (int j = 0; j < nu; j += U)
+            static_for<U>([&](auto jc) __attribute__((always_inline)) { stage(jc, j + jc); });
+        static_for<U - 1>([&](auto jc) __attribute__((always_inline)) {
+            if (nu + jc < nfull) stage(jc, nu + jc);
+        });
     }
     // Bounds-checked stages: the partial last stage, or all stages when K is
     // not a multiple of 16.  Loads are masked per piece; not pipelined.
@@ -397,21 +422,27 @@ struct GemmCfg { int wm, wn, splits; };
 
 GemmCfg gemm_config(int64_t m, int64_t n, int64_t k)
 {
-    // Prefer the largest block tile that still gives every CU a tile; split
-    // the k range when even the smallest tiles leave CUs idle.
-    const int64_t cus = 256;
-    const int cand[4][2] = {{2, 2}, {1, 2}, {2, 1}, {1, 1}};
-    for (int i = 0; i < 4; ++i) {
-        const int64_t bm = 64 * cand[i][0], bn = 64 * cand[i][1];
-        const int64_t tiles = ((m + bm - 1) / bm) * ((n + bn - 1) / bn);
-        if (tiles >= cus * 3 / 4) return {cand[i][0], cand[i][1], 1};
-    }
-    const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
+    // Chosen from timings of every tile/split combination on the 2B-, 3B- and
+    // 70B-class shapes: the largest block tile that still gives most CUs a
+    // tile, else 128 x 128 tiles with the k range split until they do.  Small
+    // M (<= 64 rows) uses 64 x 64 tiles, split when there are few of them.
     const int64_t nk = (k + BK - 1) / BK;
-    int64_t s = (cus + tiles - 1) / tiles;
-    if (s > nk) s = nk;
-    if (s > 8) s = 8;
-    return {2, 2, (int)(s < 1 ? 1 : s)};
+    auto tiles = [&](int wm, int wn) {
+        return ((m + 64 * wm - 1) / (64 * wm)) * ((n + 64 * wn - 1) / (64 * wn));
+    };
+    auto split_for = [&](int64_t t, int64_t cap) {
+        int64_t s = (192 + t - 1) / t;
+        if (s > cap) s = cap;
+        if (s > nk / 4) s = nk / 4;
+        return (int)(s < 1 ? 1 : s);
+    };
+    if (m <= 64) {
+        const int64_t t = tiles(1, 1);
+        return {1, 1, t >= 192 ? 1 : split_for(t, 4)};
+    }
+    if (tiles(2, 2) >= 192) return {2, 2, 1};
+    if (tiles(2, 1) >= 192) return {2, 1, 1};
+    return {2, 2, split_for(tiles(2, 2), 8)};
 }
 
 int64_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k)

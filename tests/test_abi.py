@@ -38,6 +38,9 @@ def test_size_queries_match_the_layout_definitions(lib):
 
 def test_path_selection(lib):
     assert bl.forward_path(1, 28672, 8192) == bl.BL_PATH_GEMV
+    assert bl.forward_path(16, 28672, 8192) == bl.BL_PATH_SKINNY
+    assert bl.forward_path(16, 8640, 3200) == bl.BL_PATH_MFMA     # K % 256 != 0
+    assert bl.forward_path(64, 3840, 2560) == bl.BL_PATH_MFMA
     assert bl.forward_path(512, 8640, 3200) == bl.BL_PATH_MFMA
     assert bl.forward_path(1, 28672, 8192, bl.BL_PACK3) == bl.BL_PATH_GEMV
 
@@ -98,6 +101,9 @@ def test_forward_argument_checks(lib):
     assert call(lay=7) == -5
     assert call(path=9) == -8
     assert call(lay=bl.BL_PACK3, path=bl.BL_PATH_MFMA) == -8
+    assert call(lay=bl.BL_PACK3, path=bl.BL_PATH_SKINNY) == -8
+    assert call(path=bl.BL_PATH_SKINNY) == -8              # K = 64 is not a multiple of 256
+    assert call(m=17, k=256, path=bl.BL_PATH_SKINNY) == -8  # more than 16 tokens
     assert call(k=0) == -2
     assert call(m=-1) == -2
     assert call(pk=ODD) == -3

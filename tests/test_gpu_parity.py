@@ -36,16 +36,23 @@ def run_case(w: np.ndarray, x: np.ndarray, layout: int, paths=(bl.BL_PATH_AUTO,)
     np.testing.assert_array_equal(host(scale), s_ref)
     np.testing.assert_array_equal(host(rowsum), r_ref)
     np.testing.assert_array_equal(host(bl.unpack_weights(packed, n, k, layout)), t)
+    m = x.shape[0]
     for path in paths:
+        if path == bl.BL_PATH_SKINNY and not skinny_ok(m, k):
+            continue
         acc = bl.matmul_i32(xq, rowsum, packed, n, k, layout, path=path)
         np.testing.assert_array_equal(host(acc), acc_ref, err_msg=f"path {path}")
         y = bl.forward(xq, scale, rowsum, packed, gamma, n, k, layout, path=path)
         assert_y_close(host(y), y_ref, acc_ref)
 
 
+def skinny_ok(m, k):
+    return 1 <= m <= 16 and k % 256 == 0
+
+
 def all_paths(layout):
     if layout == bl.BL_PACK2:
-        return (bl.BL_PATH_AUTO, bl.BL_PATH_GEMV, bl.BL_PATH_MFMA)
+        return (bl.BL_PATH_AUTO, bl.BL_PATH_GEMV, bl.BL_PATH_MFMA, bl.BL_PATH_SKINNY)
     return (bl.BL_PATH_AUTO, bl.BL_PATH_GEMV)
 
 
@@ -64,6 +71,17 @@ def test_tiny_layer_fp32(layout):
 def test_ragged_shapes_bf16(layout, m, n, k):
     w, x = inputs.random_case(10_000 + m * 7 + n * 13 + k, m, n, k, bf16=True)
     run_case(w, x, layout, all_paths(layout))
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (5, 130, 256), (16, 1000, 2560), (12, 17, 512), (1, 33, 256), (8, 2560, 6912),
+    (16, 4099, 8192), (7, 3840, 2560),
+])
+def test_skinny_shapes(m, n, k):
+    """Weight-streaming matrix-core path: ragged N, every row-block / wave split."""
+    w, x = inputs.random_case(20_000 + m * 7 + n * 13 + k, m, n, k, bf16=True)
+    run_case(w, x, bl.BL_PACK2, (bl.BL_PATH_SKINNY, bl.BL_PATH_GEMV))
+    assert bl.forward_path(m, n, k) == (bl.BL_PATH_GEMV if m <= 2 else bl.BL_PATH_SKINNY)
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
@@ -111,7 +129,7 @@ def test_repeated_calls_are_bit_identical():
     packed, gamma = bl.quantize_weights(dev(w))
     xq, scale, rowsum = bl.quantize_act(dev(x))
     n, k = w.shape
-    for path in (bl.BL_PATH_GEMV, bl.BL_PATH_MFMA):
+    for path in (bl.BL_PATH_GEMV, bl.BL_PATH_MFMA, bl.BL_PATH_SKINNY):
         ys = [host(bl.forward(xq, scale, rowsum, packed, gamma, n, k, path=path)) for _ in range(3)]
         assert all(np.array_equal(ys[0].view(np.uint32), v.view(np.uint32)) for v in ys[1:])
 
