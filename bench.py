@@ -75,6 +75,35 @@ def time_loop(fn, iters, warmup):
     return start.elapsed_time(end) / iters
 
 
+def graph_time(fn, replays, warmup):
+    """Capture fn() (a fixed sequence of launches) in one HIP graph and return
+    the average ms per replay over `replays` back-to-back replays (HIP events
+    on the replay stream).  Graph replay takes the Python and launch-queue
+    overhead out of the timed region; every kernel still runs as launched."""
+    import torch
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        fn()                               # eager warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream()
+    start.record(cur)
+    for _ in range(replays):
+        graph.replay()
+    end.record(cur)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / replays
+
+
 def decode_workload(layers):
     """Quantise the four decode matrices once; replicate the packed weights to
     `layers` distinct buffers; inputs resident in HBM."""
@@ -117,10 +146,10 @@ def main():
     log(f"decode workload ready: {step_bytes / 1e6:.1f} MB packed per step")
 
     lib = bl.load()
-    stream_ptr = torch.cuda.current_stream().cuda_stream
 
     def quant_act_into(m):
         # writes into the matrix's resident xq / scale / rowsum buffers
+        stream_ptr = torch.cuda.current_stream().cuda_stream
         st = lib.bitlinear_quantize_act(ctypes.c_void_p(m["x"].data_ptr()), bl.BL_BF16, 1, m["k"],
                                         ctypes.c_void_p(m["xq"].data_ptr()),
                                         ctypes.c_void_p(m["scale"].data_ptr()),
@@ -135,9 +164,12 @@ def main():
                 bl.forward(m["xq"], m["scale"], m["rowsum"], m["copies"][layer], m["gamma"],
                            m["n"], m["k"], y=m["y"])
 
-    ms_step = time_loop(step, args.steps, args.warmup)
+    # one step = one replay of the captured step (240 launches at 30 layers)
+    ms_step = graph_time(step, args.steps, args.warmup)
+    ms_step_eager = time_loop(step, max(2, args.steps // 10), 1)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    log(f"decode step {ms_step * 1e3:.1f} us -> {value:.1f} GB/s")
+    log(f"decode step {ms_step * 1e3:.1f} us (eager launches: {ms_step_eager * 1e3:.1f} us)"
+        f" -> {value:.1f} GB/s")
 
     # dominant kernel: the M=1 GEMV, timed alone over the same rotation
     def gemv_only():
@@ -146,13 +178,13 @@ def main():
                 bl.forward(m["xq"], m["scale"], m["rowsum"], m["copies"][layer], m["gamma"],
                            m["n"], m["k"], y=m["y"])
     launches = args.layers * len(mats)
-    ms_gemv = time_loop(gemv_only, args.steps, args.warmup)
+    ms_gemv = graph_time(gemv_only, args.steps, args.warmup)
     us_per_launch = ms_gemv * 1e3 / launches
     bytes_per_launch = step_bytes / launches
     achieved = bytes_per_launch / (us_per_launch * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "gemv2_kernel (decode, M=1)",
+                "kernel": "gemv2_kernel (decode, M=1); per-launch time = graph replay / launches",
                 "avg_launch_us": round(us_per_launch, 3),
                 "algorithmic_bytes_per_launch": int(bytes_per_launch)}
     log(f"decode GEMV alone: {us_per_launch:.2f} us/launch, {achieved:.1f} GB/s")
@@ -175,6 +207,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_eager_launch": round(ms_step_eager, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -199,11 +232,14 @@ def main():
 
 
 def measure_extra(args):
+    """The other workloads, each timed as one captured graph of launches:
+    the 70B-class layer (rotating 10 copies of each matrix, 587 MB, so the
+    weights stream from HBM) at M = 1, 16, 128 and in base-3 at M = 1; the
+    3B-class prefill GEMMs at M = 512."""
     import torch
     from ternary_weight_linear_absmax_amd import bitlinear as bl
     from ternary_weight_linear_absmax_amd import inputs
     extra = {}
-    # 70B-class: rotate 10 copies (587 MB > Infinity Cache)
     copies_n = 10
     for si, (name, k, n) in enumerate(inputs.XL_SHAPES):
         _, w, x = inputs.xl(si, m=128)
@@ -220,12 +256,11 @@ def measure_extra(args):
         xq, scale, rowsum = bl.quantize_act(to_dev(x))
         for m in inputs.XL_MS:
             y = torch.empty((m, n), dtype=torch.float32, device="cuda")
-            it = [0]
 
             def fwd2():
-                bl.forward(xq[:m], scale[:m], rowsum[:m], c2[it[0] % copies_n], g2, n, k, y=y)
-                it[0] += 1
-            ms = time_loop(fwd2, 100, 10)
+                for c in c2:
+                    bl.forward(xq[:m], scale[:m], rowsum[:m], c, g2, n, k, y=y)
+            ms = graph_time(fwd2, 20, 3) / copies_n
             gbs = p2.numel() / (ms * 1e-3) / 1e9
             tops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
             extra[f"xl_{name}_M{m}_pack2"] = {
@@ -236,10 +271,10 @@ def measure_extra(args):
             log(f"xl {name} M={m} pack2: {ms * 1e3:.1f} us {gbs:.0f} GB/s {tops:.1f} TOPS")
             if m == 1:
                 def fwd3():
-                    bl.forward(xq[:1], scale[:1], rowsum[:1], c3[it[0] % copies_n], g3, n, k,
-                               layout=bl.BL_PACK3, y=y)
-                    it[0] += 1
-                ms3 = time_loop(fwd3, 50, 5)
+                    for c in c3:
+                        bl.forward(xq[:1], scale[:1], rowsum[:1], c, g3, n, k,
+                                   layout=bl.BL_PACK3, y=y)
+                ms3 = graph_time(fwd3, 20, 3) / copies_n
                 gbs3 = p3.numel() / (ms3 * 1e-3) / 1e9
                 extra[f"xl_{name}_M1_pack3"] = {
                     "K": k, "N": n, "M": 1, "us": round(ms3 * 1e3, 2), "GB/s": round(gbs3, 1),
@@ -249,7 +284,8 @@ def measure_extra(args):
         extra[f"xl_{name}_quantize_weights_pack3_ms"] = round(quant_ms, 2)
         del c2, c3
         torch.cuda.empty_cache()
-    # prefill M=512
+    # prefill M=512 (packed weights 6.9 MB: they stay in the Infinity Cache)
+    reps = 10
     for si, (name, k, n) in enumerate(inputs.PREFILL_SHAPES):
         _, w, x = inputs.prefill(si)
         packed, gamma = bl.quantize_weights(to_dev(w))
@@ -259,14 +295,16 @@ def measure_extra(args):
         y = torch.empty((m, n), dtype=torch.float32, device="cuda")
 
         def fwd():
-            bl.forward(xq, scale, rowsum, packed, gamma, n, k, y=y)
-        ms = time_loop(fwd, 100, 10)
+            for _ in range(reps):
+                bl.forward(xq, scale, rowsum, packed, gamma, n, k, y=y)
+        ms = graph_time(fwd, 20, 3) / reps
         tops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
 
         def full():
-            bl.quantize_act(xd)
-            bl.forward(xq, scale, rowsum, packed, gamma, n, k, y=y)
-        ms_full = time_loop(full, 50, 5)
+            for _ in range(reps):
+                bl.quantize_act(xd)
+                bl.forward(xq, scale, rowsum, packed, gamma, n, k, y=y)
+        ms_full = graph_time(full, 20, 3) / reps
         extra[f"prefill_{name}_M512"] = {
             "K": k, "N": n, "M": m, "us": round(ms * 1e3, 2), "TOPS": round(tops, 2),
             "i8_frac": round(tops / I8_PEAK_TOPS, 4),
