@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the 70B / prefill lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy kernel (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
 
 
@@ -136,6 +139,9 @@ def main():
     from ternary_weight_linear_absmax_amd import bitlinear as bl
     from ternary_weight_linear_absmax_amd import inputs
 
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     bl.load()
     dev_name = torch.cuda.get_device_name(0)
     log(f"device {dev_name}")
@@ -183,7 +189,8 @@ def main():
     bytes_per_launch = step_bytes / launches
     achieved = bytes_per_launch / (us_per_launch * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(),
                 "kernel": "gemv2_kernel (decode, M=1); per-launch time = graph replay / launches",
                 "avg_launch_us": round(us_per_launch, 3),
                 "algorithmic_bytes_per_launch": int(bytes_per_launch)}
@@ -312,6 +319,53 @@ def measure_extra(args):
             "TOPS_with_act_quant": round(2.0 * m * n * k / (ms_full * 1e-3) / 1e12, 2)}
         log(f"prefill {name}: {ms * 1e3:.1f} us {tops:.1f} TOPS")
     return extra
+
+
+COPY_BYTES = 1 << 30
+
+
+def calibrate_copy():
+    """A plain copy of known size for the hardware byte counters: torch's
+    elementwise negation reads COPY_BYTES and writes COPY_BYTES once each."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_kernel": "torch.neg float32", "read_bytes": COPY_BYTES,
+                      "write_bytes": COPY_BYTES, "dispatches": 3}), flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_decode_m1_traffic.txt")
+TRAFFIC_SOURCES = ["ternary_weight_linear_absmax_amd/csrc/gemv.hip",
+                   "ternary_weight_linear_absmax_amd/csrc/internal.h"]
+
+
+def sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode GEMV launch from the committed counter summary, or
+    None when it is missing or was taken on other kernel sources."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    key, val = line.split(":", 1)
+                    fields[key.strip()] = val.strip()
+        if fields.get("sources_sha256_16") != sources_digest():
+            return None
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(seconds):
