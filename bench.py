@@ -164,11 +164,11 @@ def main():
         assert st == 0, st
 
     def step():
+        # per matrix: quantise its input, then the product (two launches)
         for layer in range(args.layers):
             for m in mats:
-                quant_act_into(m)
-                bl.forward(m["xq"], m["scale"], m["rowsum"], m["copies"][layer], m["gamma"],
-                           m["n"], m["k"], y=m["y"])
+                bl.quantize_forward(m["x"], m["copies"][layer], m["gamma"], m["n"], y=m["y"],
+                                    xq=m["xq"], scale=m["scale"], rowsum=m["rowsum"])
 
     # one step = one replay of the captured step (240 launches at 30 layers)
     ms_step = graph_time(step, args.steps, args.warmup)
@@ -223,8 +223,8 @@ def main():
         "config": {
             "workload": "decode M=1, 2B-class BitLinear shapes (QKV 2560x3840, O 2560x2560, "
                         "up/gate 2560x13824, down 6912x2560), %d layers of distinct packed "
-                        "weights; per matrix: absmax int8 quantisation + ternary GEMV + rescale"
-                        % args.layers,
+                        "weights; per matrix: absmax int8 quantisation + ternary GEMV + rescale, "
+                        "the step captured in a HIP graph" % args.layers,
             "M": 1,
             "layers": args.layers,
             "packed_bytes_per_step": step_bytes,

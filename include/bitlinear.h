@@ -179,6 +179,21 @@ int bitlinear_matmul_i32(const int8_t *xq, const int32_t *rowsum, int64_t M,
                          int32_t *acc, void *workspace, int64_t workspace_bytes, int path,
                          hipStream_t stream);
 
+/* ---- quantise and multiply in one call ---------------------------------------
+ * [cheatsheet.md summary, "What is BitNet b1.58?": activations scaled per token
+ *  in front of every BitLinear; asi.tokyo 2B4T article, packing paragraph]
+ *
+ * bitlinear_quantize_act(x, dtype, M, K, xq, scale, rowsum) followed by
+ * bitlinear_forward_ex(xq, scale, rowsum, M, packed, layout, gamma, N, K, y,
+ * workspace, workspace_bytes, path), enqueued back to back on `stream` after
+ * all arguments of both have been checked: xq, scale and rowsum (all
+ * required) are written, and y is bit-identical to the two calls.  N == 0
+ * only quantises. */
+int bitlinear_quantize_forward(const void *x, int dtype, int64_t M, int64_t K, int8_t *xq,
+                               float *scale, int32_t *rowsum, const uint8_t *packed, int layout,
+                               const float *gamma, int64_t N, float *y, void *workspace,
+                               int64_t workspace_bytes, int path, hipStream_t stream);
+
 /* Decode packed weights to int8 trits in {-1, 0, 1} (device, [N, K]). */
 int bitlinear_unpack_weights(const uint8_t *packed, int layout, int64_t N, int64_t K,
                              int8_t *trits, hipStream_t stream);

@@ -61,6 +61,8 @@ def load():
         "bitlinear_forward_ex": (i32, [p, p, p, i64, p, i32, p, i64, i64, p, p, i64, i32, p]),
         "bitlinear_matmul_i32": (i32, [p, p, i64, p, i32, i64, i64, p, p, i64, i32, p]),
         "bitlinear_unpack_weights": (i32, [p, i32, i64, i64, p, p]),
+        "bitlinear_quantize_forward": (i32, [p, i32, i64, i64, p, p, p, p, i32, p, i64, p, p, i64,
+                                             i32, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -201,6 +203,33 @@ def matmul_i32(xq, rowsum, packed, n: int, k: int, layout: int = BL_PACK2,
     return acc
 
 
+def quantize_forward(x: torch.Tensor, packed, gamma, n: int, layout: int = BL_PACK2,
+                     path: int = BL_PATH_AUTO, y=None, xq=None, scale=None, rowsum=None,
+                     workspace=None, stream=None):
+    """Per-token quantisation of x [M, K] followed by the product, in one call.
+    Returns (y, xq, scale, rowsum)."""
+    lib = load()
+    assert x.dim() == 2 and x.is_contiguous()
+    m, k = x.shape
+    dev_ = x.device
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=dev_)
+    if scale is None:
+        scale = torch.empty((m,), dtype=torch.float32, device=dev_)
+    if rowsum is None:
+        rowsum = torch.empty((m,), dtype=torch.int32, device=dev_)
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=dev_)
+    ws_bytes = forward_workspace_bytes(m, n, k, layout)
+    if workspace is None and ws_bytes > 0:
+        workspace = _zero_workspace(ws_bytes, dev_)
+    _check(lib.bitlinear_quantize_forward(
+        _ptr(x), _dtype_code(x), m, k, _ptr(xq), _ptr(scale), _ptr(rowsum), _ptr(packed), layout,
+        _ptr(gamma), n, _ptr(y), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+        path, _stream(stream)), "bitlinear_quantize_forward")
+    return y, xq, scale, rowsum
+
+
 def unpack_weights(packed, n: int, k: int, layout: int = BL_PACK2, stream=None):
     lib = load()
     trits = torch.empty((n, k), dtype=torch.int8, device=packed.device)
@@ -215,6 +244,7 @@ bitlinear_quantize_act = quantize_act
 bitlinear_forward = forward
 bitlinear_matmul_i32 = matmul_i32
 bitlinear_unpack_weights = unpack_weights
+bitlinear_quantize_forward = quantize_forward
 bitlinear_packed_bytes = packed_bytes
 bitlinear_packed_row_bytes = packed_row_bytes
 bitlinear_status_string = status_string

@@ -172,6 +172,48 @@ int bitlinear_matmul_i32(const int8_t *xq, const int32_t *rowsum, int64_t M,
                        workspace, workspace_bytes, path, stream);
 }
 
+int bitlinear_quantize_forward(const void *x, int dtype, int64_t M, int64_t K, int8_t *xq,
+                               float *scale, int32_t *rowsum, const uint8_t *packed, int layout,
+                               const float *gamma, int64_t N, float *y, void *workspace,
+                               int64_t workspace_bytes, int path, hipStream_t stream)
+{
+    if (!good_dtype(dtype)) return BL_ERR_DTYPE;
+    if (!good_layout(layout)) return BL_ERR_LAYOUT;
+    if (path != BL_PATH_AUTO && path != BL_PATH_GEMV && path != BL_PATH_MFMA &&
+        path != BL_PATH_SKINNY)
+        return BL_ERR_PATH;
+    if (M < 0 || N < 0 || !good_k(K) || M > 0x7FFFFFFF) return BL_ERR_SHAPE;
+    if ((M > 0 && K > kMaxElems / M) || (N > 0 && K > kMaxElems / N) ||
+        (M > 0 && N > kMaxElems / M))
+        return BL_ERR_SHAPE;
+    if (path == BL_PATH_AUTO) path = choose_path(M, N, K, layout);
+    if (layout == BL_PACK3 && path != BL_PATH_GEMV) return BL_ERR_PATH;
+    if (path == BL_PATH_SKINNY && M > 0 && N > 0 && !bl::skinny_supported(M, N, K))
+        return BL_ERR_PATH;
+    if (M == 0) return BL_OK;
+    if (!x || !xq || !scale || !rowsum) return BL_ERR_NULL;
+    if (!al16(x) || !al16(xq) || !al4(scale) || !al4(rowsum)) return BL_ERR_ALIGN;
+    if (N == 0) return hip_status(bl::launch_quant_act(x, dtype, M, K, xq, scale, rowsum, stream));
+    if (!packed || !gamma || !y) return BL_ERR_NULL;
+    if (!al16(packed) || !al4(gamma) || !al4(y)) return BL_ERR_ALIGN;
+    const int64_t need = path == BL_PATH_MFMA ? bl::gemm_workspace_bytes(M, N, K) : 0;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return BL_ERR_WORKSPACE;
+    if (need > 0 && !al16(workspace)) return BL_ERR_ALIGN;
+
+    bl::Out out{scale, gamma, y, nullptr};
+    hipError_t e = bl::launch_quant_act(x, dtype, M, K, xq, scale, rowsum, stream);
+    if (e != hipSuccess) return BL_ERR_HIP;
+    if (layout == BL_PACK3)
+        e = bl::launch_gemv_pack3(xq, rowsum, M, packed, N, K, out, stream);
+    else if (path == BL_PATH_GEMV)
+        e = bl::launch_gemv_pack2(xq, rowsum, M, packed, N, K, out, stream);
+    else if (path == BL_PATH_SKINNY)
+        e = bl::launch_skinny_pack2(xq, rowsum, M, packed, N, K, out, stream);
+    else
+        e = bl::launch_gemm_pack2(xq, rowsum, M, packed, N, K, out, workspace, stream);
+    return hip_status(e);
+}
+
 int bitlinear_unpack_weights(const uint8_t *packed, int layout, int64_t N, int64_t K,
                              int8_t *trits, hipStream_t stream)
 {

@@ -128,12 +128,116 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void *__restrict__
     }
 }
 
+// Register-resident variant for rows of up to 256 * NV vectors: every load of
+// the row is issued before the first use (clamped index, so unconditional),
+// the row is read from memory once, and the max and the quantisation both work
+// on the registers.  Same arithmetic and outputs as the kernel above.
+template <int DT, int NV>
+__global__ __launch_bounds__(256) void quant_act_reg_kernel(const void *__restrict__ x, int64_t k,
+                                                            int8_t *__restrict__ xq,
+                                                            float *__restrict__ scale,
+                                                            int32_t *__restrict__ rowsum)
+{
+    __shared__ float red_f[4];
+    __shared__ int red_i[4];
+    constexpr int E = DT == DT_BF16 ? 8 : 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t m = blockIdx.x;
+    const uint8_t *row = (const uint8_t *)x + m * k * (DT == DT_BF16 ? 2 : 4);
+    int8_t *qrow = xq + m * k;
+    const int nvec = (int)(k / E);
+
+    uint4 v[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int i = tid + 256 * j;
+        v[j] = load16(row + 16 * (int64_t)(i < nvec ? i : nvec - 1));
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        if (tid + 256 * j >= nvec) continue;
+        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (DT == DT_BF16)
+                amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[e])), fabsf(bf16_hi(w[e]))));
+            else
+                amax = fmaxf(amax, fabsf(__uint_as_float(w[e])));
+        }
+    }
+    amax = wave_max(amax);
+    if (lane == 0) red_f[wave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+    const float s = amax == 0.0f ? 1.0f : 127.0f / amax;
+
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int i = tid + 256 * j;
+        if (i >= nvec) continue;
+        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        if (DT == DT_BF16) {
+            uint32_t out[2] = {0, 0};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                int8_t a = quant1(bf16_lo(w[e]), s), b = quant1(bf16_hi(w[e]), s);
+                sum += a + b;
+                uint32_t pair = ((uint32_t)(uint8_t)a) | ((uint32_t)(uint8_t)b << 8);
+                out[e >> 1] |= pair << (16 * (e & 1));
+            }
+            ((uint2 *)qrow)[i] = make_uint2(out[0], out[1]);
+        } else {
+            uint32_t out = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                int8_t a = quant1(__uint_as_float(w[e]), s);
+                sum += a;
+                out |= (uint32_t)(uint8_t)a << (8 * e);
+            }
+            ((uint32_t *)qrow)[i] = out;
+        }
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) red_i[wave] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        scale[m] = s;
+        if (rowsum) rowsum[m] = red_i[0] + red_i[1] + red_i[2] + red_i[3];
+    }
+}
+
+template <int DT>
+hipError_t launch_reg(int64_t nvec, const void *x, int64_t m, int64_t k, int8_t *xq, float *scale,
+                      int32_t *rowsum, hipStream_t s)
+{
+    const dim3 grid((unsigned)m), block(256);
+    const int64_t per = (nvec + 255) / 256;
+    if (per <= 1)
+        hipLaunchKernelGGL((quant_act_reg_kernel<DT, 1>), grid, block, 0, s, x, k, xq, scale, rowsum);
+    else if (per <= 2)
+        hipLaunchKernelGGL((quant_act_reg_kernel<DT, 2>), grid, block, 0, s, x, k, xq, scale, rowsum);
+    else if (per <= 4)
+        hipLaunchKernelGGL((quant_act_reg_kernel<DT, 4>), grid, block, 0, s, x, k, xq, scale, rowsum);
+    else if (per <= 8)
+        hipLaunchKernelGGL((quant_act_reg_kernel<DT, 8>), grid, block, 0, s, x, k, xq, scale, rowsum);
+    else
+        hipLaunchKernelGGL((quant_act_reg_kernel<DT, 16>), grid, block, 0, s, x, k, xq, scale, rowsum);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_quant_act(const void *x, int dtype, int64_t m, int64_t k, int8_t *xq,
                             float *scale, int32_t *rowsum, hipStream_t s)
 {
     dim3 grid((unsigned)m), block(256);
+    // rows of up to 256 * 16 vectors (32768 bf16 / 16384 fp32) stay in registers
+    if (dtype == DT_BF16 && k % 8 == 0 && k / 8 <= 256 * 16)
+        return launch_reg<DT_BF16>(k / 8, x, m, k, xq, scale, rowsum, s);
+    if (dtype == DT_F32 && k % 4 == 0 && k / 4 <= 256 * 16)
+        return launch_reg<DT_F32>(k / 4, x, m, k, xq, scale, rowsum, s);
     if (dtype == DT_BF16) {
         if (k % 8 == 0)
             hipLaunchKernelGGL((quant_act_kernel<DT_BF16, true>), grid, block, 0, s, x, k, xq,

@@ -122,3 +122,28 @@ def test_unpack_argument_checks(lib):
     assert f(P, 0, 4, 0, P, None) == -2
     assert f(ODD, 0, 4, 64, P, None) == -3
     assert f(P, 0, 0, 64, P, None) == 0
+
+
+def test_quantize_forward_argument_checks(lib):
+    f = lib.bitlinear_quantize_forward
+
+    def call(x=P, dt=1, m=2, k=64, xq=P, s=P, r=P, pk=P, lay=0, g=P, n=8, y=P, ws=NULL, wsb=0,
+             path=0):
+        return f(x, dt, m, k, xq, s, r, pk, lay, g, n, y, ws, wsb, path, None)
+
+    assert call(x=NULL) == -1
+    assert call(xq=NULL) == -1
+    assert call(r=NULL) == -1
+    assert call(pk=NULL) == -1
+    assert call(y=NULL) == -1
+    assert call(dt=5) == -4
+    assert call(lay=4) == -5
+    assert call(path=7) == -8
+    assert call(lay=bl.BL_PACK3, path=bl.BL_PATH_MFMA) == -8
+    assert call(path=bl.BL_PATH_SKINNY) == -8               # K = 64
+    assert call(k=0) == -2
+    assert call(m=-1) == -2
+    assert call(x=ODD) == -3
+    assert call(pk=ODD) == -3
+    assert call(m=64, n=128, k=4096, path=bl.BL_PATH_MFMA) == -6   # split k needs a workspace
+    assert call(m=0, x=NULL, xq=NULL, s=NULL, r=NULL, pk=NULL, g=NULL, y=NULL) == 0

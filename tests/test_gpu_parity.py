@@ -205,3 +205,37 @@ def test_xl_layer(shape):
         if m == 1:
             acc3 = host(bl.matmul_i32(xq[:1], rowsum[:1], packed3, n, k, bl.BL_PACK3))
             np.testing.assert_array_equal(acc3, acc)      # base-3 == 2-bit, bit for bit
+
+
+# ---- quantise + multiply in one call -------------------------------------------------------
+
+@pytest.mark.parametrize("m,n,k,bf16,layout,path", [
+    (1, 300, 2560, True, bl.BL_PACK2, bl.BL_PATH_AUTO),
+    (2, 77, 1040, False, bl.BL_PACK2, bl.BL_PATH_AUTO),      # fp32, K % 64 != 0
+    (4, 129, 528, True, bl.BL_PACK2, bl.BL_PATH_GEMV),       # four tokens on the vector path
+    (3, 50, 100, True, bl.BL_PACK2, bl.BL_PATH_AUTO),        # K % 16 != 0
+    (1, 1000, 4096, False, bl.BL_PACK2, bl.BL_PATH_AUTO),
+    (8, 1000, 512, True, bl.BL_PACK2, bl.BL_PATH_AUTO),      # skinny
+    (64, 200, 384, True, bl.BL_PACK2, bl.BL_PATH_AUTO),      # tiled GEMM
+    (1, 100, 640, True, bl.BL_PACK3, bl.BL_PATH_AUTO),       # base-3
+    (1, 2560, 6912, True, bl.BL_PACK2, bl.BL_PATH_AUTO),     # decode "down" shape
+])
+def test_quantize_forward(m, n, k, bf16, layout, path):
+    w, x = inputs.random_case(40_000 + m * 7 + n * 13 + k, m, n, k, bf16=bf16)
+    if m >= 2:
+        x[1] = 0                                              # an all-zero token
+    t, g, _ = oracle_weights(w, layout)
+    q_ref, s_ref, r_ref = oracle.quantize_act(x)
+    acc_ref = oracle.matmul_i32(q_ref, t)
+    y_ref = oracle.rescale(acc_ref, s_ref, g)
+    packed, gamma = bl.quantize_weights(dev(w), layout)
+    xd = dev(x)
+    y, xq, scale, rowsum = bl.quantize_forward(xd, packed, gamma, n, layout, path=path)
+    np.testing.assert_array_equal(host(xq), q_ref)
+    np.testing.assert_array_equal(host(scale), s_ref)
+    np.testing.assert_array_equal(host(rowsum), r_ref)
+    assert_y_close(host(y), y_ref, acc_ref)
+    # bit-identical to the two separate calls
+    xq2, s2, r2 = bl.quantize_act(xd)
+    y2 = bl.forward(xq2, s2, r2, packed, gamma, n, k, layout, path=path)
+    assert np.array_equal(host(y).view(np.uint32), host(y2).view(np.uint32))
