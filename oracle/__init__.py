@@ -73,6 +73,8 @@ def _load():
         "orc_rescale": (None, [p, p, f32, i64, i64, p]),
         "orc_rmsnorm": (None, [p, i64, i64, ctypes.c_double, p]),
         "orc_relu2_mul": (None, [p, p, i64, p]),
+        "orc_add_f32": (None, [p, p, i64]),
+        "orc_gqa_expand": (None, [p, i64, i64, i64, i64, i64, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -229,3 +231,31 @@ def relu2_mul(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
     out = np.empty_like(gate)
     _load().orc_relu2_mul(_ptr(gate), _ptr(up), gate.size, _ptr(out))
     return out
+
+
+def add_f32(x: np.ndarray, y: np.ndarray) -> np.ndarray:
+    """x + y in float32 (the residual stream); returns a new array."""
+    out = np.array(x, dtype=np.float32, copy=True, order="C")
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    assert out.shape == y.shape
+    _load().orc_add_f32(_ptr(out), _ptr(y), out.size)
+    return out
+
+
+def gqa_expand(v: np.ndarray, heads: int, kv_heads: int) -> np.ndarray:
+    """v [M, kv_heads * head_dim] float32 -> [M, heads * head_dim] float64."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    m, width = v.shape
+    head_dim = width // kv_heads
+    assert head_dim * kv_heads == width and heads % kv_heads == 0
+    out = np.empty((m, heads * head_dim), dtype=np.float64)
+    _load().orc_gqa_expand(_ptr(v), m, width, heads, kv_heads, head_dim, _ptr(out))
+    return out
+
+
+def rmsnorm_quantize(v: np.ndarray, eps: float = 1e-5):
+    """The input of a BitLinear in the decoder block: RMSNorm (unit gain, in
+    double precision), rounded to float32, then the per-token absmax
+    quantiser.  Returns (q, s, rowsum)."""
+    h = rmsnorm(v, eps).astype(np.float32)
+    return quantize_act(h)

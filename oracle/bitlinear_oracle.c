@@ -269,3 +269,26 @@ void orc_relu2_mul(const double *gate, const double *up, int64_t count, double *
         out[i] = g * g * up[i];
     }
 }
+
+/* x[i] = x[i] + y[i] in single precision: the residual stream of the block. */
+void orc_add_f32(float *x, const float *y, int64_t count)
+{
+    for (int64_t i = 0; i < count; ++i)
+        x[i] = x[i] + y[i];
+}
+
+/* Attention of the first token (sequence position 0): there is one key, so
+ * the softmax weight is 1 and each query head returns the value vector of its
+ * key-value head; with grouped-query attention head h reads key-value head
+ * h / (heads / kv_heads).  v holds kv_heads * head_dim values per row, rows
+ * v_stride floats apart; out is [m_rows, heads * head_dim] in double. */
+void orc_gqa_expand(const float *v, int64_t m_rows, int64_t v_stride, int64_t heads,
+                    int64_t kv_heads, int64_t head_dim, double *out)
+{
+    const int64_t group = heads / kv_heads;
+    for (int64_t m = 0; m < m_rows; ++m)
+        for (int64_t h = 0; h < heads; ++h)
+            for (int64_t d = 0; d < head_dim; ++d)
+                out[(m * heads + h) * head_dim + d] =
+                    (double)v[m * v_stride + (h / group) * head_dim + d];
+}

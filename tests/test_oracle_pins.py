@@ -411,3 +411,42 @@ def test_rmsnorm_and_relu2():
     g = np.array([-2.0, -0.0, 0.5, 3.0])
     u = np.array([5.0, 7.0, 2.0, -1.0])
     np.testing.assert_array_equal(oracle.relu2_mul(g, u), np.array([0.0, 0.0, 0.5, -9.0]))
+
+
+# ---- decoder-block glue of the layer-stack workload ---------------------------------------
+
+def test_add_f32_is_ieee_single_addition():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(10_000).astype(np.float32) * np.float32(1e3)
+    y = rng.standard_normal(10_000).astype(np.float32)
+    got = oracle.add_f32(x, y)
+    np.testing.assert_array_equal(got.view(np.uint32), (x + y).view(np.uint32))
+    # float32, not float64, rounding: 2^24 + 1 is not representable
+    assert oracle.add_f32(np.float32([16777216.0]), np.float32([1.0]))[0] == np.float32(16777216.0)
+
+
+def test_gqa_expand_special_cases():
+    rng = np.random.default_rng(6)
+    m, kv, hd = 3, 5, 128
+    v = rng.standard_normal((m, kv * hd)).astype(np.float32)
+    # one query head per key-value head: a plain copy
+    np.testing.assert_array_equal(oracle.gqa_expand(v, kv, kv), v.astype(np.float64))
+    # a single key-value head: every query head gets the same vector
+    one = v[:, :hd]
+    out = oracle.gqa_expand(one, 4, 1).reshape(m, 4, hd)
+    for h in range(4):
+        np.testing.assert_array_equal(out[:, h], one)
+    # 20 query heads over 5 key-value heads: numpy's repeat along the head axis
+    out = oracle.gqa_expand(v, 20, kv).reshape(m, 20, hd)
+    np.testing.assert_array_equal(out, np.repeat(v.reshape(m, kv, hd), 4, axis=1))
+
+
+def test_rmsnorm_quantize_constant_magnitude_rows():
+    # |x| = c everywhere: RMSNorm gives +-1/sqrt(1 + eps/c^2), so every q is +-127
+    # and the row sum is 127 * (#positive - #negative)
+    rng = np.random.default_rng(7)
+    signs = rng.choice([-1.0, 1.0], size=(4, 2560))
+    x = signs * np.array([[0.5], [3.0], [1e-2], [7.0]])
+    q, s, r = oracle.rmsnorm_quantize(x)
+    np.testing.assert_array_equal(q, (127 * signs).astype(np.int8))
+    np.testing.assert_array_equal(r, (127 * signs.sum(axis=1)).astype(np.int32))
