@@ -11,9 +11,10 @@ product with rescale.  Weights are quantised and packed once, before timing
 (the method packs them offline).  Metric: packed-weight bytes per second.
 
 Also measured on the same line (``extra``): the 70B-class layer at M = 1
-(2-bit and base-3 layouts) and M = 16 / 128, and the 3B-class prefill GEMM at
-M = 512 in TOPS; plus the roofline of the dominant kernel and the CPU oracle
-timed on a bounded sample on this host.
+(2-bit and base-3 layouts) and M = 16 / 128, the 30-layer 2B-class decoder
+stack at M = 64 in tokens/s, and the 3B-class prefill GEMM at M = 512 in
+TOPS; plus the roofline of the dominant kernel and the CPU oracle timed on a
+bounded sample on this host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -291,6 +292,8 @@ def measure_extra(args):
         extra[f"xl_{name}_quantize_weights_pack3_ms"] = round(quant_ms, 2)
         del c2, c3
         torch.cuda.empty_cache()
+    # layer stack: 30 layers of the 2B-class decoder, M = 64 tokens at position 0
+    extra.update(measure_stack())
     # prefill M=512 (packed weights 6.9 MB: they stay in the Infinity Cache)
     reps = 10
     for si, (name, k, n) in enumerate(inputs.PREFILL_SHAPES):
@@ -319,6 +322,45 @@ def measure_extra(args):
             "TOPS_with_act_quant": round(2.0 * m * n * k / (ms_full * 1e-3) / 1e12, 2)}
         log(f"prefill {name}: {ms * 1e3:.1f} us {tops:.1f} TOPS")
     return extra
+
+
+def measure_stack(layers=30, m=64):
+    """The 2B-class layer stack (hidden 2560, 20/5 heads of 128, FFN 6912,
+    squared ReLU, RMSNorm before every BitLinear), M tokens decoded at
+    sequence position 0, one step = all layers, captured in one HIP graph.
+    Weights: bf16 N(0, 0.02) drawn on the GPU with torch's generator seeded
+    4000 + 10 * layer + matrix index; x0 ~ N(0, 1)."""
+    import torch
+    from ternary_weight_linear_absmax_amd import stack as st
+    gen = torch.Generator(device="cuda")
+
+    def weights(layer):
+        out = {}
+        for i, name in enumerate(st.MATRICES):
+            gen.manual_seed(4000 + 10 * layer + i)
+            out[name] = (torch.randn(st.SHAPES[name], generator=gen, device="cuda")
+                         * 0.02).to(torch.bfloat16)
+        return out
+
+    stack = st.DecoderStack(weights, layers, m)
+    gen.manual_seed(4999)
+    x0 = torch.randn((m, st.HIDDEN), device="cuda", generator=gen)
+
+    def step():
+        stack.x.copy_(x0)
+        stack.step()
+    ms = graph_time(step, 20, 3)
+    pb = stack.packed_bytes()
+    ops = 2.0 * m * sum(st.SHAPES[n][0] * st.SHAPES[n][1] for n in st.MATRICES) * layers
+    out = {"stack_2B_M64": {
+        "layers": layers, "M": m, "us_per_step": round(ms * 1e3, 1),
+        "tokens_per_s": round(m / (ms * 1e-3), 1), "packed_bytes": pb,
+        "GB/s": round(pb / (ms * 1e-3) / 1e9, 1), "TOPS": round(ops / (ms * 1e-3) / 1e12, 2),
+        "launches_per_step": 8 * layers + 2}}
+    log(f"stack {layers} layers M={m}: {ms * 1e3:.1f} us/step, {m / (ms * 1e-3):.0f} tokens/s")
+    del stack
+    torch.cuda.empty_cache()
+    return out
 
 
 COPY_BYTES = 1 << 30

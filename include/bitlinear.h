@@ -194,6 +194,41 @@ int bitlinear_quantize_forward(const void *x, int dtype, int64_t M, int64_t K, i
                                const float *gamma, int64_t N, float *y, void *workspace,
                                int64_t workspace_bytes, int path, hipStream_t stream);
 
+/* ---- decoder-block glue of the layer-stack workload ------------------------------
+ * [asi.tokyo 2B4T article, stabiliser paragraph: a norm in front of the
+ *  sub-layers, squared ReLU in the feed-forward block; cheatsheet.md summary,
+ *  "What is BitNet b1.58?": RMSNorm, no bias, activations scaled per token]
+ *
+ * Each call forms a [M, K] block of values v (device, float inputs), applies
+ * RMSNorm with unit gain in double precision, h = v / sqrt(mean_k v^2 + eps)
+ * rounded to float, and quantises h per token with the arithmetic of
+ * bitlinear_quantize_act: xq [M, K] int8, scale [M] float and rowsum [M] int32
+ * (device, all required, written).  1 <= K <= 8192; eps >= 0.  M == 0 is a
+ * no-op.  The double-precision sum of squares is reduced in a different order
+ * than a sequential loop, so h can differ from such a loop in the last bit in
+ * rare cases; every later step is exact. */
+
+/* v = x after x += add: x device [M, K] float, updated in place (the residual
+ * stream); add device [M, K] float, or NULL for no addition. */
+int bitlinear_residual_rmsnorm_quantize(float *x, const float *add, int64_t M, int64_t K,
+                                        float eps, int8_t *xq, float *scale, int32_t *rowsum,
+                                        hipStream_t stream);
+
+/* Attention output of the first token (sequence position 0: a single key, so
+ * the softmax weight is 1) under grouped-query attention:
+ * v[m, h * head_dim + d] = qkv[m * ld + v_col + (h / (heads / kv_heads)) * head_dim + d],
+ * K = heads * head_dim.  qkv: device, M rows of ld floats (the QKV product). */
+int bitlinear_gqa_rmsnorm_quantize(const float *qkv, int64_t M, int64_t ld, int64_t v_col,
+                                   int64_t heads, int64_t kv_heads, int64_t head_dim, float eps,
+                                   int8_t *xq, float *scale, int32_t *rowsum, hipStream_t stream);
+
+/* Squared-ReLU gate: v[m, i] = relu(g)^2 * u in double precision, with
+ * g = gate_up[m * ld + i] and u = gate_up[m * ld + F + i]; K = F.  gate_up:
+ * device, M rows of ld >= 2F floats (the fused up/gate product). */
+int bitlinear_relu2_rmsnorm_quantize(const float *gate_up, int64_t M, int64_t ld, int64_t F,
+                                     float eps, int8_t *xq, float *scale, int32_t *rowsum,
+                                     hipStream_t stream);
+
 /* Decode packed weights to int8 trits in {-1, 0, 1} (device, [N, K]). */
 int bitlinear_unpack_weights(const uint8_t *packed, int layout, int64_t N, int64_t K,
                              int8_t *trits, hipStream_t stream);

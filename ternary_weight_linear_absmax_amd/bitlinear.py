@@ -61,6 +61,10 @@ def load():
         "bitlinear_forward_ex": (i32, [p, p, p, i64, p, i32, p, i64, i64, p, p, i64, i32, p]),
         "bitlinear_matmul_i32": (i32, [p, p, i64, p, i32, i64, i64, p, p, i64, i32, p]),
         "bitlinear_unpack_weights": (i32, [p, i32, i64, i64, p, p]),
+        "bitlinear_residual_rmsnorm_quantize": (i32, [p, p, i64, i64, ctypes.c_float, p, p, p, p]),
+        "bitlinear_gqa_rmsnorm_quantize": (i32, [p, i64, i64, i64, i64, i64, i64, ctypes.c_float,
+                                                 p, p, p, p]),
+        "bitlinear_relu2_rmsnorm_quantize": (i32, [p, i64, i64, i64, ctypes.c_float, p, p, p, p]),
         "bitlinear_quantize_forward": (i32, [p, i32, i64, i64, p, p, p, p, i32, p, i64, p, p, i64,
                                              i32, p]),
     }
@@ -230,6 +234,58 @@ def quantize_forward(x: torch.Tensor, packed, gamma, n: int, layout: int = BL_PA
     return y, xq, scale, rowsum
 
 
+def _glue_outputs(m, k, device, xq, scale, rowsum):
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=device)
+    if scale is None:
+        scale = torch.empty((m,), dtype=torch.float32, device=device)
+    if rowsum is None:
+        rowsum = torch.empty((m,), dtype=torch.int32, device=device)
+    return xq, scale, rowsum
+
+
+def residual_rmsnorm_quantize(x: torch.Tensor, add=None, eps: float = 1e-5, xq=None, scale=None,
+                              rowsum=None, stream=None):
+    """x += add (in place, float32), then RMSNorm + per-token quantisation.
+    Returns (xq, scale, rowsum)."""
+    assert x.dtype == torch.float32 and x.dim() == 2 and x.is_contiguous()
+    m, k = x.shape
+    xq, scale, rowsum = _glue_outputs(m, k, x.device, xq, scale, rowsum)
+    _check(load().bitlinear_residual_rmsnorm_quantize(_ptr(x), _ptr(add), m, k, eps, _ptr(xq),
+                                                      _ptr(scale), _ptr(rowsum), _stream(stream)),
+           "bitlinear_residual_rmsnorm_quantize")
+    return xq, scale, rowsum
+
+
+def gqa_rmsnorm_quantize(qkv: torch.Tensor, v_col: int, heads: int, kv_heads: int,
+                         head_dim: int, eps: float = 1e-5, xq=None, scale=None, rowsum=None,
+                         stream=None):
+    """First-token GQA attention output from the QKV product, then RMSNorm +
+    quantisation.  Returns (xq, scale, rowsum)."""
+    assert qkv.dtype == torch.float32 and qkv.dim() == 2 and qkv.is_contiguous()
+    m, ld = qkv.shape
+    k = heads * head_dim
+    xq, scale, rowsum = _glue_outputs(m, k, qkv.device, xq, scale, rowsum)
+    _check(load().bitlinear_gqa_rmsnorm_quantize(_ptr(qkv), m, ld, v_col, heads, kv_heads,
+                                                 head_dim, eps, _ptr(xq), _ptr(scale),
+                                                 _ptr(rowsum), _stream(stream)),
+           "bitlinear_gqa_rmsnorm_quantize")
+    return xq, scale, rowsum
+
+
+def relu2_rmsnorm_quantize(gate_up: torch.Tensor, f: int, eps: float = 1e-5, xq=None,
+                           scale=None, rowsum=None, stream=None):
+    """relu(gate)^2 * up from the fused up/gate product, then RMSNorm +
+    quantisation.  Returns (xq, scale, rowsum)."""
+    assert gate_up.dtype == torch.float32 and gate_up.dim() == 2 and gate_up.is_contiguous()
+    m, ld = gate_up.shape
+    xq, scale, rowsum = _glue_outputs(m, f, gate_up.device, xq, scale, rowsum)
+    _check(load().bitlinear_relu2_rmsnorm_quantize(_ptr(gate_up), m, ld, f, eps, _ptr(xq),
+                                                   _ptr(scale), _ptr(rowsum), _stream(stream)),
+           "bitlinear_relu2_rmsnorm_quantize")
+    return xq, scale, rowsum
+
+
 def unpack_weights(packed, n: int, k: int, layout: int = BL_PACK2, stream=None):
     lib = load()
     trits = torch.empty((n, k), dtype=torch.int8, device=packed.device)
@@ -245,6 +301,9 @@ bitlinear_forward = forward
 bitlinear_matmul_i32 = matmul_i32
 bitlinear_unpack_weights = unpack_weights
 bitlinear_quantize_forward = quantize_forward
+bitlinear_residual_rmsnorm_quantize = residual_rmsnorm_quantize
+bitlinear_gqa_rmsnorm_quantize = gqa_rmsnorm_quantize
+bitlinear_relu2_rmsnorm_quantize = relu2_rmsnorm_quantize
 bitlinear_packed_bytes = packed_bytes
 bitlinear_packed_row_bytes = packed_row_bytes
 bitlinear_status_string = status_string

@@ -214,6 +214,61 @@ int bitlinear_quantize_forward(const void *x, int dtype, int64_t M, int64_t K, i
     return hip_status(e);
 }
 
+namespace {
+
+int glue_common(int64_t M, int64_t K, float eps, int8_t *xq, float *scale, int32_t *rowsum)
+{
+    if (M < 0 || K < 1 || K > bl::GLUE_MAX_K || M > 0x7FFFFFFF) return BL_ERR_SHAPE;
+    if (!(eps >= 0.0f)) return BL_ERR_SHAPE;
+    if (M == 0) return BL_OK;
+    if (!xq || !scale || !rowsum) return BL_ERR_NULL;
+    if (!al16(xq) || !al4(scale) || !al4(rowsum)) return BL_ERR_ALIGN;
+    return 1;   // proceed
+}
+
+}  // namespace
+
+int bitlinear_residual_rmsnorm_quantize(float *x, const float *add, int64_t M, int64_t K,
+                                        float eps, int8_t *xq, float *scale, int32_t *rowsum,
+                                        hipStream_t stream)
+{
+    const int c = glue_common(M, K, eps, xq, scale, rowsum);
+    if (c != 1) return c;
+    if (!x) return BL_ERR_NULL;
+    if (!al4(x) || (add && !al4(add))) return BL_ERR_ALIGN;
+    bl::GlueArgs a{x, add, nullptr, 0, 0, 1, 1};
+    return hip_status(bl::launch_glue(bl::GLUE_RESIDUAL, a, M, K, eps, xq, scale, rowsum, stream));
+}
+
+int bitlinear_gqa_rmsnorm_quantize(const float *qkv, int64_t M, int64_t ld, int64_t v_col,
+                                   int64_t heads, int64_t kv_heads, int64_t head_dim, float eps,
+                                   int8_t *xq, float *scale, int32_t *rowsum, hipStream_t stream)
+{
+    if (heads < 1 || kv_heads < 1 || head_dim < 1 || heads % kv_heads != 0) return BL_ERR_SHAPE;
+    if (heads > bl::GLUE_MAX_K || head_dim > bl::GLUE_MAX_K) return BL_ERR_SHAPE;
+    if (v_col < 0 || ld < 1 || v_col + kv_heads * head_dim > ld) return BL_ERR_SHAPE;
+    const int c = glue_common(M, heads * head_dim, eps, xq, scale, rowsum);
+    if (c != 1) return c;
+    if (!qkv) return BL_ERR_NULL;
+    if (!al4(qkv)) return BL_ERR_ALIGN;
+    bl::GlueArgs a{nullptr, nullptr, qkv, ld, v_col, heads / kv_heads, head_dim};
+    return hip_status(bl::launch_glue(bl::GLUE_GQA, a, M, heads * head_dim, eps, xq, scale,
+                                      rowsum, stream));
+}
+
+int bitlinear_relu2_rmsnorm_quantize(const float *gate_up, int64_t M, int64_t ld, int64_t F,
+                                     float eps, int8_t *xq, float *scale, int32_t *rowsum,
+                                     hipStream_t stream)
+{
+    if (F < 1 || ld < 2 * F) return BL_ERR_SHAPE;
+    const int c = glue_common(M, F, eps, xq, scale, rowsum);
+    if (c != 1) return c;
+    if (!gate_up) return BL_ERR_NULL;
+    if (!al4(gate_up)) return BL_ERR_ALIGN;
+    bl::GlueArgs a{nullptr, nullptr, gate_up, ld, F, 1, 1};
+    return hip_status(bl::launch_glue(bl::GLUE_RELU2, a, M, F, eps, xq, scale, rowsum, stream));
+}
+
 int bitlinear_unpack_weights(const uint8_t *packed, int layout, int64_t N, int64_t K,
                              int8_t *trits, hipStream_t stream)
 {

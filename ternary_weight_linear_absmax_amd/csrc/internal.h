@@ -38,6 +38,21 @@ hipError_t launch_unpack(const uint8_t *packed, int layout, int64_t n, int64_t k
 hipError_t launch_quant_act(const void *x, int dtype, int64_t m, int64_t k, int8_t *xq,
                             float *scale, int32_t *rowsum, hipStream_t s);
 
+// ---- decoder-block glue (glue.hip) ----
+enum : int { GLUE_RESIDUAL = 0, GLUE_GQA = 1, GLUE_RELU2 = 2 };
+constexpr int64_t GLUE_MAX_K = 256 * 32;
+struct GlueArgs {
+    float *x;             // residual: [M, K] float, updated in place
+    const float *add;     // residual: [M, K] float or nullptr
+    const float *src;     // gqa / relu2: source rows
+    int64_t ld;           // gqa / relu2: source row stride (floats)
+    int64_t col;          // gqa: first value column; relu2: offset of "up" from "gate"
+    int64_t group;        // gqa: query heads per key-value head
+    int64_t head_dim;     // gqa
+};
+hipError_t launch_glue(int mode, const GlueArgs &a, int64_t m, int64_t k, double eps,
+                       int8_t *xq, float *scale, int32_t *rowsum, hipStream_t s);
+
 // ---- products ----
 // 2-bit layout, vector dot-product kernel; tokens handled in groups of up to 4.
 hipError_t launch_gemv_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
@@ -73,6 +88,19 @@ __device__ inline uint4 load16(const void *p)
     const u32x4 v = *(const u32x4 *)p;
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+
+// ---- per-token activation quantiser arithmetic, shared by the quantiser and
+// the decoder-block glue so that both produce the same bytes ----
+__device__ inline int8_t quant1(float x, float s)
+{
+    float r = rintf(x * s);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int8_t)(int)r;
+}
+__device__ inline float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ inline float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+// s = 127 / max|x|, or 1 for an all-zero token.
+__device__ inline float act_scale(float amax) { return amax == 0.0f ? 1.0f : 127.0f / amax; }
 
 // Writes the output element (m, n) from the code-weighted sum sum_k (t+1) q
 // and the token's rowsum: acc = codesum - rowsum.

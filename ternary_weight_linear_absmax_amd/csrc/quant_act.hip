@@ -29,15 +29,6 @@ __device__ inline int wave_sum(int v)
     return v;
 }
 
-__device__ inline int8_t quant1(float x, float s)
-{
-    float r = rintf(x * s);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int8_t)(int)r;
-}
-
-__device__ inline float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ inline float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
 // Vector path: 16-byte loads (8 bf16 or 4 fp32); requires K to be a multiple
 // of the vector width so that every row stays 16-byte aligned.
@@ -81,7 +72,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void *__restrict__
     if (lane == 0) red_f[wave] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
-    const float s = amax == 0.0f ? 1.0f : 127.0f / amax;
+    const float s = act_scale(amax);
 
     int sum = 0;
     if (VEC) {
@@ -170,7 +161,7 @@ __global__ __launch_bounds__(256) void quant_act_reg_kernel(const void *__restri
     if (lane == 0) red_f[wave] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
-    const float s = amax == 0.0f ? 1.0f : 127.0f / amax;
+    const float s = act_scale(amax);
 
     int sum = 0;
 #pragma unroll

@@ -1,0 +1,106 @@
+"""The 2B-class decoder layer stack of the layer-stack workload, driven through
+the C ABI (argument marshalling only; every step runs in the library's
+kernels).
+
+Model shape (asi.tokyo BitNet b1.58 2B4T article; cheatsheet.md summary,
+"What is BitNet b1.58?"): hidden 2560, 20 query heads and 5 key-value heads of
+128, feed-forward 6912 with squared ReLU, RMSNorm in front of every BitLinear,
+no bias.  The workload decodes the first token of M independent sequences
+(sequence position 0), so attention reduces to the value vector of each
+token's key-value head, expanded over its query-head group.
+
+Per layer (x is the float residual stream, [M, 2560]):
+
+    xq = quant(RMSNorm(x))                      bitlinear_residual_rmsnorm_quantize
+    qkv = BitLinear_qkv(xq)                     [M, 3840]: Q 0..2559, K 2560..3199, V 3200..3839
+    xq = quant(RMSNorm(GQA-expand(V)))          bitlinear_gqa_rmsnorm_quantize
+    o = BitLinear_o(xq)
+    x += o; xq = quant(RMSNorm(x))              bitlinear_residual_rmsnorm_quantize
+    gu = BitLinear_up_gate(xq)                  [M, 13824]: gate 0..6911, up 6912..13823
+    xq = quant(RMSNorm(relu(gate)^2 * up))      bitlinear_relu2_rmsnorm_quantize
+    d = BitLinear_down(xq)
+    x += d                                      (folded into the next layer's first call)
+"""
+from __future__ import annotations
+
+import torch
+
+from . import bitlinear as bl
+
+HIDDEN, HEADS, KV_HEADS, HEAD_DIM, FFN = 2560, 20, 5, 128, 6912
+QKV = HIDDEN + 2 * KV_HEADS * HEAD_DIM
+V_COL = HIDDEN + KV_HEADS * HEAD_DIM
+EPS = 1e-5
+MATRICES = ("qkv", "o", "up_gate", "down")
+SHAPES = {"qkv": (QKV, HIDDEN), "o": (HIDDEN, HIDDEN), "up_gate": (2 * FFN, HIDDEN),
+          "down": (HIDDEN, FFN)}
+
+
+class DecoderStack:
+    """Packed weights of `layers` layers plus the activation buffers of M
+    tokens, all resident on the GPU."""
+
+    def __init__(self, layer_weights, layers: int, m: int, device="cuda"):
+        """layer_weights(l) -> dict name -> [N, K] bf16/fp32 tensor on the GPU
+        (quantised and packed here, then released)."""
+        self.layers, self.m = layers, m
+        self.packed, self.gamma = [], []
+        for layer in range(layers):
+            w = layer_weights(layer)
+            p, g = {}, {}
+            for name in MATRICES:
+                assert tuple(w[name].shape) == SHAPES[name], (name, w[name].shape)
+                p[name], g[name] = bl.quantize_weights(w[name])
+            self.packed.append(p)
+            self.gamma.append(g)
+            del w
+        f32 = dict(dtype=torch.float32, device=device)
+        self.x = torch.zeros((m, HIDDEN), **f32)
+        self.y = {name: torch.empty((m, SHAPES[name][0]), **f32) for name in MATRICES}
+        self.xq = torch.empty((m, FFN), dtype=torch.int8, device=device)
+        self.scale = torch.empty((m,), **f32)
+        self.rowsum = torch.empty((m,), dtype=torch.int32, device=device)
+
+    def packed_bytes(self) -> int:
+        return sum(p.numel() for layer in self.packed for p in layer.values())
+
+    def _q(self, k: int):
+        """Quantiser outputs for an input of width k (views of one buffer)."""
+        return dict(xq=self.xq.view(-1)[: self.m * k].view(self.m, k), scale=self.scale,
+                    rowsum=self.rowsum)
+
+    def _linear(self, layer: int, name: str, k: int):
+        n = SHAPES[name][0]
+        q = self._q(k)
+        bl.forward(q["xq"], self.scale, self.rowsum, self.packed[layer][name],
+                   self.gamma[layer][name], n, k, y=self.y[name])
+
+    def layer(self, layer: int, trace=None):
+        """One decoder layer on the resident buffers.  trace: optional callback
+        trace(op_name) called after every step (for tests)."""
+        note = trace or (lambda op: None)
+        add = self.y["down"] if layer > 0 else None
+        bl.residual_rmsnorm_quantize(self.x, add, EPS, **self._q(HIDDEN))
+        note("norm_attn")
+        self._linear(layer, "qkv", HIDDEN)
+        note("qkv")
+        bl.gqa_rmsnorm_quantize(self.y["qkv"], V_COL, HEADS, KV_HEADS, HEAD_DIM, EPS,
+                                **self._q(HIDDEN))
+        note("attn_norm")
+        self._linear(layer, "o", HIDDEN)
+        note("o")
+        bl.residual_rmsnorm_quantize(self.x, self.y["o"], EPS, **self._q(HIDDEN))
+        note("norm_ffn")
+        self._linear(layer, "up_gate", HIDDEN)
+        note("up_gate")
+        bl.relu2_rmsnorm_quantize(self.y["up_gate"], FFN, EPS, **self._q(FFN))
+        note("ffn_norm")
+        self._linear(layer, "down", FFN)
+        note("down")
+
+    def step(self):
+        """All layers on the current residual stream self.x, then the last
+        residual addition; self.x holds the stack's output."""
+        for layer in range(self.layers):
+            self.layer(layer)
+        bl.residual_rmsnorm_quantize(self.x, self.y["down"], EPS, **self._q(HIDDEN))

@@ -147,3 +147,22 @@ def test_quantize_forward_argument_checks(lib):
     assert call(pk=ODD) == -3
     assert call(m=64, n=128, k=4096, path=bl.BL_PATH_MFMA) == -6   # split k needs a workspace
     assert call(m=0, x=NULL, xq=NULL, s=NULL, r=NULL, pk=NULL, g=NULL, y=NULL) == 0
+
+
+def test_glue_argument_checks(lib):
+    f = lib.bitlinear_residual_rmsnorm_quantize
+    assert f(NULL, NULL, 4, 64, 1e-5, P, P, P, None) == -1
+    assert f(P, NULL, 4, 64, 1e-5, NULL, P, P, None) == -1
+    assert f(P, NULL, 4, 0, 1e-5, P, P, P, None) == -2
+    assert f(P, NULL, 4, 8193, 1e-5, P, P, P, None) == -2      # longer than one block holds
+    assert f(P, NULL, 4, 64, -1.0, P, P, P, None) == -2
+    assert f(P, NULL, 0, 64, 1e-5, NULL, NULL, NULL, None) == 0
+    assert f(P, ODD, 4, 64, 1e-5, P, P, P, None) == -3
+    g = lib.bitlinear_gqa_rmsnorm_quantize
+    assert g(P, 4, 3840, 3200, 20, 3, 128, 1e-5, P, P, P, None) == -2    # 20 % 3 != 0
+    assert g(P, 4, 3800, 3200, 20, 5, 128, 1e-5, P, P, P, None) == -2    # V past the row
+    assert g(NULL, 4, 3840, 3200, 20, 5, 128, 1e-5, P, P, P, None) == -1
+    h = lib.bitlinear_relu2_rmsnorm_quantize
+    assert h(P, 4, 13823, 6912, 1e-5, P, P, P, None) == -2               # ld < 2F
+    assert h(NULL, 4, 13824, 6912, 1e-5, P, P, P, None) == -1
+    assert h(P, 0, 13824, 6912, 1e-5, NULL, NULL, NULL, None) == 0

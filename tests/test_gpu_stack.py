@@ -1,0 +1,133 @@
+"""The 2B-class layer stack (M = 64 tokens at sequence position 0), checked
+step by step against the oracle.
+
+Each step is fed, on the oracle side, the GPU's own input to that step: the
+float glue (RMSNorm in double precision, summed in a different order) can
+move a normalised value across a float rounding boundary in rare cases, which
+would then shift an int8 code by one; every product is required bit-exact in
+int32 for the int8 input the GPU actually used, and every output within 1e-5.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ternary_weight_linear_absmax_amd import bitlinear as bl
+from ternary_weight_linear_absmax_amd import inputs
+from ternary_weight_linear_absmax_amd import stack as st
+
+from gpu_helpers import assert_y_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+M = 64
+
+
+def np_weights(layer):
+    return inputs.stack_layer_weights(layer)
+
+
+def assert_quant_close(got, want):
+    """xq / scale / rowsum of the glue against the oracle's: codes may differ
+    by one in at most 1 in 10^5 positions (rounding edges), scales by 1e-6."""
+    q, s, r = got
+    q_ref, s_ref, r_ref = want
+    diff = q.astype(np.int32) - q_ref.astype(np.int32)
+    assert np.abs(diff).max() <= 1
+    assert np.count_nonzero(diff) <= max(1, q.size // 100_000), np.count_nonzero(diff)
+    np.testing.assert_allclose(s, s_ref, rtol=1e-6)
+    np.testing.assert_array_equal(r - r_ref, diff.sum(axis=1))
+    assert np.array_equal(r, q.astype(np.int64).sum(axis=1))
+
+
+def test_stack_layer_against_oracle():
+    torch.cuda.synchronize()
+    w_np = {layer: np_weights(layer) for layer in range(2)}
+    stack = st.DecoderStack(lambda layer: {k: dev(v) for k, v in w_np[layer].items()}, 2, M)
+    trits = {}
+    for name in st.MATRICES:
+        t, g = oracle.quantize_weights(w_np[0][name])
+        trits[name] = (t, g)
+        assert host(stack.gamma[0][name])[0] == g
+    x0 = inputs.bf16_bits_to_f32(inputs.stack_input(M))
+    stack.x.copy_(dev(x0))
+
+    snaps = []
+
+    def snap(op):
+        torch.cuda.synchronize()
+        snaps.append((op, {
+            "x": host(stack.x).copy(), "xq": host(stack.xq).copy(),
+            "scale": host(stack.scale).copy(), "rowsum": host(stack.rowsum).copy(),
+            **{f"y_{n}": host(stack.y[n]).copy() for n in st.MATRICES}}))
+
+    snaps.append(("start", {"x": x0.copy()}))
+    stack.layer(0, trace=snap)
+    ops = dict(snaps)
+
+    def quant_of(state, k):
+        return (state["xq"].reshape(-1)[: M * k].reshape(M, k), state["scale"], state["rowsum"])
+
+    def check_linear(before, after, name, k):
+        t, g = trits[name]
+        q, s, r = quant_of(before, k)
+        acc = host(bl.matmul_i32(dev(q), dev(r), stack.packed[0][name], t.shape[0], k))
+        acc_ref = oracle.matmul_i32(q, t)
+        np.testing.assert_array_equal(acc, acc_ref, err_msg=name)
+        assert_y_close(after[f"y_{name}"], oracle.rescale(acc_ref, s, g), acc_ref)
+
+    # attention input: RMSNorm of the stream (no residual before layer 0)
+    np.testing.assert_array_equal(ops["norm_attn"]["x"], x0)
+    assert_quant_close(quant_of(ops["norm_attn"], st.HIDDEN), oracle.rmsnorm_quantize(x0))
+    check_linear(ops["norm_attn"], ops["qkv"], "qkv", st.HIDDEN)
+    v = ops["qkv"]["y_qkv"][:, st.V_COL:]
+    assert_quant_close(quant_of(ops["attn_norm"], st.HIDDEN),
+                       oracle.rmsnorm_quantize(oracle.gqa_expand(v, st.HEADS, st.KV_HEADS)))
+    check_linear(ops["attn_norm"], ops["o"], "o", st.HIDDEN)
+    x1 = oracle.add_f32(x0, ops["o"]["y_o"])
+    np.testing.assert_array_equal(ops["norm_ffn"]["x"].view(np.uint32), x1.view(np.uint32))
+    assert_quant_close(quant_of(ops["norm_ffn"], st.HIDDEN), oracle.rmsnorm_quantize(x1))
+    check_linear(ops["norm_ffn"], ops["up_gate"], "up_gate", st.HIDDEN)
+    gu = ops["up_gate"]["y_up_gate"]
+    assert_quant_close(quant_of(ops["ffn_norm"], st.FFN),
+                       oracle.rmsnorm_quantize(oracle.relu2_mul(gu[:, :st.FFN], gu[:, st.FFN:])))
+    check_linear(ops["ffn_norm"], ops["down"], "down", st.FFN)
+
+    # layer 1 starts with the residual of layer 0's down projection
+    snaps.clear()
+    stack.layer(1, trace=snap)
+    x2 = oracle.add_f32(x1, ops["down"]["y_down"])
+    first = snaps[0][1]
+    np.testing.assert_array_equal(first["x"].view(np.uint32), x2.view(np.uint32))
+    assert_quant_close(quant_of(first, st.HIDDEN), oracle.rmsnorm_quantize(x2))
+
+
+def test_stack_graph_replay_matches_eager():
+    gen = torch.Generator(device="cuda")
+
+    def weights(layer):
+        gen.manual_seed(4000 + layer)
+        return {n: (torch.randn(st.SHAPES[n], generator=gen, device="cuda") * 0.02)
+                .to(torch.bfloat16) for n in st.MATRICES}
+
+    stack = st.DecoderStack(weights, 3, M)
+    x0 = torch.randn((M, st.HIDDEN), device="cuda", generator=gen)
+    stack.x.copy_(x0)
+    stack.step()
+    torch.cuda.synchronize()
+    ref = host(stack.x).copy()
+    assert np.isfinite(ref).all()
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    stack.x.copy_(x0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        stack.step()
+    for _ in range(3):
+        stack.x.copy_(x0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(stack.x).view(np.uint32), ref.view(np.uint32))
