@@ -214,6 +214,7 @@ def test_xl_layer(shape):
     (2, 77, 1040, False, bl.BL_PACK2, bl.BL_PATH_AUTO),      # fp32, K % 64 != 0
     (4, 129, 528, True, bl.BL_PACK2, bl.BL_PATH_GEMV),       # four tokens on the vector path
     (3, 50, 100, True, bl.BL_PACK2, bl.BL_PATH_AUTO),        # K % 16 != 0
+    (5, 130, 320, True, bl.BL_PACK2, bl.BL_PATH_GEMV),       # two groups of tokens
     (1, 1000, 4096, False, bl.BL_PACK2, bl.BL_PATH_AUTO),
     (8, 1000, 512, True, bl.BL_PACK2, bl.BL_PATH_AUTO),      # skinny
     (64, 200, 384, True, bl.BL_PACK2, bl.BL_PATH_AUTO),      # tiled GEMM
@@ -235,6 +236,10 @@ def test_quantize_forward(m, n, k, bf16, layout, path):
     np.testing.assert_array_equal(host(scale), s_ref)
     np.testing.assert_array_equal(host(rowsum), r_ref)
     assert_y_close(host(y), y_ref, acc_ref)
+    # a workspace the call used is left all-zero
+    torch.cuda.synchronize()
+    for ws in bl._workspaces.values():
+        assert int(ws[:256].count_nonzero()) == 0
     # bit-identical to the two separate calls
     xq2, s2, r2 = bl.quantize_act(xd)
     y2 = bl.forward(xq2, s2, r2, packed, gamma, n, k, layout, path=path)
