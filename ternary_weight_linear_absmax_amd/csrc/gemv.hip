@@ -97,29 +97,40 @@ __device__ inline void load_x64(const int8_t *__restrict__ xrow, int64_t k, int6
 // combined once at the end.
 constexpr int GEMV_R = 2;
 constexpr int GEMV_KS_MAX = 8;
+constexpr int GEMV_WAVES = 4;   // waves per block when K is short
+#ifndef GEMV_PF
+#define GEMV_PF 1               // steps of weight loads in flight ahead
+#endif
 
 template <int MT, int CPL, int ST, bool AL>
 __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
     const int8_t *__restrict__ xq, const int32_t *__restrict__ rowsum, int64_t k,
     const uint4 *__restrict__ packed, int64_t n, int64_t chunks, int64_t share, Out out,
-    int64_t ldy, int64_t m0)
+    int64_t ldy, int64_t m0, int ks)
 {
     constexpr int R = GEMV_R, RB = GEMV_R * ST;
-    __shared__ int part[GEMV_KS_MAX][RB][MT];
-    const int ks = blockDim.x >> 6;
+    // A block is ks x wr waves: wave w takes k-share w % ks of the rows of
+    // row group w / ks; the block's wr * RB rows are contiguous, and their
+    // outputs are written together at the end.
+    __shared__ int part[GEMV_KS_MAX][GEMV_KS_MAX * RB][MT];
+    const int wr = (int)(blockDim.x >> 6) / ks;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t row0 = (int64_t)blockIdx.x * RB;
+    const int kw = wave % ks, rw = wave / ks;
+    const int64_t blk0 = (int64_t)blockIdx.x * wr * RB;
+    const int64_t row0 = blk0 + (int64_t)rw * RB;
 
     int64_t coff[CPL];
     bool ok[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-        const int64_t c = wave * share + lane + 64 * j;
+        const int64_t c = kw * share + lane + 64 * j;
         ok[j] = (lane + 64 * j < share) && c < chunks;
         coff[j] = ok[j] ? c : 0;
     }
 
-    uint4 w[2][R][CPL];
+    // weight ring: GEMV_PF steps of loads in flight ahead of the arithmetic
+    constexpr int PF = GEMV_PF < ST ? GEMV_PF : ST;
+    uint4 w[PF + 1][R][CPL];
     auto load = [&](uint4(&wb)[R][CPL], int s) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -129,8 +140,21 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
             for (int j = 0; j < CPL; ++j) wb[r][j] = load_nt16(packed + row * chunks + coff[j]);
         }
     };
-    load(w[0], 0);
+#pragma unroll
+    for (int q = 0; q < PF; ++q) load(w[q], q);
     __builtin_amdgcn_sched_barrier(0);
+
+    // Epilogue operands (row sum, gamma / s) of the output this thread writes
+    // at the end (wr * RB * MT <= blockDim outputs, one per thread), loaded
+    // now so that their latency overlaps the weight stream.
+    const int nout = wr * RB * MT;
+    const int e_rr = threadIdx.x / MT, e_t = threadIdx.x % MT;
+    int32_t e_rs = 0;
+    float e_gs = 0.0f;
+    if (threadIdx.x < nout) {
+        e_rs = rowsum[m0 + e_t];
+        if (!out.acc) e_gs = out.gamma[0] / out.scale[m0 + e_t];
+    }
 
     uint4 xv[MT][CPL][4];
 #pragma unroll
@@ -145,9 +169,9 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
 
 #pragma unroll
     for (int s = 0; s < ST; ++s) {
-        if (s + 1 < ST) load(w[(s + 1) & 1], s + 1);
+        if (s + PF < ST) load(w[(s + PF) % (PF + 1)], s + PF);
         __builtin_amdgcn_sched_barrier(0);
-        const int b = s & 1;
+        const int b = s % (PF + 1);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
 #pragma unroll
@@ -161,16 +185,20 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
                     dot_word(w[b][r][j].w, xv[t][j][3], lo, hi);
                 }
                 const int v = wave_sum_dpp(lo + (hi >> 2));
-                if (lane == 63) part[wave][s * R + r][t] = v;
+                if (lane == 63) part[kw][rw * RB + s * R + r][t] = v;
             }
         }
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < RB * MT; e += blockDim.x) {
-        const int rr = e / MT, t = e % MT;
+    if (threadIdx.x < nout && blk0 + e_rr < n) {
         int sum = 0;
-        for (int q = 0; q < ks; ++q) sum += part[q][rr][t];
-        if (row0 + rr < n) store_out(out, ldy, m0 + t, row0 + rr, sum, rowsum[m0 + t]);
+        for (int q = 0; q < ks; ++q) sum += part[q][e_rr][e_t];
+        const int32_t acc = sum - e_rs;
+        const int64_t idx = (m0 + e_t) * ldy + blk0 + e_rr;
+        if (out.acc)
+            out.acc[idx] = acc;
+        else
+            out.y[idx] = (float)acc * e_gs;
     }
 }
 
@@ -224,8 +252,15 @@ __global__ __launch_bounds__(256) void gemv3_kernel(const int8_t *__restrict__ x
     const int64_t row = (int64_t)blockIdx.x * 4 + wave;
     if (row >= n) return;
     int acc[MT];
+    int32_t e_rs[MT];
+    float e_gs[MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = 0;
+    for (int t = 0; t < MT; ++t) {
+        acc[t] = 0;
+        // epilogue operands, loaded before the weight stream starts
+        e_rs[t] = rowsum[m0 + t];
+        e_gs[t] = out.acc ? 0.0f : out.gamma[0] / out.scale[m0 + t];
+    }
 
     for (int64_t c = lane; c < chunks; c += LG) {
         const uint4 wv = load_nt16(packed + row * chunks + c);
@@ -272,18 +307,29 @@ __global__ __launch_bounds__(256) void gemv3_kernel(const int8_t *__restrict__ x
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         int v = group_sum<64>(acc[t]);
-        if (lane == 0) store_out(out, ldy, m0 + t, row, v, rowsum[m0 + t]);
+        if (lane != 0) continue;
+        const int32_t a = v - e_rs[t];
+        if (out.acc)
+            out.acc[(m0 + t) * ldy + row] = a;
+        else
+            out.y[(m0 + t) * ldy + row] = (float)a * e_gs[t];
     }
 }
 
 // Launch shape of the 2-bit GEMV for (N, K): waves per block KS (so that each
 // lane holds at most 2 chunks of activations per token), chunks per lane CPL,
 // and steps per block ST (a power of two, about 1792 waves in total).
-struct Gemv2Shape { int ks, cpl, st; int64_t share; };
+// Row waves per block WR: blocks of about four waves (fewer, larger
+// workgroups dispatch faster, and their outputs are stored together).
+struct Gemv2Shape { int ks, cpl, st; int64_t share; int wr; };
 
 Gemv2Shape gemv2_shape(int64_t n, int64_t chunks, int mt)
 {
-    const int cpl_max = mt <= 2 ? 2 : 1;
+    // Two chunks per lane halve the waves per row; on short matrices with up
+    // to 128 chunks per row the extra waves of one chunk per lane are faster
+    // (measured on the 2B-class down projection, K = 6912).
+    int cpl_max = mt <= 2 ? 2 : 1;
+    if (chunks <= 128 && n * ((chunks + 63) / 64) <= 8192) cpl_max = 1;
     int ks = (int)((chunks + 64 * cpl_max - 1) / (64 * cpl_max));
     if (ks > GEMV_KS_MAX) ks = GEMV_KS_MAX;
     const int64_t share = (chunks + ks - 1) / ks;
@@ -291,7 +337,9 @@ Gemv2Shape gemv2_shape(int64_t n, int64_t chunks, int mt)
     int64_t per = n * ks / (GEMV_R * 1792);
     int st = 1;
     while (st < 8 && 2 * st <= per) st *= 2;
-    return {ks, cpl, st, share};
+    int wr = ks >= GEMV_WAVES ? 1 : GEMV_WAVES / ks;
+    while (wr > 1 && (n + (int64_t)wr * GEMV_R * st - 1) / ((int64_t)wr * GEMV_R * st) < 256) wr /= 2;
+    return {ks, cpl, st, share, wr};
 }
 
 template <int MT, int CPL, int ST>
@@ -300,14 +348,14 @@ hipError_t launch2_st(bool al, const int8_t *xq, const int32_t *rowsum, int64_t 
                       hipStream_t s)
 {
     const int64_t chunks = pack2_pitch(k) / 16;
-    const int64_t rb = (int64_t)GEMV_R * ST;
-    const dim3 grid((unsigned)((n + rb - 1) / rb)), block((unsigned)(64 * sh.ks));
+    const int64_t rb = (int64_t)GEMV_R * ST * sh.wr;
+    const dim3 grid((unsigned)((n + rb - 1) / rb)), block((unsigned)(64 * sh.ks * sh.wr));
     if (al)
         hipLaunchKernelGGL((gemv2_kernel<MT, CPL, ST, true>), grid, block, 0, s, xq, rowsum, k,
-                           (const uint4 *)packed, n, chunks, sh.share, out, n, m0);
+                           (const uint4 *)packed, n, chunks, sh.share, out, n, m0, sh.ks);
     else
         hipLaunchKernelGGL((gemv2_kernel<MT, CPL, ST, false>), grid, block, 0, s, xq, rowsum, k,
-                           (const uint4 *)packed, n, chunks, sh.share, out, n, m0);
+                           (const uint4 *)packed, n, chunks, sh.share, out, n, m0, sh.ks);
     return hipGetLastError();
 }
 

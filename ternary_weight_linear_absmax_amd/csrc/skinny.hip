@@ -1,5 +1,5 @@
-// Ternary x int8 product for a few tokens (5 <= M <= 16): weight-streaming
-// kernel on the 16x16x64 int8 matrix cores.
+// Ternary x int8 product for a few tokens (up to 16): weight-streaming kernel
+// on the 16x16x64 int8 matrix cores.
 //
 // Source: asi.tokyo BitNet b1.58 2B4T article, packing paragraph (trits packed
 // four per byte, unpacked beside the arithmetic units, multiplied with 8-bit
@@ -96,6 +96,11 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(const int8_t *__restric
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) acc[rb] = v4i{0, 0, 0, 0};
 
+    // Epilogue operands of this lane's token, loaded now (their latency
+    // overlaps the weight stream).
+    const int32_t e_rs = rowsum[tok];
+    const float e_g = out.acc ? 0.0f : out.gamma[0] / out.scale[tok];
+
     auto compute = [&](const SkinnyLoads<RB> &L) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -127,8 +132,8 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(const int8_t *__restric
     for (int rb = 0; rb < RB; ++rb) red[wave][rb][lane] = acc[rb];
     __syncthreads();
     if (wave != 0 || r >= m) return;
-    const int32_t rs = rowsum[r];
-    const float g = out.acc ? 0.0f : out.gamma[0] / out.scale[r];
+    const int32_t rs = e_rs;
+    const float g = e_g;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         v4i t = red[0][rb][lane];
