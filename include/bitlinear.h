@@ -80,12 +80,12 @@ typedef enum {
 
 typedef enum {
     BL_PATH_AUTO = 0,        /* choose by M, K and layout (the default): GEMV for
-                                PACK3 and M <= 2; SKINNY for M <= 16 when it can
+                                PACK3 and M <= 2; SKINNY for M <= 32 when it can
                                 run the shape; else GEMV for M <= 4, MFMA above */
     BL_PATH_GEMV = 1,        /* vector dot-product kernel, tokens in passes of 4 */
     BL_PATH_MFMA = 2,        /* int8 matrix-core tiled kernel, any M (PACK2 only) */
     BL_PATH_SKINNY = 3       /* int8 matrix-core weight-streaming kernel for
-                                1 <= M <= 16 and K a multiple of 256 (PACK2 only) */
+                                1 <= M <= 64 and K a multiple of 256 (PACK2 only) */
 } bl_path;
 
 #define BITLINEAR_MAX_K (1 << 20)

@@ -16,12 +16,13 @@ inline bool good_k(int64_t k) { return k >= 1 && k <= BITLINEAR_MAX_K; }
 inline int hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
 
 // M = 1, 2: the vector kernel reads each weight word once per pass of up to
-// four tokens and is the fastest; 3..16 tokens: the weight-streaming matrix-core
-// kernel (one pass over the weights for all tokens); more: the tiled GEMM.
+// four tokens and is the fastest; 3..32 tokens: the weight-streaming
+// matrix-core kernel (one pass over the weights for all tokens; measured
+// faster than the tiled GEMM up to 32 tokens); more: the tiled GEMM.
 int choose_path(int64_t m, int64_t n, int64_t k, int layout)
 {
     if (layout == BL_PACK3 || m <= 2) return BL_PATH_GEMV;
-    if (bl::skinny_supported(m, n, k)) return BL_PATH_SKINNY;
+    if (m <= 32 && bl::skinny_supported(m, n, k)) return BL_PATH_SKINNY;
     return m <= 4 ? BL_PATH_GEMV : BL_PATH_MFMA;
 }
 

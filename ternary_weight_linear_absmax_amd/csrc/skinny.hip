@@ -36,6 +36,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int SK_CHUNK = 256;   // k per chunk
 constexpr int SK_MAX_KS = 8;
+constexpr int64_t SK_MAX_M = 64;   // four groups of 16 token slots
 
 __device__ inline v4i unpack_word16(uint32_t w)
 {
@@ -52,13 +53,15 @@ __device__ inline uint32_t word_at(const uint4 &v, int u)
     return u == 0 ? v.x : u == 1 ? v.y : u == 2 ? v.z : v.w;
 }
 
-template <int RB>
+template <int RB, int TG>
 struct SkinnyLoads {
     uint4 w[RB];      // 16 packed bytes per row block
-    uint4 x[4];       // 64 activation bytes
+    uint4 x[TG][4];   // 64 activation bytes per token group
 };
 
-template <int RB, int KS>
+// TG groups of 16 token slots (M <= 16 TG); every unpacked weight operand
+// feeds TG MFMAs.
+template <int RB, int KS, int TG>
 __global__ __launch_bounds__(64 * KS) void skinny_kernel(const int8_t *__restrict__ xq,
                                                          const int32_t *__restrict__ rowsum,
                                                          int64_t m, int64_t k,
@@ -66,7 +69,8 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(const int8_t *__restric
                                                          int64_t n, int64_t pitch, Out out,
                                                          int64_t ldy)
 {
-    __shared__ v4i red[KS][RB][64];
+    static_assert(KS * RB * TG <= 64, "partial sums must fit in 64 KB of LDS");
+    __shared__ v4i red[KS][RB * TG][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, b = lane >> 4;
     const int64_t n0 = (int64_t)blockIdx.x * 16 * RB;
@@ -81,42 +85,55 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(const int8_t *__restric
         row = row < n ? row : n - 1;
         wrow[rb] = packed + row * pitch + 16 * b;
     }
-    const int64_t tok = r < m ? r : m - 1;
-    const int8_t *xrow = xq + tok * k + 64 * b;
+    const int8_t *xrow[TG];
+    int32_t e_rs[TG];
+    float e_g[TG];
+#pragma unroll
+    for (int g = 0; g < TG; ++g) {
+        const int64_t tok = 16 * g + r < m ? 16 * g + r : m - 1;
+        xrow[g] = xq + tok * k + 64 * b;
+        // epilogue operands of this lane's tokens, loaded before the stream
+        e_rs[g] = rowsum[tok];
+        e_g[g] = out.acc ? 0.0f : out.gamma[0] / out.scale[tok];
+    }
 
-    auto load = [&](SkinnyLoads<RB> &L, int c) __attribute__((always_inline)) {
+    auto load = [&](SkinnyLoads<RB, TG> &L, int c) __attribute__((always_inline)) {
         const int cc = c < nchunks ? c : nchunks - 1;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) L.w[rb] = load_nt16(wrow[rb] + (int64_t)cc * 64);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) L.x[q] = load16(xrow + (int64_t)cc * SK_CHUNK + 16 * q);
+        for (int g = 0; g < TG; ++g)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                L.x[g][q] = load16(xrow[g] + (int64_t)cc * SK_CHUNK + 16 * q);
     };
 
-    v4i acc[RB];
+    v4i acc[RB][TG];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) acc[rb] = v4i{0, 0, 0, 0};
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int g = 0; g < TG; ++g) acc[rb][g] = v4i{0, 0, 0, 0};
 
-    // Epilogue operands of this lane's token, loaded now (their latency
-    // overlaps the weight stream).
-    const int32_t e_rs = rowsum[tok];
-    const float e_g = out.acc ? 0.0f : out.gamma[0] / out.scale[tok];
-
-    auto compute = [&](const SkinnyLoads<RB> &L) __attribute__((always_inline)) {
+    auto compute = [&](const SkinnyLoads<RB, TG> &L) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const v4i xb = v4i{(int)L.x[u].x, (int)L.x[u].y, (int)L.x[u].z, (int)L.x[u].w};
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-                acc[rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack_word16(word_at(L.w[rb], u)),
-                                                                xb, acc[rb], 0, 0, 0);
-        }
+            for (int rb = 0; rb < RB; ++rb) {
+                const v4i a = unpack_word16(word_at(L.w[rb], u));
+#pragma unroll
+                for (int g = 0; g < TG; ++g) {
+                    const v4i xb = v4i{(int)L.x[g][u].x, (int)L.x[g][u].y, (int)L.x[g][u].z,
+                                       (int)L.x[g][u].w};
+                    acc[rb][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, xb, acc[rb][g], 0, 0, 0);
+                }
+            }
     };
 
     // Chunks wave, wave + KS, ...: one chunk of loads in flight ahead of the
     // compute.  Loads are unconditional (clamped chunk index), so the waits
     // are exact; a step past the end computes nothing.
     const int steps = (nchunks - wave + KS - 1) / KS;
-    SkinnyLoads<RB> cur, nxt;
+    SkinnyLoads<RB, TG> cur, nxt;
     load(cur, wave);
     for (int s = 0; s < steps; ++s) {
         load(nxt, wave + KS * (s + 1));
@@ -127,71 +144,88 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(const int8_t *__restric
     }
 
     // Combine the waves' partial sums, then the epilogue on wave 0: lane
-    // (r, b) holds rows n0 + 16 rb + 4b + q of token r.
+    // (r, b) holds rows n0 + 16 rb + 4b + q of tokens 16 g + r.
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) red[wave][rb][lane] = acc[rb];
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int g = 0; g < TG; ++g) red[wave][rb * TG + g][lane] = acc[rb][g];
     __syncthreads();
-    if (wave != 0 || r >= m) return;
-    const int32_t rs = e_rs;
-    const float g = e_g;
+    if (wave != 0) return;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        v4i t = red[0][rb][lane];
+    for (int g = 0; g < TG; ++g) {
+        const int64_t tok = 16 * g + r;
+        if (tok >= m) continue;
 #pragma unroll
-        for (int w = 1; w < KS; ++w) t += red[w][rb][lane];
-        const int64_t row0 = n0 + 16 * rb + 4 * b;
+        for (int rb = 0; rb < RB; ++rb) {
+            v4i t = red[0][rb * TG + g][lane];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (row0 + q >= n) break;
-            const int32_t v = t[q] - rs;
-            if (out.acc)
-                out.acc[r * ldy + row0 + q] = v;
-            else
-                out.y[r * ldy + row0 + q] = (float)v * g;
+            for (int w = 1; w < KS; ++w) t += red[w][rb * TG + g][lane];
+            const int64_t row0 = n0 + 16 * rb + 4 * b;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (row0 + q >= n) break;
+                const int32_t v = t[q] - e_rs[g];
+                if (out.acc)
+                    out.acc[tok * ldy + row0 + q] = v;
+                else
+                    out.y[tok * ldy + row0 + q] = (float)v * e_g[g];
+            }
         }
     }
 }
 
-template <int RB, int KS>
+template <int RB, int KS, int TG>
 hipError_t launch_rb_ks(const int8_t *xq, const int32_t *rowsum, int64_t m,
                         const uint8_t *packed, int64_t n, int64_t k, Out out, hipStream_t s)
 {
     const int64_t blocks = (n + 16 * RB - 1) / (16 * RB);
-    hipLaunchKernelGGL((skinny_kernel<RB, KS>), dim3((unsigned)blocks), dim3(64 * KS), 0, s, xq,
-                       rowsum, m, k, packed, n, pack2_pitch(k), out, (int64_t)n);
+    hipLaunchKernelGGL((skinny_kernel<RB, KS, TG>), dim3((unsigned)blocks), dim3(64 * KS), 0, s,
+                       xq, rowsum, m, k, packed, n, pack2_pitch(k), out, (int64_t)n);
     return hipGetLastError();
+}
+
+template <int TG>
+hipError_t launch_tg(const int8_t *xq, const int32_t *rowsum, int64_t m, const uint8_t *packed,
+                     int64_t n, int64_t k, Out out, hipStream_t s)
+{
+    // Rows per wave (16 RB) and waves per block (KS): keep about 2048 waves
+    // in flight, with RB as large as that allows (RB row blocks share one
+    // activation fragment), and the partial sums within 64 KB of LDS.
+    const int64_t chunks = k / SK_CHUNK;
+    const int64_t target = 2048;
+    const int rb_max = TG >= 4 ? 2 : 4;
+    int rb = rb_max;
+    while (rb > 1 &&
+           ((n + 16 * rb - 1) / (16 * rb)) * (chunks < SK_MAX_KS ? chunks : SK_MAX_KS) < target)
+        rb /= 2;
+    const int64_t blocks = (n + 16 * rb - 1) / (16 * rb);
+    int64_t ks = (target + blocks - 1) / blocks;
+    if (ks > chunks) ks = chunks;
+    const int ksel = ks <= 1 ? 1 : ks <= 2 ? 2 : ks <= 4 ? 4 : 8;
+#define SK_CASE(RB_, KS_)                                                                      \
+    if (rb == RB_ && ksel == KS_)                                                              \
+        return launch_rb_ks<RB_, KS_, TG>(xq, rowsum, m, packed, n, k, out, s);
+    if constexpr (TG <= 2) { SK_CASE(4, 1) SK_CASE(4, 2) SK_CASE(4, 4) SK_CASE(4, 8) }
+    SK_CASE(2, 1) SK_CASE(2, 2) SK_CASE(2, 4) SK_CASE(2, 8)
+    SK_CASE(1, 1) SK_CASE(1, 2) SK_CASE(1, 4) SK_CASE(1, 8)
+#undef SK_CASE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 bool skinny_supported(int64_t m, int64_t n, int64_t k)
 {
-    return m >= 1 && m <= 16 && k % SK_CHUNK == 0 && n >= 1 && n <= ((int64_t)1 << 31) / 64;
+    return m >= 1 && m <= SK_MAX_M && k % SK_CHUNK == 0 && n >= 1 && n <= ((int64_t)1 << 31) / 64;
 }
 
-// Rows per wave (16 RB) and waves per block (KS): keep about 2048 waves in
-// flight, with RB as large as that allows (RB row blocks share one activation
-// fragment).
 hipError_t launch_skinny_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
                                const uint8_t *packed, int64_t n, int64_t k, Out out,
                                hipStream_t s)
 {
-    const int64_t chunks = k / SK_CHUNK;
-    const int64_t target = 2048;
-    int rb = 4;
-    while (rb > 1 && ((n + 16 * rb - 1) / (16 * rb)) * (chunks < SK_MAX_KS ? chunks : SK_MAX_KS) < target)
-        rb /= 2;
-    const int64_t blocks = (n + 16 * rb - 1) / (16 * rb);
-    int64_t ks = (target + blocks - 1) / blocks;
-    if (ks > chunks) ks = chunks;
-    const int ksel = ks <= 1 ? 1 : ks <= 2 ? 2 : ks <= 4 ? 4 : 8;
-#define SK_CASE(RB_, KS_) \
-    if (rb == RB_ && ksel == KS_) return launch_rb_ks<RB_, KS_>(xq, rowsum, m, packed, n, k, out, s);
-    SK_CASE(4, 1) SK_CASE(4, 2) SK_CASE(4, 4) SK_CASE(4, 8)
-    SK_CASE(2, 1) SK_CASE(2, 2) SK_CASE(2, 4) SK_CASE(2, 8)
-    SK_CASE(1, 1) SK_CASE(1, 2) SK_CASE(1, 4) SK_CASE(1, 8)
-#undef SK_CASE
-    return hipErrorInvalidValue;
+    if (m <= 16) return launch_tg<1>(xq, rowsum, m, packed, n, k, out, s);
+    if (m <= 32) return launch_tg<2>(xq, rowsum, m, packed, n, k, out, s);
+    return launch_tg<4>(xq, rowsum, m, packed, n, k, out, s);
 }
 
 }  // namespace bl

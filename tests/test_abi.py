@@ -103,7 +103,7 @@ def test_forward_argument_checks(lib):
     assert call(lay=bl.BL_PACK3, path=bl.BL_PATH_MFMA) == -8
     assert call(lay=bl.BL_PACK3, path=bl.BL_PATH_SKINNY) == -8
     assert call(path=bl.BL_PATH_SKINNY) == -8              # K = 64 is not a multiple of 256
-    assert call(m=17, k=256, path=bl.BL_PATH_SKINNY) == -8  # more than 16 tokens
+    assert call(m=65, k=256, path=bl.BL_PATH_SKINNY) == -8  # more than 64 tokens
     assert call(k=0) == -2
     assert call(m=-1) == -2
     assert call(pk=ODD) == -3

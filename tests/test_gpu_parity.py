@@ -47,7 +47,7 @@ def run_case(w: np.ndarray, x: np.ndarray, layout: int, paths=(bl.BL_PATH_AUTO,)
 
 
 def skinny_ok(m, k):
-    return 1 <= m <= 16 and k % 256 == 0
+    return 1 <= m <= 64 and k % 256 == 0
 
 
 def all_paths(layout):
@@ -75,13 +75,16 @@ def test_ragged_shapes_bf16(layout, m, n, k):
 
 @pytest.mark.parametrize("m,n,k", [
     (5, 130, 256), (16, 1000, 2560), (12, 17, 512), (1, 33, 256), (8, 2560, 6912),
-    (16, 4099, 8192), (7, 3840, 2560),
+    (16, 4099, 8192), (7, 3840, 2560), (17, 300, 512), (32, 1000, 2560), (33, 130, 256),
+    (64, 2560, 6912), (50, 4099, 1024),
 ])
 def test_skinny_shapes(m, n, k):
-    """Weight-streaming matrix-core path: ragged N, every row-block / wave split."""
+    """Weight-streaming matrix-core path: ragged N and M, every row-block /
+    wave split and token-group count."""
     w, x = inputs.random_case(20_000 + m * 7 + n * 13 + k, m, n, k, bf16=True)
-    run_case(w, x, bl.BL_PACK2, (bl.BL_PATH_SKINNY, bl.BL_PATH_GEMV))
-    assert bl.forward_path(m, n, k) == (bl.BL_PATH_GEMV if m <= 2 else bl.BL_PATH_SKINNY)
+    run_case(w, x, bl.BL_PACK2, (bl.BL_PATH_SKINNY, bl.BL_PATH_MFMA))
+    if m <= 16:
+        assert bl.forward_path(m, n, k) == (bl.BL_PATH_GEMV if m <= 2 else bl.BL_PATH_SKINNY)
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
