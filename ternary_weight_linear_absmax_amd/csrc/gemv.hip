@@ -316,6 +316,159 @@ __global__ __launch_bounds__(256) void gemv3_kernel(const int8_t *__restrict__ x
     }
 }
 
+// ---- base-3 layout, one token: table decode ----------------------------------
+// A 243-entry table in LDS maps a packed byte to its five codes (digits) in
+// byte lanes (entry.x = digits 0..3, entry.y = digit 4).  Four packed bytes
+// (20 trits) are decoded by four table reads and a 4 x 4 byte transpose
+// (v_perm), which leaves digit i of the four bytes in one dword D_i; the
+// activations of the same 20 k are prearranged once per block into dwords X_i
+// holding x[5j + i] for j = 0..3, so the 20 products are five dot4s.
+// Block layout as in the 2-bit kernel: ks x wr waves, lanes own up to two
+// 16-byte chunks (80 trits) of every row of the block.
+__device__ inline uint32_t perm_b(uint32_t a, uint32_t b, uint32_t sel)
+{
+    return __builtin_amdgcn_perm(a, b, sel);
+}
+
+// X[g][i] for group g (20 k) of an 80-activation chunk: bytes x[20g + 5j + i].
+__device__ inline void arrange_x80(const uint32_t (&r)[20], uint32_t (&X)[4][5])
+{
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int idx = 20 * g + 5 * j + i;
+                v |= ((r[idx >> 2] >> (8 * (idx & 3))) & 0xFFu) << (8 * j);
+            }
+            X[g][i] = v;
+        }
+}
+
+// sum over the 20 trits of packed word w (4 bytes) against X[5].
+__device__ inline int dot_word3(uint32_t w, const uint32_t (&X)[5], const uint2 *lut)
+{
+    const uint2 e0 = lut[w & 0xFFu], e1 = lut[(w >> 8) & 0xFFu];
+    const uint2 e2 = lut[(w >> 16) & 0xFFu], e3 = lut[w >> 24];
+    const uint32_t t01l = perm_b(e1.x, e0.x, 0x05010400u), t01h = perm_b(e1.x, e0.x, 0x07030602u);
+    const uint32_t t23l = perm_b(e3.x, e2.x, 0x05010400u), t23h = perm_b(e3.x, e2.x, 0x07030602u);
+    const uint32_t d0 = perm_b(t23l, t01l, 0x05040100u), d1 = perm_b(t23l, t01l, 0x07060302u);
+    const uint32_t d2 = perm_b(t23h, t01h, 0x05040100u), d3 = perm_b(t23h, t01h, 0x07060302u);
+    const uint32_t u01 = perm_b(e1.y, e0.y, 0x05010400u), u23 = perm_b(e3.y, e2.y, 0x05010400u);
+    const uint32_t d4 = perm_b(u23, u01, 0x05040100u);
+    int a = __builtin_amdgcn_sdot4((int)d0, (int)X[0], 0, false);
+    a = __builtin_amdgcn_sdot4((int)d1, (int)X[1], a, false);
+    a = __builtin_amdgcn_sdot4((int)d2, (int)X[2], a, false);
+    a = __builtin_amdgcn_sdot4((int)d3, (int)X[3], a, false);
+    return __builtin_amdgcn_sdot4((int)d4, (int)X[4], a, false);
+}
+
+template <int CPL, int ST>
+__global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv3lut_kernel(
+    const int8_t *__restrict__ xq, const int32_t *__restrict__ rowsum, int64_t k,
+    const uint4 *__restrict__ packed, int64_t n, int64_t chunks, int64_t share, Out out,
+    int64_t ldy, int64_t m0, int ks)
+{
+    constexpr int R = GEMV_R, RB = GEMV_R * ST;
+    __shared__ uint2 lut[256];
+    __shared__ int part[GEMV_KS_MAX][GEMV_KS_MAX * RB];
+    const int wr = (int)(blockDim.x >> 6) / ks;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kw = wave % ks, rw = wave / ks;
+    const int64_t blk0 = (int64_t)blockIdx.x * wr * RB;
+    const int64_t row0 = blk0 + (int64_t)rw * RB;
+
+    for (int b = threadIdx.x; b < 243; b += blockDim.x) {
+        uint32_t v = (uint32_t)b, lo = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lo |= (v % 3u) << (8 * i);
+            v /= 3u;
+        }
+        lut[b] = make_uint2(lo, v);
+    }
+
+    int64_t coff[CPL];
+    bool ok[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int64_t c = kw * share + lane + 64 * j;
+        ok[j] = (lane + 64 * j < share) && c < chunks;
+        coff[j] = ok[j] ? c : 0;
+    }
+
+    uint4 w[2][R][CPL];
+    auto load = [&](uint4(&wb)[R][CPL], int s) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            int64_t row = row0 + s * R + r;
+            row = row < n ? row : n - 1;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) wb[r][j] = load_nt16(packed + row * chunks + coff[j]);
+        }
+    };
+    load(w[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    const int e_rr = threadIdx.x;
+    int32_t e_rs = 0;
+    float e_gs = 0.0f;
+    if (threadIdx.x < wr * RB) {
+        e_rs = rowsum[m0];
+        if (!out.acc) e_gs = out.gamma[0] / out.scale[m0];
+    }
+
+    // Activations of this lane's chunks (80 each), prearranged; pieces past K
+    // (K a multiple of 16) and chunks the lane does not own are zero.
+    uint32_t X[CPL][4][5];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        uint32_t r[20];
+        const int64_t k0 = 80 * coff[j];
+#pragma unroll
+        for (int d = 0; d < 5; ++d) {
+            uint4 v = zero4();
+            if (ok[j] && k0 + 16 * d < k) v = load16(xq + m0 * k + k0 + 16 * d);
+            r[4 * d] = v.x; r[4 * d + 1] = v.y; r[4 * d + 2] = v.z; r[4 * d + 3] = v.w;
+        }
+        arrange_x80(r, X[j]);
+    }
+    __syncthreads();   // table ready
+
+#pragma unroll
+    for (int s = 0; s < ST; ++s) {
+        if (s + 1 < ST) load(w[(s + 1) & 1], s + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int b = s & 1;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            int a = 0;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                a += dot_word3(w[b][r][j].x, X[j][0], lut);
+                a += dot_word3(w[b][r][j].y, X[j][1], lut);
+                a += dot_word3(w[b][r][j].z, X[j][2], lut);
+                a += dot_word3(w[b][r][j].w, X[j][3], lut);
+            }
+            const int v = wave_sum_dpp(a);
+            if (lane == 63) part[kw][rw * RB + s * R + r] = v;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < wr * RB && blk0 + e_rr < n) {
+        int sum = 0;
+        for (int q = 0; q < ks; ++q) sum += part[q][e_rr];
+        const int32_t acc = sum - e_rs;
+        const int64_t idx = m0 * ldy + blk0 + e_rr;
+        if (out.acc)
+            out.acc[idx] = acc;
+        else
+            out.y[idx] = (float)acc * e_gs;
+    }
+}
+
 // Launch shape of the 2-bit GEMV for (N, K): waves per block KS (so that each
 // lane holds at most 2 chunks of activations per token), chunks per lane CPL,
 // and steps per block ST (a power of two, about 1792 waves in total).
@@ -431,6 +584,24 @@ hipError_t launch_gemv_pack3(const int8_t *xq, const int32_t *rowsum, int64_t m,
                              const uint8_t *packed, int64_t n, int64_t k, Out out, hipStream_t s)
 {
     const bool al = (k % 16) == 0;
+    const int64_t chunks3 = pack3_pitch(k) / 16;
+    if (m == 1 && al && chunks3 <= (int64_t)GEMV_KS_MAX * 128) {
+        // one token: table decode, shaped like the 2-bit kernel
+        const Gemv2Shape sh = gemv2_shape(n, chunks3, 1);
+        const int64_t rb = (int64_t)GEMV_R * sh.st * sh.wr;
+        const dim3 grid((unsigned)((n + rb - 1) / rb)), block((unsigned)(64 * sh.ks * sh.wr));
+        const uint4 *pk = (const uint4 *)packed;
+#define G3_CASE(CPL_, ST_)                                                                      \
+        if (sh.cpl == CPL_ && sh.st == ST_) {                                                   \
+            hipLaunchKernelGGL((gemv3lut_kernel<CPL_, ST_>), grid, block, 0, s, xq, rowsum, k,  \
+                               pk, n, chunks3, sh.share, out, n, (int64_t)0, sh.ks);            \
+            return hipGetLastError();                                                           \
+        }
+        G3_CASE(1, 1) G3_CASE(1, 2) G3_CASE(1, 4) G3_CASE(1, 8)
+        G3_CASE(2, 1) G3_CASE(2, 2) G3_CASE(2, 4) G3_CASE(2, 8)
+#undef G3_CASE
+        return hipErrorInvalidValue;
+    }
     for (int64_t m0 = 0; m0 < m; m0 += 4) {
         const int64_t mt = (m - m0) < 4 ? (m - m0) : 4;
         hipError_t e;

@@ -87,6 +87,14 @@ def test_skinny_shapes(m, n, k):
         assert bl.forward_path(m, n, k) == (bl.BL_PATH_GEMV if m <= 2 else bl.BL_PATH_SKINNY)
 
 
+@pytest.mark.parametrize("n,k", [(129, 16), (77, 1040), (1000, 8000), (33, 80), (2049, 5120)])
+def test_base3_one_token_shapes(n, k):
+    """Table-decoded base-3 GEMV (one token, K a multiple of 16): ragged N,
+    chunks of 80 trits that run past K, one and two chunks per lane."""
+    w, x = inputs.random_case(50_000 + n + k, 1, n, k, bf16=True)
+    run_case(w, x, bl.BL_PACK3, (bl.BL_PATH_AUTO,))
+
+
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_ragged_shapes_fp32_unaligned_k(layout):
     w, x = inputs.random_case(555, 6, 150, 201, bf16=False)
