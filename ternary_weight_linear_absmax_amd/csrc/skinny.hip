@@ -37,6 +37,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int SK_CHUNK = 256;   // k per chunk
 constexpr int SK_MAX_KS = 8;
 constexpr int64_t SK_MAX_M = 64;   // four groups of 16 token slots
+#ifndef SKINNY_CH
+#define SKINNY_CH 1                   // chunks per step (2 and 4 measured slower)
+#endif
 
 __device__ inline v4i unpack_word16(uint32_t w)
 {
@@ -53,15 +56,15 @@ __device__ inline uint32_t word_at(const uint4 &v, int u)
     return u == 0 ? v.x : u == 1 ? v.y : u == 2 ? v.z : v.w;
 }
 
-template <int RB, int TG>
+template <int RB, int TG, int CH>
 struct SkinnyLoads {
-    uint4 w[RB];      // 16 packed bytes per row block
-    uint4 x[TG][4];   // 64 activation bytes per token group
+    uint4 w[CH][RB];      // 16 packed bytes per chunk and row block
+    uint4 x[CH][TG][4];   // 64 activation bytes per chunk and token group
 };
 
 // TG groups of 16 token slots (M <= 16 TG); every unpacked weight operand
 // feeds TG MFMAs.
-template <int RB, int KS, int TG>
+template <int RB, int KS, int TG, int CH>
 __global__ __launch_bounds__(64 * KS) void skinny_kernel(const int8_t *__restrict__ xq,
                                                          const int32_t *__restrict__ rowsum,
                                                          int64_t m, int64_t k,
@@ -97,15 +100,26 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(const int8_t *__restric
         e_g[g] = out.acc ? 0.0f : out.gamma[0] / out.scale[tok];
     }
 
-    auto load = [&](SkinnyLoads<RB, TG> &L, int c) __attribute__((always_inline)) {
-        const int cc = c < nchunks ? c : nchunks - 1;
+    // Step c covers chunks CH c .. CH c + CH - 1, so the four k-block lanes of
+    // a row read 64 CH contiguous packed bytes per step.  Chunks past the end
+    // load a clamped (valid) address and get zero activations.
+    const int ngroups = (nchunks + CH - 1) / CH;
+    auto load = [&](SkinnyLoads<RB, TG, CH> &L, int c) __attribute__((always_inline)) {
+        const int cg = c < ngroups ? c : ngroups - 1;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) L.w[rb] = load_nt16(wrow[rb] + (int64_t)cc * 64);
+        for (int h = 0; h < CH; ++h) {
+            const int ch = CH * cg + h;
+            const int cc = ch < nchunks ? ch : nchunks - 1;
 #pragma unroll
-        for (int g = 0; g < TG; ++g)
+            for (int rb = 0; rb < RB; ++rb) L.w[h][rb] = load_nt16(wrow[rb] + (int64_t)cc * 64);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                L.x[g][q] = load16(xrow[g] + (int64_t)cc * SK_CHUNK + 16 * q);
+            for (int g = 0; g < TG; ++g)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint4 v = load16(xrow[g] + (int64_t)cc * SK_CHUNK + 16 * q);
+                    L.x[h][g][q] = ch < nchunks ? v : make_uint4(0u, 0u, 0u, 0u);
+                }
+        }
     };
 
     v4i acc[RB][TG];
@@ -114,26 +128,29 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(const int8_t *__restric
 #pragma unroll
         for (int g = 0; g < TG; ++g) acc[rb][g] = v4i{0, 0, 0, 0};
 
-    auto compute = [&](const SkinnyLoads<RB, TG> &L) __attribute__((always_inline)) {
+    auto compute = [&](const SkinnyLoads<RB, TG, CH> &L) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int h = 0; h < CH; ++h)
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                const v4i a = unpack_word16(word_at(L.w[rb], u));
+            for (int u = 0; u < 4; ++u)
 #pragma unroll
-                for (int g = 0; g < TG; ++g) {
-                    const v4i xb = v4i{(int)L.x[g][u].x, (int)L.x[g][u].y, (int)L.x[g][u].z,
-                                       (int)L.x[g][u].w};
-                    acc[rb][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, xb, acc[rb][g], 0, 0, 0);
+                for (int rb = 0; rb < RB; ++rb) {
+                    const v4i a = unpack_word16(word_at(L.w[h][rb], u));
+#pragma unroll
+                    for (int g = 0; g < TG; ++g) {
+                        const uint4 &xv = L.x[h][g][u];
+                        const v4i xb = v4i{(int)xv.x, (int)xv.y, (int)xv.z, (int)xv.w};
+                        acc[rb][g] =
+                            __builtin_amdgcn_mfma_i32_16x16x64_i8(a, xb, acc[rb][g], 0, 0, 0);
+                    }
                 }
-            }
     };
 
-    // Chunks wave, wave + KS, ...: one chunk of loads in flight ahead of the
-    // compute.  Loads are unconditional (clamped chunk index), so the waits
+    // Steps wave, wave + KS, ...: one step of loads in flight ahead of the
+    // compute.  Loads are unconditional (clamped step index), so the waits
     // are exact; a step past the end computes nothing.
-    const int steps = (nchunks - wave + KS - 1) / KS;
-    SkinnyLoads<RB, TG> cur, nxt;
+    const int steps = (ngroups - wave + KS - 1) / KS;
+    SkinnyLoads<RB, TG, CH> cur, nxt;
     load(cur, wave);
     for (int s = 0; s < steps; ++s) {
         load(nxt, wave + KS * (s + 1));
@@ -179,8 +196,9 @@ hipError_t launch_rb_ks(const int8_t *xq, const int32_t *rowsum, int64_t m,
                         const uint8_t *packed, int64_t n, int64_t k, Out out, hipStream_t s)
 {
     const int64_t blocks = (n + 16 * RB - 1) / (16 * RB);
-    hipLaunchKernelGGL((skinny_kernel<RB, KS, TG>), dim3((unsigned)blocks), dim3(64 * KS), 0, s,
-                       xq, rowsum, m, k, packed, n, pack2_pitch(k), out, (int64_t)n);
+    hipLaunchKernelGGL((skinny_kernel<RB, KS, TG, SKINNY_CH>), dim3((unsigned)blocks),
+                       dim3(64 * KS), 0, s, xq, rowsum, m, k, packed, n, pack2_pitch(k), out,
+                       (int64_t)n);
     return hipGetLastError();
 }
 
@@ -191,7 +209,7 @@ hipError_t launch_tg(const int8_t *xq, const int32_t *rowsum, int64_t m, const u
     // Rows per wave (16 RB) and waves per block (KS): keep about 2048 waves
     // in flight, with RB as large as that allows (RB row blocks share one
     // activation fragment), and the partial sums within 64 KB of LDS.
-    const int64_t chunks = k / SK_CHUNK;
+    const int64_t chunks = (k / SK_CHUNK + SKINNY_CH - 1) / SKINNY_CH;   // steps along K
     const int64_t target = 2048;
     const int rb_max = TG >= 4 ? 2 : 4;
     int rb = rb_max;
