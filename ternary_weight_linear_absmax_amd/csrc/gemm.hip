@@ -165,6 +165,12 @@ __device__ __forceinline__ void st_a(uint8_t *lds_buf, const uint4 (&r)[BM / 32]
 #ifndef GEMM_NA
 #define GEMM_NA 2
 #endif
+#ifndef GEMM_SPECIALISED
+#define GEMM_SPECIALISED 1
+#endif
+#ifndef GEMM3_R
+#define GEMM3_R 3
+#endif
 #ifndef GEMM_NB
 #define GEMM_NB 4
 #endif
@@ -400,6 +406,238 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
     }
 }
 
+// ---- warp-specialised variant ------------------------------------------------
+// Eight waves: four math waves (the 2 x 2 arrangement above) and four
+// producer waves.  With one math wave per SIMD, a wave that issues the stage's
+// global loads stalls its own MFMAs while the loads are accepted; here the
+// producers own every global load, and the math waves read both operands from
+// LDS.  LDS holds a ring of NS = 3 stages (activations [BM][LDA] and packed
+// weights [BN][LDB]); producers keep R stages of loads in flight in registers.
+// Iteration j (one block barrier each):
+//   producers: write stage j + 2 from registers to LDS slot (j + 2) % 3, then
+//              issue the global loads of stage j + 2 + R;
+//   math:      read the fragments of stage j + 1 from slot (j + 1) % 3 and run
+//              the MFMAs of stage j from registers.
+// A slot is rewritten two iterations after its stage was read, so one barrier
+// per iteration orders every access.  Activation pieces past K are zero;
+// weight bytes past the row are clamped (they meet zero activations).
+constexpr int LDB = 48;   // LDS row of a packed weight tile (32 bytes + pad)
+constexpr int G3_NS = 3;
+
+template <int WM, int WN, int R>
+__global__ __launch_bounds__(512) void gemm3_kernel(const int8_t *__restrict__ xq,
+                                                    const int32_t *__restrict__ rowsum,
+                                                    int64_t m, int64_t k,
+                                                    const uint8_t *__restrict__ packed, int64_t n,
+                                                    int64_t pitch, int tiles_m, int64_t tiles,
+                                                    int64_t per_xcd, int splits, int stages_per,
+                                                    Out out, int64_t ldy, int32_t *__restrict__ ws)
+{
+    constexpr int BM = 64 * WM, BN = 64 * WN;
+    constexpr int SA = BM * LDA, SB = BN * LDB, SS = SA + SB;     // bytes per stage slot
+    constexpr int PA = BM / 32;                                   // activation pieces / producer
+    constexpr int PB = (BN * 2 + 255) / 256;                      // weight pieces / producer
+    __shared__ __attribute__((aligned(16))) uint8_t lds[G3_NS * SS];
+    const int64_t t = tile_of_block(blockIdx.x, per_xcd);
+    if (t >= tiles * splits) return;
+    const int64_t tile = t / splits;
+    const int split = (int)(t % splits);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const bool producer = wave >= 4;
+    const int tm = (int)(tile % tiles_m);
+    const int64_t tn = tile / tiles_m;
+    const int64_t m0 = (int64_t)tm * BM, n0 = tn * BN;
+    const int nk_total = (int)((k + BK - 1) / BK);
+    const int kt0 = split * stages_per;
+    const int kt1 = kt0 + stages_per < nk_total ? kt0 + stages_per : nk_total;
+    const int nk = kt1 - kt0;
+    if (nk <= 0) return;
+    constexpr int U3 = G3_NS * R / gcd_int(G3_NS, R);
+    constexpr int U = U3 % 2 == 0 ? U3 : 2 * U3;   // ring slots and fragment parity fixed per J
+
+    if (producer) {
+        const int pt = threadIdx.x - 256;
+        // per-thread sources, fixed for the loop (rows clamped into the matrices)
+        uint32_t aoff[PA], alds[PA];
+        int acol[PA];
+#pragma unroll
+        for (int i = 0; i < PA; ++i) {
+            const int e = pt + 256 * i;
+            int64_t gm = m0 + (e >> 3);
+            gm = gm < m ? gm : m - 1;
+            acol[i] = (e & 7) * 16;
+            aoff[i] = (uint32_t)(gm * k + acol[i]);
+            alds[i] = (uint32_t)((e >> 3) * LDA + acol[i]);
+        }
+        uint32_t boff[PB], blds[PB];
+        int bhalf[PB];
+        bool bon[PB];
+#pragma unroll
+        for (int i = 0; i < PB; ++i) {
+            const int e = pt + 256 * i;
+            bon[i] = e < BN * 2;
+            int64_t row = n0 + (e >> 1);
+            row = row < n ? row : n - 1;
+            bhalf[i] = 16 * (e & 1);
+            boff[i] = (uint32_t)(row * pitch);
+            blds[i] = (uint32_t)(SA + (e >> 1) * LDB + 16 * (e & 1));
+        }
+        uint4 ra[R][PA], rb[R][PB];
+        auto gload = [&](uint4 (&a)[PA], uint4 (&b)[PB], int st) __attribute__((always_inline)) {
+            const int sc = st < nk ? st : nk - 1;
+            const int64_t k0 = (int64_t)(kt0 + sc) * BK;
+#pragma unroll
+            for (int i = 0; i < PA; ++i) {
+                const int64_t kk = k0 + acol[i] < k ? k0 : k - 16 - acol[i];
+                a[i] = load16(xq + aoff[i] + kk);
+            }
+#pragma unroll
+            for (int i = 0; i < PB; ++i) {
+                int64_t byte = k0 / 4 + bhalf[i];
+                byte = byte + 16 <= pitch ? byte : pitch - 16;
+                b[i] = load_nt16(packed + boff[i] + byte);
+            }
+        };
+        auto lstore = [&](const uint4 (&a)[PA], const uint4 (&b)[PB], int st)
+            __attribute__((always_inline)) {
+            uint8_t *slot = lds + (st % G3_NS) * SS;
+            const int64_t k0 = (int64_t)(kt0 + st) * BK;
+#pragma unroll
+            for (int i = 0; i < PA; ++i)
+                *(uint4 *)(slot + alds[i]) = (k0 + acol[i] < k) ? a[i] : zero4();
+#pragma unroll
+            for (int i = 0; i < PB; ++i)
+                if (bon[i]) *(uint4 *)(slot + blds[i]) = b[i];
+        };
+        // prologue: stages 0 and 1 straight into LDS, stages 2 .. 2+R-1 in flight
+        {
+            uint4 a0[PA], b0[PB], a1[PA], b1[PB];
+            gload(a0, b0, 0);
+            gload(a1, b1, 1);
+#pragma unroll
+            for (int r = 0; r < R; ++r) gload(ra[(2 + r) % R], rb[(2 + r) % R], 2 + r);
+            lstore(a0, b0, 0);
+            if (nk > 1) lstore(a1, b1, 1);
+        }
+        __syncthreads();
+        auto iter = [&](auto jc, int j) __attribute__((always_inline)) {
+            constexpr int J = decltype(jc)::value;
+            constexpr int RS = (J + 2) % R;
+            if (j + 2 < nk) lstore(ra[RS], rb[RS], j + 2);
+            gload(ra[RS], rb[RS], j + 2 + R);
+            __syncthreads();
+        };
+        const int nu = nk - nk % U;
+        for (int j = 0; j < nu; j += U)
+            static_for<U>([&](auto jc) __attribute__((always_inline)) { iter(jc, j + jc); });
+        static_for<U - 1>([&](auto jc) __attribute__((always_inline)) {
+            if (nu + jc < nk) iter(jc, nu + jc);
+        });
+        return;
+    }
+
+    // ---- math waves ----
+    const int wm = wave & 1, wn = wave >> 1;
+    const int h = lane >> 5, l32 = lane & 31;
+    v16i acc[WM][WN];
+#pragma unroll
+    for (int a = 0; a < WM; ++a)
+#pragma unroll
+        for (int s = 0; s < WN; ++s)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][s][r] = 0;
+    int64_t nrow[WN];
+#pragma unroll
+    for (int s = 0; s < WN; ++s) nrow[s] = n0 + wn * 32 * WN + 32 * s + l32;
+
+    struct Frag { v4i a[4][WM]; uint4 b[WN]; };
+    auto read_frag = [&](Frag &f, int st) __attribute__((always_inline)) {
+        const uint8_t *slot = lds + (st % G3_NS) * SS;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int a = 0; a < WM; ++a) {
+                const int row = wm * 32 * WM + 32 * a + l32;
+                const uint4 v = load16(slot + row * LDA + 64 * h + 16 * p);
+                f.a[p][a] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+            }
+#pragma unroll
+        for (int s = 0; s < WN; ++s)
+            f.b[s] = load16(slot + SA + (wn * 32 * WN + 32 * s + l32) * LDB + 16 * h);
+    };
+    auto mma = [&](const Frag &f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            v4i bf[WN];
+#pragma unroll
+            for (int s = 0; s < WN; ++s) bf[s] = unpack_word(word_of(f.b[s], p));
+#pragma unroll
+            for (int a = 0; a < WM; ++a)
+#pragma unroll
+                for (int s = 0; s < WN; ++s)
+                    acc[a][s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[p][a], bf[s], acc[a][s],
+                                                                      0, 0, 0);
+        }
+    };
+    Frag fr[2];
+    __syncthreads();          // stages 0 and 1 are in LDS
+    read_frag(fr[0], 0);
+    auto iter = [&](auto jc, int j) __attribute__((always_inline)) {
+        constexpr int C = decltype(jc)::value & 1;
+        if (j + 1 < nk) read_frag(fr[C ^ 1], j + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(fr[C]);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+    };
+    const int nu = nk - nk % U;
+    for (int j = 0; j < nu; j += U)
+        static_for<U>([&](auto jc) __attribute__((always_inline)) { iter(jc, j + jc); });
+    static_for<U - 1>([&](auto jc) __attribute__((always_inline)) {
+        if (nu + jc < nk) iter(jc, nu + jc);
+    });
+
+    // Epilogue.
+    if (splits > 1) {
+#pragma unroll
+        for (int a = 0; a < WM; ++a)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t gm = m0 + wm * 32 * WM + 32 * a + 8 * (r / 4) + 4 * h + (r % 4);
+#pragma unroll
+                for (int s = 0; s < WN; ++s)
+                    if (gm < m && nrow[s] < n) atomicAdd(ws + gm * n + nrow[s], acc[a][s][r]);
+            }
+        return;
+    }
+    const float gamma = out.acc ? 0.0f : out.gamma[0];
+#pragma unroll
+    for (int a = 0; a < WM; ++a) {
+        int32_t rs[16];
+        float gs[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            int64_t gm = m0 + wm * 32 * WM + 32 * a + 8 * (r / 4) + 4 * h + (r % 4);
+            gm = gm < m ? gm : m - 1;
+            rs[r] = rowsum[gm];
+            gs[r] = out.acc ? 0.0f : gamma / out.scale[gm];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int64_t gm = m0 + wm * 32 * WM + 32 * a + 8 * (r / 4) + 4 * h + (r % 4);
+#pragma unroll
+            for (int s = 0; s < WN; ++s) {
+                if (gm >= m || nrow[s] >= n) continue;
+                const int32_t v = acc[a][s][r] - rs[r];
+                if (out.acc)
+                    out.acc[gm * ldy + nrow[s]] = v;
+                else
+                    out.y[gm * ldy + nrow[s]] = (float)v * gs[r];
+            }
+        }
+    }
+}
+
 // Split-K epilogue: y (or acc) from the summed codes in the workspace, which
 // is cleared again for the next call.
 __global__ __launch_bounds__(256) void splitk_finish_kernel(int32_t *__restrict__ ws,
@@ -422,27 +660,26 @@ struct GemmCfg { int wm, wn, splits; };
 
 GemmCfg gemm_config(int64_t m, int64_t n, int64_t k)
 {
-    // Chosen from timings of every tile/split combination on the 2B-, 3B- and
-    // 70B-class shapes: the largest block tile that still gives most CUs a
-    // tile, else 128 x 128 tiles with the k range split until they do.  Small
-    // M (<= 64 rows) uses 64 x 64 tiles, split when there are few of them.
+    // Chosen from timings of every tile / split combination on the 2B-, 3B-
+    // and 70B-class shapes.  M <= 64, or a product with few 64 x 64 tiles:
+    // 64 x 64 tiles, the k range split in two when there are few of them.
+    // Larger: 128 x 128 tiles when they fill one round of the 256 CUs or many;
+    // 64 x 128 tiles when 128 x 128 ones would spill a few tiles into a second
+    // round; 128 x 128 tiles with the k range split when they are too few.
     const int64_t nk = (k + BK - 1) / BK;
     auto tiles = [&](int wm, int wn) {
         return ((m + 64 * wm - 1) / (64 * wm)) * ((n + 64 * wn - 1) / (64 * wn));
     };
-    auto split_for = [&](int64_t t, int64_t cap) {
-        int64_t s = (192 + t - 1) / t;
-        if (s > cap) s = cap;
-        if (s > nk / 4) s = nk / 4;
-        return (int)(s < 1 ? 1 : s);
-    };
-    if (m <= 64) {
-        const int64_t t = tiles(1, 1);
-        return {1, 1, t >= 192 ? 1 : split_for(t, 4)};
-    }
-    if (tiles(2, 2) >= 192) return {2, 2, 1};
-    if (tiles(2, 1) >= 192) return {2, 1, 1};
-    return {2, 2, split_for(tiles(2, 2), 8)};
+    const int64_t t11 = tiles(1, 1);
+    if (m <= 64 || t11 < 192) return {1, 1, (t11 < 192 && nk >= 16) ? 2 : 1};
+    const int64_t t22 = tiles(2, 2);
+    if (t22 >= 192 && t22 <= 256) return {2, 2, 1};
+    if (t22 > 256 && t22 < 512) return {1, 2, 1};
+    if (t22 >= 512) return {2, 2, 1};
+    int64_t sp = 256 / t22;
+    if (sp > 8) sp = 8;
+    if (sp > nk / 4) sp = nk / 4;
+    return {2, 2, (int)(sp < 1 ? 1 : sp)};
 }
 
 int64_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k)
@@ -466,7 +703,13 @@ hipError_t launch_gemm_cfg(const int8_t *xq, const int32_t *rowsum, int64_t m,
     const dim3 grid((unsigned)(per_xcd * NXCD)), block(256);
     const int64_t pitch = pack2_pitch(k);
     if (ldy < 0) ldy = n;
-    if (k % 16 == 0)
+    // the producer/consumer kernel pays off once a block has two weight-column
+    // blocks per wave (WN >= 2); narrower tiles keep the single-role kernel
+    if (k % 16 == 0 && GEMM_SPECIALISED && WN >= 2)
+        hipLaunchKernelGGL((gemm3_kernel<WM, WN, GEMM3_R>), grid, dim3(512), 0, s, xq, rowsum, m,
+                           k, packed, n, pitch, tiles_m, tiles, per_xcd, splits, stages_per, out,
+                           ldy, ws);
+    else if (k % 16 == 0)
         hipLaunchKernelGGL((gemm2_kernel<WM, WN, true>), grid, block, 0, s, xq, rowsum, m, k,
                            packed, n, pitch, tiles_m, tiles, per_xcd, splits, stages_per, out, ldy,
                            ws);

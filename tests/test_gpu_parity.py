@@ -187,6 +187,32 @@ def test_prefill_shapes_m512_sampled(shape):
     assert 0.40 < zero_frac < 0.50
 
 
+# ---- tiled GEMM block shapes with ragged edges ------------------------------------------------
+
+@pytest.mark.parametrize("m,n,k", [
+    (260, 12850, 272),    # 64 x 128 tiles (about 300 tiles of 128 x 128), K = 2 BK + 16
+    (200, 14083, 400),    # 128 x 128 tiles, one round of the CUs, K = 3 BK + 16
+    (129, 5121, 2000),    # 128 x 128 tiles, k range split three ways, K = 15 BK + 80
+    (70, 3000, 4000),     # 64 x 64 tiles, k range split in two
+])
+def test_tiled_gemm_block_shapes(m, n, k):
+    """Every block tile and split-K choice of the tiled path, each with a
+    partial last tile in M, in N and in K (sampled tokens, every row)."""
+    w, x = inputs.random_case(70_000 + m + n + k, m, n, k, bf16=True)
+    t, g, packed_ref = oracle_weights(w, bl.BL_PACK2)
+    q_ref, s_ref, _ = oracle.quantize_act(x)
+    packed, gamma = bl.quantize_weights(dev(w))
+    np.testing.assert_array_equal(host(packed), packed_ref)
+    xq, scale, rowsum = bl.quantize_act(dev(x))
+    assert bl.forward_path(m, n, k) == bl.BL_PATH_MFMA
+    acc = host(bl.matmul_i32(xq, rowsum, packed, n, k))
+    y = host(bl.forward(xq, scale, rowsum, packed, gamma, n, k))
+    rows = np.array(sorted(r for r in {0, 1, 63, 64, 127, 128, m // 2, m - 2, m - 1} if r < m))
+    acc_ref = oracle.matmul_i32(q_ref[rows], t)
+    np.testing.assert_array_equal(acc[rows], acc_ref)
+    assert_y_close(y[rows], oracle.rescale(acc_ref, s_ref[rows], g), acc_ref)
+
+
 # ---- 70B-class layer (single GPU), M in {1, 16, 128}; base-3 at M = 1 -------------------------
 
 @pytest.mark.parametrize("shape", range(len(inputs.XL_SHAPES)))
