@@ -21,7 +21,6 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 from __future__ import annotations
 
 import argparse
-import ctypes
 import json
 import os
 import sys
@@ -152,50 +151,44 @@ def main():
     step_bytes = sum(m["bytes"] for m in mats) * args.layers
     log(f"decode workload ready: {step_bytes / 1e6:.1f} MB packed per step")
 
-    lib = bl.load()
-
-    def quant_act_into(m):
-        # writes into the matrix's resident xq / scale / rowsum buffers
-        stream_ptr = torch.cuda.current_stream().cuda_stream
-        st = lib.bitlinear_quantize_act(ctypes.c_void_p(m["x"].data_ptr()), bl.BL_BF16, 1, m["k"],
-                                        ctypes.c_void_p(m["xq"].data_ptr()),
-                                        ctypes.c_void_p(m["scale"].data_ptr()),
-                                        ctypes.c_void_p(m["rowsum"].data_ptr()),
-                                        ctypes.c_void_p(stream_ptr))
-        assert st == 0, st
-
     def step():
-        # per matrix: quantise its input, then the product (two launches)
+        # per matrix: quantise its input and multiply (bitlinear_quantize_forward)
         for layer in range(args.layers):
             for m in mats:
                 bl.quantize_forward(m["x"], m["copies"][layer], m["gamma"], m["n"], y=m["y"],
                                     xq=m["xq"], scale=m["scale"], rowsum=m["rowsum"])
 
-    # one step = one replay of the captured step (240 launches at 30 layers)
+    # one step = one replay of the captured step (120 launches at 30 layers)
     ms_step = graph_time(step, args.steps, args.warmup)
     ms_step_eager = time_loop(step, max(2, args.steps // 10), 1)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"decode step {ms_step * 1e3:.1f} us (eager launches: {ms_step_eager * 1e3:.1f} us)"
         f" -> {value:.1f} GB/s")
 
-    # dominant kernel: the M=1 GEMV, timed alone over the same rotation
-    def gemv_only():
-        for layer in range(args.layers):
-            for m in mats:
-                bl.forward(m["xq"], m["scale"], m["rowsum"], m["copies"][layer], m["gamma"],
-                           m["n"], m["k"], y=m["y"])
+    # dominant kernel: the step is one launch per matrix (one-token quantisation
+    # fused into the 2-bit GEMV), so its per-launch time is the step's
     launches = args.layers * len(mats)
-    ms_gemv = graph_time(gemv_only, args.steps, args.warmup)
-    us_per_launch = ms_gemv * 1e3 / launches
+    us_per_launch = ms_step * 1e3 / launches
     bytes_per_launch = step_bytes / launches
     achieved = bytes_per_launch / (us_per_launch * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(),
-                "kernel": "gemv2_kernel (decode, M=1); per-launch time = graph replay / launches",
+                "kernel": "gemv2_kernel<1,CPL,ST,true,bf16> (decode, M=1, activation "
+                          "quantisation inside); per-launch time = graph replay / launches",
                 "avg_launch_us": round(us_per_launch, 3),
                 "algorithmic_bytes_per_launch": int(bytes_per_launch)}
-    log(f"decode GEMV alone: {us_per_launch:.2f} us/launch, {achieved:.1f} GB/s")
+
+    # the same GEMV on pre-quantised activations, timed alone over the same rotation
+    def gemv_only():
+        for layer in range(args.layers):
+            for m in mats:
+                bl.forward(m["xq"], m["scale"], m["rowsum"], m["copies"][layer], m["gamma"],
+                           m["n"], m["k"], y=m["y"])
+    ms_gemv = graph_time(gemv_only, args.steps, args.warmup)
+    roofline["prequantised_gemv_us_per_launch"] = round(ms_gemv * 1e3 / launches, 3)
+    log(f"decode per launch: {us_per_launch:.2f} us with quantisation, "
+        f"{ms_gemv * 1e3 / launches:.2f} us GEMV alone")
 
     # ---------------- extra: 70B-class layer and prefill ------------------------
     extra = {}

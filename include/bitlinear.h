@@ -183,12 +183,16 @@ int bitlinear_matmul_i32(const int8_t *xq, const int32_t *rowsum, int64_t M,
  * [cheatsheet.md summary, "What is BitNet b1.58?": activations scaled per token
  *  in front of every BitLinear; asi.tokyo 2B4T article, packing paragraph]
  *
- * bitlinear_quantize_act(x, dtype, M, K, xq, scale, rowsum) followed by
- * bitlinear_forward_ex(xq, scale, rowsum, M, packed, layout, gamma, N, K, y,
- * workspace, workspace_bytes, path), enqueued back to back on `stream` after
- * all arguments of both have been checked: xq, scale and rowsum (all
- * required) are written, and y is bit-identical to the two calls.  N == 0
- * only quantises. */
+ * Same results as bitlinear_quantize_act(x, dtype, M, K, xq, scale, rowsum)
+ * followed by bitlinear_forward_ex(xq, scale, rowsum, M, packed, layout,
+ * gamma, N, K, y, workspace, workspace_bytes, path), after all arguments of
+ * both have been checked: xq, scale and rowsum (all required) are written, and
+ * y is bit-identical to the two calls.  N == 0 only quantises.  One token on
+ * the vector path with the 2-bit layout (M == 1, K % 16 == 0, K <= 16384;
+ * fp32 tokens longer than 8192 on matrices of few rows excepted) is one
+ * launch: every block of the product quantises the token itself (same
+ * arithmetic) and the first block also stores xq, scale and rowsum; other
+ * shapes are two launches back to back on `stream`.  x must not overlap xq. */
 int bitlinear_quantize_forward(const void *x, int dtype, int64_t M, int64_t K, int8_t *xq,
                                float *scale, int32_t *rowsum, const uint8_t *packed, int layout,
                                const float *gamma, int64_t N, float *y, void *workspace,

@@ -202,6 +202,9 @@ int bitlinear_quantize_forward(const void *x, int dtype, int64_t M, int64_t K, i
     if (need > 0 && !al16(workspace)) return BL_ERR_ALIGN;
 
     bl::Out out{scale, gamma, y, nullptr};
+    if (layout == BL_PACK2 && path == BL_PATH_GEMV && bl::gemv_fused_supported(M, N, K, dtype))
+        return hip_status(bl::launch_gemv_pack2_fused(x, dtype, xq, scale, rowsum, packed, N, K,
+                                                      out, stream));
     hipError_t e = bl::launch_quant_act(x, dtype, M, K, xq, scale, rowsum, stream);
     if (e != hipSuccess) return BL_ERR_HIP;
     if (layout == BL_PACK3)

@@ -56,6 +56,26 @@ __device__ inline int wave_sum_dpp(int v)
     return v;
 }
 
+// Maximum of non-negative floats over the wave, same DPP pattern (disabled
+// lanes contribute 0, the identity here); lane 63 holds the result.
+template <int CTRL, int ROWS>
+__device__ inline float max_dpp_step(float v)
+{
+    const int t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false);
+    return fmaxf(v, __int_as_float(t));
+}
+
+__device__ inline float wave_max_dpp(float v)
+{
+    v = max_dpp_step<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+    v = max_dpp_step<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+    v = max_dpp_step<0x141, 0xF>(v);   // row_half_mirror
+    v = max_dpp_step<0x140, 0xF>(v);   // row_mirror
+    v = max_dpp_step<0x142, 0xA>(v);   // row_bcast:15
+    v = max_dpp_step<0x143, 0xC>(v);   // row_bcast:31
+    return v;
+}
+
 // 64 activation bytes k = 64c .. 64c+63 of one token; zero past K.  AL: K is a
 // multiple of 16, so every 16-byte piece is wholly inside or outside the row.
 template <bool AL>
@@ -102,17 +122,36 @@ constexpr int GEMV_WAVES = 4;   // waves per block when K is short
 #define GEMV_PF 1               // steps of weight loads in flight ahead
 #endif
 
-template <int MT, int CPL, int ST, bool AL>
+// One token quantised inside the product (QDT = input type, VPT = 16-byte
+// input vectors per thread): the block's threads split the token, reduce
+// max |x| over the block, quantise their vectors with the same arithmetic as
+// the activation quantiser (s = 127 / max|x|, q = rint(x s) clamped) into an
+// LDS copy of the int8 token, and sum the bytes for the row sum; every lane
+// then reads its chunks' activations from LDS.  Block 0 also writes xq, s and
+// the row sum.
+struct FuseQ {
+    const void *x;        // [K] input token (bf16 or fp32)
+    int8_t *xq;           // [K]
+    float *scale;         // [1]
+    int32_t *rowsum;      // [1]
+};
+
+template <int MT, int CPL, int ST, bool AL, int QDT = -1, int VPT = 0>
 __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
     const int8_t *__restrict__ xq, const int32_t *__restrict__ rowsum, int64_t k,
     const uint4 *__restrict__ packed, int64_t n, int64_t chunks, int64_t share, Out out,
-    int64_t ldy, int64_t m0, int ks)
+    int64_t ldy, int64_t m0, int ks, FuseQ fq)
 {
     constexpr int R = GEMV_R, RB = GEMV_R * ST;
+    constexpr bool FUSED = QDT >= 0;
+    static_assert(!FUSED || (MT == 1 && AL), "fused quantisation: one token, K % 16 == 0");
     // A block is ks x wr waves: wave w takes k-share w % ks of the rows of
     // row group w / ks; the block's wr * RB rows are contiguous, and their
     // outputs are written together at the end.
     __shared__ int part[GEMV_KS_MAX][GEMV_KS_MAX * RB][MT];
+    __shared__ float q_max[GEMV_KS_MAX];
+    __shared__ int q_sum[GEMV_KS_MAX];
+    extern __shared__ uint4 q_lds[];   // fused: the int8 token, K bytes
     const int wr = (int)(blockDim.x >> 6) / ks;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kw = wave % ks, rw = wave / ks;
@@ -126,6 +165,20 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
         const int64_t c = kw * share + lane + 64 * j;
         ok[j] = (lane + 64 * j < share) && c < chunks;
         coff[j] = ok[j] ? c : 0;
+    }
+
+    // fused: the token's input vectors are loaded before the weights, so that
+    // the quantisation waits only for them while the weight loads stay in flight
+    constexpr int QE = QDT == DT_BF16 ? 8 : 4;   // values per 16-byte input vector
+    uint4 raw[FUSED ? VPT : 1];
+    if constexpr (FUSED) {
+        const int nvec = (int)(k / QE);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int i = threadIdx.x + (int)blockDim.x * v;
+            raw[v] = i < nvec ? load16((const uint8_t *)fq.x + 16 * (int64_t)i) : zero4();
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // weight ring: GEMV_PF steps of loads in flight ahead of the arithmetic
@@ -151,21 +204,90 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
     const int e_rr = threadIdx.x / MT, e_t = threadIdx.x % MT;
     int32_t e_rs = 0;
     float e_gs = 0.0f;
-    if (threadIdx.x < nout) {
+    if (!FUSED && threadIdx.x < nout) {
         e_rs = rowsum[m0 + e_t];
         if (!out.acc) e_gs = out.gamma[0] / out.scale[m0 + e_t];
     }
 
     uint4 xv[MT][CPL][4];
+    float q_s = 0.0f;
+    if constexpr (!FUSED) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+        for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            load_x64<AL>(xq + (m0 + t) * k, k, coff[j], xv[t][j]);
-            if (!ok[j])
+            for (int j = 0; j < CPL; ++j) {
+                load_x64<AL>(xq + (m0 + t) * k, k, coff[j], xv[t][j]);
+                if (!ok[j])
 #pragma unroll
-                for (int d = 0; d < 4; ++d) xv[t][j][d] = zero4();
+                    for (int d = 0; d < 4; ++d) xv[t][j][d] = zero4();
+            }
+    } else {
+        const int nvec = (int)(k / QE), nthr = (int)blockDim.x;
+        const float gamma = out.gamma[0];
+        float amax = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const uint32_t u[4] = {raw[v].x, raw[v].y, raw[v].z, raw[v].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                amax = QDT == DT_BF16
+                           ? fmaxf(amax, fmaxf(fabsf(bf16_lo(u[i])), fabsf(bf16_hi(u[i]))))
+                           : fmaxf(amax, fabsf(__uint_as_float(u[i])));
         }
+        amax = wave_max_dpp(amax);
+        if (lane == 63) q_max[wave] = amax;
+        __syncthreads();
+        amax = 0.0f;
+        for (int q = 0; q < nthr / 64; ++q) amax = fmaxf(amax, q_max[q]);
+        q_s = act_scale(amax);
+
+        int sum = 0;
+        uint8_t *ql = (uint8_t *)q_lds;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int i = threadIdx.x + nthr * v;
+            if (i >= nvec) continue;
+            const uint32_t u[4] = {raw[v].x, raw[v].y, raw[v].z, raw[v].w};
+            if (QDT == DT_BF16) {
+                uint32_t d[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    d[h] = 0;
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int8_t a = quant1(bf16_lo(u[2 * h + e]), q_s);
+                        const int8_t b = quant1(bf16_hi(u[2 * h + e]), q_s);
+                        sum += a + b;
+                        d[h] |= ((uint32_t)(uint8_t)a | ((uint32_t)(uint8_t)b << 8)) << (16 * e);
+                    }
+                }
+                const uint2 qv = make_uint2(d[0], d[1]);
+                *(uint2 *)(ql + 8 * i) = qv;
+                if (blockIdx.x == 0) *(uint2 *)(fq.xq + 8 * (int64_t)i) = qv;
+            } else {
+                uint32_t d = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int8_t a = quant1(__uint_as_float(u[e]), q_s);
+                    sum += a;
+                    d |= (uint32_t)(uint8_t)a << (8 * e);
+                }
+                *(uint32_t *)(ql + 4 * i) = d;
+                if (blockIdx.x == 0) *(uint32_t *)(fq.xq + 4 * (int64_t)i) = d;
+            }
+        }
+        sum = wave_sum_dpp(sum);
+        if (lane == 63) q_sum[wave] = sum;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int64_t e0 = 64 * coff[j] + 16 * d;   // K % 16 == 0: pieces are whole
+                xv[0][j][d] = (ok[j] && e0 < k) ? q_lds[e0 / 16] : zero4();
+            }
+        if (!out.acc) e_gs = gamma / q_s;
+    }
 
 #pragma unroll
     for (int s = 0; s < ST; ++s) {
@@ -190,6 +312,13 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
         }
     }
     __syncthreads();
+    if (FUSED) {
+        for (int q = 0; q < (int)(blockDim.x >> 6); ++q) e_rs += q_sum[q];
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            fq.scale[0] = q_s;
+            fq.rowsum[0] = e_rs;
+        }
+    }
     if (threadIdx.x < nout && blk0 + e_rr < n) {
         int sum = 0;
         for (int q = 0; q < ks; ++q) sum += part[q][e_rr][e_t];
@@ -505,11 +634,63 @@ hipError_t launch2_st(bool al, const int8_t *xq, const int32_t *rowsum, int64_t 
     const dim3 grid((unsigned)((n + rb - 1) / rb)), block((unsigned)(64 * sh.ks * sh.wr));
     if (al)
         hipLaunchKernelGGL((gemv2_kernel<MT, CPL, ST, true>), grid, block, 0, s, xq, rowsum, k,
-                           (const uint4 *)packed, n, chunks, sh.share, out, n, m0, sh.ks);
+                           (const uint4 *)packed, n, chunks, sh.share, out, n, m0, sh.ks,
+                           FuseQ{});
     else
         hipLaunchKernelGGL((gemv2_kernel<MT, CPL, ST, false>), grid, block, 0, s, xq, rowsum, k,
-                           (const uint4 *)packed, n, chunks, sh.share, out, n, m0, sh.ks);
+                           (const uint4 *)packed, n, chunks, sh.share, out, n, m0, sh.ks,
+                           FuseQ{});
     return hipGetLastError();
+}
+
+// Fused one-token launches: input vectors per thread (VPT) from the token
+// length and the block size.
+constexpr int GEMV_FUSED_VPT_MAX = 16;
+
+template <int CPL, int ST, int QDT, int VPT>
+hipError_t launch2_fused_vpt(const FuseQ &fq, int64_t n, int64_t k, const uint8_t *packed,
+                             Out out, const Gemv2Shape &sh, hipStream_t s)
+{
+    const int64_t chunks = pack2_pitch(k) / 16;
+    const int64_t rb = (int64_t)GEMV_R * ST * sh.wr;
+    const dim3 grid((unsigned)((n + rb - 1) / rb)), block((unsigned)(64 * sh.ks * sh.wr));
+    const size_t lds = (size_t)((k + 15) / 16) * 16;
+    hipLaunchKernelGGL((gemv2_kernel<1, CPL, ST, true, QDT, VPT>), grid, block, lds, s,
+                       (const int8_t *)nullptr, (const int32_t *)nullptr, k,
+                       (const uint4 *)packed, n, chunks, sh.share, out, n, (int64_t)0, sh.ks, fq);
+    return hipGetLastError();
+}
+
+template <int CPL, int ST, int QDT>
+hipError_t launch2_fused_dt(const FuseQ &fq, int64_t n, int64_t k, const uint8_t *packed,
+                            Out out, const Gemv2Shape &sh, hipStream_t s)
+{
+    const int64_t nvec = k / (QDT == DT_BF16 ? 8 : 4), nthr = 64 * sh.ks * sh.wr;
+    const int64_t per = (nvec + nthr - 1) / nthr;
+    if (per <= 2) return launch2_fused_vpt<CPL, ST, QDT, 2>(fq, n, k, packed, out, sh, s);
+    if (per <= 4) return launch2_fused_vpt<CPL, ST, QDT, 4>(fq, n, k, packed, out, sh, s);
+    if (per <= 8) return launch2_fused_vpt<CPL, ST, QDT, 8>(fq, n, k, packed, out, sh, s);
+    return launch2_fused_vpt<CPL, ST, QDT, 16>(fq, n, k, packed, out, sh, s);
+}
+
+template <int CPL, int ST>
+hipError_t launch2_fused_st(int dtype, const FuseQ &fq, int64_t n, int64_t k,
+                            const uint8_t *packed, Out out, const Gemv2Shape &sh, hipStream_t s)
+{
+    if (dtype == DT_BF16) return launch2_fused_dt<CPL, ST, DT_BF16>(fq, n, k, packed, out, sh, s);
+    return launch2_fused_dt<CPL, ST, DT_F32>(fq, n, k, packed, out, sh, s);
+}
+
+template <int CPL>
+hipError_t launch2_fused_cpl(int dtype, const FuseQ &fq, int64_t n, int64_t k,
+                             const uint8_t *packed, Out out, const Gemv2Shape &sh, hipStream_t s)
+{
+    switch (sh.st) {
+    case 1: return launch2_fused_st<CPL, 1>(dtype, fq, n, k, packed, out, sh, s);
+    case 2: return launch2_fused_st<CPL, 2>(dtype, fq, n, k, packed, out, sh, s);
+    case 4: return launch2_fused_st<CPL, 4>(dtype, fq, n, k, packed, out, sh, s);
+    default: return launch2_fused_st<CPL, 8>(dtype, fq, n, k, packed, out, sh, s);
+    }
 }
 
 template <int MT, int CPL>
@@ -578,6 +759,27 @@ hipError_t launch_gemv_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+bool gemv_fused_supported(int64_t m, int64_t n, int64_t k, int dtype)
+{
+    // one token, whole 16-value pieces, the int8 token within 16 KB of LDS and
+    // at most 16 input vectors per thread
+    if (m != 1 || n < 1 || k % 16 != 0 || k > 16384) return false;
+    const Gemv2Shape sh = gemv2_shape(n, pack2_pitch(k) / 16, 1);
+    const int64_t nvec = k / (dtype == DT_BF16 ? 8 : 4), nthr = 64 * sh.ks * sh.wr;
+    return nvec <= nthr * GEMV_FUSED_VPT_MAX;
+}
+
+hipError_t launch_gemv_pack2_fused(const void *x, int dtype, int8_t *xq, float *scale,
+                                   int32_t *rowsum, const uint8_t *packed, int64_t n, int64_t k,
+                                   Out out, hipStream_t s)
+{
+    if (!gemv_fused_supported(1, n, k, dtype) || out.acc) return hipErrorInvalidValue;
+    const FuseQ fq{x, xq, scale, rowsum};
+    const Gemv2Shape sh = gemv2_shape(n, pack2_pitch(k) / 16, 1);
+    if (sh.cpl == 1) return launch2_fused_cpl<1>(dtype, fq, n, k, packed, out, sh, s);
+    return launch2_fused_cpl<2>(dtype, fq, n, k, packed, out, sh, s);
 }
 
 hipError_t launch_gemv_pack3(const int8_t *xq, const int32_t *rowsum, int64_t m,

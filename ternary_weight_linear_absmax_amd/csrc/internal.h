@@ -58,6 +58,13 @@ hipError_t launch_glue(int mode, const GlueArgs &a, int64_t m, int64_t k, double
 hipError_t launch_gemv_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
                              const uint8_t *packed, int64_t n, int64_t k, Out out,
                              hipStream_t s);
+// One token (m = 1, k % 16 == 0, k <= 16384): the activation quantiser runs
+// inside the 2-bit vector kernel, one launch; x is bf16 or fp32; xq, scale and
+// rowsum are written as bitlinear_quantize_act would write them.
+bool gemv_fused_supported(int64_t m, int64_t n, int64_t k, int dtype);
+hipError_t launch_gemv_pack2_fused(const void *x, int dtype, int8_t *xq, float *scale,
+                                   int32_t *rowsum, const uint8_t *packed, int64_t n, int64_t k,
+                                   Out out, hipStream_t s);
 // base-3 layout, vector kernel.
 hipError_t launch_gemv_pack3(const int8_t *xq, const int32_t *rowsum, int64_t m,
                              const uint8_t *packed, int64_t n, int64_t k, Out out,

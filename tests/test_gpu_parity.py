@@ -257,6 +257,14 @@ def test_xl_layer(shape):
     (64, 200, 384, True, bl.BL_PACK2, bl.BL_PATH_AUTO),      # tiled GEMM
     (1, 100, 640, True, bl.BL_PACK3, bl.BL_PATH_AUTO),       # base-3
     (1, 2560, 6912, True, bl.BL_PACK2, bl.BL_PATH_AUTO),     # decode "down" shape
+    # one token, quantised inside the vector kernel: two chunks per lane,
+    # four waves per row, partial last chunk, both input types
+    (1, 5000, 8192, True, bl.BL_PACK2, bl.BL_PATH_AUTO),
+    (1, 300, 28672, False, bl.BL_PACK2, bl.BL_PATH_AUTO),    # too long: two launches
+    (1, 100, 8192, False, bl.BL_PACK2, bl.BL_PATH_AUTO),     # 16 input vectors per thread
+    (1, 77, 1040, True, bl.BL_PACK2, bl.BL_PATH_GEMV),
+    (1, 129, 1040, False, bl.BL_PACK2, bl.BL_PATH_AUTO),
+    (1, 40, 16, True, bl.BL_PACK2, bl.BL_PATH_AUTO),
 ])
 def test_quantize_forward(m, n, k, bf16, layout, path):
     w, x = inputs.random_case(40_000 + m * 7 + n * 13 + k, m, n, k, bf16=bf16)
@@ -281,3 +289,17 @@ def test_quantize_forward(m, n, k, bf16, layout, path):
     xq2, s2, r2 = bl.quantize_act(xd)
     y2 = bl.forward(xq2, s2, r2, packed, gamma, n, k, layout, path=path)
     assert np.array_equal(host(y).view(np.uint32), host(y2).view(np.uint32))
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_quantize_forward_zero_token(bf16):
+    """One all-zero token through the fused one-token kernel: s = 1, q = 0,
+    row sum 0, y = 0 exactly."""
+    n, k = 333, 2560
+    w, x = inputs.random_case(41_000 + int(bf16), 1, n, k, bf16=bf16)
+    x[:] = 0
+    packed, gamma = bl.quantize_weights(dev(w))
+    y, xq, scale, rowsum = bl.quantize_forward(dev(x), packed, gamma, n)
+    assert host(scale)[0] == 1.0 and host(rowsum)[0] == 0
+    assert not host(xq).any()
+    assert np.array_equal(host(y), np.zeros((1, n), dtype=np.float32))
