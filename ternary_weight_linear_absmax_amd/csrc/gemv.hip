@@ -3,17 +3,20 @@
 //
 // Source: asi.tokyo BitNet b1.58 2B4T article, packing paragraph: the trits
 // travel packed (four per byte) and are unpacked right next to the arithmetic
-// units, where they are multiplied with the 8-bit activations.  On gfx950 the
-// arithmetic unit is v_dot4_i32_i8: the 2-bit layout is chosen so that
-// (word >> 2i) & 0x03030303 gives four consecutive k as int8 codes t + 1, which
-// dot4 multiplies with four consecutive int8 activations in one instruction.
-// The codes are offset by one, so sum_k (t+1) q = acc + rowsum(q); the row sum
-// from the activation quantiser is subtracted once per output.
+// units, where they are multiplied with the 8-bit activations.  The codes are
+// offset by one, so sum_k (t+1) q = acc + rowsum(q); the row sum from the
+// activation quantiser is subtracted once per output.
 //
-// Two masks avoid two of the four shifts: word & 0x0C0C0C0C is 4x the codes of
-// the second quarter, whose dot products are collected in a separate
-// accumulator and divided by 4 (exactly) at the end: 9 ALU operations per 16
-// trits.
+// Arithmetic of the 2-bit kernel: a packed word masked with 0x33333333 holds
+// eight 2-bit codes in eight nibbles (k = j and 8 + j of its 16 trits), and
+// shifted right by 2 first, the other eight (4 + j, 12 + j).  The activations
+// are split once per block into their low (unsigned) and high (signed) nibbles
+// in the same order, so that v_dot8 (4-bit dot products of eight) gives
+// sum c x = 16 sum c hi + sum c lo: 7 ALU operations per 16 trits.  Kernels
+// that read the activations with the weights use v_dot4 on
+// (word >> 2i) & 0x03030303 (four consecutive k as int8 codes) instead, with
+// two of the four shifts replaced by a second mask whose products are 4x
+// too large and collected apart: 9 operations per 16 trits.
 #include "internal.h"
 
 namespace bl {
@@ -33,6 +36,34 @@ __device__ inline void dot_word(uint32_t w, uint4 x, int &lo, int &hi)
     hi = __builtin_amdgcn_sdot4(u1, (int)x.y, hi, false);
     lo = __builtin_amdgcn_sdot4(u2, (int)x.z, lo, false);
     hi = __builtin_amdgcn_sdot4(u3, (int)x.w, hi, false);
+}
+
+// Nibble form of 16 activation bytes for the 4-bit dot products: x = 16 hi + lo
+// with lo = x & 15 (unsigned) and hi = x >> 4 (signed).  Byte j of l02 holds
+// lo(x[j]) | lo(x[8 + j]) << 4, of h02 the two hi nibbles, and l13 / h13 the
+// same for x[4 + j] and x[12 + j]: the nibble order of a packed word masked
+// with 0x33333333 (codes of k = j and 8 + j) or shifted by 2 first (4 + j,
+// 12 + j).
+__device__ inline uint4 nibble_split(uint4 x)
+{
+    uint4 r;
+    r.x = (x.x & 0x0F0F0F0Fu) | ((x.z & 0x0F0F0F0Fu) << 4);          // l02
+    r.y = ((x.x >> 4) & 0x0F0F0F0Fu) | (x.z & 0xF0F0F0F0u);          // h02
+    r.z = (x.y & 0x0F0F0F0Fu) | ((x.w & 0x0F0F0F0Fu) << 4);          // l13
+    r.w = ((x.y >> 4) & 0x0F0F0F0Fu) | (x.w & 0xF0F0F0F0u);          // h13
+    return r;
+}
+
+// One packed word (16 trits) against 16 activation bytes in nibble form:
+// 4-bit dot products of the codes with the signed high nibbles (ah) and the
+// unsigned low nibbles (al); the word's sum is 16 ah + al.  7 ALU operations.
+__device__ inline void dot8_word(uint32_t w, uint4 xs, int &ah, uint32_t &al)
+{
+    const uint32_t c02 = w & 0x33333333u, c13 = (w >> 2) & 0x33333333u;
+    ah = __builtin_amdgcn_sdot8((int)c02, (int)xs.y, ah, false);
+    ah = __builtin_amdgcn_sdot8((int)c13, (int)xs.w, ah, false);
+    al = __builtin_amdgcn_udot8(c02, xs.x, al, false);
+    al = __builtin_amdgcn_udot8(c13, xs.z, al, false);
 }
 
 template <int LG>
@@ -129,6 +160,9 @@ constexpr int GEMV_WAVES = 4;   // waves per block when K is short
 // LDS copy of the int8 token, and sum the bytes for the row sum; every lane
 // then reads its chunks' activations from LDS.  Block 0 also writes xq, s and
 // the row sum.
+constexpr int GEMV_X_LDS = -2;   // QDT value: int8 token staged in LDS
+constexpr int64_t GEMV_X_LDS_MAX_K = 32768;
+
 struct FuseQ {
     const void *x;        // [K] input token (bf16 or fp32)
     int8_t *xq;           // [K]
@@ -144,7 +178,8 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
 {
     constexpr int R = GEMV_R, RB = GEMV_R * ST;
     constexpr bool FUSED = QDT >= 0;
-    static_assert(!FUSED || (MT == 1 && AL), "fused quantisation: one token, K % 16 == 0");
+    constexpr bool XLDS = QDT == GEMV_X_LDS;   // int8 token staged once per block in LDS
+    static_assert(!(FUSED || XLDS) || (MT == 1 && AL), "one token, K % 16 == 0");
     // A block is ks x wr waves: wave w takes k-share w % ks of the rows of
     // row group w / ks; the block's wr * RB rows are contiguous, and their
     // outputs are written together at the end.
@@ -167,16 +202,19 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
         coff[j] = ok[j] ? c : 0;
     }
 
-    // fused: the token's input vectors are loaded before the weights, so that
-    // the quantisation waits only for them while the weight loads stay in flight
-    constexpr int QE = QDT == DT_BF16 ? 8 : 4;   // values per 16-byte input vector
-    uint4 raw[FUSED ? VPT : 1];
-    if constexpr (FUSED) {
+    // One token read once per block (fused quantisation, or the int8 token
+    // staged in LDS): its 16-byte vectors are loaded before the weights, so
+    // that the first use waits only for them while the weight loads stay in
+    // flight.
+    constexpr int QE = QDT == DT_BF16 ? 8 : QDT == DT_F32 ? 4 : 16;   // values per vector
+    uint4 raw[(FUSED || XLDS) ? VPT : 1];
+    if constexpr (FUSED || XLDS) {
         const int nvec = (int)(k / QE);
+        const uint8_t *src = FUSED ? (const uint8_t *)fq.x : (const uint8_t *)(xq + m0 * k);
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             const int i = threadIdx.x + (int)blockDim.x * v;
-            raw[v] = i < nvec ? load16((const uint8_t *)fq.x + 16 * (int64_t)i) : zero4();
+            raw[v] = i < nvec ? load16(src + 16 * (int64_t)i) : zero4();
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -211,7 +249,22 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
 
     uint4 xv[MT][CPL][4];
     float q_s = 0.0f;
-    if constexpr (!FUSED) {
+    if constexpr (XLDS) {
+        const int nvec = (int)(k / 16);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int i = threadIdx.x + (int)blockDim.x * v;
+            if (i < nvec) q_lds[i] = raw[v];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int64_t e0 = 64 * coff[j] + 16 * d;   // K % 16 == 0: pieces are whole
+                xv[0][j][d] = (ok[j] && e0 < k) ? q_lds[e0 / 16] : zero4();
+            }
+    } else if constexpr (!FUSED) {
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -288,6 +341,12 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
             }
         if (!out.acc) e_gs = gamma / q_s;
     }
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) xv[t][j][d] = nibble_split(xv[t][j][d]);
 
 #pragma unroll
     for (int s = 0; s < ST; ++s) {
@@ -298,15 +357,16 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
         for (int r = 0; r < R; ++r) {
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
-                int lo = 0, hi = 0;
+                int ah = 0;
+                uint32_t al = 0;
 #pragma unroll
                 for (int j = 0; j < CPL; ++j) {
-                    dot_word(w[b][r][j].x, xv[t][j][0], lo, hi);
-                    dot_word(w[b][r][j].y, xv[t][j][1], lo, hi);
-                    dot_word(w[b][r][j].z, xv[t][j][2], lo, hi);
-                    dot_word(w[b][r][j].w, xv[t][j][3], lo, hi);
+                    dot8_word(w[b][r][j].x, xv[t][j][0], ah, al);
+                    dot8_word(w[b][r][j].y, xv[t][j][1], ah, al);
+                    dot8_word(w[b][r][j].z, xv[t][j][2], ah, al);
+                    dot8_word(w[b][r][j].w, xv[t][j][3], ah, al);
                 }
-                const int v = wave_sum_dpp(lo + (hi >> 2));
+                const int v = wave_sum_dpp(16 * ah + (int)al);
                 if (lane == 63) part[kw][rw * RB + s * R + r][t] = v;
             }
         }
@@ -600,12 +660,16 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv3lut_kernel(
 
 // Launch shape of the 2-bit GEMV for (N, K): waves per block KS (so that each
 // lane holds at most 2 chunks of activations per token), chunks per lane CPL,
-// and steps per block ST (a power of two, about 1792 waves in total).
+// and steps per block ST (a power of two, about 1792 waves in total; with the
+// int8 token staged once per block in LDS, about 7168 waves, or 1024 when
+// rows are long enough for four waves each, which then share a longer token;
+// the kernel that quantises the token in every block keeps 1792, since more
+// blocks repeat more of that work).
 // Row waves per block WR: blocks of about four waves (fewer, larger
 // workgroups dispatch faster, and their outputs are stored together).
 struct Gemv2Shape { int ks, cpl, st; int64_t share; int wr; };
 
-Gemv2Shape gemv2_shape(int64_t n, int64_t chunks, int mt)
+Gemv2Shape gemv2_shape(int64_t n, int64_t chunks, int mt, bool token_in_lds = false)
 {
     // Two chunks per lane halve the waves per row; on short matrices with up
     // to 128 chunks per row the extra waves of one chunk per lane are faster
@@ -616,7 +680,8 @@ Gemv2Shape gemv2_shape(int64_t n, int64_t chunks, int mt)
     if (ks > GEMV_KS_MAX) ks = GEMV_KS_MAX;
     const int64_t share = (chunks + ks - 1) / ks;
     const int cpl = (int)((share + 63) / 64);
-    int64_t per = n * ks / (GEMV_R * 1792);
+    const int64_t waves = token_in_lds ? (ks >= 4 ? 1024 : 7168) : 1792;
+    int64_t per = n * ks / (GEMV_R * waves);
     int st = 1;
     while (st < 8 && 2 * st <= per) st *= 2;
     int wr = ks >= GEMV_WAVES ? 1 : GEMV_WAVES / ks;
@@ -632,6 +697,20 @@ hipError_t launch2_st(bool al, const int8_t *xq, const int32_t *rowsum, int64_t 
     const int64_t chunks = pack2_pitch(k) / 16;
     const int64_t rb = (int64_t)GEMV_R * ST * sh.wr;
     const dim3 grid((unsigned)((n + rb - 1) / rb)), block((unsigned)(64 * sh.ks * sh.wr));
+    // one token: staged once per block in LDS (up to 8 vectors per thread)
+    const int64_t per = (k / 16 + 64 * sh.ks * sh.wr - 1) / (64 * sh.ks * sh.wr);
+    if (MT == 1 && al && k <= GEMV_X_LDS_MAX_K && per <= 8) {
+        const size_t lds = (size_t)((k + 15) / 16) * 16;
+#define X_CASE(V_)                                                                              \
+        if (per <= V_) {                                                                        \
+            hipLaunchKernelGGL((gemv2_kernel<1, CPL, ST, true, GEMV_X_LDS, V_>), grid, block,    \
+                               lds, s, xq, rowsum, k, (const uint4 *)packed, n, chunks,         \
+                               sh.share, out, n, m0, sh.ks, FuseQ{});                           \
+            return hipGetLastError();                                                           \
+        }
+        X_CASE(1) X_CASE(2) X_CASE(4) X_CASE(8)
+#undef X_CASE
+    }
     if (al)
         hipLaunchKernelGGL((gemv2_kernel<MT, CPL, ST, true>), grid, block, 0, s, xq, rowsum, k,
                            (const uint4 *)packed, n, chunks, sh.share, out, n, m0, sh.ks,
@@ -710,7 +789,8 @@ template <int MT>
 hipError_t launch2(bool al, const int8_t *xq, const int32_t *rowsum, int64_t n, int64_t k,
                    const uint8_t *packed, Out out, int64_t m0, hipStream_t s)
 {
-    const Gemv2Shape sh = gemv2_shape(n, pack2_pitch(k) / 16, MT);
+    const Gemv2Shape sh =
+        gemv2_shape(n, pack2_pitch(k) / 16, MT, MT == 1 && al && k <= GEMV_X_LDS_MAX_K);
     if (sh.cpl == 1) return launch2_cpl<MT, 1>(al, xq, rowsum, n, k, packed, out, m0, sh, s);
     return launch2_cpl<MT, 2>(al, xq, rowsum, n, k, packed, out, m0, sh, s);
 }

@@ -56,29 +56,44 @@ __global__ __launch_bounds__(256) void glue_kernel(GlueArgs a, int64_t k, double
     __shared__ int red_i[4];
     const int tid = threadIdx.x;
     const int64_t m = blockIdx.x;
+    const int kk = (int)k;
+
+    // All of the thread's loads first (indices clamped into the row, values
+    // past K unused), so that they are in flight together.
+    float f0[EPT], f1[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int i = tid + 256 * j;
+        const int ic = i < kk ? i : kk - 1;
+        if (MODE == GLUE_RESIDUAL) {
+            f0[j] = a.x[m * k + ic];
+            f1[j] = a.add ? a.add[m * k + ic] : 0.0f;
+        } else if (MODE == GLUE_GQA) {
+            const unsigned hd = (unsigned)a.head_dim, head = (unsigned)ic / hd;
+            const unsigned d = (unsigned)ic - head * hd;
+            f0[j] = a.src[m * a.ld + a.col + (int64_t)(head / (unsigned)a.group) * hd + d];
+        } else {
+            f0[j] = a.src[m * a.ld + ic];             // gate
+            f1[j] = a.src[m * a.ld + a.col + ic];     // up
+        }
+    }
 
     double v[EPT];
     double ss = 0.0;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-        const int64_t i = tid + 256 * j;
-        v[j] = 0.0;
-        if (i >= k) continue;
+        const int i = tid + 256 * j;
         if (MODE == GLUE_RESIDUAL) {
-            float xv = a.x[m * k + i];
-            if (a.add) {
-                xv = xv + a.add[m * k + i];
-                a.x[m * k + i] = xv;
-            }
+            const float xv = a.add ? f0[j] + f1[j] : f0[j];
+            if (a.add && i < kk) a.x[m * k + i] = xv;
             v[j] = (double)xv;
         } else if (MODE == GLUE_GQA) {
-            const int64_t head = i / a.head_dim, d = i % a.head_dim;
-            v[j] = (double)a.src[m * a.ld + a.col + (head / a.group) * a.head_dim + d];
+            v[j] = (double)f0[j];
         } else {
-            const float g = a.src[m * a.ld + i], u = a.src[m * a.ld + a.col + i];
-            const double gd = g > 0.0f ? (double)g : 0.0;
-            v[j] = gd * gd * (double)u;
+            const double gd = f0[j] > 0.0f ? (double)f0[j] : 0.0;
+            v[j] = gd * gd * (double)f1[j];
         }
+        if (i >= kk) v[j] = 0.0;
         ss += v[j] * v[j];
     }
     ss = block_sum_d(ss, red_d);
@@ -97,8 +112,8 @@ __global__ __launch_bounds__(256) void glue_kernel(GlueArgs a, int64_t k, double
     int sum = 0;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-        const int64_t i = tid + 256 * j;
-        if (i >= k) continue;
+        const int i = tid + 256 * j;
+        if (i >= kk) continue;
         const int8_t q = quant1(h[j], s);
         sum += q;
         xq[m * k + i] = q;
