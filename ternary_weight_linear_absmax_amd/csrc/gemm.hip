@@ -175,24 +175,11 @@ __device__ __forceinline__ void st_a(uint8_t *lds_buf, const uint4 (&r)[BM / 32]
 #define GEMM_NB 4
 #endif
 
-constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
 // Stages after which every register/LDS ring is back at slot 0.
 constexpr int ring_period(int na, int nb)
 {
     const int l = 2 * na / gcd_int(2, na);
     return l * nb / gcd_int(l, nb);
-}
-
-template <class F, int... I>
-__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
-{
-    (f(std::integral_constant<int, I>{}), ...);
-}
-// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), unrolled.
-template <int N, class F>
-__device__ __forceinline__ void static_for(F &&f)
-{
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // Tile of block b: consecutive tile ids on one XCD (blocks b, b+8, ... share an

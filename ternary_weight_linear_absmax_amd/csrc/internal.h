@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <utility>
 
 namespace bl {
 
@@ -108,6 +109,20 @@ __device__ inline float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ inline float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 // s = 127 / max|x|, or 1 for an all-zero token.
 __device__ inline float act_scale(float amax) { return amax == 0.0f ? 1.0f : 127.0f / amax; }
+
+constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), unrolled.
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Writes the output element (m, n) from the code-weighted sum sum_k (t+1) q
 // and the token's rowsum: acc = codesum - rowsum.

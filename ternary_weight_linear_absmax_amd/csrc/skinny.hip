@@ -237,10 +237,191 @@ bool skinny_supported(int64_t m, int64_t n, int64_t k)
     return m >= 1 && m <= SK_MAX_M && k % SK_CHUNK == 0 && n >= 1 && n <= ((int64_t)1 << 31) / 64;
 }
 
+
+// ---- shared-activation variant ------------------------------------------------
+// Block: 4 waves on BN = 64 RB weight rows and all M (<= 16 TG) tokens, over
+// all k stages of 256; used when the row blocks alone fill the CUs.  Per
+// stage the block copies the
+// activations [16 TG tokens][256 bytes] into an LDS ring with contiguous
+// 16-byte loads (each wave instruction reads whole token rows); each wave
+// streams the packed bytes of its RB row blocks of 16 rows straight from HBM
+// into registers, several stages ahead, and reads every token's activation
+// fragments from LDS.  Same k mapping as above: lane (r, b), word u of its 16
+// packed bytes <-> activation bytes 64 b + 16 u .. +15 of the stage.
+// (Splitting the k range over blocks, with device-scope atomics into a
+// workspace and the last block of a tile finishing, measured several times
+// slower than not splitting: the atomics dominate.)
+namespace {
+
+constexpr int SK2_LDA = 256 + 16;   // LDS row of one token's stage (bytes)
+constexpr int SK2_NS = 3;           // LDS ring
+constexpr int SK2_DA = 2;   // activation stages in flight ahead (registers; deeper: slower)
+constexpr int SK2_PW = 4;   // weight stages in flight ahead (registers; deeper: slower)
+
+template <int TG, int RB>
+__global__ __launch_bounds__(256) void skinny2_kernel(const int8_t *__restrict__ xq,
+                                                      const int32_t *__restrict__ rowsum,
+                                                      int64_t m, int64_t k,
+                                                      const uint8_t *__restrict__ packed,
+                                                      int64_t n, int64_t pitch, Out out,
+                                                      int64_t ldy)
+{
+    constexpr int MT = 16 * TG, BN = 64 * RB;
+    constexpr int SLOT = MT * SK2_LDA;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[SK2_NS * SLOT];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, b = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * BN;
+    const int ns = (int)(k / SK_CHUNK);   // stages, >= 1
+
+    // activation pieces of this thread: piece p = tid + 256 i of the stage,
+    // token p / 16, bytes 16 (p % 16) .. +15 (tokens past M clamped: they
+    // only feed outputs that are never stored)
+    const int8_t *asrc[TG];
+    uint32_t adst[TG];
+#pragma unroll
+    for (int i = 0; i < TG; ++i) {
+        const int p = tid + 256 * i;
+        int64_t tok = p >> 4;
+        tok = tok < m ? tok : m - 1;
+        asrc[i] = xq + tok * k + 16 * (p & 15);
+        adst[i] = (uint32_t)((p >> 4) * SK2_LDA + 16 * (p & 15));
+    }
+    // weight rows of this lane (clamped into the matrix)
+    const uint8_t *wsrc[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        int64_t row = n0 + 16 * (wave * RB + rb) + r;
+        row = row < n ? row : n - 1;
+        wsrc[rb] = packed + row * pitch + 16 * b;
+    }
+
+    auto aload = [&](uint4 (&a)[TG], int st) __attribute__((always_inline)) {
+        const int sc = st < ns ? st : ns - 1;
+        const int64_t k0 = (int64_t)sc * SK_CHUNK;
+#pragma unroll
+        for (int i = 0; i < TG; ++i) a[i] = load16(asrc[i] + k0);
+    };
+    auto astore = [&](const uint4 (&a)[TG], int st) __attribute__((always_inline)) {
+        uint8_t *slot = lds + (st % SK2_NS) * SLOT;
+#pragma unroll
+        for (int i = 0; i < TG; ++i) *(uint4 *)(slot + adst[i]) = a[i];
+    };
+    auto wload = [&](uint4 (&w)[RB], int st) __attribute__((always_inline)) {
+        const int sc = st < ns ? st : ns - 1;
+        const int64_t off = (int64_t)sc * (SK_CHUNK / 4);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) w[rb] = load_nt16(wsrc[rb] + off);
+    };
+
+    v4i acc[RB][TG];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int g = 0; g < TG; ++g) acc[rb][g] = v4i{0, 0, 0, 0};
+
+    // prologue: stage 0 into LDS; activations of stages 1 .. DA and weights
+    // of stages 0 .. PW-1 in flight
+    uint4 ra[SK2_DA][TG], rw[SK2_PW][RB];
+    {
+        uint4 a0[TG];
+        aload(a0, 0);
+#pragma unroll
+        for (int d = 0; d < SK2_DA; ++d) aload(ra[d], 1 + d);
+#pragma unroll
+        for (int q = 0; q < SK2_PW; ++q) wload(rw[q], q);
+        astore(a0, 0);
+    }
+    __syncthreads();
+
+    // Iteration j: store the activations of stage j+1 (loaded DA iterations
+    // ago) into slot (j+1) % 3, issue the loads of stage j+1+DA (activations)
+    // and j+PW (weights), then the MFMAs of stage j from slot j % 3; one
+    // barrier.  Slot (j+1) % 3 was last read in iteration j-2.
+    constexpr int UR = SK2_DA * SK2_PW / gcd_int(SK2_DA, SK2_PW);
+    constexpr int U = UR * SK2_NS / gcd_int(UR, SK2_NS);
+    auto iter = [&](auto jc, int j) __attribute__((always_inline)) {
+        constexpr int J = decltype(jc)::value;
+        constexpr int AS = J % SK2_DA, WS = J % SK2_PW;
+        if (j + 1 < ns) astore(ra[AS], j + 1);
+        aload(ra[AS], j + 1 + SK2_DA);
+        uint4 wcur[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) wcur[rb] = rw[WS][rb];
+        wload(rw[WS], j + SK2_PW);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint8_t *slot = lds + (J % SK2_NS) * SLOT;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            v4i xb[TG];
+#pragma unroll
+            for (int g = 0; g < TG; ++g) {
+                const uint4 v = load16(slot + (16 * g + r) * SK2_LDA + 64 * b + 16 * u);
+                xb[g] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+            }
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const v4i a = unpack_word16(word_at(wcur[rb], u));
+#pragma unroll
+                for (int g = 0; g < TG; ++g)
+                    acc[rb][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, xb[g], acc[rb][g], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    };
+    const int nu = ns - ns % U;
+    for (int j = 0; j < nu; j += U)
+        static_for<U>([&](auto jc) __attribute__((always_inline)) { iter(jc, j + jc); });
+    static_for<U - 1>([&](auto jc) __attribute__((always_inline)) {
+        if (nu + jc < ns) iter(jc, nu + jc);
+    });
+
+    // Epilogue: lane (r, b) holds rows 16 (wave RB + rb) + 4 b + q of token
+    // 16 g + r.
+#pragma unroll
+    for (int g = 0; g < TG; ++g) {
+        const int64_t tok = 16 * g + r;
+        if (tok >= m) continue;
+        const int32_t rs = rowsum[tok];
+        const float gs = out.acc ? 0.0f : out.gamma[0] / out.scale[tok];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t row = n0 + 16 * (wave * RB + rb) + 4 * b + q;
+                if (row >= n) continue;
+                const int32_t v = acc[rb][g][q] - rs;
+                if (out.acc)
+                    out.acc[tok * ldy + row] = v;
+                else
+                    out.y[tok * ldy + row] = (float)v * gs;
+            }
+    }
+}
+
+}  // namespace
+
+namespace {
+
+template <int TG>
+hipError_t launch_sk2(const int8_t *xq, const int32_t *rowsum, int64_t m, const uint8_t *packed,
+                      int64_t n, int64_t k, Out out, hipStream_t s)
+{
+    hipLaunchKernelGGL((skinny2_kernel<TG, 1>), dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s,
+                       xq, rowsum, m, k, packed, n, pack2_pitch(k), out, (int64_t)n);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_skinny_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
                                const uint8_t *packed, int64_t n, int64_t k, Out out,
                                hipStream_t s)
 {
+    // up to 16 tokens on matrices whose 64-row blocks fill the CUs: the
+    // shared-activation kernel (measured faster there); otherwise the
+    // per-wave kernel, which splits k over the waves of a block
+    if (m <= 16 && (n + 63) / 64 >= 192) return launch_sk2<1>(xq, rowsum, m, packed, n, k, out, s);
     if (m <= 16) return launch_tg<1>(xq, rowsum, m, packed, n, k, out, s);
     if (m <= 32) return launch_tg<2>(xq, rowsum, m, packed, n, k, out, s);
     return launch_tg<4>(xq, rowsum, m, packed, n, k, out, s);

@@ -77,6 +77,9 @@ def test_ragged_shapes_bf16(layout, m, n, k):
     (5, 130, 256), (16, 1000, 2560), (12, 17, 512), (1, 33, 256), (8, 2560, 6912),
     (16, 4099, 8192), (7, 3840, 2560), (17, 300, 512), (32, 1000, 2560), (33, 130, 256),
     (64, 2560, 6912), (50, 4099, 1024),
+    # up to 16 tokens on at least 192 blocks of 64 rows: activations shared
+    # through LDS, ragged last row block and token slots
+    (13, 12300, 512), (16, 13824, 2560), (1, 12289, 256), (5, 12352, 1024),
 ])
 def test_skinny_shapes(m, n, k):
     """Weight-streaming matrix-core path: ragged N and M, every row-block /
