@@ -38,6 +38,19 @@ __device__ inline void dot_word(uint32_t w, uint4 x, int &lo, int &hi)
     hi = __builtin_amdgcn_sdot4(u3, (int)x.w, hi, false);
 }
 
+// Four values quantised with the activation quantiser's arithmetic
+// (rint(x s) clamped to +-127, as quant1) and packed into the bytes of one
+// word, value a in the lowest byte.
+__device__ inline uint32_t quant4(float a, float b, float c, float d, float s)
+{
+    auto q = [&](float x) __attribute__((always_inline)) {
+        return (uint32_t)(int)__builtin_amdgcn_fmed3f(rintf(x * s), -127.0f, 127.0f);
+    };
+    const uint32_t ab = __builtin_amdgcn_perm(q(b), q(a), 0x0c0c0400u);   // a, b in bytes 0, 1
+    const uint32_t cd = __builtin_amdgcn_perm(q(d), q(c), 0x0c0c0400u);
+    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
 // Nibble form of 16 activation bytes for the 4-bit dot products: x = 16 hi + lo
 // with lo = x & 15 (unsigned) and hi = x >> 4 (signed).  Byte j of l02 holds
 // lo(x[j]) | lo(x[8 + j]) << 4, of h02 the two hi nibbles, and l13 / h13 the
@@ -305,26 +318,17 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
                 uint32_t d[2];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    d[h] = 0;
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const int8_t a = quant1(bf16_lo(u[2 * h + e]), q_s);
-                        const int8_t b = quant1(bf16_hi(u[2 * h + e]), q_s);
-                        sum += a + b;
-                        d[h] |= ((uint32_t)(uint8_t)a | ((uint32_t)(uint8_t)b << 8)) << (16 * e);
-                    }
+                    d[h] = quant4(bf16_lo(u[2 * h]), bf16_hi(u[2 * h]), bf16_lo(u[2 * h + 1]),
+                                  bf16_hi(u[2 * h + 1]), q_s);
+                    sum = __builtin_amdgcn_sdot4((int)d[h], 0x01010101, sum, false);
                 }
                 const uint2 qv = make_uint2(d[0], d[1]);
                 *(uint2 *)(ql + 8 * i) = qv;
                 if (blockIdx.x == 0) *(uint2 *)(fq.xq + 8 * (int64_t)i) = qv;
             } else {
-                uint32_t d = 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int8_t a = quant1(__uint_as_float(u[e]), q_s);
-                    sum += a;
-                    d |= (uint32_t)(uint8_t)a << (8 * e);
-                }
+                const uint32_t d = quant4(__uint_as_float(u[0]), __uint_as_float(u[1]),
+                                          __uint_as_float(u[2]), __uint_as_float(u[3]), q_s);
+                sum = __builtin_amdgcn_sdot4((int)d, 0x01010101, sum, false);
                 *(uint32_t *)(ql + 4 * i) = d;
                 if (blockIdx.x == 0) *(uint32_t *)(fq.xq + 4 * (int64_t)i) = d;
             }
@@ -663,8 +667,8 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv3lut_kernel(
 // and steps per block ST (a power of two, about 1792 waves in total; with the
 // int8 token staged once per block in LDS, about 7168 waves, or 1024 when
 // rows are long enough for four waves each, which then share a longer token;
-// the kernel that quantises the token in every block keeps 1792, since more
-// blocks repeat more of that work).
+// the kernel that quantises the token in every block has its own shape,
+// gemv2_fused_shape).
 // Row waves per block WR: blocks of about four waves (fewer, larger
 // workgroups dispatch faster, and their outputs are stored together).
 struct Gemv2Shape { int ks, cpl, st; int64_t share; int wr; };
@@ -687,6 +691,21 @@ Gemv2Shape gemv2_shape(int64_t n, int64_t chunks, int mt, bool token_in_lds = fa
     int wr = ks >= GEMV_WAVES ? 1 : GEMV_WAVES / ks;
     while (wr > 1 && (n + (int64_t)wr * GEMV_R * st - 1) / ((int64_t)wr * GEMV_R * st) < 256) wr /= 2;
     return {ks, cpl, st, share, wr};
+}
+
+// Shape of the kernel that quantises the token in every block: the same
+// k split, but blocks of up to 8 waves and as many rows per block as still
+// give about one block per CU, since every block repeats the quantisation
+// (measured on the 2B-class decode matrices).
+Gemv2Shape gemv2_fused_shape(int64_t n, int64_t chunks)
+{
+    Gemv2Shape sh = gemv2_shape(n, chunks, 1);
+    auto blocks = [&](int wr, int st) { return (n + (int64_t)wr * GEMV_R * st - 1) / ((int64_t)wr * GEMV_R * st); };
+    sh.wr = GEMV_KS_MAX / sh.ks;
+    while (sh.wr > 1 && blocks(sh.wr, 1) < 160) sh.wr /= 2;
+    sh.st = 1;
+    while (sh.st < 8 && blocks(sh.wr, 2 * sh.st) >= 160) sh.st *= 2;
+    return sh;
 }
 
 template <int MT, int CPL, int ST>
@@ -846,7 +865,7 @@ bool gemv_fused_supported(int64_t m, int64_t n, int64_t k, int dtype)
     // one token, whole 16-value pieces, the int8 token within 16 KB of LDS and
     // at most 16 input vectors per thread
     if (m != 1 || n < 1 || k % 16 != 0 || k > 16384) return false;
-    const Gemv2Shape sh = gemv2_shape(n, pack2_pitch(k) / 16, 1);
+    const Gemv2Shape sh = gemv2_fused_shape(n, pack2_pitch(k) / 16);
     const int64_t nvec = k / (dtype == DT_BF16 ? 8 : 4), nthr = 64 * sh.ks * sh.wr;
     return nvec <= nthr * GEMV_FUSED_VPT_MAX;
 }
@@ -857,7 +876,7 @@ hipError_t launch_gemv_pack2_fused(const void *x, int dtype, int8_t *xq, float *
 {
     if (!gemv_fused_supported(1, n, k, dtype) || out.acc) return hipErrorInvalidValue;
     const FuseQ fq{x, xq, scale, rowsum};
-    const Gemv2Shape sh = gemv2_shape(n, pack2_pitch(k) / 16, 1);
+    const Gemv2Shape sh = gemv2_fused_shape(n, pack2_pitch(k) / 16);
     if (sh.cpl == 1) return launch2_fused_cpl<1>(dtype, fq, n, k, packed, out, sh, s);
     return launch2_fused_cpl<2>(dtype, fq, n, k, packed, out, sh, s);
 }
