@@ -314,7 +314,56 @@ def measure_extra(args):
             "us_with_act_quant": round(ms_full * 1e3, 2),
             "TOPS_with_act_quant": round(2.0 * m * n * k / (ms_full * 1e-3) / 1e12, 2)}
         log(f"prefill {name}: {ms * 1e3:.1f} us {tops:.1f} TOPS")
+    extra.update(measure_variants())
     return extra
+
+
+def measure_variants():
+    """The variants on their natural shapes: sign-binarised 70B-class weights
+    at M = 1 (10 rotating copies) and 4-bit activations on the 3B-class
+    prefill product at M = 512 (quantiser + product)."""
+    import torch
+    from ternary_weight_linear_absmax_amd import bitlinear as bl
+    from ternary_weight_linear_absmax_amd import inputs
+    out = {}
+    name, k, n = inputs.XL_SHAPES[0]
+    _, w, x = inputs.xl(0, m=1)
+    wd = to_dev(w)
+    pb, beta = bl.quantize_weights(wd, binary=True)
+    del wd
+    copies = [pb] + [pb.clone() for _ in range(9)]
+    xq, scale, rowsum = bl.quantize_act(to_dev(x))
+    y = torch.empty((1, n), dtype=torch.float32, device="cuda")
+
+    def fwd():
+        for c in copies:
+            bl.forward(xq, scale, rowsum, c, beta, n, k, y=y)
+    ms = graph_time(fwd, 20, 3) / len(copies)
+    gbs = pb.numel() / (ms * 1e-3) / 1e9
+    out[f"binary_weights_xl_{name}_M1"] = {"K": k, "N": n, "M": 1, "us": round(ms * 1e3, 2),
+                                            "GB/s": round(gbs, 1),
+                                            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    log(f"binary weights xl {name} M=1: {ms * 1e3:.1f} us {gbs:.0f} GB/s")
+    del copies
+    name, k, n = inputs.PREFILL_SHAPES[0]
+    _, w, x = inputs.prefill(0)
+    packed, gamma = bl.quantize_weights(to_dev(w))
+    xd = to_dev(x)
+    m = x.shape[0]
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    reps = 10
+
+    def full4():
+        for _ in range(reps):
+            q4, s4, r4 = bl.quantize_act(xd, bits=4)
+            bl.forward(q4, s4, r4, packed, gamma, n, k, y=y)
+    ms = graph_time(full4, 20, 3) / reps
+    tops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+    out[f"act4_prefill_{name}_M512"] = {"K": k, "N": n, "M": m, "us_with_act_quant": round(ms * 1e3, 2),
+                                         "TOPS_with_act_quant": round(tops, 2),
+                                         "i8_frac": round(tops / I8_PEAK_TOPS, 4)}
+    log(f"4-bit activations prefill {name}: {ms * 1e3:.1f} us {tops:.1f} TOPS")
+    return out
 
 
 def measure_stack(layers=30, m=64):

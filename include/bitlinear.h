@@ -133,6 +133,21 @@ int bitlinear_quantize_weights(const void *W, int dtype, int64_t N, int64_t K, i
                                uint8_t *packed, float *gamma, void *workspace,
                                int64_t workspace_bytes, hipStream_t stream);
 
+/* ---- weights, 1-bit variant: sign binariser (offline) ----------------------
+ * [lumen-it.ai article on the original 1-bit BitNet: weights binarised to +1
+ *  or -1 with the signum function; group quantisation for model parallelism]
+ *
+ * Same arguments, layout, packing and errors as bitlinear_quantize_weights,
+ * with t = -1 for w < 0 and t = +1 otherwise (a zero weight of either sign
+ * maps to +1; the pages give no tie rule), so the packed matrix holds no zero
+ * trits and every product kernel runs it unchanged.
+ * beta    device, one float, written: the scale of the binary weights, mean|W|
+ *         computed exactly as gamma above (one group: the whole matrix on one
+ *         device).  Pass it where the products take gamma. */
+int bitlinear_quantize_weights_binary(const void *W, int dtype, int64_t N, int64_t K, int layout,
+                                      uint8_t *packed, float *beta, void *workspace,
+                                      int64_t workspace_bytes, hipStream_t stream);
+
 /* ---- activations: per-token absmax to int8 -----------------------------------
  * [cheatsheet.md BitNet b1.58 summary, "What is BitNet b1.58?", activation
  *  bullet; asi.tokyo 2B4T article, 8-bit messages; lumen-it.ai BitNet, absmax]
@@ -146,6 +161,18 @@ int bitlinear_quantize_weights(const void *W, int dtype, int64_t N, int64_t K, i
  */
 int bitlinear_quantize_act(const void *x, int dtype, int64_t M, int64_t K, int8_t *xq,
                            float *scale, int32_t *rowsum, hipStream_t stream);
+
+/* ---- activations with fewer bits ------------------------------------------------
+ * [cheatsheet.md BitNet b1.58 summary, outlook: activations compressed below
+ *  8 bits, to 4 bits or fewer]
+ *
+ * bitlinear_quantize_act with Q = 2^(bits-1) - 1 in place of 127:
+ * s = Q / max_k |x[m, k]| (IEEE float division; 1 for an all-zero token) and
+ * xq = clamp(rint(x * s), -Q, Q), stored as int8.  bits in [2, 8]
+ * (BL_ERR_SHAPE otherwise); bits = 8 is bitlinear_quantize_act.  The products
+ * take the result unchanged (y = acc * gamma / s). */
+int bitlinear_quantize_act_bits(const void *x, int dtype, int64_t M, int64_t K, int bits,
+                                int8_t *xq, float *scale, int32_t *rowsum, hipStream_t stream);
 
 /* ---- forward: exact integer product and rescale ---------------------------------
  * [asi.tokyo 2B4T article, packing paragraph: unpack next to the arithmetic

@@ -69,6 +69,8 @@ def _load():
         "orc_pack3": (None, [p, i64, i64, p]),
         "orc_unpack3": (None, [p, i64, i64, p]),
         "orc_quantize_act": (None, [p, i32, i64, i64, p, p, p]),
+        "orc_quantize_act_bits": (None, [p, i32, i64, i64, i32, p, p, p]),
+        "orc_sign_trits": (None, [p, i32, i64, i64, p]),
         "orc_matmul_i32": (None, [p, i64, p, i64, i64, p]),
         "orc_rescale": (None, [p, p, f32, i64, i64, p]),
         "orc_rmsnorm": (None, [p, i64, i64, ctypes.c_double, p]),
@@ -137,6 +139,20 @@ def quantize_weights(w: np.ndarray):
     return absmean_trits(w, g), g
 
 
+def sign_trits(w: np.ndarray) -> np.ndarray:
+    """1-bit variant [LUMEN]: -1 for w < 0, +1 otherwise."""
+    w, dt = _as_input(w)
+    n, k = w.shape
+    t = np.empty((n, k), dtype=np.int8)
+    _load().orc_sign_trits(_ptr(w), dt, n, k, _ptr(t))
+    return t
+
+
+def quantize_weights_binary(w: np.ndarray):
+    """W -> (binary trits int8 [N,K] in {-1, +1}, beta = mean|W| float32)."""
+    return sign_trits(w), absmean_gamma(w)
+
+
 def pack2(t: np.ndarray) -> np.ndarray:
     t = np.ascontiguousarray(t, dtype=np.int8)
     n, k = t.shape
@@ -181,6 +197,17 @@ def quantize_act(x: np.ndarray):
     s = np.empty((m,), dtype=np.float32)
     r = np.empty((m,), dtype=np.int32)
     _load().orc_quantize_act(_ptr(x), dt, m, k, _ptr(q), _ptr(s), _ptr(r))
+    return q, s, r
+
+
+def quantize_act_bits(x: np.ndarray, bits: int):
+    """b-bit activations [CS, outlook]: Q = 2^(bits-1) - 1 in place of 127."""
+    x, dt = _as_input(x)
+    m, k = x.shape
+    q = np.empty((m, k), dtype=np.int8)
+    s = np.empty((m,), dtype=np.float32)
+    r = np.empty((m,), dtype=np.int32)
+    _load().orc_quantize_act_bits(_ptr(x), dt, m, k, int(bits), _ptr(q), _ptr(s), _ptr(r))
     return q, s, r
 
 

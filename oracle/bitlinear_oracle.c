@@ -94,6 +94,15 @@ void orc_absmean_trits(const void *w, int dtype, int64_t n_rows, int64_t k_cols,
     }
 }
 
+/* ---- weights, 1-bit variant [LUMEN: binary weights +1 / -1 by the signum
+ *      function]: t = -1 for w < 0, +1 otherwise (zero maps to +1; its scale
+ *      is orc_absmean_gamma, one group per matrix). -------------------------- */
+void orc_sign_trits(const void *w, int dtype, int64_t n_rows, int64_t k_cols, int8_t *t)
+{
+    for (int64_t i = 0; i < n_rows * k_cols; ++i)
+        t[i] = load_elem(w, dtype, i) < 0.0f ? -1 : 1;
+}
+
 /* ---- 2-bit packing, four trits per byte [ASI, custom-software paragraph] --
  * Row n occupies pitch2(K) bytes, a whole number of 16-byte groups of 64 trits.
  * Inside a row, 32-bit little-endian word g holds trits k = 16g .. 16g+15: the
@@ -184,6 +193,40 @@ void orc_unpack3(const uint8_t *packed, int64_t n_rows, int64_t k_cols, int8_t *
 
 /* ---- activations: per-token absmax to 8 bits [CS "What is BitNet b1.58?",
  *      activation bullet; ASI, 8-bit messages; LUMEN, absmax] ------------- */
+
+/* b-bit activations [CS, outlook: activations compressed to 4 bits or fewer]:
+ * the same quantiser with Q = 2^(b-1) - 1 in place of 127. */
+void orc_quantize_act_bits(const void *x, int dtype, int64_t m_rows, int64_t k_cols, int bits,
+                           int8_t *q, float *scale, int32_t *rowsum)
+{
+    const float qmax = (float)((1 << (bits - 1)) - 1);
+    for (int64_t m = 0; m < m_rows; ++m) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < k_cols; ++k) {
+            float a = fabsf(load_elem(x, dtype, m * k_cols + k));
+            if (a > amax)
+                amax = a;
+        }
+        int32_t sum = 0;
+        if (amax == 0.0f) {
+            scale[m] = 1.0f;
+            for (int64_t k = 0; k < k_cols; ++k)
+                q[m * k_cols + k] = 0;
+        } else {
+            float s = qmax / amax;
+            scale[m] = s;
+            for (int64_t k = 0; k < k_cols; ++k) {
+                float r = rintf(load_elem(x, dtype, m * k_cols + k) * s);
+                if (r > qmax) r = qmax;
+                if (r < -qmax) r = -qmax;
+                q[m * k_cols + k] = (int8_t)r;
+                sum += (int32_t)r;
+            }
+        }
+        if (rowsum)
+            rowsum[m] = sum;
+    }
+}
 
 void orc_quantize_act(const void *x, int dtype, int64_t m_rows, int64_t k_cols,
                       int8_t *q, float *scale, int32_t *rowsum)

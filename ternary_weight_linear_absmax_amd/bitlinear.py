@@ -57,6 +57,8 @@ def load():
         "bitlinear_status_string": (ctypes.c_char_p, [i32]),
         "bitlinear_quantize_weights": (i32, [p, i32, i64, i64, i32, p, p, p, i64, p]),
         "bitlinear_quantize_act": (i32, [p, i32, i64, i64, p, p, p, p]),
+        "bitlinear_quantize_weights_binary": (i32, [p, i32, i64, i64, i32, p, p, p, i64, p]),
+        "bitlinear_quantize_act_bits": (i32, [p, i32, i64, i64, i32, p, p, p, p]),
         "bitlinear_forward": (i32, [p, p, p, i64, p, i32, p, i64, i64, p, p, i64, p]),
         "bitlinear_forward_ex": (i32, [p, p, p, i64, p, i32, p, i64, i64, p, p, i64, i32, p]),
         "bitlinear_matmul_i32": (i32, [p, p, i64, p, i32, i64, i64, p, p, i64, i32, p]),
@@ -142,8 +144,9 @@ def _zero_workspace(nbytes: int, device):
     return ws
 
 
-def quantize_weights(w: torch.Tensor, layout: int = BL_PACK2, stream=None):
-    """w [N, K] (float32/bfloat16, on the GPU) -> (packed uint8 [N, row_bytes], gamma float32 [1])."""
+def quantize_weights(w: torch.Tensor, layout: int = BL_PACK2, stream=None, binary: bool = False):
+    """w [N, K] (float32/bfloat16, on the GPU) -> (packed uint8 [N, row_bytes], gamma float32 [1]).
+    binary: the sign binariser (bitlinear_quantize_weights_binary); gamma is then its scale."""
     lib = load()
     assert w.dim() == 2 and w.is_contiguous()
     n, k = w.shape
@@ -151,23 +154,29 @@ def quantize_weights(w: torch.Tensor, layout: int = BL_PACK2, stream=None):
     gamma = torch.empty((1,), dtype=torch.float32, device=w.device)
     ws_bytes = quantize_weights_workspace_bytes(n, k)
     ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=w.device)
-    _check(lib.bitlinear_quantize_weights(_ptr(w), _dtype_code(w), n, k, layout, _ptr(packed),
-                                          _ptr(gamma), _ptr(ws), ws.numel(), _stream(stream)),
-           "bitlinear_quantize_weights")
+    name = "bitlinear_quantize_weights_binary" if binary else "bitlinear_quantize_weights"
+    _check(getattr(lib, name)(_ptr(w), _dtype_code(w), n, k, layout, _ptr(packed), _ptr(gamma),
+                              _ptr(ws), ws.numel(), _stream(stream)), name)
     return packed, gamma
 
 
-def quantize_act(x: torch.Tensor, stream=None):
-    """x [M, K] -> (xq int8 [M, K], scale float32 [M], rowsum int32 [M])."""
+def quantize_act(x: torch.Tensor, stream=None, bits: int = 8):
+    """x [M, K] -> (xq int8 [M, K], scale float32 [M], rowsum int32 [M]).
+    bits < 8: bitlinear_quantize_act_bits (range +-(2^(bits-1) - 1))."""
     lib = load()
     assert x.dim() == 2 and x.is_contiguous()
     m, k = x.shape
     xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
     scale = torch.empty((m,), dtype=torch.float32, device=x.device)
     rowsum = torch.empty((m,), dtype=torch.int32, device=x.device)
-    _check(lib.bitlinear_quantize_act(_ptr(x), _dtype_code(x), m, k, _ptr(xq), _ptr(scale),
-                                      _ptr(rowsum), _stream(stream)),
-           "bitlinear_quantize_act")
+    if bits == 8:
+        _check(lib.bitlinear_quantize_act(_ptr(x), _dtype_code(x), m, k, _ptr(xq), _ptr(scale),
+                                          _ptr(rowsum), _stream(stream)),
+               "bitlinear_quantize_act")
+    else:
+        _check(lib.bitlinear_quantize_act_bits(_ptr(x), _dtype_code(x), m, k, bits, _ptr(xq),
+                                               _ptr(scale), _ptr(rowsum), _stream(stream)),
+               "bitlinear_quantize_act_bits")
     return xq, scale, rowsum
 
 

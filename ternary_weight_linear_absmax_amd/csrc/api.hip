@@ -135,6 +135,37 @@ int bitlinear_quantize_weights(const void *W, int dtype, int64_t N, int64_t K, i
     return hip_status(e);
 }
 
+int bitlinear_quantize_weights_binary(const void *W, int dtype, int64_t N, int64_t K, int layout,
+                                      uint8_t *packed, float *beta, void *workspace,
+                                      int64_t workspace_bytes, hipStream_t stream)
+{
+    if (!W || !packed || !beta || !workspace) return BL_ERR_NULL;
+    if (!good_dtype(dtype)) return BL_ERR_DTYPE;
+    if (!good_layout(layout)) return BL_ERR_LAYOUT;
+    if (N < 1 || !good_k(K) || K > kMaxElems / N) return BL_ERR_SHAPE;
+    if (!al16(W) || !al16(packed) || !al16(workspace) || !al4(beta)) return BL_ERR_ALIGN;
+    if (workspace_bytes < bitlinear_quantize_weights_workspace_bytes(N, K)) return BL_ERR_WORKSPACE;
+    double *rowsums = (double *)workspace;
+    hipError_t e = bl::launch_gamma_rows(W, dtype, N, K, rowsums, stream);
+    if (e == hipSuccess) e = bl::launch_gamma_final(rowsums, N, K, beta, stream);
+    if (e == hipSuccess) e = bl::launch_pack(W, dtype, N, K, layout, beta, packed, stream, true);
+    return hip_status(e);
+}
+
+int bitlinear_quantize_act_bits(const void *x, int dtype, int64_t M, int64_t K, int bits,
+                                int8_t *xq, float *scale, int32_t *rowsum, hipStream_t stream)
+{
+    if (!good_dtype(dtype)) return BL_ERR_DTYPE;
+    if (bits < 2 || bits > 8) return BL_ERR_SHAPE;
+    if (M < 0 || !good_k(K) || (M > 0 && K > kMaxElems / M) || M > 0x7FFFFFFF)
+        return BL_ERR_SHAPE;
+    if (M == 0) return BL_OK;
+    if (!x || !xq || !scale) return BL_ERR_NULL;
+    if (!al16(x) || !al16(xq) || !al4(scale) || (rowsum && !al4(rowsum))) return BL_ERR_ALIGN;
+    return hip_status(
+        bl::launch_quant_act(x, dtype, M, K, xq, scale, rowsum, stream, (1 << (bits - 1)) - 1));
+}
+
 int bitlinear_quantize_act(const void *x, int dtype, int64_t M, int64_t K, int8_t *xq,
                            float *scale, int32_t *rowsum, hipStream_t stream)
 {

@@ -31,13 +31,13 @@ hipError_t launch_gamma_rows(const void *w, int dtype, int64_t n, int64_t k, dou
 hipError_t launch_gamma_final(const double *rowsums, int64_t n, int64_t k, float *gamma,
                               hipStream_t s);
 hipError_t launch_pack(const void *w, int dtype, int64_t n, int64_t k, int layout,
-                       const float *gamma, uint8_t *packed, hipStream_t s);
+                       const float *gamma, uint8_t *packed, hipStream_t s, bool binary = false);
 hipError_t launch_unpack(const uint8_t *packed, int layout, int64_t n, int64_t k,
                          int8_t *trits, hipStream_t s);
 
 // ---- activations (quant_act.hip) ----
 hipError_t launch_quant_act(const void *x, int dtype, int64_t m, int64_t k, int8_t *xq,
-                            float *scale, int32_t *rowsum, hipStream_t s);
+                            float *scale, int32_t *rowsum, hipStream_t s, int qmax = 127);
 
 // ---- decoder-block glue (glue.hip) ----
 enum : int { GLUE_RESIDUAL = 0, GLUE_GQA = 1, GLUE_RELU2 = 2 };
@@ -105,10 +105,19 @@ __device__ inline int8_t quant1(float x, float s)
     r = fminf(fmaxf(r, -127.0f), 127.0f);
     return (int8_t)(int)r;
 }
+// The same with a narrower symmetric range [-qmax, qmax] (qmax = 2^(b-1) - 1
+// for b-bit activations); qmax = 127 gives quant1.
+__device__ inline int8_t quant1q(float x, float s, float qmax)
+{
+    float r = rintf(x * s);
+    r = fminf(fmaxf(r, -qmax), qmax);
+    return (int8_t)(int)r;
+}
 __device__ inline float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ inline float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 // s = 127 / max|x|, or 1 for an all-zero token.
 __device__ inline float act_scale(float amax) { return amax == 0.0f ? 1.0f : 127.0f / amax; }
+__device__ inline float act_scale_q(float amax, float qmax) { return amax == 0.0f ? 1.0f : qmax / amax; }
 
 constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
 

@@ -7,6 +7,8 @@
 //
 // s = 127 / max|x| (IEEE float division), q = clamp(rint(x * s), -127, 127)
 // with a float multiply and round-half-to-even; an all-zero token gets s = 1.
+// Narrower activations (b bits, a future direction the cheatsheet.md summary
+// names in its outlook) use Q = 2^(b-1) - 1 in place of 127.
 // The row sum of q is emitted as well: the products use the 2-bit codes
 // t + 1 and subtract it once per token.
 //
@@ -36,7 +38,8 @@ template <int DT, bool VEC>
 __global__ __launch_bounds__(256) void quant_act_kernel(const void *__restrict__ x, int64_t k,
                                                         int8_t *__restrict__ xq,
                                                         float *__restrict__ scale,
-                                                        int32_t *__restrict__ rowsum)
+                                                        int32_t *__restrict__ rowsum,
+                                                        float qmax)
 {
     __shared__ float red_f[4];
     __shared__ int red_i[4];
@@ -72,7 +75,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void *__restrict__
     if (lane == 0) red_f[wave] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
-    const float s = act_scale(amax);
+    const float s = act_scale_q(amax, qmax);
 
     int sum = 0;
     if (VEC) {
@@ -84,7 +87,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void *__restrict__
                 uint32_t out[2] = {0, 0};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    int8_t a = quant1(bf16_lo(w[e]), s), b = quant1(bf16_hi(w[e]), s);
+                    int8_t a = quant1q(bf16_lo(w[e]), s, qmax), b = quant1q(bf16_hi(w[e]), s, qmax);
                     sum += a + b;
                     uint32_t pair = ((uint32_t)(uint8_t)a) | ((uint32_t)(uint8_t)b << 8);
                     out[e >> 1] |= pair << (16 * (e & 1));
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void *__restrict__
                 uint32_t out = 0;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    int8_t a = quant1(__uint_as_float(w[e]), s);
+                    int8_t a = quant1q(__uint_as_float(w[e]), s, qmax);
                     sum += a;
                     out |= (uint32_t)(uint8_t)a << (8 * e);
                 }
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void *__restrict__
         for (int64_t i = tid; i < k; i += 256) {
             float f = DT == DT_BF16 ? __uint_as_float((uint32_t)((const uint16_t *)row)[i] << 16)
                                     : ((const float *)row)[i];
-            int8_t a = quant1(f, s);
+            int8_t a = quant1q(f, s, qmax);
             sum += a;
             qrow[i] = a;
         }
@@ -127,7 +130,8 @@ template <int DT, int NV>
 __global__ __launch_bounds__(256) void quant_act_reg_kernel(const void *__restrict__ x, int64_t k,
                                                             int8_t *__restrict__ xq,
                                                             float *__restrict__ scale,
-                                                            int32_t *__restrict__ rowsum)
+                                                            int32_t *__restrict__ rowsum,
+                                                        float qmax)
 {
     __shared__ float red_f[4];
     __shared__ int red_i[4];
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(256) void quant_act_reg_kernel(const void *__restri
     if (lane == 0) red_f[wave] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
-    const float s = act_scale(amax);
+    const float s = act_scale_q(amax, qmax);
 
     int sum = 0;
 #pragma unroll
@@ -173,7 +177,7 @@ __global__ __launch_bounds__(256) void quant_act_reg_kernel(const void *__restri
             uint32_t out[2] = {0, 0};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                int8_t a = quant1(bf16_lo(w[e]), s), b = quant1(bf16_hi(w[e]), s);
+                int8_t a = quant1q(bf16_lo(w[e]), s, qmax), b = quant1q(bf16_hi(w[e]), s, qmax);
                 sum += a + b;
                 uint32_t pair = ((uint32_t)(uint8_t)a) | ((uint32_t)(uint8_t)b << 8);
                 out[e >> 1] |= pair << (16 * (e & 1));
@@ -183,7 +187,7 @@ __global__ __launch_bounds__(256) void quant_act_reg_kernel(const void *__restri
             uint32_t out = 0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                int8_t a = quant1(__uint_as_float(w[e]), s);
+                int8_t a = quant1q(__uint_as_float(w[e]), s, qmax);
                 sum += a;
                 out |= (uint32_t)(uint8_t)a << (8 * e);
             }
@@ -201,48 +205,49 @@ __global__ __launch_bounds__(256) void quant_act_reg_kernel(const void *__restri
 
 template <int DT>
 hipError_t launch_reg(int64_t nvec, const void *x, int64_t m, int64_t k, int8_t *xq, float *scale,
-                      int32_t *rowsum, hipStream_t s)
+                      int32_t *rowsum, hipStream_t s, float qmax)
 {
     const dim3 grid((unsigned)m), block(256);
     const int64_t per = (nvec + 255) / 256;
     if (per <= 1)
-        hipLaunchKernelGGL((quant_act_reg_kernel<DT, 1>), grid, block, 0, s, x, k, xq, scale, rowsum);
+        hipLaunchKernelGGL((quant_act_reg_kernel<DT, 1>), grid, block, 0, s, x, k, xq, scale, rowsum, qmax);
     else if (per <= 2)
-        hipLaunchKernelGGL((quant_act_reg_kernel<DT, 2>), grid, block, 0, s, x, k, xq, scale, rowsum);
+        hipLaunchKernelGGL((quant_act_reg_kernel<DT, 2>), grid, block, 0, s, x, k, xq, scale, rowsum, qmax);
     else if (per <= 4)
-        hipLaunchKernelGGL((quant_act_reg_kernel<DT, 4>), grid, block, 0, s, x, k, xq, scale, rowsum);
+        hipLaunchKernelGGL((quant_act_reg_kernel<DT, 4>), grid, block, 0, s, x, k, xq, scale, rowsum, qmax);
     else if (per <= 8)
-        hipLaunchKernelGGL((quant_act_reg_kernel<DT, 8>), grid, block, 0, s, x, k, xq, scale, rowsum);
+        hipLaunchKernelGGL((quant_act_reg_kernel<DT, 8>), grid, block, 0, s, x, k, xq, scale, rowsum, qmax);
     else
-        hipLaunchKernelGGL((quant_act_reg_kernel<DT, 16>), grid, block, 0, s, x, k, xq, scale, rowsum);
+        hipLaunchKernelGGL((quant_act_reg_kernel<DT, 16>), grid, block, 0, s, x, k, xq, scale, rowsum, qmax);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_quant_act(const void *x, int dtype, int64_t m, int64_t k, int8_t *xq,
-                            float *scale, int32_t *rowsum, hipStream_t s)
+                            float *scale, int32_t *rowsum, hipStream_t s, int qmax_i)
 {
+    const float qmax = (float)qmax_i;
     dim3 grid((unsigned)m), block(256);
     // rows of up to 256 * 16 vectors (32768 bf16 / 16384 fp32) stay in registers
     if (dtype == DT_BF16 && k % 8 == 0 && k / 8 <= 256 * 16)
-        return launch_reg<DT_BF16>(k / 8, x, m, k, xq, scale, rowsum, s);
+        return launch_reg<DT_BF16>(k / 8, x, m, k, xq, scale, rowsum, s, qmax);
     if (dtype == DT_F32 && k % 4 == 0 && k / 4 <= 256 * 16)
-        return launch_reg<DT_F32>(k / 4, x, m, k, xq, scale, rowsum, s);
+        return launch_reg<DT_F32>(k / 4, x, m, k, xq, scale, rowsum, s, qmax);
     if (dtype == DT_BF16) {
         if (k % 8 == 0)
             hipLaunchKernelGGL((quant_act_kernel<DT_BF16, true>), grid, block, 0, s, x, k, xq,
-                               scale, rowsum);
+                               scale, rowsum, qmax);
         else
             hipLaunchKernelGGL((quant_act_kernel<DT_BF16, false>), grid, block, 0, s, x, k, xq,
-                               scale, rowsum);
+                               scale, rowsum, qmax);
     } else {
         if (k % 4 == 0)
             hipLaunchKernelGGL((quant_act_kernel<DT_F32, true>), grid, block, 0, s, x, k, xq,
-                               scale, rowsum);
+                               scale, rowsum, qmax);
         else
             hipLaunchKernelGGL((quant_act_kernel<DT_F32, false>), grid, block, 0, s, x, k, xq,
-                               scale, rowsum);
+                               scale, rowsum, qmax);
     }
     return hipGetLastError();
 }

@@ -33,6 +33,17 @@ __device__ inline uint32_t trit_code(float w, float gamma)
     return w > 0.0f ? 2u : 0u;
 }
 
+// Code of one weight under the sign binariser of the original 1-bit BitNet
+// (lumen-it.ai article: weights to +1 or -1 with the signum function): -1
+// for w < 0, +1 otherwise (zero, of either sign, maps to +1).
+__device__ inline uint32_t sign_code(float w) { return w < 0.0f ? 0u : 2u; }
+
+template <bool BIN>
+__device__ inline uint32_t weight_code(float w, float gamma)
+{
+    return BIN ? sign_code(w) : trit_code(w, gamma);
+}
+
 // ---- row sums of |w| in double, k ascending -------------------------------
 // A block owns 64 rows.  The tile [64 rows x 128 k] is staged through LDS with
 // coalesced loads; then lane r of the first wave adds row r's 128 values in
@@ -78,6 +89,7 @@ __global__ void gamma_final_kernel(const double *__restrict__ rowsums, int64_t n
 
 // ---- 2-bit packing: one thread per 32-bit word (16 trits) ----------------------
 // Word g of row r holds k = 16g + 4i + j at byte j, bits 2i..2i+1.
+template <bool BIN>
 __global__ __launch_bounds__(256) void pack2_kernel(const void *__restrict__ w, int dtype,
                                                     int64_t n, int64_t k,
                                                     const float *__restrict__ gamma_p,
@@ -94,7 +106,7 @@ __global__ __launch_bounds__(256) void pack2_kernel(const void *__restrict__ w, 
         for (int j = 0; j < 4; ++j) {
             int64_t kk = 16 * g + 4 * i + j;
             uint32_t code = 1u;
-            if (kk < k) code = trit_code(load_w(w, dtype, base + 4 * i + j), gamma);
+            if (kk < k) code = weight_code<BIN>(load_w(w, dtype, base + 4 * i + j), gamma);
             word |= code << (8 * j + 2 * i);
         }
     }
@@ -102,6 +114,7 @@ __global__ __launch_bounds__(256) void pack2_kernel(const void *__restrict__ w, 
 }
 
 // ---- base-3 packing: one thread per 32-bit word (4 bytes, 20 trits) ---------------
+template <bool BIN>
 __global__ __launch_bounds__(256) void pack3_kernel(const void *__restrict__ w, int dtype,
                                                     int64_t n, int64_t k,
                                                     const float *__restrict__ gamma_p,
@@ -119,7 +132,7 @@ __global__ __launch_bounds__(256) void pack3_kernel(const void *__restrict__ w, 
         for (int i = 0; i < 5; ++i) {
             int64_t kk = 5 * byte_idx + i;
             uint32_t code = 1u;
-            if (kk < k) code = trit_code(load_w(w, dtype, row * k + kk), gamma);
+            if (kk < k) code = weight_code<BIN>(load_w(w, dtype, row * k + kk), gamma);
             value += code * weight;
             weight *= 3u;
         }
@@ -185,16 +198,24 @@ hipError_t launch_gamma_final(const double *rowsums, int64_t n, int64_t k, float
 }
 
 hipError_t launch_pack(const void *w, int dtype, int64_t n, int64_t k, int layout,
-                       const float *gamma, uint8_t *packed, hipStream_t s)
+                       const float *gamma, uint8_t *packed, hipStream_t s, bool binary)
 {
     if (layout == LAYOUT_PACK2) {
         int64_t words = n * (pack2_pitch(k) / 4);
-        hipLaunchKernelGGL(pack2_kernel, dim3(blocks_for(words, 256)), dim3(256), 0, s, w, dtype,
-                           n, k, gamma, (uint32_t *)packed);
+        if (binary)
+            hipLaunchKernelGGL(pack2_kernel<true>, dim3(blocks_for(words, 256)), dim3(256), 0, s,
+                               w, dtype, n, k, gamma, (uint32_t *)packed);
+        else
+            hipLaunchKernelGGL(pack2_kernel<false>, dim3(blocks_for(words, 256)), dim3(256), 0, s,
+                               w, dtype, n, k, gamma, (uint32_t *)packed);
     } else {
         int64_t words = n * (pack3_pitch(k) / 4);
-        hipLaunchKernelGGL(pack3_kernel, dim3(blocks_for(words, 256)), dim3(256), 0, s, w, dtype,
-                           n, k, gamma, (uint32_t *)packed);
+        if (binary)
+            hipLaunchKernelGGL(pack3_kernel<true>, dim3(blocks_for(words, 256)), dim3(256), 0, s,
+                               w, dtype, n, k, gamma, (uint32_t *)packed);
+        else
+            hipLaunchKernelGGL(pack3_kernel<false>, dim3(blocks_for(words, 256)), dim3(256), 0, s,
+                               w, dtype, n, k, gamma, (uint32_t *)packed);
     }
     return hipGetLastError();
 }

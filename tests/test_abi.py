@@ -88,6 +88,31 @@ def test_quantize_act_argument_checks(lib):
     assert f(P, 1, 0, 64, P, P, P, None) == 0            # empty batch: no launch
 
 
+def test_quantize_weights_binary_argument_checks(lib):
+    f = lib.bitlinear_quantize_weights_binary
+
+    def call(W=P, dt=bl.BL_BF16, N=8, K=64, lay=bl.BL_PACK2, packed=P, beta=P, ws=P, wsb=64):
+        return f(W, dt, N, K, lay, packed, beta, ws, wsb, None)
+
+    assert call(W=NULL) == -1
+    assert call(beta=NULL) == -1
+    assert call(dt=3) == -4
+    assert call(lay=2) == -5
+    assert call(N=0) == -2
+    assert call(W=ODD) == -3
+    assert call(wsb=63) == -6
+
+
+def test_quantize_act_bits_argument_checks(lib):
+    f = lib.bitlinear_quantize_act_bits
+    for bits in (-1, 0, 1, 9, 16):
+        assert f(P, 1, 4, 64, bits, P, P, P, None) == -2
+    assert f(NULL, 1, 4, 64, 4, P, P, P, None) == -1
+    assert f(P, 2, 4, 64, 4, P, P, P, None) == -4
+    assert f(ODD, 1, 4, 64, 4, P, P, P, None) == -3
+    assert f(P, 1, 0, 64, 4, P, P, P, None) == 0            # empty batch: no launch
+
+
 def test_forward_argument_checks(lib):
     f = lib.bitlinear_forward_ex
 

@@ -450,3 +450,84 @@ def test_rmsnorm_quantize_constant_magnitude_rows():
     q, s, r = oracle.rmsnorm_quantize(x)
     np.testing.assert_array_equal(q, (127 * signs).astype(np.int8))
     np.testing.assert_array_equal(r, (127 * signs.sum(axis=1)).astype(np.int32))
+
+
+# ---- variants: b-bit activations, sign-binarised weights --------------------------
+
+def test_act_bits_worked_examples():
+    """Hand-derived: x = [14, 1, -7, 3]; 4 bits: s = 7/14 = 0.5, x s = [7, 0.5,
+    -3.5, 1.5], half-to-even -> [7, 0, -4, 2]; 2 bits: s = 1/14, x s = [1,
+    1/14, -1/2, 3/14] -> [1, 0, 0, 0] (-0.5 rounds to zero)."""
+    x = np.array([[14.0, 1.0, -7.0, 3.0]], dtype=np.float32)
+    q, s, r = oracle.quantize_act_bits(x, 4)
+    assert s[0] == np.float32(0.5)
+    assert q.tolist() == [[7, 0, -4, 2]] and r[0] == 5
+    q, s, r = oracle.quantize_act_bits(x, 2)
+    assert s[0] == np.float32(1.0) / np.float32(14.0)
+    assert q.tolist() == [[1, 0, 0, 0]] and r[0] == 1
+
+
+def test_act_bits_eight_is_the_pinned_quantiser():
+    _, _, x = inputs.decode(0, m=3)
+    for a, b in zip(oracle.quantize_act_bits(x, 8), oracle.quantize_act(x)):
+        np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 7])
+def test_act_bits_range_and_extreme_invariants(bits):
+    qmax = 2 ** (bits - 1) - 1
+    rng = np.random.default_rng(bits)
+    x = rng.standard_normal((6, 257)).astype(np.float32)
+    x[2] = 0.0
+    q, s, r = oracle.quantize_act_bits(x, bits)
+    assert np.abs(q).max() <= qmax
+    for m in range(6):
+        if m == 2:
+            assert s[m] == 1.0 and not q[m].any() and r[m] == 0
+            continue
+        j = int(np.argmax(np.abs(x[m])))
+        assert abs(int(q[m, j])) == qmax                  # the extreme hits the range end
+        assert r[m] == int(q[m].astype(np.int64).sum())
+    # powers of two scale x and 1/s exactly: q is unchanged
+    q2, s2, _ = oracle.quantize_act_bits(x * np.float32(8.0), bits)
+    np.testing.assert_array_equal(q2, q)
+    nz = np.arange(6) != 2                                 # the zero token keeps s = 1
+    np.testing.assert_array_equal(s2[nz] * np.float32(8.0), s[nz])
+
+
+def test_sign_trits_worked_example_and_zero_reading():
+    w = np.array([[0.5, -0.25, 0.0, -0.0], [1e-30, -1e-30, 3.0, -2.0]], dtype=np.float32)
+    t, beta = oracle.quantize_weights_binary(w)
+    assert t.tolist() == [[1, -1, 1, 1], [1, -1, 1, -1]]
+    # beta = mean |W|, by hand: (0.5 + 0.25 + 3 + 2 + 2e-30) / 8
+    assert beta == np.float32((0.5 + 0.25 + 3.0 + 2.0 + 2e-30) / 8.0)
+
+
+def test_sign_trits_identity_with_the_scale():
+    """t = sign(w) makes t w = |w| for every weight, so mean(t w) is the scale."""
+    _, w, _ = inputs.decode(1, m=1)
+    t, beta = oracle.quantize_weights_binary(w)
+    assert set(np.unique(t).tolist()) == {-1, 1}
+    wf = oracle.bf16_to_f32(w[:64]) if w.dtype == np.uint16 else w[:64]
+    tw = t[:64].astype(np.float64) * wf.astype(np.float64)
+    np.testing.assert_array_equal(tw, np.abs(wf.astype(np.float64)))
+    _, beta64 = oracle.quantize_weights_binary(w[:64])
+    assert abs(float(beta64) - float(np.abs(wf.astype(np.float64)).mean())) <= \
+        np.spacing(np.float32(beta64))
+
+
+def test_sign_trits_pack_to_codes_zero_and_two():
+    rng = np.random.default_rng(7)
+    w = rng.standard_normal((5, 130)).astype(np.float32)
+    t = oracle.sign_trits(w)
+    p = oracle.pack2(t)
+    np.testing.assert_array_equal(oracle.unpack2(p, 130), t)
+    k_pad = p.shape[1] * 4 - 130
+    codes = np.stack([(p >> (2 * i)) & 3 for i in range(4)], axis=-1).reshape(5, -1)
+    # every code of a real weight is 0 or 2; padding holds code 1 (trit 0)
+    assert np.isin(codes, [0, 1, 2]).all()
+    assert (codes == 1).sum() == 5 * k_pad
+    # all-positive weights: the contraction is the activation row sum
+    q, _, r = oracle.quantize_act(rng.standard_normal((3, 130)).astype(np.float32))
+    acc = oracle.matmul_i32(q, oracle.sign_trits(np.abs(w) + np.float32(1e-3)))
+    np.testing.assert_array_equal(acc, np.repeat(r[:, None], 5, axis=1))
