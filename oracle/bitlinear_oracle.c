@@ -36,6 +36,9 @@
  *     evaluated here in double precision.
  *   - packed layouts are the ones the library header documents (2-bit codes
  *     t+1 in 32-bit words of 16 trits; base-3 bytes of 5 trits).
+ *   - variants: sign binarisation maps w < 0 to -1 and everything else (zero
+ *     included) to +1, with the absmean scale of the whole matrix; b-bit
+ *     activations use Q = 2^(b-1) - 1 in place of 127.
  */
 #include <math.h>
 #include <stdint.h>
