@@ -71,6 +71,7 @@ def _load():
         "orc_quantize_act": (None, [p, i32, i64, i64, p, p, p]),
         "orc_quantize_act_bits": (None, [p, i32, i64, i64, i32, p, p, p]),
         "orc_sign_trits": (None, [p, i32, i64, i64, p]),
+        "orc_backward_input": (None, [p, i32, i64, i64, p, i64, f32, p]),
         "orc_matmul_i32": (None, [p, i64, p, i64, i64, p]),
         "orc_rescale": (None, [p, p, f32, i64, i64, p]),
         "orc_rmsnorm": (None, [p, i64, i64, ctypes.c_double, p]),
@@ -209,6 +210,20 @@ def quantize_act_bits(x: np.ndarray, bits: int):
     r = np.empty((m,), dtype=np.int32)
     _load().orc_quantize_act_bits(_ptr(x), dt, m, k, int(bits), _ptr(q), _ptr(s), _ptr(r))
     return q, s, r
+
+
+# ---- backward (straight-through estimators) -----------------------------------
+
+def backward_input(grad_y: np.ndarray, t: np.ndarray, gamma) -> np.ndarray:
+    """grad_x [M,K] = gamma * grad_y [M,N] @ t [N,K], in float64."""
+    g, dt = _as_input(grad_y)
+    t = np.ascontiguousarray(t, dtype=np.int8)
+    m, n = g.shape
+    n2, k = t.shape
+    assert n == n2
+    out = np.empty((m, k), dtype=np.float64)
+    _load().orc_backward_input(_ptr(g), dt, m, n, _ptr(t), k, float(np.float32(gamma)), _ptr(out))
+    return out
 
 
 # ---- contraction and rescale ------------------------------------------------

@@ -263,6 +263,23 @@ void orc_quantize_act(const void *x, int dtype, int64_t m_rows, int64_t k_cols,
     }
 }
 
+/* ---- backward through BitLinear with straight-through estimators [LUMEN:
+ *      training uses straight-through estimators for the gradient flow] ------
+ * Both quantisers pass the gradient unchanged, so the layer acts on x as the
+ * matrix gamma * t: grad_x[m][k] = gamma * sum_n grad_y[m][n] * t[n][k],
+ * evaluated in double precision from the exact inputs. */
+void orc_backward_input(const void *grad_y, int dtype, int64_t m_rows, int64_t n_rows,
+                        const int8_t *t, int64_t k_cols, float gamma, double *grad_x)
+{
+    for (int64_t m = 0; m < m_rows; ++m)
+        for (int64_t k = 0; k < k_cols; ++k) {
+            double acc = 0.0;
+            for (int64_t n = 0; n < n_rows; ++n)
+                acc += (double)load_elem(grad_y, dtype, m * n_rows + n) * (double)t[n * k_cols + k];
+            grad_x[m * k_cols + k] = (double)gamma * acc;
+        }
+}
+
 /* ---- integer contraction and rescale [ASI, custom-software paragraph: the
  *      trits are multiplied with the 8-bit activations] ------------------- */
 

@@ -531,3 +531,50 @@ def test_sign_trits_pack_to_codes_zero_and_two():
     q, _, r = oracle.quantize_act(rng.standard_normal((3, 130)).astype(np.float32))
     acc = oracle.matmul_i32(q, oracle.sign_trits(np.abs(w) + np.float32(1e-3)))
     np.testing.assert_array_equal(acc, np.repeat(r[:, None], 5, axis=1))
+
+
+# ---- backward through BitLinear (straight-through estimators) ---------------------
+
+def test_backward_identity_and_hadamard():
+    rng = np.random.default_rng(11)
+    g = rng.standard_normal((3, 64)).astype(np.float32)
+    eye = np.eye(64, dtype=np.int8)
+    np.testing.assert_array_equal(oracle.backward_input(g, eye, 0.5), 0.5 * g.astype(np.float64))
+    h = scipy.linalg.hadamard(64).astype(np.int8)
+    ref = g.astype(np.float64) @ h.astype(np.float64) * 0.25
+    np.testing.assert_allclose(oracle.backward_input(g, h, 0.25), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_backward_integer_gradients_exact():
+    """Small-integer gradients: every partial sum is an exact integer, so the
+    result equals the int64 matrix product times gamma."""
+    rng = np.random.default_rng(12)
+    g = rng.integers(-50, 51, size=(5, 70)).astype(np.float32)
+    t = rng.integers(-1, 2, size=(70, 33)).astype(np.int8)
+    exact = (g.astype(np.int64) @ t.astype(np.int64)).astype(np.float64) * np.float64(np.float32(0.125))
+    np.testing.assert_array_equal(oracle.backward_input(g, t, 0.125), exact)
+
+
+def test_backward_is_the_adjoint_of_the_forward_contraction():
+    """<grad_y, q t^T> = <grad_y t, q>: pins the transposition against the
+    (separately pinned) forward contraction."""
+    rng = np.random.default_rng(13)
+    m, n, k = 4, 37, 53
+    w = rng.standard_normal((n, k)).astype(np.float32)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    g = rng.integers(-9, 10, size=(m, n)).astype(np.float32)
+    t, _ = oracle.quantize_weights(w)
+    q, _, _ = oracle.quantize_act(x)
+    lhs = int((g.astype(np.int64) * oracle.matmul_i32(q, t).astype(np.int64)).sum())
+    rhs = float((oracle.backward_input(g, t, 1.0) * q.astype(np.float64)).sum())
+    assert float(lhs) == rhs
+
+
+def test_backward_bf16_gradients_widen_exactly():
+    rng = np.random.default_rng(14)
+    gf = rng.standard_normal((2, 40)).astype(np.float32)
+    bits = inputs.f32_to_bf16_bits(gf)
+    t = rng.integers(-1, 2, size=(40, 17)).astype(np.int8)
+    widened = oracle.bf16_to_f32(bits)
+    np.testing.assert_array_equal(oracle.backward_input(bits, t, 1.0),
+                                  oracle.backward_input(widened, t, 1.0))
