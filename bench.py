@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector peak
 I8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, TOP/s
 METRIC = "BitLinear weight GB/s (% HBM peak) at M=1; TOPS (% int8 MFMA peak) at M=512"
 
@@ -315,7 +316,36 @@ def measure_extra(args):
             "TOPS_with_act_quant": round(2.0 * m * n * k / (ms_full * 1e-3) / 1e12, 2)}
         log(f"prefill {name}: {ms * 1e3:.1f} us {tops:.1f} TOPS")
     extra.update(measure_variants())
+    extra.update(measure_backward())
     return extra
+
+
+def measure_backward():
+    """Input gradient through BitLinear (straight-through estimators) on the
+    3B-class prefill matrices at M = 512, bf16 gradients: fp32 FMA work
+    2 M N K against the fp32 vector peak."""
+    import torch
+    from ternary_weight_linear_absmax_amd import bitlinear as bl
+    from ternary_weight_linear_absmax_amd import inputs
+    out = {}
+    reps = 5
+    for si, (name, k, n) in enumerate(inputs.PREFILL_SHAPES):
+        _, w, _ = inputs.prefill(si)
+        packed, gamma = bl.quantize_weights(to_dev(w))
+        m = 512
+        gy = (torch.randn((m, n), device="cuda") * 1e-3).to(torch.bfloat16)
+        gx = torch.empty((m, k), dtype=torch.float32, device="cuda")
+
+        def bwd():
+            for _ in range(reps):
+                bl.backward_input(gy, packed, gamma, k, grad_x=gx)
+        ms = graph_time(bwd, 10, 2) / reps
+        tflops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+        out[f"backward_input_{name}_M512"] = {
+            "K": k, "N": n, "M": m, "us": round(ms * 1e3, 2), "TFLOP/s": round(tflops, 2),
+            "fp32_frac": round(tflops / FP32_PEAK_TFLOPS, 4)}
+        log(f"backward input {name}: {ms * 1e3:.1f} us {tflops:.1f} TFLOP/s")
+    return out
 
 
 def measure_variants():

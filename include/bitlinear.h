@@ -206,6 +206,28 @@ int bitlinear_matmul_i32(const int8_t *xq, const int32_t *rowsum, int64_t M,
                          int32_t *acc, void *workspace, int64_t workspace_bytes, int path,
                          hipStream_t stream);
 
+/* ---- backward through BitLinear: input gradient -------------------------------
+ * [lumen-it.ai BitNet article, training paragraph: straight-through estimators
+ *  carry the gradient through the quantisers]
+ *
+ * With both quantisers passed straight through, the layer acts on x as the
+ * matrix gamma * t, so
+ *     grad_x[m, k] = gamma * sum_n grad_y[m, n] * t[n, k]
+ * over the same packed weights (2-bit layout only; BL_ERR_LAYOUT for base-3),
+ * in fp32 arithmetic.  The weight gradient passes straight through to the
+ * latent weights (a dense product of grad_y and the activations) and is not
+ * part of this library.
+ * grad_y  device, [M, N] of `dtype` (bf16 or fp32), row-major, 4-byte aligned
+ *         (may be NULL when N == 0).
+ * packed  device, bitlinear_packed_bytes(N, K, BL_PACK2) bytes (may be NULL
+ *         when N == 0: then grad_x is all zero).
+ * gamma   device, one float: the scale the weights were quantised with.
+ * grad_x  device, [M, K] float32, written.
+ * M == 0: nothing to do.  M <= 65535 * 64. */
+int bitlinear_backward_input(const void *grad_y, int dtype, int64_t M, int64_t N,
+                             const uint8_t *packed, int layout, const float *gamma, int64_t K,
+                             float *grad_x, hipStream_t stream);
+
 /* ---- quantise and multiply in one call ---------------------------------------
  * [cheatsheet.md summary, "What is BitNet b1.58?": activations scaled per token
  *  in front of every BitLinear; asi.tokyo 2B4T article, packing paragraph]

@@ -59,6 +59,7 @@ def load():
         "bitlinear_quantize_act": (i32, [p, i32, i64, i64, p, p, p, p]),
         "bitlinear_quantize_weights_binary": (i32, [p, i32, i64, i64, i32, p, p, p, i64, p]),
         "bitlinear_quantize_act_bits": (i32, [p, i32, i64, i64, i32, p, p, p, p]),
+        "bitlinear_backward_input": (i32, [p, i32, i64, i64, p, i32, p, i64, p, p]),
         "bitlinear_forward": (i32, [p, p, p, i64, p, i32, p, i64, i64, p, p, i64, p]),
         "bitlinear_forward_ex": (i32, [p, p, p, i64, p, i32, p, i64, i64, p, p, i64, i32, p]),
         "bitlinear_matmul_i32": (i32, [p, p, i64, p, i32, i64, i64, p, p, i64, i32, p]),
@@ -178,6 +179,19 @@ def quantize_act(x: torch.Tensor, stream=None, bits: int = 8):
                                                _ptr(scale), _ptr(rowsum), _stream(stream)),
                "bitlinear_quantize_act_bits")
     return xq, scale, rowsum
+
+
+def backward_input(grad_y: torch.Tensor, packed, gamma, k: int, grad_x=None, stream=None):
+    """grad_x [M, K] float32 = gamma * grad_y [M, N] @ t [N, K] (straight-through estimators)."""
+    lib = load()
+    assert grad_y.dim() == 2 and grad_y.is_contiguous()
+    m, n = grad_y.shape
+    if grad_x is None:
+        grad_x = torch.empty((m, k), dtype=torch.float32, device=grad_y.device)
+    _check(lib.bitlinear_backward_input(_ptr(grad_y), _dtype_code(grad_y), m, n, _ptr(packed),
+                                        BL_PACK2, _ptr(gamma), k, _ptr(grad_x), _stream(stream)),
+           "bitlinear_backward_input")
+    return grad_x
 
 
 def forward(xq, scale, rowsum, packed, gamma, n: int, k: int, layout: int = BL_PACK2,

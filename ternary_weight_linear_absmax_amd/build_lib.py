@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libbitlinear.so")
 
-SOURCES = ["api.hip", "quant_weights.hip", "quant_act.hip", "gemv.hip", "gemm.hip", "skinny.hip", "glue.hip"]
+SOURCES = ["api.hip", "quant_weights.hip", "quant_act.hip", "gemv.hip", "gemm.hip", "skinny.hip",
+           "glue.hip", "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

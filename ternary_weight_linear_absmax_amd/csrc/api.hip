@@ -166,6 +166,25 @@ int bitlinear_quantize_act_bits(const void *x, int dtype, int64_t M, int64_t K, 
         bl::launch_quant_act(x, dtype, M, K, xq, scale, rowsum, stream, (1 << (bits - 1)) - 1));
 }
 
+int bitlinear_backward_input(const void *grad_y, int dtype, int64_t M, int64_t N,
+                             const uint8_t *packed, int layout, const float *gamma, int64_t K,
+                             float *grad_x, hipStream_t stream)
+{
+    if (!good_dtype(dtype)) return BL_ERR_DTYPE;
+    if (!good_layout(layout)) return BL_ERR_LAYOUT;
+    if (layout != BL_PACK2) return BL_ERR_LAYOUT;
+    if (M < 0 || N < 0 || !good_k(K)) return BL_ERR_SHAPE;
+    if ((M > 0 && N > kMaxElems / M) || (M > 0 && K > kMaxElems / M) ||
+        (N > 0 && K > kMaxElems / N) || M > (int64_t)65535 * 64)
+        return BL_ERR_SHAPE;
+    if (M == 0) return BL_OK;
+    if (!grad_x || !gamma || (N > 0 && (!grad_y || !packed))) return BL_ERR_NULL;
+    if ((grad_y && !al4(grad_y)) || !al4(grad_x) || !al4(gamma) || (packed && !al16(packed)))
+        return BL_ERR_ALIGN;
+    return hip_status(
+        bl::launch_backward_input(grad_y, dtype, M, N, packed, K, gamma, grad_x, stream));
+}
+
 int bitlinear_quantize_act(const void *x, int dtype, int64_t M, int64_t K, int8_t *xq,
                            float *scale, int32_t *rowsum, hipStream_t stream)
 {

@@ -81,6 +81,12 @@ hipError_t launch_gemm_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
                              hipStream_t s);
 int64_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
+// ---- backward (backward.hip) ----
+// grad_x [m, k] fp32 = gamma * grad_y [m, n] (bf16 / fp32) * t [n, k] (2-bit layout).
+hipError_t launch_backward_input(const void *grad_y, int dtype, int64_t m, int64_t n,
+                                 const uint8_t *packed, int64_t k, const float *gamma,
+                                 float *grad_x, hipStream_t s);
+
 // 128-bit streaming load (the packed weights are read once per call).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ inline uint4 load_nt16(const void *p)

@@ -113,6 +113,27 @@ def test_quantize_act_bits_argument_checks(lib):
     assert f(P, 1, 0, 64, 4, P, P, P, None) == 0            # empty batch: no launch
 
 
+def test_backward_input_argument_checks(lib):
+    f = lib.bitlinear_backward_input
+
+    def call(g=P, dt=bl.BL_F32, m=4, n=8, pk=P, lay=bl.BL_PACK2, gam=P, k=64, gx=P):
+        return f(g, dt, m, n, pk, lay, gam, k, gx, None)
+
+    assert call(g=NULL) == -1
+    assert call(gx=NULL) == -1
+    assert call(gam=NULL) == -1
+    assert call(pk=NULL) == -1
+    assert call(n=0, g=NULL, pk=NULL, gx=ODD) == -3          # N == 0 needs no grad_y / weights
+    assert call(dt=2) == -4
+    assert call(lay=bl.BL_PACK3) == -5
+    assert call(lay=7) == -5
+    assert call(m=-1) == -2
+    assert call(k=0) == -2
+    assert call(m=65535 * 64 + 1) == -2
+    assert call(pk=ODD) == -3
+    assert call(m=0, g=NULL, gx=NULL, gam=NULL, pk=NULL) == 0   # nothing to do
+
+
 def test_forward_argument_checks(lib):
     f = lib.bitlinear_forward_ex
 
