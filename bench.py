@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector peak
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 I8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, TOP/s
 METRIC = "BitLinear weight GB/s (% HBM peak) at M=1; TOPS (% int8 MFMA peak) at M=512"
 
@@ -322,8 +323,9 @@ def measure_extra(args):
 
 def measure_backward():
     """Input gradient through BitLinear (straight-through estimators) on the
-    3B-class prefill matrices at M = 512, bf16 gradients: fp32 FMA work
-    2 M N K against the fp32 vector peak."""
+    3B-class prefill matrices at M = 512, bf16 gradients: 2 M N K flops,
+    against the fp32 vector peak and, as run (three bf16 MFMAs per product),
+    against the bf16 matrix-core peak."""
     import torch
     from ternary_weight_linear_absmax_amd import bitlinear as bl
     from ternary_weight_linear_absmax_amd import inputs
@@ -341,9 +343,12 @@ def measure_backward():
                 bl.backward_input(gy, packed, gamma, k, grad_x=gx)
         ms = graph_time(bwd, 10, 2) / reps
         tflops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+        # the kernel runs three bf16 MFMAs per product (gradient split in three parts)
         out[f"backward_input_{name}_M512"] = {
             "K": k, "N": n, "M": m, "us": round(ms * 1e3, 2), "TFLOP/s": round(tflops, 2),
-            "fp32_frac": round(tflops / FP32_PEAK_TFLOPS, 4)}
+            "fp32_equiv_frac": round(tflops / FP32_PEAK_TFLOPS, 4),
+            "bf16_mfma_TFLOP/s": round(3 * tflops, 1),
+            "bf16_mfma_frac": round(3 * tflops / BF16_PEAK_TFLOPS, 4)}
         log(f"backward input {name}: {ms * 1e3:.1f} us {tflops:.1f} TFLOP/s")
     return out
 

@@ -21,6 +21,9 @@ namespace bl {
 namespace {
 
 constexpr int BW_BM = 64, BW_BK = 128, BW_BN = 32;
+#ifndef BACKWARD_MFMA
+#define BACKWARD_MFMA 1
+#endif
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(256) void backward_input_kernel(const void *__restrict__ grad_y,
@@ -140,6 +143,182 @@ __global__ __launch_bounds__(256) void backward_input_kernel(const void *__restr
     }
 }
 
+// ---- matrix-core variant ---------------------------------------------------------
+// The same product on v_mfma_f32_32x32x16_bf16: each fp32 gradient is split
+// into three bf16 parts hi + mid + lo (round to nearest at each step; the
+// parts carry 8 significant bits each, so for normal values their sum is the
+// gradient exactly), the trits are exact in bf16, and the matrix cores
+// accumulate the three products in fp32.  Block tile 64 (m) x 128 (k), four
+// waves of 32 x 64; per stage of 32 n the block writes the three gradient
+// parts [m][n] and the raw packed bytes into LDS, unpacks the trits into a
+// [k][n] bf16 tile (n contiguous: one 16-byte operand per lane), then runs
+// 2 (n steps) x 2 (k tiles) x 3 (parts) MFMAs per wave; the next stage's
+// global data is loaded during the MFMAs.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int BM2 = 64, BK2 = 128, BN2 = 32;
+constexpr int LDAB = BN2 * 2 + 16;   // bytes per LDS row of 32 bf16 (+16 pad)
+
+__device__ inline uint32_t bf16_pair(__bf16 a, __bf16 b)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(256) void backward_mfma_kernel(const void *__restrict__ grad_y,
+                                                            int64_t m, int64_t n,
+                                                            const uint8_t *__restrict__ packed,
+                                                            int64_t pitch, int64_t k,
+                                                            const float *__restrict__ gamma_p,
+                                                            float *__restrict__ grad_x)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t as[2][3][BM2 * LDAB];
+    __shared__ __attribute__((aligned(16))) uint8_t bs[2][BK2 * LDAB];
+    __shared__ __attribute__((aligned(16))) uint32_t traw[BN2][BK2 / 16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wk = wave >> 1;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int64_t m0 = (int64_t)blockIdx.y * BM2, k0 = (int64_t)blockIdx.x * BK2;
+    const int nst = (int)((n + BN2 - 1) / BN2);
+    const int64_t words = pitch / 4;
+
+    // staging roles: gradient row m0 + tid / 4, columns 8 (tid % 4) .. +7;
+    // raw packed word tid % 8 of row tid / 8 (threads 0..255: 32 rows x 8 words)
+    const int gr = tid >> 2, gc = 8 * (tid & 3);
+    const int64_t gm = m0 + gr;
+    const int tr = tid >> 3, tw = tid & 7;
+    const int64_t wkk = k0 / 16 + tw;
+    float gv[8];
+    uint32_t tv = 0;
+
+    auto load = [&](int st) __attribute__((always_inline)) {
+        const int64_t nb = (int64_t)st * BN2;
+        if (VEC && gm < m && nb + gc + 8 <= n) {
+            if (DT == DT_BF16) {
+                const uint4 v = load16((const uint16_t *)grad_y + gm * n + nb + gc);
+                const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    gv[2 * e] = bf16_lo(u[e]);
+                    gv[2 * e + 1] = bf16_hi(u[e]);
+                }
+            } else {
+                const float *p = (const float *)grad_y + gm * n + nb + gc;
+                const uint4 a = load16(p), b = load16(p + 4);
+                gv[0] = __uint_as_float(a.x); gv[1] = __uint_as_float(a.y);
+                gv[2] = __uint_as_float(a.z); gv[3] = __uint_as_float(a.w);
+                gv[4] = __uint_as_float(b.x); gv[5] = __uint_as_float(b.y);
+                gv[6] = __uint_as_float(b.z); gv[7] = __uint_as_float(b.w);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t nn = nb + gc + e;
+                float v = 0.0f;
+                if (gm < m && nn < n) {
+                    if (DT == DT_BF16)
+                        v = __uint_as_float((uint32_t)((const uint16_t *)grad_y)[gm * n + nn] << 16);
+                    else
+                        v = ((const float *)grad_y)[gm * n + nn];
+                }
+                gv[e] = v;
+            }
+        }
+        const int64_t tn = nb + tr;
+        tv = (tn < n && wkk < words) ? ((const uint32_t *)(packed + tn * pitch))[wkk] : 0x55555555u;
+    };
+    // three bf16 parts of the 8 gradient values, and the raw packed word
+    auto store = [&](int buf) __attribute__((always_inline)) {
+        uint32_t part[3][4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a = gv[2 * e], b = gv[2 * e + 1];
+            const __bf16 ah = (__bf16)a, bh = (__bf16)b;
+            const float ar = a - (float)ah, br = b - (float)bh;
+            const __bf16 am = (__bf16)ar, bm = (__bf16)br;
+            const __bf16 al = (__bf16)(ar - (float)am), bl2 = (__bf16)(br - (float)bm);
+            part[0][e] = bf16_pair(ah, bh);
+            part[1][e] = bf16_pair(am, bm);
+            part[2][e] = bf16_pair(al, bl2);
+        }
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            *(uint4 *)(&as[buf][q][gr * LDAB + 2 * gc]) =
+                make_uint4(part[q][0], part[q][1], part[q][2], part[q][3]);
+        traw[tr][tw] = tv;
+    };
+    // trits of the stage into bs[buf][k][n]: thread -> k = tid % 128, n half
+    // tid / 128 (16 n): 16 codes gathered from the raw words, two 16-byte writes
+    auto unpack = [&](int buf) __attribute__((always_inline)) {
+        const int kk = tid & 127, nh = tid >> 7;
+        const int g = kk >> 4, i = (kk & 15) >> 2, j = kk & 3;
+        const int sh = 8 * j + 2 * i;
+        uint32_t v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int n0r = 16 * nh + 2 * q;
+            const float t0 = (float)(int)((traw[n0r][g] >> sh) & 3u) - 1.0f;
+            const float t1 = (float)(int)((traw[n0r + 1][g] >> sh) & 3u) - 1.0f;
+            v[q] = bf16_pair((__bf16)t0, (__bf16)t1);
+        }
+        uint4 *dst = (uint4 *)(&bs[buf][kk * LDAB + 32 * nh]);
+        dst[0] = make_uint4(v[0], v[1], v[2], v[3]);
+        dst[1] = make_uint4(v[4], v[5], v[6], v[7]);
+    };
+
+    f32x16 acc[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+
+    load(0);
+    store(0);
+    __syncthreads();
+    unpack(0);
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+        const int buf = st & 1;
+        if (st + 1 < nst) load(st + 1);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            bf16x8 b[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                b[c] = *(const bf16x8 *)(&bs[buf][(64 * wk + 32 * c + l32) * LDAB + 32 * s + 16 * h]);
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                const bf16x8 a =
+                    *(const bf16x8 *)(&as[buf][q][(32 * wm + l32) * LDAB + 32 * s + 16 * h]);
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+                    acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[c], acc[c], 0, 0, 0);
+            }
+        }
+        if (st + 1 < nst) {
+            store(buf ^ 1);
+            __syncthreads();
+            unpack(buf ^ 1);
+        }
+        __syncthreads();
+    }
+
+    // lane (l32, h), register r: row 8 (r / 4) + 4 h + r % 4 of the wave's 32
+    // m rows, column l32 of k tile c
+    const float gamma = gamma_p[0];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + 32 * wm + 8 * (r / 4) + 4 * h + (r % 4);
+        if (row >= m) continue;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int64_t col = k0 + 64 * wk + 32 * c + l32;
+            if (col < k) grad_x[row * k + col] = gamma * acc[c][r];
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_backward_input(const void *grad_y, int dtype, int64_t m, int64_t n,
@@ -150,6 +329,25 @@ hipError_t launch_backward_input(const void *grad_y, int dtype, int64_t m, int64
     const int64_t pitch = pack2_pitch(k);
     // 16-byte loads need every grad_y row 16-byte aligned
     const bool vec = dtype == DT_BF16 ? n % 8 == 0 : n % 4 == 0;
+    if (BACKWARD_MFMA) {
+        const dim3 g2((unsigned)((k + BK2 - 1) / BK2), (unsigned)((m + BM2 - 1) / BM2));
+        if (dtype == DT_BF16) {
+            if (vec)
+                hipLaunchKernelGGL((backward_mfma_kernel<DT_BF16, true>), g2, dim3(256), 0, s,
+                                   grad_y, m, n, packed, pitch, k, gamma, grad_x);
+            else
+                hipLaunchKernelGGL((backward_mfma_kernel<DT_BF16, false>), g2, dim3(256), 0, s,
+                                   grad_y, m, n, packed, pitch, k, gamma, grad_x);
+        } else {
+            if (vec)
+                hipLaunchKernelGGL((backward_mfma_kernel<DT_F32, true>), g2, dim3(256), 0, s,
+                                   grad_y, m, n, packed, pitch, k, gamma, grad_x);
+            else
+                hipLaunchKernelGGL((backward_mfma_kernel<DT_F32, false>), g2, dim3(256), 0, s,
+                                   grad_y, m, n, packed, pitch, k, gamma, grad_x);
+        }
+        return hipGetLastError();
+    }
     if (dtype == DT_BF16) {
         if (vec)
             hipLaunchKernelGGL((backward_input_kernel<DT_BF16, true>), grid, dim3(256), 0, s,
