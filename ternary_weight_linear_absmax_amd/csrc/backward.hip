@@ -8,13 +8,16 @@
 // (The weight gradient passes straight through to the latent weights and is
 // a dense product of grad_y and the activations, not a ternary one.)
 //
-// fp32 arithmetic (the gradient is a float; no quantisation of it is implied
-// by the sources).  Block tile 64 (m) x 128 (k), 256 threads with 4 x 8
-// outputs each; the reduction over n runs in stages of 32: the grad_y tile
-// [64 m x 32 n] is staged transposed in LDS, the packed tile [32 n x 128 k]
-// (32 bytes per row) is unpacked once into floats in LDS and then used by all
-// 64 m rows; the next stage's global data is loaded into registers while the
-// current one is computed (double-buffered LDS).
+// The gradient stays a float (no quantisation of it is implied by the
+// sources): every product g * t is exact and the sums are accumulated in fp32.
+// Two kernels: backward_mfma_kernel (the default, on the bf16 matrix cores
+// with the gradient split into three exact bf16 parts) and
+// backward_input_kernel (plain fp32 FMAs: block tile 64 (m) x 128 (k), 256
+// threads with 4 x 8 outputs each; the reduction over n runs in stages of 32:
+// the grad_y tile [64 m x 32 n] is staged transposed in LDS, the packed tile
+// [32 n x 128 k] (32 bytes per row) is unpacked once into floats in LDS and
+// then used by all 64 m rows; the next stage's global data is loaded into
+// registers while the current one is computed).
 #include "internal.h"
 
 namespace bl {
