@@ -104,9 +104,9 @@ int64_t bitlinear_quantize_weights_workspace_bytes(int64_t N, int64_t K);
 
 /* Workspace that bitlinear_forward / bitlinear_matmul_i32 need for this shape
  * on any path (0 when none; then workspace may be NULL).  A non-empty
- * workspace holds int32 partial sums when the matrix-core path splits the k
- * range: it must be all-zero before its first use, every call leaves it
- * all-zero again, and calls that share one workspace must not overlap. */
+ * workspace is scratch for the int32 partial sums of the matrix-core path
+ * when it splits the k range (one [M, N] tile per split): it needs no initial
+ * contents, and calls that share one workspace must not overlap. */
 int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int layout);
 
 /* Kernel path that BL_PATH_AUTO selects for this shape (a bl_path value). */

@@ -134,9 +134,9 @@ _workspaces = {}
 
 
 def _zero_workspace(nbytes: int, device):
-    """A per-device zero-initialised workspace, grown on demand and reused (the
-    library leaves it all-zero after every call).  Calls on different streams
-    that share it must not overlap; pass your own workspace for that."""
+    """A per-device workspace, grown on demand and reused (the library needs no
+    initial contents in it).  Calls on different streams that share it must not
+    overlap; pass your own workspace for that."""
     key = torch.device(device)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:

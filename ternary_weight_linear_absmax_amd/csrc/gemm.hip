@@ -26,13 +26,15 @@
 // stages ahead) into a double-buffered, padded LDS tile; packed weights go
 // into a four-slot register ring (loads issued three stages ahead).  Within
 // the loop every address is a per-lane offset fixed at the start plus a
-// uniform stage offset, so the stage costs no address arithmetic.  Blocks are numbered so that consecutive tiles (which share weight
-// columns) land on the same XCD and its L2.
+// uniform stage offset, so the stage costs no address arithmetic.  Blocks are
+// numbered so that consecutive tiles (which share weight columns) land on the
+// same XCD and its L2.
 //
-// Split-K (S > 1 slices of the k range) adds int32 partial tiles into a
-// workspace with device-scope atomics; a second kernel applies the epilogue
-// and clears the workspace again, so it stays all-zero between calls.  Integer
-// addition makes the result independent of the order of the slices.
+// Split-K (S > 1 slices of the k range) stores each slice's int32 partial
+// tile into its own slice of a workspace [S][M][N] (plain stores, no
+// atomics); a second kernel adds the S partial sums in slice order and
+// applies the epilogue.  Integer addition makes the result exact; the
+// workspace needs no initial contents.
 #include <type_traits>
 #include <utility>
 
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
                 const int64_t gm = m0 + wm * 32 * WM + 32 * a + 8 * (r / 4) + 4 * h + (r % 4);
 #pragma unroll
                 for (int s = 0; s < WN; ++s)
-                    if (gm < m && nrow[s] < n) atomicAdd(ws + gm * n + nrow[s], acc[a][s][r]);
+                    if (gm < m && nrow[s] < n) ws[((int64_t)split * m + gm) * n + nrow[s]] = acc[a][s][r];
             }
         return;
     }
@@ -593,7 +595,7 @@ __global__ __launch_bounds__(512) void gemm3_kernel(const int8_t *__restrict__ x
                 const int64_t gm = m0 + wm * 32 * WM + 32 * a + 8 * (r / 4) + 4 * h + (r % 4);
 #pragma unroll
                 for (int s = 0; s < WN; ++s)
-                    if (gm < m && nrow[s] < n) atomicAdd(ws + gm * n + nrow[s], acc[a][s][r]);
+                    if (gm < m && nrow[s] < n) ws[((int64_t)split * m + gm) * n + nrow[s]] = acc[a][s][r];
             }
         return;
     }
@@ -627,16 +629,18 @@ __global__ __launch_bounds__(512) void gemm3_kernel(const int8_t *__restrict__ x
 
 // Split-K epilogue: y (or acc) from the summed codes in the workspace, which
 // is cleared again for the next call.
-__global__ __launch_bounds__(256) void splitk_finish_kernel(int32_t *__restrict__ ws,
+// Sum of the splits' partial tiles, slice by slice in split order (exact
+// int32), then the epilogue.
+__global__ __launch_bounds__(256) void splitk_finish_kernel(const int32_t *__restrict__ ws,
                                                             const int32_t *__restrict__ rowsum,
-                                                            int64_t m, int64_t n, Out out,
-                                                            int64_t ldy)
+                                                            int64_t m, int64_t n, int splits,
+                                                            Out out, int64_t ldy)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= m * n) return;
     const int64_t gm = i / n, gn = i % n;
-    const int32_t v = ws[i];
-    ws[i] = 0;
+    int32_t v = 0;
+    for (int sp = 0; sp < splits; ++sp) v += ws[sp * m * n + i];
     store_out(out, ldy, gm, gn, v, rowsum[gm]);
 }
 
@@ -669,10 +673,33 @@ GemmCfg gemm_config(int64_t m, int64_t n, int64_t k)
     return {2, 2, (int)(sp < 1 ? 1 : sp)};
 }
 
+// Row / column blocks of a product whose operands exceed 32-bit offsets.
+static void gemm_chunks(int64_t m, int64_t n, int64_t k, int64_t &mc, int64_t &nc)
+{
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t pitch = pack2_pitch(k);
+    mc = m;
+    nc = n;
+    if (mc * k >= lim) mc = ((lim - 1) / k) / 128 * 128;
+    if (nc * pitch >= lim) nc = ((lim - 1) / pitch) / 128 * 128;
+    if (mc < 1) mc = 1;
+    if (nc < 1) nc = 1;
+}
+
+// One int32 partial tile per split: splits x M x N (largest over the blocks).
 int64_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k)
 {
-    const GemmCfg c = gemm_config(m, n, k);
-    return c.splits > 1 ? 4 * m * n : 0;
+    int64_t mc, nc, need = 0;
+    gemm_chunks(m, n, k, mc, nc);
+    for (int64_t m0 = 0; m0 < m; m0 += mc)
+        for (int64_t n0 = 0; n0 < n; n0 += nc) {
+            const int64_t mb = m - m0 < mc ? m - m0 : mc;
+            const int64_t nb = n - n0 < nc ? n - n0 : nc;
+            const GemmCfg c = gemm_config(mb, nb, k);
+            const int64_t b = c.splits > 1 ? 4 * c.splits * mb * nb : 0;
+            need = b > need ? b : need;
+        }
+    return need;
 }
 
 template <int WM, int WN>
@@ -708,7 +735,7 @@ hipError_t launch_gemm_cfg(const int8_t *xq, const int32_t *rowsum, int64_t m,
     if (e != hipSuccess || splits == 1) return e;
     const int64_t total = m * n;
     hipLaunchKernelGGL(splitk_finish_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                       s, ws, rowsum, m, n, out, ldy);
+                       s, ws, rowsum, m, n, splits, out, ldy);
     return hipGetLastError();
 }
 
@@ -718,13 +745,9 @@ hipError_t launch_gemm_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
 {
     // The kernel addresses each operand with 32-bit per-lane offsets: larger
     // operands are processed in blocks of rows of x and of weight rows.
-    const int64_t lim = (int64_t)1 << 31;
     const int64_t pitch = pack2_pitch(k);
-    int64_t mc = m, nc = n;
-    if (mc * k >= lim) mc = ((lim - 1) / k) / 128 * 128;
-    if (nc * pitch >= lim) nc = ((lim - 1) / pitch) / 128 * 128;
-    if (mc < 1) mc = 1;
-    if (nc < 1) nc = 1;
+    int64_t mc, nc;
+    gemm_chunks(m, n, k, mc, nc);
     for (int64_t m0 = 0; m0 < m; m0 += mc) {
         for (int64_t n0 = 0; n0 < n; n0 += nc) {
             const int64_t mb = m - m0 < mc ? m - m0 : mc;

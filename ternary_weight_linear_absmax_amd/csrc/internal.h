@@ -71,7 +71,7 @@ hipError_t launch_gemv_pack3(const int8_t *xq, const int32_t *rowsum, int64_t m,
                              const uint8_t *packed, int64_t n, int64_t k, Out out,
                              hipStream_t s);
 // 2-bit layout, int8 matrix-core kernel.  ws: gemm_workspace_bytes(m, n, k)
-// bytes, all-zero on entry and left all-zero (used only when k is split).
+// bytes of scratch, any contents (one int32 partial tile per split of k).
 bool skinny_supported(int64_t m, int64_t n, int64_t k);
 hipError_t launch_skinny_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
                                const uint8_t *packed, int64_t n, int64_t k, Out out,

@@ -34,6 +34,9 @@ def test_size_queries_match_the_layout_definitions(lib):
     assert bl.packed_bytes(7, 0) == 0 and bl.packed_row_bytes(64, 9) == 0
     assert bl.quantize_weights_workspace_bytes(100, 64) == 800
     assert bl.forward_workspace_bytes(512, 8640, 3200) >= 0
+    # a split-k shape: one int32 [M, N] partial tile per split
+    ws = bl.forward_workspace_bytes(64, 128, 4096)
+    assert ws > 0 and ws % (4 * 64 * 128) == 0
 
 
 def test_path_selection(lib):

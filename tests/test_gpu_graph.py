@@ -34,7 +34,7 @@ def test_graph_replays_match_eager():
         bufs.append(dict(m=m, n=n, k=k, path=path, packed=packed, gamma=gamma, x=xd, xq=xq,
                          scale=scale, rowsum=rowsum, y=y))
     # the split-K case needs the workspace: the eager pass allocates the
-    # binding's shared zeroed workspace before capture
+    # binding's shared workspace before capture
     assert bl.forward_workspace_bytes(64, 128, 4096) > 0
 
     lib = bl.load()

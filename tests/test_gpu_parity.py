@@ -284,10 +284,12 @@ def test_quantize_forward(m, n, k, bf16, layout, path):
     np.testing.assert_array_equal(host(scale), s_ref)
     np.testing.assert_array_equal(host(rowsum), r_ref)
     assert_y_close(host(y), y_ref, acc_ref)
-    # a workspace the call used is left all-zero
+    # the workspace contents do not matter: garbage in it gives the same y
     torch.cuda.synchronize()
     for ws in bl._workspaces.values():
-        assert int(ws[:256].count_nonzero()) == 0
+        ws.fill_(0xA5)
+    y3, _, _, _ = bl.quantize_forward(xd, packed, gamma, n, layout, path=path)
+    assert np.array_equal(host(y).view(np.uint32), host(y3).view(np.uint32))
     # bit-identical to the two separate calls
     xq2, s2, r2 = bl.quantize_act(xd)
     y2 = bl.forward(xq2, s2, r2, packed, gamma, n, k, layout, path=path)
