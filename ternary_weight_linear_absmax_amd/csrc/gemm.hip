@@ -653,7 +653,8 @@ GemmCfg gemm_config(int64_t m, int64_t n, int64_t k)
 {
     // Chosen from timings of every tile / split combination on the 2B-, 3B-
     // and 70B-class shapes.  M <= 64, or a product with few 64 x 64 tiles:
-    // 64 x 64 tiles, the k range split in two when there are few of them.
+    // 64 x 64 tiles, the k range split (up to four ways, at least six stages
+    // each) when there are few of them.
     // Larger: 128 x 128 tiles when they fill one round of the 256 CUs or many;
     // 64 x 128 tiles when 128 x 128 ones would spill a few tiles into a second
     // round; 128 x 128 tiles with the k range split when they are too few.
@@ -662,7 +663,12 @@ GemmCfg gemm_config(int64_t m, int64_t n, int64_t k)
         return ((m + 64 * wm - 1) / (64 * wm)) * ((n + 64 * wn - 1) / (64 * wn));
     };
     const int64_t t11 = tiles(1, 1);
-    if (m <= 64 || t11 < 192) return {1, 1, (t11 < 192 && nk >= 16) ? 2 : 1};
+    if (m <= 64 || t11 < 192) {
+        int64_t sp = t11 < 192 ? 256 / t11 : 1;   // splits: up to 4, >= 6 stages each
+        if (sp > 4) sp = 4;
+        if (sp > nk / 6) sp = nk / 6;
+        return {1, 1, (int)(sp < 1 ? 1 : sp)};
+    }
     const int64_t t22 = tiles(2, 2);
     if (t22 >= 192 && t22 <= 256) return {2, 2, 1};
     if (t22 > 256 && t22 < 512) return {1, 2, 1};
