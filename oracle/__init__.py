@@ -58,9 +58,11 @@ def _load():
         build()
     lib = ctypes.CDLL(_LIB_PATH)
     p, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    f64 = ctypes.c_double
     sig = {
         "orc_bf16_to_f32": (f32, [ctypes.c_uint16]),
         "orc_absmean_gamma": (f32, [p, i32, i64, i64]),
+        "orc_abs_sum": (f64, [p, i32, i64, p]),
         "orc_absmean_trits": (None, [p, i32, i64, i64, f32, p]),
         "orc_pack2_pitch": (i64, [i64]),
         "orc_pack2": (None, [p, i64, i64, p]),
@@ -124,6 +126,14 @@ def absmean_gamma(w: np.ndarray) -> np.float32:
     w, dt = _as_input(w)
     n, k = w.shape
     return np.float32(_load().orc_absmean_gamma(_ptr(w), dt, n, k))
+
+
+def abs_sum(w: np.ndarray):
+    """(sum of |w| rounded once to double, nonfinite flag: 0, 1 = inf, 2 = NaN)."""
+    w, dt = _as_input(w)
+    flag = np.zeros(1, dtype=np.int32)
+    total = float(_load().orc_abs_sum(_ptr(w), dt, w.size, _ptr(flag)))
+    return total, int(flag[0])
 
 
 def absmean_trits(w: np.ndarray, gamma) -> np.ndarray:

@@ -23,9 +23,9 @@
  *
  * Readings taken where the sources are silent (each is listed with its reason
  * in the design notes):
- *   - gamma is one scalar per weight matrix, accumulated in double precision in
- *     a fixed order (row by row, k ascending inside a row), then divided by N*K
- *     and rounded once to float.
+ *   - gamma is one scalar per weight matrix: the sum of |w| is formed exactly
+ *     and rounded once to double, divided by N*K in double precision and
+ *     rounded once to float (so it does not depend on any summation order).
  *   - "round to the nearest integer" is round-half-to-even on the exact
  *     quotient w/gamma; the result is clipped to [-1, 1].
  *   - activation quantisation is symmetric 8-bit: s = 127 / max|x| per token,
@@ -67,16 +67,88 @@ static float load_elem(const void *p, int dtype, int64_t i)
 /* ---- weights: absmean quantiser [CS "What is BitNet b1.58?", first bullet;
  *      ASI, absmean-quantiser paragraph] --------------------------------- */
 
-/* gamma = mean |W| over the whole N x K matrix. */
+/* Sum of |w| over `count` elements without any rounding, then rounded once to
+ * the nearest double (ties to even).  A finite binary32 magnitude is an integer
+ * significand m < 2^24 times 2^(e - 150), with e = max(biased exponent, 1) and
+ * the implicit leading bit included for e >= 1.  The significands are added
+ * per exponent in 64-bit integers (fewer than 2^40 terms of less than 2^24
+ * each, so no overflow), the per-exponent totals are added, shifted, into one
+ * multi-word binary integer B, and B * 2^-150 is rounded to a double.
+ * *nonfinite is set to 2 if an element is NaN, else 1 if one is infinite,
+ * else 0. */
+double orc_abs_sum(const void *w, int dtype, int64_t count, int *nonfinite)
+{
+    uint64_t per_exp[256];
+    memset(per_exp, 0, sizeof per_exp);
+    int nan_seen = 0, inf_seen = 0;
+    for (int64_t i = 0; i < count; ++i) {
+        float f = load_elem(w, dtype, i);
+        uint32_t u;
+        memcpy(&u, &f, sizeof u);
+        uint32_t e = (u >> 23) & 0xffu, frac = u & 0x7fffffu;
+        if (e == 255u) {
+            if (frac) nan_seen = 1;
+            else inf_seen = 1;
+            continue;
+        }
+        uint32_t m = e ? (frac | 0x800000u) : frac;
+        per_exp[e ? e : 1] += m;
+    }
+    *nonfinite = nan_seen ? 2 : (inf_seen ? 1 : 0);
+
+    /* B = sum_e per_exp[e] * 2^e as 16 little-endian 32-bit digits. */
+    uint32_t digit[16];
+    memset(digit, 0, sizeof digit);
+    for (int e = 1; e < 255; ++e) {
+        uint64_t v = per_exp[e];
+        int pos = e / 32, sh = e % 32;
+        /* v << sh spans at most three digits; add them with carry */
+        uint32_t part[3];
+        part[0] = (uint32_t)(v << sh);
+        part[1] = (uint32_t)(sh ? (v >> (32 - sh)) : (v >> 32));
+        part[2] = (uint32_t)(sh ? (v >> (64 - sh)) : 0);
+        uint64_t carry = 0;
+        for (int d = pos; d < 16; ++d) {
+            uint64_t add = (d - pos < 3) ? part[d - pos] : 0;
+            uint64_t t = (uint64_t)digit[d] + add + carry;
+            digit[d] = (uint32_t)t;
+            carry = t >> 32;
+            if (d - pos >= 2 && carry == 0) break;
+        }
+    }
+
+    /* highest set bit of B */
+    int top = -1;
+    for (int d = 15; d >= 0 && top < 0; --d)
+        for (int b = 31; b >= 0; --b)
+            if ((digit[d] >> b) & 1u) {
+                top = 32 * d + b;
+                break;
+            }
+    if (top < 0) return 0.0;
+#define ORC_BIT(pos) ((digit[(pos) / 32] >> ((pos) % 32)) & 1u)
+    /* keep the 53 bits top-52 .. top, round on the rest */
+    int low = top - 52;
+    uint64_t mant = 0;
+    for (int b = top; b >= (low > 0 ? low : 0); --b) mant = (mant << 1) | ORC_BIT(b);
+    if (low <= 0) return ldexp((double)mant, -150);      /* B < 2^53: exact */
+    int half = ORC_BIT(low - 1);
+    int sticky = 0;
+    for (int b = 0; b < low - 1; ++b) sticky |= ORC_BIT(b);
+#undef ORC_BIT
+    if (half && (sticky || (mant & 1u))) mant += 1;      /* may reach 2^53: still exact */
+    return ldexp((double)mant, low - 150);
+}
+
+/* gamma = mean |W| over the whole N x K matrix: the exact sum of |w| rounded
+ * once to double, divided by N*K in double precision, rounded to float.  A NaN
+ * element makes gamma NaN; otherwise an infinite one makes it +inf. */
 float orc_absmean_gamma(const void *w, int dtype, int64_t n_rows, int64_t k_cols)
 {
-    double total = 0.0;
-    for (int64_t n = 0; n < n_rows; ++n) {
-        double row = 0.0;
-        for (int64_t k = 0; k < k_cols; ++k)
-            row += fabs((double)load_elem(w, dtype, n * k_cols + k));
-        total += row;
-    }
+    int nonfinite = 0;
+    double total = orc_abs_sum(w, dtype, n_rows * k_cols, &nonfinite);
+    if (nonfinite == 2) return NAN;
+    if (nonfinite == 1) return INFINITY;
     return (float)(total / ((double)n_rows * (double)k_cols));
 }
 

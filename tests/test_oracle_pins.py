@@ -106,6 +106,74 @@ def test_gamma_gaussian_expectation():
     assert abs(g - mean) < 5 * sd
 
 
+def _f32_from_bits(bits):
+    return np.asarray(bits, dtype=np.uint32).view(np.float32)
+
+
+@pytest.mark.parametrize("kind", ["normal", "wide", "any_finite", "subnormal", "near_max"])
+def test_abs_sum_is_correctly_rounded_like_fsum(kind):
+    # math.fsum returns the exactly rounded sum of its (double) inputs; every
+    # float32 magnitude is exact in double, so the two must agree bit for bit.
+    rng = np.random.default_rng({"normal": 1, "wide": 2, "any_finite": 3,
+                                 "subnormal": 4, "near_max": 5}[kind])
+    for n in (1, 2, 3, 17, 255, 4096):
+        if kind == "normal":
+            w = rng.standard_normal(n, dtype=np.float32) * np.float32(0.02)
+        elif kind == "wide":
+            w = (rng.standard_normal(n) * np.exp2(rng.integers(-149, 128, n))).astype(np.float32)
+        elif kind == "any_finite":
+            w = _f32_from_bits(rng.integers(0, 0x7F800000, n) | (rng.integers(0, 2, n) << 31))
+        elif kind == "subnormal":
+            w = _f32_from_bits(rng.integers(0, 0x00800000, n))
+        else:
+            w = _f32_from_bits(rng.integers(0x7F000000, 0x7F800000, n))
+        total, flag = oracle.abs_sum(w.reshape(1, -1))
+        assert flag == 0
+        assert total == math.fsum(np.abs(w.astype(np.float64)).tolist())
+
+
+def test_abs_sum_round_half_to_even_and_sticky():
+    # 2^60 + 2^7 lies halfway between the doubles 2^60 and 2^60 + 2^8: even wins.
+    assert oracle.abs_sum(np.array([[2.0**60, 2.0**7]], np.float32))[0] == 2.0**60
+    # 2^60 + 2^8 + 2^7: halfway again, and the even neighbour is now above.
+    assert oracle.abs_sum(np.array([[2.0**60, 2.0**8, 2.0**7]], np.float32))[0] == 2.0**60 + 2.0**9
+    # the same tie plus the smallest subnormal: no longer a tie, rounds up
+    w = np.array([[2.0**60, 2.0**7, 2.0**-149]], np.float32)
+    assert oracle.abs_sum(w)[0] == 2.0**60 + 2.0**8
+    # a sum below 2^53 units of 2^-150 is exact: 2^-149 + 2^-126
+    assert oracle.abs_sum(np.array([[2.0**-149, -2.0**-126]], np.float32))[0] == 2.0**-149 + 2.0**-126
+
+
+def test_abs_sum_exact_by_fractions():
+    from fractions import Fraction
+    rng = np.random.default_rng(9)
+    for _ in range(20):
+        w = (rng.standard_normal(37) * np.exp2(rng.integers(-60, 60, 37))).astype(np.float32)
+        exact = sum(Fraction(float(abs(v))) for v in w)
+        assert oracle.abs_sum(w.reshape(1, -1))[0] == float(exact)   # float(Fraction) rounds once
+        n, k = 1, 37
+        assert oracle.absmean_gamma(w.reshape(1, -1)) == np.float32(float(exact) / (n * k))
+
+
+def test_gamma_independent_of_element_order():
+    # The sum is exact before its one rounding, so any permutation of W gives
+    # the same gamma, also for magnitudes spread over many binades.
+    rng = np.random.default_rng(12)
+    w = (rng.standard_normal((24, 40)) * np.exp2(rng.integers(-100, 100, (24, 40)))).astype(np.float32)
+    g = oracle.absmean_gamma(w)
+    for _ in range(5):
+        p = rng.permutation(w.size)
+        assert oracle.absmean_gamma(w.ravel()[p].reshape(40, 24)) == g
+
+
+def test_gamma_nonfinite_elements():
+    w = np.ones((3, 4), np.float32)
+    w[1, 2] = np.inf
+    assert oracle.absmean_gamma(w) == np.inf
+    w[0, 0] = np.nan
+    assert np.isnan(oracle.absmean_gamma(w))
+
+
 # ---- trits ------------------------------------------------------------------------
 
 def test_trit_golden_cases():
