@@ -248,12 +248,19 @@ def measure_extra(args):
         _, w, x = inputs.xl(si, m=128)
         wd = to_dev(w)
         p2, g2 = bl.quantize_weights(wd)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
         p3, g3 = bl.quantize_weights(wd, bl.BL_PACK3)
-        torch.cuda.synchronize()
-        quant_ms = (time.perf_counter() - t0) * 1e3
-        del wd
+        # weight quantiser (offline step): gamma pass + packing pass over W
+        ws_w = torch.empty((bl.quantize_weights_workspace_bytes(n, k),), dtype=torch.uint8,
+                           device="cuda")
+        for lay, (pk, gk), tag in ((bl.BL_PACK2, (p2, g2), "pack2"), (bl.BL_PACK3, (p3, g3), "pack3")):
+            ms_q = graph_time(lambda: bl.quantize_weights(wd, lay, out=(pk, gk), workspace=ws_w), 5, 1)
+            moved = 2 * wd.numel() * wd.element_size() + pk.numel()
+            extra[f"xl_{name}_quantize_weights_{tag}"] = {
+                "us": round(ms_q * 1e3, 1), "GB/s": round(moved / (ms_q * 1e-3) / 1e9, 1),
+                "hbm_frac": round(moved / (ms_q * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "bytes": moved}
+            log(f"xl {name} quantize_weights {tag}: {ms_q * 1e3:.1f} us")
+        del wd, ws_w
         c2 = [p2] + [p2.clone() for _ in range(copies_n - 1)]
         c3 = [p3] + [p3.clone() for _ in range(copies_n - 1)]
         xq, scale, rowsum = bl.quantize_act(to_dev(x))
@@ -284,7 +291,6 @@ def measure_extra(args):
                     "hbm_frac": round(gbs3 / HBM_PEAK_GBS, 4),
                     "trits_per_s": round(n * k / (ms3 * 1e-3), 1)}
                 log(f"xl {name} M=1 pack3: {ms3 * 1e3:.1f} us {gbs3:.0f} GB/s")
-        extra[f"xl_{name}_quantize_weights_pack3_ms"] = round(quant_ms, 2)
         del c2, c3
         torch.cuda.empty_cache()
     # layer stack: 30 layers of the 2B-class decoder, M = 64 tokens at position 0

@@ -98,8 +98,9 @@ int64_t bitlinear_packed_row_bytes(int64_t K, int layout);
 /* Bytes of a packed [N, K] matrix: N * bitlinear_packed_row_bytes(K, layout). */
 int64_t bitlinear_packed_bytes(int64_t N, int64_t K, int layout);
 
-/* Workspace that bitlinear_quantize_weights needs: 8 * N bytes (one double per
- * row for the fixed-order absolute sums). */
+/* Workspace that bitlinear_quantize_weights needs: 128 bytes per summing block,
+ * min(2048, max(1, ceil(N*K / 8192))) blocks (partial sums of |w| as exact
+ * multi-word integers; no initial contents needed); 0 for N < 1 or K < 1. */
 int64_t bitlinear_quantize_weights_workspace_bytes(int64_t N, int64_t K);
 
 /* Workspace that bitlinear_forward / bitlinear_matmul_i32 need for this shape
@@ -122,9 +123,10 @@ const char *bitlinear_status_string(int status);
  *
  * W       device, [N, K] of `dtype`.
  * packed  device, bitlinear_packed_bytes(N, K, layout) bytes, written.
- * gamma   device, one float, written: gamma = mean|W|, summed in double
- *         precision row by row (k ascending within a row, rows in order), then
- *         divided by N*K and rounded once to float.
+ * gamma   device, one float, written: gamma = mean|W|: the sum of |w| is formed
+ *         exactly (independent of element order) and rounded once to double,
+ *         divided by N*K in double precision and rounded to float.  A NaN
+ *         element gives gamma = NaN, else an infinite one gives +inf.
  * t       t = sign(w) when 2|w| > gamma, else 0: round-half-to-even of the
  *         exact quotient w / gamma, clipped to [-1, 1].
  * workspace  device, >= bitlinear_quantize_weights_workspace_bytes(N, K).

@@ -145,16 +145,24 @@ def _zero_workspace(nbytes: int, device):
     return ws
 
 
-def quantize_weights(w: torch.Tensor, layout: int = BL_PACK2, stream=None, binary: bool = False):
+def quantize_weights(w: torch.Tensor, layout: int = BL_PACK2, stream=None, binary: bool = False,
+                     out=None, workspace: torch.Tensor = None):
     """w [N, K] (float32/bfloat16, on the GPU) -> (packed uint8 [N, row_bytes], gamma float32 [1]).
-    binary: the sign binariser (bitlinear_quantize_weights_binary); gamma is then its scale."""
+    binary: the sign binariser (bitlinear_quantize_weights_binary); gamma is then its scale.
+    out: optional (packed, gamma) to write into; workspace: optional uint8 scratch of at
+    least quantize_weights_workspace_bytes(N, K) bytes (no initial contents needed)."""
     lib = load()
     assert w.dim() == 2 and w.is_contiguous()
     n, k = w.shape
-    packed = torch.empty((n, packed_row_bytes(k, layout)), dtype=torch.uint8, device=w.device)
-    gamma = torch.empty((1,), dtype=torch.float32, device=w.device)
-    ws_bytes = quantize_weights_workspace_bytes(n, k)
-    ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=w.device)
+    if out is None:
+        packed = torch.empty((n, packed_row_bytes(k, layout)), dtype=torch.uint8, device=w.device)
+        gamma = torch.empty((1,), dtype=torch.float32, device=w.device)
+    else:
+        packed, gamma = out
+    ws = workspace
+    if ws is None:
+        ws_bytes = quantize_weights_workspace_bytes(n, k)
+        ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=w.device)
     name = "bitlinear_quantize_weights_binary" if binary else "bitlinear_quantize_weights"
     _check(getattr(lib, name)(_ptr(w), _dtype_code(w), n, k, layout, _ptr(packed), _ptr(gamma),
                               _ptr(ws), ws.numel(), _stream(stream)), name)

@@ -85,8 +85,8 @@ int64_t bitlinear_packed_bytes(int64_t N, int64_t K, int layout)
 
 int64_t bitlinear_quantize_weights_workspace_bytes(int64_t N, int64_t K)
 {
-    (void)K;
-    return N > 0 ? 8 * N : 0;
+    if (N < 1 || K < 1 || K > kMaxElems / N) return 0;
+    return bl::gamma_workspace_bytes(N * K);
 }
 
 int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int layout)
@@ -128,9 +128,7 @@ int bitlinear_quantize_weights(const void *W, int dtype, int64_t N, int64_t K, i
     if (N < 1 || !good_k(K) || K > kMaxElems / N) return BL_ERR_SHAPE;
     if (!al16(W) || !al16(packed) || !al16(workspace) || !al4(gamma)) return BL_ERR_ALIGN;
     if (workspace_bytes < bitlinear_quantize_weights_workspace_bytes(N, K)) return BL_ERR_WORKSPACE;
-    double *rowsums = (double *)workspace;
-    hipError_t e = bl::launch_gamma_rows(W, dtype, N, K, rowsums, stream);
-    if (e == hipSuccess) e = bl::launch_gamma_final(rowsums, N, K, gamma, stream);
+    hipError_t e = bl::launch_gamma(W, dtype, N, K, workspace, gamma, stream);
     if (e == hipSuccess) e = bl::launch_pack(W, dtype, N, K, layout, gamma, packed, stream);
     return hip_status(e);
 }
@@ -145,9 +143,7 @@ int bitlinear_quantize_weights_binary(const void *W, int dtype, int64_t N, int64
     if (N < 1 || !good_k(K) || K > kMaxElems / N) return BL_ERR_SHAPE;
     if (!al16(W) || !al16(packed) || !al16(workspace) || !al4(beta)) return BL_ERR_ALIGN;
     if (workspace_bytes < bitlinear_quantize_weights_workspace_bytes(N, K)) return BL_ERR_WORKSPACE;
-    double *rowsums = (double *)workspace;
-    hipError_t e = bl::launch_gamma_rows(W, dtype, N, K, rowsums, stream);
-    if (e == hipSuccess) e = bl::launch_gamma_final(rowsums, N, K, beta, stream);
+    hipError_t e = bl::launch_gamma(W, dtype, N, K, workspace, beta, stream);
     if (e == hipSuccess) e = bl::launch_pack(W, dtype, N, K, layout, beta, packed, stream, true);
     return hip_status(e);
 }

@@ -26,10 +26,11 @@ struct Out {
 };
 
 // ---- weights (quant_weights.hip) ----
-hipError_t launch_gamma_rows(const void *w, int dtype, int64_t n, int64_t k, double *rowsums,
-                             hipStream_t s);
-hipError_t launch_gamma_final(const double *rowsums, int64_t n, int64_t k, float *gamma,
-                              hipStream_t s);
+// Exact absmean scale: gamma = float(round_to_double(sum |w|) / (N*K)).
+// The workspace holds gamma_workspace_bytes(N*K) bytes of scratch.
+int64_t gamma_workspace_bytes(int64_t count);
+hipError_t launch_gamma(const void *w, int dtype, int64_t n, int64_t k, void *workspace,
+                        float *gamma, hipStream_t s);
 hipError_t launch_pack(const void *w, int dtype, int64_t n, int64_t k, int layout,
                        const float *gamma, uint8_t *packed, hipStream_t s, bool binary = false);
 hipError_t launch_unpack(const uint8_t *packed, int layout, int64_t n, int64_t k,

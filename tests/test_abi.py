@@ -32,7 +32,11 @@ def test_size_queries_match_the_layout_definitions(lib):
         assert bl.packed_row_bytes(k, bl.BL_PACK3) == oracle.pack3_pitch(k)
     assert bl.packed_bytes(28672, 8192) == 58_720_256
     assert bl.packed_bytes(7, 0) == 0 and bl.packed_row_bytes(64, 9) == 0
-    assert bl.quantize_weights_workspace_bytes(100, 64) == 800
+    # 128 bytes per summing block, one block per 8192 elements, at most 2048
+    assert bl.quantize_weights_workspace_bytes(100, 64) == 128
+    assert bl.quantize_weights_workspace_bytes(1000, 2000) == 128 * 245
+    assert bl.quantize_weights_workspace_bytes(28672, 8192) == 128 * 2048
+    assert bl.quantize_weights_workspace_bytes(0, 64) == 0
     assert bl.forward_workspace_bytes(512, 8640, 3200) >= 0
     # a split-k shape: one int32 [M, N] partial tile per split
     ws = bl.forward_workspace_bytes(64, 128, 4096)
