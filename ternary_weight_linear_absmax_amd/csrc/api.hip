@@ -26,6 +26,14 @@ int choose_path(int64_t m, int64_t n, int64_t k, int layout)
     return m <= 4 ? BL_PATH_GEMV : BL_PATH_MFMA;
 }
 
+// Workspace bytes the chosen path needs (partial sums of a split k range).
+int64_t workspace_need(int path, int64_t m, int64_t n, int64_t k)
+{
+    if (path == BL_PATH_MFMA) return bl::gemm_workspace_bytes(m, n, k);
+    if (path == BL_PATH_SKINNY) return bl::skinny_workspace_bytes(m, n, k);
+    return 0;
+}
+
 // Shared body of bitlinear_forward_ex and bitlinear_matmul_i32.
 int run_product(const int8_t *xq, const float *scale, const int32_t *rowsum, int64_t m,
                 const uint8_t *packed, int layout, const float *gamma, int64_t n, int64_t k,
@@ -50,7 +58,7 @@ int run_product(const int8_t *xq, const float *scale, const int32_t *rowsum, int
     if (!al16(xq) || !al16(packed) || !al4(rowsum)) return BL_ERR_ALIGN;
     if (y && (!al4(y) || !al4(scale) || !al4(gamma))) return BL_ERR_ALIGN;
     if (acc && !al4(acc)) return BL_ERR_ALIGN;
-    const int64_t need = path == BL_PATH_MFMA ? bl::gemm_workspace_bytes(m, n, k) : 0;
+    const int64_t need = workspace_need(path, m, n, k);
     if (need > 0 && (!workspace || workspace_bytes < need)) return BL_ERR_WORKSPACE;
     if (need > 0 && !al16(workspace)) return BL_ERR_ALIGN;
 
@@ -61,7 +69,7 @@ int run_product(const int8_t *xq, const float *scale, const int32_t *rowsum, int
     else if (path == BL_PATH_GEMV)
         e = bl::launch_gemv_pack2(xq, rowsum, m, packed, n, k, out, stream);
     else if (path == BL_PATH_SKINNY)
-        e = bl::launch_skinny_pack2(xq, rowsum, m, packed, n, k, out, stream);
+        e = bl::launch_skinny_pack2(xq, rowsum, m, packed, n, k, out, workspace, stream);
     else
         e = bl::launch_gemm_pack2(xq, rowsum, m, packed, n, k, out, workspace, stream);
     return hip_status(e);
@@ -94,7 +102,8 @@ int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int l
     if (M < 1 || N < 1 || !good_k(K) || !good_layout(layout)) return 0;
     if (layout == BL_PACK3) return 0;
     // the largest need over the paths the caller may force
-    return bl::gemm_workspace_bytes(M, N, K);
+    const int64_t g = bl::gemm_workspace_bytes(M, N, K), sk = bl::skinny_workspace_bytes(M, N, K);
+    return g > sk ? g : sk;
 }
 
 int bitlinear_forward_path(int64_t M, int64_t N, int64_t K, int layout)
@@ -243,7 +252,7 @@ int bitlinear_quantize_forward(const void *x, int dtype, int64_t M, int64_t K, i
     if (N == 0) return hip_status(bl::launch_quant_act(x, dtype, M, K, xq, scale, rowsum, stream));
     if (!packed || !gamma || !y) return BL_ERR_NULL;
     if (!al16(packed) || !al4(gamma) || !al4(y)) return BL_ERR_ALIGN;
-    const int64_t need = path == BL_PATH_MFMA ? bl::gemm_workspace_bytes(M, N, K) : 0;
+    const int64_t need = workspace_need(path, M, N, K);
     if (need > 0 && (!workspace || workspace_bytes < need)) return BL_ERR_WORKSPACE;
     if (need > 0 && !al16(workspace)) return BL_ERR_ALIGN;
 
@@ -258,7 +267,7 @@ int bitlinear_quantize_forward(const void *x, int dtype, int64_t M, int64_t K, i
     else if (path == BL_PATH_GEMV)
         e = bl::launch_gemv_pack2(xq, rowsum, M, packed, N, K, out, stream);
     else if (path == BL_PATH_SKINNY)
-        e = bl::launch_skinny_pack2(xq, rowsum, M, packed, N, K, out, stream);
+        e = bl::launch_skinny_pack2(xq, rowsum, M, packed, N, K, out, workspace, stream);
     else
         e = bl::launch_gemm_pack2(xq, rowsum, M, packed, N, K, out, workspace, stream);
     return hip_status(e);

@@ -646,6 +646,15 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const int32_t *__res
 
 }  // namespace
 
+hipError_t launch_splitk_finish(const int32_t *ws, const int32_t *rowsum, int64_t m, int64_t n,
+                                int splits, Out out, int64_t ldy, hipStream_t s)
+{
+    const int64_t total = m * n;
+    hipLaunchKernelGGL(splitk_finish_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                       s, ws, rowsum, m, n, splits, out, ldy);
+    return hipGetLastError();
+}
+
 // Kernel configuration of the GEMM for (M, N, K).
 struct GemmCfg { int wm, wn, splits; };
 
@@ -739,10 +748,7 @@ hipError_t launch_gemm_cfg(const int8_t *xq, const int32_t *rowsum, int64_t m,
                            ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
-    const int64_t total = m * n;
-    hipLaunchKernelGGL(splitk_finish_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                       s, ws, rowsum, m, n, splits, out, ldy);
-    return hipGetLastError();
+    return launch_splitk_finish(ws, rowsum, m, n, splits, out, ldy, s);
 }
 
 hipError_t launch_gemm_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,

@@ -74,9 +74,16 @@ hipError_t launch_gemv_pack3(const int8_t *xq, const int32_t *rowsum, int64_t m,
 // 2-bit layout, int8 matrix-core kernel.  ws: gemm_workspace_bytes(m, n, k)
 // bytes of scratch, any contents (one int32 partial tile per split of k).
 bool skinny_supported(int64_t m, int64_t n, int64_t k);
+// Skinny path: k splits of the shared-activation kernel (1: unsplit, 0: the
+// per-wave kernel instead) and the partial-sum workspace they need.
+int skinny_splits(int64_t m, int64_t n, int64_t k);
+int64_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_skinny_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
-                               const uint8_t *packed, int64_t n, int64_t k, Out out,
+                               const uint8_t *packed, int64_t n, int64_t k, Out out, void *ws,
                                hipStream_t s);
+// Sums `splits` int32 [M, N] slices of ws in split order, then the epilogue.
+hipError_t launch_splitk_finish(const int32_t *ws, const int32_t *rowsum, int64_t m, int64_t n,
+                                int splits, Out out, int64_t ldy, hipStream_t s);
 hipError_t launch_gemm_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
                              const uint8_t *packed, int64_t n, int64_t k, Out out, void *ws,
                              hipStream_t s);

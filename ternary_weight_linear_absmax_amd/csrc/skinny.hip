@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void skinny2_kernel(const int8_t *__restrict__
                                                       int64_t m, int64_t k,
                                                       const uint8_t *__restrict__ packed,
                                                       int64_t n, int64_t pitch, Out out,
-                                                      int64_t ldy)
+                                                      int64_t ldy, int32_t *__restrict__ part)
 {
     constexpr int MT = 16 * TG, BN = 64 * RB;
     constexpr int SLOT = MT * SK2_LDA;
@@ -272,7 +272,11 @@ __global__ __launch_bounds__(256) void skinny2_kernel(const int8_t *__restrict__
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, b = lane >> 4;
     const int64_t n0 = (int64_t)blockIdx.x * BN;
-    const int ns = (int)(k / SK_CHUNK);   // stages, >= 1
+    // split y of gridDim.y takes stages [s0, s1) of the k range (>= 1 each)
+    const int ns_all = (int)(k / SK_CHUNK);
+    const int s0 = (int)((int64_t)blockIdx.y * ns_all / gridDim.y);
+    const int s1 = (int)((int64_t)(blockIdx.y + 1) * ns_all / gridDim.y);
+    const int ns = s1 - s0;
 
     // activation pieces of this thread: piece p = tid + 256 i of the stage,
     // token p / 16, bytes 16 (p % 16) .. +15 (tokens past M clamped: they
@@ -284,7 +288,7 @@ __global__ __launch_bounds__(256) void skinny2_kernel(const int8_t *__restrict__
         const int p = tid + 256 * i;
         int64_t tok = p >> 4;
         tok = tok < m ? tok : m - 1;
-        asrc[i] = xq + tok * k + 16 * (p & 15);
+        asrc[i] = xq + tok * k + (int64_t)s0 * SK_CHUNK + 16 * (p & 15);
         adst[i] = (uint32_t)((p >> 4) * SK2_LDA + 16 * (p & 15));
     }
     // weight rows of this lane (clamped into the matrix)
@@ -293,7 +297,7 @@ __global__ __launch_bounds__(256) void skinny2_kernel(const int8_t *__restrict__
     for (int rb = 0; rb < RB; ++rb) {
         int64_t row = n0 + 16 * (wave * RB + rb) + r;
         row = row < n ? row : n - 1;
-        wsrc[rb] = packed + row * pitch + 16 * b;
+        wsrc[rb] = packed + row * pitch + (int64_t)s0 * (SK_CHUNK / 4) + 16 * b;
     }
 
     auto aload = [&](uint4 (&a)[TG], int st) __attribute__((always_inline)) {
@@ -377,25 +381,59 @@ __global__ __launch_bounds__(256) void skinny2_kernel(const int8_t *__restrict__
     });
 
     // Epilogue: lane (r, b) holds rows 16 (wave RB + rb) + 4 b + q of token
-    // 16 g + r.
+    // 16 g + r.  The block's [MT tokens][BN rows] tile is transposed through
+    // LDS (the ring is free after the last barrier) so that every thread then
+    // writes four consecutive rows of one token: stores are contiguous along
+    // the output rows.  Split k range: the raw code sums go to this split's
+    // slice of the partial buffer, the finish kernel adds the slices in order.
+    static_assert(MT * (BN + 4) * 4 <= SK2_NS * SLOT, "epilogue tile fits the ring");
+    int32_t *tile = (int32_t *)lds;   // [MT][BN + 4]
 #pragma unroll
-    for (int g = 0; g < TG; ++g) {
-        const int64_t tok = 16 * g + r;
-        if (tok >= m) continue;
-        const int32_t rs = rowsum[tok];
-        const float gs = out.acc ? 0.0f : out.gamma[0] / out.scale[tok];
+    for (int g = 0; g < TG; ++g)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t row = n0 + 16 * (wave * RB + rb) + 4 * b + q;
-                if (row >= n) continue;
-                const int32_t v = acc[rb][g][q] - rs;
-                if (out.acc)
-                    out.acc[tok * ldy + row] = v;
-                else
-                    out.y[tok * ldy + row] = (float)v * gs;
+            *(v4i *)(tile + (16 * g + r) * (BN + 4) + 16 * (wave * RB + rb) + 4 * b) = acc[rb][g];
+    __syncthreads();
+    // 16-byte stores where rows of four stay 16-byte aligned (the partial
+    // buffer always is)
+    const uintptr_t base = part ? 0 : out.acc ? (uintptr_t)out.acc : (uintptr_t)out.y;
+    const bool vec = (n % 4) == 0 && (part || ((ldy % 4) == 0 && (base & 15) == 0));
+    for (int e = tid; e < MT * (BN / 4); e += 256) {
+        const int tok = e / (BN / 4), c4 = 4 * (e % (BN / 4));
+        if (tok >= m) continue;
+        const int64_t row = n0 + c4;
+        if (row >= n) continue;
+        const v4i v = *(const v4i *)(tile + tok * (BN + 4) + c4);
+        if (part) {
+            int32_t *dst = part + ((int64_t)blockIdx.y * m + tok) * n + row;
+            if (vec && row + 3 < n) {
+                *(v4i *)dst = v;
+            } else {
+                for (int j = 0; j < 4 && row + j < n; ++j) dst[j] = v[j];
             }
+            continue;
+        }
+        const int32_t rs = rowsum[tok];
+        if (out.acc) {
+            int32_t *dst = out.acc + tok * ldy + row;
+            const v4i a = v - rs;
+            if (vec && row + 3 < n) *(v4i *)dst = a;
+            else
+                for (int j = 0; j < 4 && row + j < n; ++j) dst[j] = a[j];
+        } else {
+            const float gs = out.gamma[0] / out.scale[tok];
+            float *dst = out.y + tok * ldy + row;
+            float4 f;
+            f.x = (float)(v[0] - rs) * gs;
+            f.y = (float)(v[1] - rs) * gs;
+            f.z = (float)(v[2] - rs) * gs;
+            f.w = (float)(v[3] - rs) * gs;
+            if (vec && row + 3 < n) *(float4 *)dst = f;
+            else {
+                const float fa[4] = {f.x, f.y, f.z, f.w};
+                for (int j = 0; j < 4 && row + j < n; ++j) dst[j] = fa[j];
+            }
+        }
     }
 }
 
@@ -405,23 +443,51 @@ namespace {
 
 template <int TG>
 hipError_t launch_sk2(const int8_t *xq, const int32_t *rowsum, int64_t m, const uint8_t *packed,
-                      int64_t n, int64_t k, Out out, hipStream_t s)
+                      int64_t n, int64_t k, Out out, int splits, int32_t *part, hipStream_t s)
 {
-    hipLaunchKernelGGL((skinny2_kernel<TG, 1>), dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s,
-                       xq, rowsum, m, k, packed, n, pack2_pitch(k), out, (int64_t)n);
-    return hipGetLastError();
+    hipLaunchKernelGGL((skinny2_kernel<TG, 1>), dim3((unsigned)((n + 63) / 64), (unsigned)splits),
+                       dim3(256), 0, s, xq, rowsum, m, k, packed, n, pack2_pitch(k), out,
+                       (int64_t)n, splits > 1 ? part : (int32_t *)nullptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    return launch_splitk_finish(part, rowsum, m, n, splits, out, n, s);
 }
 
 }  // namespace
 
+int skinny_splits(int64_t m, int64_t n, int64_t k)
+{
+    if (m > 16 || k % SK_CHUNK != 0) return 0;   // 0: the per-wave kernel
+    // Measured on the 2B- and 70B-class shapes at M = 16: with >= 192 blocks of
+    // 64 rows the unsplit kernel is fastest; with 96..191 blocks and long rows
+    // (>= 32 stages of 256 k) splitting k up to about 512 blocks pays for the
+    // extra finish launch (70B-class K = 28672, N = 8192: 26.1 -> 22.3 us);
+    // smaller matrices run faster on the per-wave kernel.
+    const int64_t blocks = (n + 63) / 64, stages = k / SK_CHUNK;
+    if (blocks >= 192) return 1;
+    if (blocks < 96 || stages < 32) return 0;
+    int64_t sp = (512 + blocks - 1) / blocks;
+    if (sp > stages / 8) sp = stages / 8;
+    return (int)sp;
+}
+
+int64_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k)
+{
+    if (!skinny_supported(m, n, k)) return 0;
+    const int sp = skinny_splits(m, n, k);
+    return sp > 1 ? 4 * (int64_t)sp * m * n : 0;
+}
+
 hipError_t launch_skinny_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
-                               const uint8_t *packed, int64_t n, int64_t k, Out out,
+                               const uint8_t *packed, int64_t n, int64_t k, Out out, void *ws,
                                hipStream_t s)
 {
-    // up to 16 tokens on matrices whose 64-row blocks fill the CUs: the
-    // shared-activation kernel (measured faster there); otherwise the
-    // per-wave kernel, which splits k over the waves of a block
-    if (m <= 16 && (n + 63) / 64 >= 192) return launch_sk2<1>(xq, rowsum, m, packed, n, k, out, s);
+    // up to 16 tokens: the shared-activation kernel, its k range split over
+    // blocks when the matrix has too few 64-row blocks to keep enough bytes in
+    // flight; otherwise the per-wave kernel, which splits k over the waves of
+    // a block
+    const int sp = skinny_splits(m, n, k);
+    if (sp >= 1) return launch_sk2<1>(xq, rowsum, m, packed, n, k, out, sp, (int32_t *)ws, s);
     if (m <= 16) return launch_tg<1>(xq, rowsum, m, packed, n, k, out, s);
     if (m <= 32) return launch_tg<2>(xq, rowsum, m, packed, n, k, out, s);
     return launch_tg<4>(xq, rowsum, m, packed, n, k, out, s);

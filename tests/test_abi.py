@@ -38,6 +38,8 @@ def test_size_queries_match_the_layout_definitions(lib):
     assert bl.quantize_weights_workspace_bytes(28672, 8192) == 128 * 2048
     assert bl.quantize_weights_workspace_bytes(0, 64) == 0
     assert bl.forward_workspace_bytes(512, 8640, 3200) >= 0
+    # skinny path with its k range split four ways: 4 * 4 * M * N bytes
+    assert bl.forward_workspace_bytes(16, 8192, 28672) == 4 * 4 * 16 * 8192
     # a split-k shape: one int32 [M, N] partial tile per split
     ws = bl.forward_workspace_bytes(64, 128, 4096)
     assert ws > 0 and ws % (4 * 64 * 128) == 0

@@ -80,6 +80,9 @@ def test_ragged_shapes_bf16(layout, m, n, k):
     # up to 16 tokens on at least 192 blocks of 64 rows: activations shared
     # through LDS, ragged last row block and token slots
     (13, 12300, 512), (16, 13824, 2560), (1, 12289, 256), (5, 12352, 1024),
+    # 96..191 row blocks with long rows: the k range split over blocks (4 and 6
+    # splits), partial sums added by the finish kernel; ragged and aligned N
+    (13, 6150, 8192), (16, 6144, 12288),
 ])
 def test_skinny_shapes(m, n, k):
     """Weight-streaming matrix-core path: ragged N and M, every row-block /
@@ -88,6 +91,24 @@ def test_skinny_shapes(m, n, k):
     run_case(w, x, bl.BL_PACK2, (bl.BL_PATH_SKINNY, bl.BL_PATH_MFMA))
     if m <= 16:
         assert bl.forward_path(m, n, k) == (bl.BL_PATH_GEMV if m <= 2 else bl.BL_PATH_SKINNY)
+
+
+@pytest.mark.parametrize("n", [13824, 6144])
+def test_skinny_output_not_16_byte_aligned(n):
+    """The skinny epilogue stores rows of four as 16-byte vectors only where
+    the output stays aligned; an output offset by one float takes the
+    element-wise stores (unsplit and split k range)."""
+    m, k = 9, 8192
+    w, x = inputs.random_case(20_500 + n, m, n, k, bf16=True)
+    t, g, _ = oracle_weights(w, bl.BL_PACK2)
+    q_ref, s_ref, r_ref = oracle.quantize_act(x)
+    acc_ref = oracle.matmul_i32(q_ref, t)
+    packed, gamma = bl.quantize_weights(dev(w))
+    xq, scale, rowsum = bl.quantize_act(dev(x))
+    buf = torch.empty(m * n + 1, dtype=torch.float32, device="cuda")
+    y = buf[1:].view(m, n)
+    bl.forward(xq, scale, rowsum, packed, gamma, n, k, y=y, path=bl.BL_PATH_SKINNY)
+    assert_y_close(host(y), oracle.rescale(acc_ref, s_ref, g), acc_ref)
 
 
 @pytest.mark.parametrize("n,k", [(129, 16), (77, 1040), (1000, 8000), (33, 80), (2049, 5120)])
