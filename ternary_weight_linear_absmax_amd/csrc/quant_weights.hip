@@ -167,17 +167,41 @@ __global__ __launch_bounds__(GAMMA_THREADS) void gamma_partial_kernel(
     __syncthreads();
 
     GammaLane L;
+    // Block b streams the contiguous vectors [b nvec / G, (b + 1) nvec / G),
+    // four per thread and step (16 KB per block and step), the next step's
+    // loads issued before this step's arithmetic.  Indices past the range load
+    // a clamped (valid) address and are replaced by zero vectors, which add
+    // nothing.
     const uint4 *v = (const uint4 *)w;
-    const int64_t stride = (int64_t)gridDim.x * GAMMA_THREADS;
-    int64_t i = (int64_t)blockIdx.x * GAMMA_THREADS + tid;
-    for (; i + 3 * stride < nvec; i += 4 * stride) {
-        const uint4 a = v[i], b = v[i + stride], c = v[i + 2 * stride], d = v[i + 3 * stride];
-        gamma_vector<DT>(L, a, width, bins);
-        gamma_vector<DT>(L, b, width, bins);
-        gamma_vector<DT>(L, c, width, bins);
-        gamma_vector<DT>(L, d, width, bins);
+    const int64_t vbeg = (int64_t)blockIdx.x * nvec / gridDim.x;
+    const int64_t vend = (int64_t)(blockIdx.x + 1) * nvec / gridDim.x;
+    constexpr int64_t stride = GAMMA_THREADS;
+    constexpr int U = 4;
+    auto fetch = [&](uint4 (&buf)[U], int64_t base) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // the load is unconditional and its value always used (masked),
+            // so no branch separates it from the others
+            const int64_t idx = base + u * stride;
+            const uint4 q = v[idx < vend ? idx : vend - 1];
+            const uint32_t msk = idx < vend ? 0xffffffffu : 0u;
+            buf[u] = make_uint4(q.x & msk, q.y & msk, q.z & msk, q.w & msk);
+        }
+    };
+    int64_t i = vbeg + tid;
+    if (vend > vbeg) {
+        uint4 cur[U];
+        fetch(cur, i);
+        for (; i < vend; i += U * stride) {
+            uint4 nxt[U];
+            fetch(nxt, i + U * stride);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < U; ++u) gamma_vector<DT>(L, cur[u], width, bins);
+#pragma unroll
+            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+        }
     }
-    for (; i < nvec; i += stride) gamma_vector<DT>(L, v[i], width, bins);
     if (blockIdx.x == 0 && tid == 0) {
         for (int64_t t = nvec * E; t < count; ++t) {
             const float f = load_w(w, DT, t);
@@ -216,32 +240,48 @@ __global__ __launch_bounds__(GAMMA_THREADS) void gamma_partial_kernel(
 }
 
 // Adds the blocks' limbs, normalises the carries and rounds B * 2^-150 to the
-// nearest double (ties to even); gamma = float(sum / (N*K)).
-__global__ __launch_bounds__(GAMMA_THREADS) void gamma_finish_kernel(const ull *__restrict__ ws,
-                                                                     int nblocks, int64_t n,
-                                                                     int64_t k,
-                                                                     float *__restrict__ gamma)
+// nearest double (ties to even); gamma = float(sum / (N*K)).  1024 threads:
+// thread t adds entry t % 16 of blocks t / 16, t / 16 + 64, ... (coalesced,
+// eight loads in flight), then two levels of LDS sums.
+constexpr int GAMMA_FIN_THREADS = 1024;
+constexpr int GAMMA_FIN_J = GAMMA_FIN_THREADS / GAMMA_SLOT;   // partials per entry
+
+__global__ __launch_bounds__(GAMMA_FIN_THREADS) void gamma_finish_kernel(
+    const ull *__restrict__ ws, int nblocks, int64_t n, int64_t k, float *__restrict__ gamma)
 {
-    __shared__ ull part[GAMMA_SLOT][GAMMA_THREADS / GAMMA_SLOT];
+    __shared__ ull part[GAMMA_SLOT][GAMMA_FIN_J + 1];
+    __shared__ ull part2[GAMMA_SLOT][8];
     const int tid = threadIdx.x, e = tid % GAMMA_SLOT, j = tid / GAMMA_SLOT;
     ull s = 0;
-    if (e <= GAMMA_FLAG)
-        for (int b = j; b < nblocks; b += GAMMA_THREADS / GAMMA_SLOT) {
+    if (e <= GAMMA_FLAG) {
+#pragma unroll 8
+        for (int b = j; b < nblocks; b += GAMMA_FIN_J) {
             const ull x = ws[(int64_t)b * GAMMA_SLOT + e];
             s = e == GAMMA_FLAG ? (s | x) : s + x;
         }
+    }
     part[e][j] = s;
+    __syncthreads();
+    if (tid < GAMMA_SLOT * 8) {
+        const int e2 = tid / 8, q = tid % 8;
+        ull t = 0;
+        for (int r = 0; r < GAMMA_FIN_J / 8; ++r) {
+            const ull x = part[e2][8 * q + r];
+            t = e2 == GAMMA_FLAG ? (t | x) : t + x;
+        }
+        part2[e2][q] = t;
+    }
     __syncthreads();
     if (tid != 0) return;
     uint32_t d[GAMMA_LIMBS + 3] = {};
     ull carry = 0, flags = 0;
     for (int l = 0; l < GAMMA_LIMBS; ++l) {
         ull t = carry;
-        for (int q = 0; q < GAMMA_THREADS / GAMMA_SLOT; ++q) t += part[l][q];
+        for (int q = 0; q < 8; ++q) t += part2[l][q];
         d[l] = (uint32_t)t;
         carry = t >> 32;
     }
-    for (int q = 0; q < GAMMA_THREADS / GAMMA_SLOT; ++q) flags |= part[GAMMA_FLAG][q];
+    for (int q = 0; q < 8; ++q) flags |= part2[GAMMA_FLAG][q];
     if (flags & 2u) {
         gamma[0] = __uint_as_float(0x7fc00000u);
         return;
@@ -315,7 +355,10 @@ __global__ __launch_bounds__(256) void pack2_kernel(const void *__restrict__ w, 
                                                     uint32_t *__restrict__ packed)
 {
     const int64_t words_per_row = pack2_pitch(k) / 4;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // blocks walk W from its end: the tail that the gamma pass read last is
+    // still in the last-level cache when the first blocks run
+    const int64_t idx =
+        (int64_t)(gridDim.x - 1 - blockIdx.x) * blockDim.x + threadIdx.x;
     if (idx >= n * words_per_row) return;
     const int64_t row = idx / words_per_row, g = idx % words_per_row;
     const float gamma = gamma_p[0];
@@ -357,7 +400,10 @@ __global__ __launch_bounds__(256) void pack3_kernel(const void *__restrict__ w, 
                                                     uint32_t *__restrict__ packed)
 {
     const int64_t words_per_row = pack3_pitch(k) / 4;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // blocks walk W from its end: the tail that the gamma pass read last is
+    // still in the last-level cache when the first blocks run
+    const int64_t idx =
+        (int64_t)(gridDim.x - 1 - blockIdx.x) * blockDim.x + threadIdx.x;
     if (idx >= n * words_per_row) return;
     const int64_t row = idx / words_per_row, g = idx % words_per_row;
     const float gamma = gamma_p[0];
@@ -467,8 +513,9 @@ hipError_t launch_gamma(const void *w, int dtype, int64_t n, int64_t k, void *wo
     const int64_t nvec = count / per_vec;
     const int blocks = gamma_blocks(count);
     // the most elements one lane adds to its accumulators, as a power of two
-    const int64_t lanes = (int64_t)blocks * GAMMA_THREADS;
-    const int64_t per_lane = ((nvec + lanes - 1) / lanes) * per_vec;
+    // (a block's range holds at most ceil(nvec / blocks) vectors)
+    const int64_t per_block = (nvec + blocks - 1) / blocks;
+    const int64_t per_lane = ((per_block + GAMMA_THREADS - 1) / GAMMA_THREADS) * per_vec;
     int p = 0;
     while (((int64_t)1 << p) < per_lane) ++p;
     const int width = 29 + (dtype == DT_BF16 ? 16 : 0) - p;
@@ -482,8 +529,8 @@ hipError_t launch_gamma(const void *w, int dtype, int64_t n, int64_t k, void *wo
                            nvec, count, width, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gamma_finish_kernel, dim3(1), dim3(GAMMA_THREADS), 0, s, (const ull *)ws,
-                       blocks, n, k, gamma);
+    hipLaunchKernelGGL(gamma_finish_kernel, dim3(1), dim3(GAMMA_FIN_THREADS), 0, s,
+                       (const ull *)ws, blocks, n, k, gamma);
     return hipGetLastError();
 }
 
