@@ -44,6 +44,8 @@ def _grad(rng, m, n, bf16):
     (1, 300, 2560, True), (5, 130, 320, False), (64, 1000, 512, True), (3, 77, 100, False),
     (2, 77, 100, True), (130, 257, 200, False), (65, 64, 129, True), (1, 1, 1, False),
     (7, 4099, 64, False),
+    # long rows of grad_x (171 k tiles), ragged M and K
+    (130, 64, 21800, True),
 ])
 def test_backward_input_shapes(m, n, k, bf16):
     rng = np.random.default_rng(80_000 + m + n + k)
