@@ -248,9 +248,10 @@ bool skinny_supported(int64_t m, int64_t n, int64_t k)
 // into registers, several stages ahead, and reads every token's activation
 // fragments from LDS.  Same k mapping as above: lane (r, b), word u of its 16
 // packed bytes <-> activation bytes 64 b + 16 u .. +15 of the stage.
-// (Splitting the k range over blocks, with device-scope atomics into a
-// workspace and the last block of a tile finishing, measured several times
-// slower than not splitting: the atomics dominate.)
+// gridDim.y > 1 splits the stages over blocks: each split stores its raw code
+// sums into its own slice of a partial buffer, which a finish kernel adds in
+// split order (device-scope atomics with a last-block finish instead measured
+// several times slower: the atomics dominate).
 namespace {
 
 constexpr int SK2_LDA = 256 + 16;   // LDS row of one token's stage (bytes)
