@@ -105,9 +105,10 @@ int64_t bitlinear_quantize_weights_workspace_bytes(int64_t N, int64_t K);
 
 /* Workspace that bitlinear_forward / bitlinear_matmul_i32 need for this shape
  * on any path (0 when none; then workspace may be NULL).  A non-empty
- * workspace is scratch for the int32 partial sums of the matrix-core path
- * when it splits the k range (one [M, N] tile per split): it needs no initial
- * contents, and calls that share one workspace must not overlap. */
+ * workspace is scratch for the int32 partial sums of the GEMM path, or of the
+ * skinny path (M <= 16), when it splits the k range (one [M, N] int32 slice
+ * per split, added in split order): it needs no initial contents, and calls
+ * that share one workspace must not overlap. */
 int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int layout);
 
 /* Kernel path that BL_PATH_AUTO selects for this shape (a bl_path value). */
