@@ -1,8 +1,9 @@
 """The hot path captured in a HIP graph: every replay must equal the eager
 result on the same inputs, also with other eager work and fresh inputs in
 between (the decode benchmark times graph replays).  Covers the vector path,
-the weight-streaming path and the tiled GEMM with its split-K workspace
-(cleared by a kernel, so the graph holds no memset node)."""
+the weight-streaming path (also with its k range split over blocks) and the
+tiled GEMM with its split-K workspace (partial sums stored per split and added
+by a finish kernel: nothing is cleared, so the graph holds no memset node)."""
 import numpy as np
 import pytest
 import torch
@@ -19,6 +20,7 @@ CASES = [  # (m, n, k, path); the first case goes through bitlinear_quantize_for
     (8, 1000, 512, bl.BL_PATH_SKINNY),
     (64, 128, 4096, bl.BL_PATH_MFMA),     # few tiles: k range split, workspace used
     (40, 700, 384, bl.BL_PATH_MFMA),
+    (13, 6150, 8192, bl.BL_PATH_SKINNY),  # 97 row blocks: k split four ways, workspace used
 ]
 
 
@@ -36,6 +38,7 @@ def test_graph_replays_match_eager():
     # the split-K case needs the workspace: the eager pass allocates the
     # binding's shared workspace before capture
     assert bl.forward_workspace_bytes(64, 128, 4096) > 0
+    assert bl.forward_workspace_bytes(13, 6150, 8192) > 0
 
     lib = bl.load()
 
