@@ -133,8 +133,8 @@ def decode_workload(layers):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1 "
-                          "(multi-GPU sharding is a design note, not built)"}))
+        print(json.dumps({"error": "this benchmark measures one GPU only; run with --gpus 1 "
+                          "(sharding over several GPUs is described, not implemented)"}))
         sys.exit(2)
 
     import torch
