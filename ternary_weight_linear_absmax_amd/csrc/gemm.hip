@@ -627,9 +627,7 @@ __global__ __launch_bounds__(512) void gemm3_kernel(const int8_t *__restrict__ x
     }
 }
 
-// Split-K epilogue: y (or acc) from the summed codes in the workspace, which
-// is cleared again for the next call.
-// Sum of the splits' partial tiles, slice by slice in split order (exact
+// Split-K epilogue: sum of the splits' partial tiles, slice by slice in split order (exact
 // int32), then the epilogue.
 __global__ __launch_bounds__(256) void splitk_finish_kernel(const int32_t *__restrict__ ws,
                                                             const int32_t *__restrict__ rowsum,
