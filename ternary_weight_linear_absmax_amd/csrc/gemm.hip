@@ -191,6 +191,75 @@ __device__ inline int64_t tile_of_block(int64_t b, int64_t q)
     return (b % NXCD) * q + b / NXCD;
 }
 
+// ---- epilogue through LDS ---------------------------------------------------------
+// The block's accumulators are written, with the epilogue applied, into a
+// [BM][BN + 4] int32 tile in LDS (y values as float bits), and then all the
+// block's threads store the tile row by row with 16-byte stores.  The MFMA
+// register layout would otherwise give 4-byte stores of 32 consecutive
+// columns and two rows per instruction, a quarter of the store width, all
+// issued at the end of every block; the row operands (row sum, gamma / s)
+// are read into LDS before the k loop instead of after it.
+enum : int { EP_PARTIAL = 0, EP_ACC = 1, EP_Y = 2 };
+
+template <int BM, int BN>
+constexpr int ep_tile_bytes() { return BM * (BN + 4) * 4; }
+
+// Row operands of rows m0 .. m0 + BM - 1 (clamped), by threads 0 .. BM - 1.
+template <int BM>
+__device__ inline void ep_rows(int tid, int64_t m0, int64_t m, const int32_t *rowsum,
+                               const Out &out, int mode, int32_t *ep_rs, float *ep_gs)
+{
+    if (tid >= BM || mode == EP_PARTIAL) return;
+    int64_t gm = m0 + tid;
+    gm = gm < m ? gm : m - 1;
+    ep_rs[tid] = rowsum[gm];
+    ep_gs[tid] = mode == EP_Y ? out.gamma[0] / out.scale[gm] : 0.0f;
+}
+
+// Lane (l32, h) of math wave (wm, wn), register r of acc[a][s]: row
+// 32 WM wm + 32 a + 8 (r / 4) + 4 h + r % 4, column 32 WN wn + 32 s + l32.
+template <int WM, int WN>
+__device__ inline void ep_put(int32_t *tile, const v16i (&acc)[WM][WN], int wm, int wn, int h,
+                              int l32, const int32_t *ep_rs, const float *ep_gs, int mode)
+{
+    constexpr int LT = 64 * WN + 4;
+#pragma unroll
+    for (int a = 0; a < WM; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = wm * 32 * WM + 32 * a + 8 * (r / 4) + 4 * h + (r % 4);
+            const int32_t rs = mode == EP_PARTIAL ? 0 : ep_rs[row];
+            const float gs = mode == EP_Y ? ep_gs[row] : 0.0f;
+#pragma unroll
+            for (int s = 0; s < WN; ++s) {
+                const int32_t v = acc[a][s][r] - rs;
+                tile[row * LT + wn * 32 * WN + 32 * s + l32] =
+                    mode == EP_Y ? __float_as_int((float)v * gs) : v;
+            }
+        }
+}
+
+// Stores the tile to dst[(row) * ld + col] for rows m0.. < m, columns n0.. < n.
+template <int BM, int BN>
+__device__ inline void ep_store(const int32_t *tile, int tid, int nthreads, int64_t m0,
+                                int64_t n0, int64_t m, int64_t n, int32_t *dst, int64_t ld)
+{
+    constexpr int LT = BN + 4, C4 = BN / 4;
+    const bool vec = (ld % 4) == 0 && ((uintptr_t)dst & 15) == 0;
+    for (int e = tid; e < BM * C4; e += nthreads) {
+        const int row = e / C4, c = 4 * (e % C4);
+        const int64_t gm = m0 + row, gn = n0 + c;
+        if (gm >= m || gn >= n) continue;
+        const v4i v = *(const v4i *)(tile + row * LT + c);
+        int32_t *d = dst + gm * ld + gn;
+        if (vec && gn + 3 < n) {
+            *(v4i *)d = v;
+        } else {
+            for (int j = 0; j < 4 && gn + j < n; ++j) d[j] = v[j];
+        }
+    }
+}
+
 template <int WM, int WN, bool AL, int NA = GEMM_NA, int NB = GEMM_NB>
 __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ xq,
                                                     const int32_t *__restrict__ rowsum,
@@ -201,7 +270,11 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
                                                     Out out, int64_t ldy, int32_t *__restrict__ ws)
 {
     constexpr int BM = 64 * WM, BN = 64 * WN;
+    // the LDS epilogue needs the A double buffer to hold the output tile
+    constexpr bool LDS_EP = ep_tile_bytes<BM, BN>() <= 2 * BM * LDA;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM * LDA];
+    __shared__ int32_t ep_rs[BM];
+    __shared__ float ep_gs[BM];
     const int64_t t = tile_of_block(blockIdx.x, per_xcd);
     if (t >= tiles * splits) return;
     const int64_t tile = t / splits;
@@ -216,6 +289,8 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
     const int kt0 = split * stages_per;
     const int kt1 = kt0 + stages_per < nk_total ? kt0 + stages_per : nk_total;
     const int nk = kt1 - kt0;
+    const int ep_mode = splits > 1 ? EP_PARTIAL : out.acc ? EP_ACC : EP_Y;
+    if (LDS_EP) ep_rows<BM>(tid, m0, m, rowsum, out, ep_mode, ep_rs, ep_gs);
 
     v16i acc[WM][WN];
 #pragma unroll
@@ -353,8 +428,20 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
         mma(af, bw);
     }
 
-    // Epilogue.  Per-row operands are loaded for all of this lane's rows first
-    // (clamped indices, unconditional), then the stores are predicated.
+    if constexpr (LDS_EP) {
+        __syncthreads();   // every wave is done with the A buffers
+        int32_t *tile_lds = (int32_t *)&lds[0][0];
+        ep_put<WM, WN>(tile_lds, acc, wm, wn, h, l32, ep_rs, ep_gs, ep_mode);
+        __syncthreads();
+        int32_t *dst = ep_mode == EP_PARTIAL ? ws + (int64_t)split * m * n
+                       : ep_mode == EP_ACC   ? out.acc
+                                             : (int32_t *)out.y;
+        ep_store<BM, BN>(tile_lds, tid, 256, m0, n0, m, n, dst, ep_mode == EP_PARTIAL ? n : ldy);
+        return;
+    }
+    // Epilogue for tiles larger than the A buffers.  Per-row operands are
+    // loaded for all of this lane's rows first (clamped indices,
+    // unconditional), then the stores are predicated.
     if (splits > 1) {
 #pragma unroll
         for (int a = 0; a < WM; ++a)
@@ -427,6 +514,9 @@ __global__ __launch_bounds__(512) void gemm3_kernel(const int8_t *__restrict__ x
     constexpr int PA = BM / 32;                                   // activation pieces / producer
     constexpr int PB = (BN * 2 + 255) / 256;                      // weight pieces / producer
     __shared__ __attribute__((aligned(16))) uint8_t lds[G3_NS * SS];
+    __shared__ int32_t ep_rs[BM];
+    __shared__ float ep_gs[BM];
+    static_assert(ep_tile_bytes<BM, BN>() <= G3_NS * SS, "the output tile fits the LDS ring");
     const int64_t t = tile_of_block(blockIdx.x, per_xcd);
     if (t >= tiles * splits) return;
     const int64_t tile = t / splits;
@@ -443,9 +533,12 @@ __global__ __launch_bounds__(512) void gemm3_kernel(const int8_t *__restrict__ x
     if (nk <= 0) return;
     constexpr int U3 = G3_NS * R / gcd_int(G3_NS, R);
     constexpr int U = U3 % 2 == 0 ? U3 : 2 * U3;   // ring slots and fragment parity fixed per J
+    const int ep_mode = splits > 1 ? EP_PARTIAL : out.acc ? EP_ACC : EP_Y;
 
     if (producer) {
         const int pt = threadIdx.x - 256;
+        // row operands of the epilogue, visible after the first barrier
+        ep_rows<BM>(pt, m0, m, rowsum, out, ep_mode, ep_rs, ep_gs);
         // per-thread sources, fixed for the loop (rows clamped into the matrices)
         uint32_t aoff[PA], alds[PA];
         int acol[PA];
@@ -522,9 +615,7 @@ __global__ __launch_bounds__(512) void gemm3_kernel(const int8_t *__restrict__ x
         static_for<U - 1>([&](auto jc) __attribute__((always_inline)) {
             if (nu + jc < nk) iter(jc, nu + jc);
         });
-        return;
-    }
-
+    } else {
     // ---- math waves ----
     const int wm = wave & 1, wn = wave >> 1;
     const int h = lane >> 5, l32 = lane & 31;
@@ -586,45 +677,17 @@ __global__ __launch_bounds__(512) void gemm3_kernel(const int8_t *__restrict__ x
         if (nu + jc < nk) iter(jc, nu + jc);
     });
 
-    // Epilogue.
-    if (splits > 1) {
-#pragma unroll
-        for (int a = 0; a < WM; ++a)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t gm = m0 + wm * 32 * WM + 32 * a + 8 * (r / 4) + 4 * h + (r % 4);
-#pragma unroll
-                for (int s = 0; s < WN; ++s)
-                    if (gm < m && nrow[s] < n) ws[((int64_t)split * m + gm) * n + nrow[s]] = acc[a][s][r];
-            }
-        return;
+    // Epilogue: the accumulators into the output tile in the ring (every
+    // wave is past its last ring access after the final barrier of the loop)
+    ep_put<WM, WN>((int32_t *)lds, acc, wm, wn, h, l32, ep_rs, ep_gs, ep_mode);
     }
-    const float gamma = out.acc ? 0.0f : out.gamma[0];
-#pragma unroll
-    for (int a = 0; a < WM; ++a) {
-        int32_t rs[16];
-        float gs[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            int64_t gm = m0 + wm * 32 * WM + 32 * a + 8 * (r / 4) + 4 * h + (r % 4);
-            gm = gm < m ? gm : m - 1;
-            rs[r] = rowsum[gm];
-            gs[r] = out.acc ? 0.0f : gamma / out.scale[gm];
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t gm = m0 + wm * 32 * WM + 32 * a + 8 * (r / 4) + 4 * h + (r % 4);
-#pragma unroll
-            for (int s = 0; s < WN; ++s) {
-                if (gm >= m || nrow[s] >= n) continue;
-                const int32_t v = acc[a][s][r] - rs[r];
-                if (out.acc)
-                    out.acc[gm * ldy + nrow[s]] = v;
-                else
-                    out.y[gm * ldy + nrow[s]] = (float)v * gs[r];
-            }
-        }
-    }
+    // all waves store the tile
+    __syncthreads();
+    int32_t *dst = ep_mode == EP_PARTIAL ? ws + (int64_t)split * m * n
+                   : ep_mode == EP_ACC   ? out.acc
+                                         : (int32_t *)out.y;
+    ep_store<BM, BN>((const int32_t *)lds, threadIdx.x, 512, m0, n0, m, n, dst,
+                     ep_mode == EP_PARTIAL ? n : ldy);
 }
 
 // Split-K epilogue: sum of the splits' partial tiles, slice by slice in split order (exact
@@ -642,12 +705,48 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const int32_t *__res
     store_out(out, ldy, gm, gn, v, rowsum[gm]);
 }
 
+// Same sums, four consecutive columns of one row per thread (N a multiple of
+// 4, so the slices and the output rows stay 16-byte aligned; vec: the
+// output too): 16-byte loads and stores, one gamma / s per four outputs.
+__global__ __launch_bounds__(256) void splitk_finish4_kernel(const int32_t *__restrict__ ws,
+                                                             const int32_t *__restrict__ rowsum,
+                                                             int64_t m, int64_t n, int splits,
+                                                             Out out, int64_t ldy, bool vec)
+{
+    const int64_t e = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+    if (e >= m * n) return;
+    const int64_t gm = e / n, gn = e % n;
+    v4i v = {0, 0, 0, 0};
+    for (int sp = 0; sp < splits; ++sp) v += *(const v4i *)(ws + sp * m * n + e);
+    const v4i a = v - rowsum[gm];
+    if (out.acc) {
+        int32_t *d = out.acc + gm * ldy + gn;
+        if (vec) *(v4i *)d = a;
+        else
+            for (int j = 0; j < 4; ++j) d[j] = a[j];
+    } else {
+        const float gs = out.gamma[0] / out.scale[gm];
+        float *d = out.y + gm * ldy + gn;
+        const float f[4] = {(float)a[0] * gs, (float)a[1] * gs, (float)a[2] * gs, (float)a[3] * gs};
+        if (vec) *(float4 *)d = make_float4(f[0], f[1], f[2], f[3]);
+        else
+            for (int j = 0; j < 4; ++j) d[j] = f[j];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_splitk_finish(const int32_t *ws, const int32_t *rowsum, int64_t m, int64_t n,
                                 int splits, Out out, int64_t ldy, hipStream_t s)
 {
     const int64_t total = m * n;
+    if (n % 4 == 0 && ((uintptr_t)ws & 15) == 0) {
+        const uintptr_t base = out.acc ? (uintptr_t)out.acc : (uintptr_t)out.y;
+        const bool vec = (ldy % 4) == 0 && (base & 15) == 0;
+        hipLaunchKernelGGL(splitk_finish4_kernel, dim3((unsigned)((total / 4 + 255) / 256)),
+                           dim3(256), 0, s, ws, rowsum, m, n, splits, out, ldy, vec);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(splitk_finish_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
                        s, ws, rowsum, m, n, splits, out, ldy);
     return hipGetLastError();
