@@ -428,20 +428,23 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
         mma(af, bw);
     }
 
+    // LDS epilogue where the tile fits the A buffers (split partial tiles of
+    // these small blocks are stored directly: measured faster than the extra
+    // barrier and LDS round trip)
     if constexpr (LDS_EP) {
-        __syncthreads();   // every wave is done with the A buffers
-        int32_t *tile_lds = (int32_t *)&lds[0][0];
-        ep_put<WM, WN>(tile_lds, acc, wm, wn, h, l32, ep_rs, ep_gs, ep_mode);
-        __syncthreads();
-        int32_t *dst = ep_mode == EP_PARTIAL ? ws + (int64_t)split * m * n
-                       : ep_mode == EP_ACC   ? out.acc
-                                             : (int32_t *)out.y;
-        ep_store<BM, BN>(tile_lds, tid, 256, m0, n0, m, n, dst, ep_mode == EP_PARTIAL ? n : ldy);
-        return;
+        if (ep_mode != EP_PARTIAL) {
+            __syncthreads();   // every wave is done with the A buffers
+            int32_t *tile_lds = (int32_t *)&lds[0][0];
+            ep_put<WM, WN>(tile_lds, acc, wm, wn, h, l32, ep_rs, ep_gs, ep_mode);
+            __syncthreads();
+            int32_t *dst = ep_mode == EP_ACC ? out.acc : (int32_t *)out.y;
+            ep_store<BM, BN>(tile_lds, tid, 256, m0, n0, m, n, dst, ldy);
+            return;
+        }
     }
-    // Epilogue for tiles larger than the A buffers.  Per-row operands are
-    // loaded for all of this lane's rows first (clamped indices,
-    // unconditional), then the stores are predicated.
+    // Direct epilogue (split partial tiles, and tiles larger than the A
+    // buffers).  Per-row operands are loaded for all of this lane's rows
+    // first (clamped indices, unconditional), then the stores are predicated.
     if (splits > 1) {
 #pragma unroll
         for (int a = 0; a < WM; ++a)
