@@ -290,7 +290,6 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
     const int kt1 = kt0 + stages_per < nk_total ? kt0 + stages_per : nk_total;
     const int nk = kt1 - kt0;
     const int ep_mode = splits > 1 ? EP_PARTIAL : out.acc ? EP_ACC : EP_Y;
-    if (LDS_EP) ep_rows<BM>(tid, m0, m, rowsum, out, ep_mode, ep_rs, ep_gs);
 
     v16i acc[WM][WN];
 #pragma unroll
@@ -383,6 +382,8 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
         st_a<BM>(lds[1], areg[1], tid);
 #pragma unroll
         for (int j = 0; j < NA; ++j) ld_a<BM>(areg[j], abase, aoff, 2 + j, nfull);
+        // row operands of the epilogue, read while the stage loads are in flight
+        if (LDS_EP) ep_rows<BM>(tid, m0, m, rowsum, out, ep_mode, ep_rs, ep_gs);
         __syncthreads();
         read_frags(af[0], lds[0]);
         __syncthreads();   // buffer 0 is rewritten in stage 0
@@ -411,6 +412,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
             if (nu + jc < nfull) stage(jc, nu + jc);
         });
     }
+    if (LDS_EP && nfull == 0) ep_rows<BM>(tid, m0, m, rowsum, out, ep_mode, ep_rs, ep_gs);
     // Bounds-checked stages: the partial last stage, or all stages when K is
     // not a multiple of 16.  Loads are masked per piece; not pipelined.
     for (int kt = nfull; kt < nk; ++kt) {
@@ -540,8 +542,6 @@ __global__ __launch_bounds__(512) void gemm3_kernel(const int8_t *__restrict__ x
 
     if (producer) {
         const int pt = threadIdx.x - 256;
-        // row operands of the epilogue, visible after the first barrier
-        ep_rows<BM>(pt, m0, m, rowsum, out, ep_mode, ep_rs, ep_gs);
         // per-thread sources, fixed for the loop (rows clamped into the matrices)
         uint32_t aoff[PA], alds[PA];
         int acol[PA];
@@ -601,6 +601,9 @@ __global__ __launch_bounds__(512) void gemm3_kernel(const int8_t *__restrict__ x
             gload(a1, b1, 1);
 #pragma unroll
             for (int r = 0; r < R; ++r) gload(ra[(2 + r) % R], rb[(2 + r) % R], 2 + r);
+            // row operands of the epilogue (visible after the first barrier),
+            // read while the stage loads are in flight
+            ep_rows<BM>(pt, m0, m, rowsum, out, ep_mode, ep_rs, ep_gs);
             lstore(a0, b0, 0);
             if (nk > 1) lstore(a1, b1, 1);
         }
