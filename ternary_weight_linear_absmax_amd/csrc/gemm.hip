@@ -35,6 +35,10 @@
 // atomics); a second kernel adds the S partial sums in slice order and
 // applies the epilogue.  Integer addition makes the result exact; the
 // workspace needs no initial contents.
+//
+// Outputs leave through LDS: the finished tile is written there with the
+// epilogue applied and stored row by row with 16-byte stores (see the
+// epilogue helpers below).
 #include <type_traits>
 #include <utility>
 
@@ -632,9 +636,6 @@ __global__ __launch_bounds__(512) void gemm3_kernel(const int8_t *__restrict__ x
         for (int s = 0; s < WN; ++s)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][s][r] = 0;
-    int64_t nrow[WN];
-#pragma unroll
-    for (int s = 0; s < WN; ++s) nrow[s] = n0 + wn * 32 * WN + 32 * s + l32;
 
     struct Frag { v4i a[4][WM]; uint4 b[WN]; };
     auto read_frag = [&](Frag &f, int st) __attribute__((always_inline)) {
