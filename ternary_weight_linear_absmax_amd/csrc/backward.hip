@@ -39,22 +39,31 @@ __device__ inline uint32_t bf16_pair(__bf16 a, __bf16 b)
     return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(256) void backward_mfma_kernel(const void *__restrict__ grad_y,
+template <int DT, bool VEC, int G>
+__global__ __launch_bounds__(256 * G) void backward_mfma_kernel(const void *__restrict__ grad_y,
                                                             int64_t m, int64_t n,
                                                             const uint8_t *__restrict__ packed,
                                                             int64_t pitch, int64_t k,
                                                             const float *__restrict__ gamma_p,
                                                             float *__restrict__ grad_x)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t as[2][3][BM2 * LDAB];
-    __shared__ __attribute__((aligned(16))) uint8_t bs[2][BK2 * LDAB];
-    __shared__ __attribute__((aligned(16))) uint32_t traw[BN2][BK2 / 16];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // G groups of four waves share the block's tile; group g takes the
+    // n stages g, g + G, ... with its own LDS buffers, and the groups' sums
+    // are added at the end (G = 2 for matrices with few tiles: half the
+    // serial chain of stages per block)
+    __shared__ __attribute__((aligned(16))) uint8_t as_all[G][2][3][BM2 * LDAB];
+    __shared__ __attribute__((aligned(16))) uint8_t bs_all[G][2][BK2 * LDAB];
+    __shared__ __attribute__((aligned(16))) uint32_t traw_all[G][BN2][BK2 / 16];
+    const int grp = (int)(threadIdx.x >> 8);
+    auto &as = as_all[grp];
+    auto &bs = bs_all[grp];
+    auto &traw = traw_all[grp];
+    const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wk = wave >> 1;
     const int h = lane >> 5, l32 = lane & 31;
     const int64_t m0 = (int64_t)blockIdx.y * BM2, k0 = (int64_t)blockIdx.x * BK2;
-    const int nst = (int)((n + BN2 - 1) / BN2);
+    const int nst_all = (int)((n + BN2 - 1) / BN2);
+    const int nst = (nst_all + G - 1) / G;   // iterations; stage of iteration j: G j + grp
     const int64_t words = pitch / 4;
 
     // staging roles: gradient row m0 + tid / 4, columns 8 (tid % 4) .. +7;
@@ -66,8 +75,8 @@ __global__ __launch_bounds__(256) void backward_mfma_kernel(const void *__restri
     float gv[8];
     uint32_t tv = 0;
 
-    auto load = [&](int st) __attribute__((always_inline)) {
-        const int64_t nb = (int64_t)st * BN2;
+    auto load = [&](int it) __attribute__((always_inline)) {
+        const int64_t nb = (int64_t)(G * it + grp) * BN2;   // past N: zeros
         if (VEC && gm < m && nb + gc + 8 <= n) {
             if (DT == DT_BF16) {
                 const uint4 v = load16((const uint16_t *)grad_y + gm * n + nb + gc);
@@ -178,6 +187,26 @@ __global__ __launch_bounds__(256) void backward_mfma_kernel(const void *__restri
         __syncthreads();
     }
 
+    if constexpr (G == 2) {
+        // group 1's sums into LDS (free after the loop's last barrier), then
+        // group 0 adds them: a fixed order, group 0 + group 1
+        float *tile = (float *)&as_all[0][0][0][0];   // [64][128 + 4]
+        static_assert(64 * 132 * 4 <= (int)sizeof(as_all), "tile fits");
+        if (grp == 1)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+                    tile[(32 * wm + 8 * (r / 4) + 4 * h + (r % 4)) * 132 + 64 * wk + 32 * c + l32] =
+                        acc[c][r];
+        __syncthreads();
+        if (grp == 1) return;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                acc[c][r] += tile[(32 * wm + 8 * (r / 4) + 4 * h + (r % 4)) * 132 + 64 * wk + 32 * c + l32];
+    }
     // lane (l32, h), register r: row 8 (r / 4) + 4 h + r % 4 of the wave's 32
     // m rows, column l32 of k tile c
     const float gamma = gamma_p[0];
@@ -195,6 +224,31 @@ __global__ __launch_bounds__(256) void backward_mfma_kernel(const void *__restri
 
 }  // namespace
 
+namespace {
+template <int G>
+void launch_g(const void *grad_y, int dtype, bool vec, int64_t m, int64_t n, const uint8_t *packed,
+              int64_t pitch, int64_t k, const float *gamma, float *grad_x, hipStream_t s)
+{
+    const dim3 grid((unsigned)((k + BK2 - 1) / BK2), (unsigned)((m + BM2 - 1) / BM2));
+    const dim3 block(256 * G);
+    if (dtype == DT_BF16) {
+        if (vec)
+            hipLaunchKernelGGL((backward_mfma_kernel<DT_BF16, true, G>), grid, block, 0, s, grad_y, m,
+                               n, packed, pitch, k, gamma, grad_x);
+        else
+            hipLaunchKernelGGL((backward_mfma_kernel<DT_BF16, false, G>), grid, block, 0, s, grad_y,
+                               m, n, packed, pitch, k, gamma, grad_x);
+    } else {
+        if (vec)
+            hipLaunchKernelGGL((backward_mfma_kernel<DT_F32, true, G>), grid, block, 0, s, grad_y, m,
+                               n, packed, pitch, k, gamma, grad_x);
+        else
+            hipLaunchKernelGGL((backward_mfma_kernel<DT_F32, false, G>), grid, block, 0, s, grad_y, m,
+                               n, packed, pitch, k, gamma, grad_x);
+    }
+}
+}  // namespace
+
 hipError_t launch_backward_input(const void *grad_y, int dtype, int64_t m, int64_t n,
                                  const uint8_t *packed, int64_t k, const float *gamma,
                                  float *grad_x, hipStream_t s)
@@ -202,22 +256,12 @@ hipError_t launch_backward_input(const void *grad_y, int dtype, int64_t m, int64
     const int64_t pitch = pack2_pitch(k);
     // 16-byte loads need every grad_y row 16-byte aligned
     const bool vec = dtype == DT_BF16 ? n % 8 == 0 : n % 4 == 0;
-    const dim3 grid((unsigned)((k + BK2 - 1) / BK2), (unsigned)((m + BM2 - 1) / BM2));
-    if (dtype == DT_BF16) {
-        if (vec)
-            hipLaunchKernelGGL((backward_mfma_kernel<DT_BF16, true>), grid, dim3(256), 0, s,
-                               grad_y, m, n, packed, pitch, k, gamma, grad_x);
-        else
-            hipLaunchKernelGGL((backward_mfma_kernel<DT_BF16, false>), grid, dim3(256), 0, s,
-                               grad_y, m, n, packed, pitch, k, gamma, grad_x);
-    } else {
-        if (vec)
-            hipLaunchKernelGGL((backward_mfma_kernel<DT_F32, true>), grid, dim3(256), 0, s,
-                               grad_y, m, n, packed, pitch, k, gamma, grad_x);
-        else
-            hipLaunchKernelGGL((backward_mfma_kernel<DT_F32, false>), grid, dim3(256), 0, s,
-                               grad_y, m, n, packed, pitch, k, gamma, grad_x);
-    }
+    // two wave groups per block when the tiles do not fill the CUs
+    const int64_t tiles = ((k + BK2 - 1) / BK2) * ((m + BM2 - 1) / BM2);
+    if (tiles < 256 && n >= 2 * BN2)
+        launch_g<2>(grad_y, dtype, vec, m, n, packed, pitch, k, gamma, grad_x, s);
+    else
+        launch_g<1>(grad_y, dtype, vec, m, n, packed, pitch, k, gamma, grad_x, s);
     return hipGetLastError();
 }
 
