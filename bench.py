@@ -335,9 +335,10 @@ def measure_extra(args):
 
 def measure_backward():
     """Input gradient through BitLinear (straight-through estimators) on the
-    3B-class prefill matrices at M = 512, bf16 gradients: 2 M N K flops,
-    against the fp32 vector peak and, as run (three bf16 MFMAs per product),
-    against the bf16 matrix-core peak."""
+    3B-class prefill matrices at M = 512: 2 M N K flops, against the fp32
+    vector peak and, as run, against the bf16 matrix-core peak (bf16
+    gradients: one bf16 MFMA per product; fp32 gradients: three, the gradient
+    split in three bf16 parts)."""
     import torch
     from ternary_weight_linear_absmax_amd import bitlinear as bl
     from ternary_weight_linear_absmax_amd import inputs
@@ -347,21 +348,21 @@ def measure_backward():
         _, w, _ = inputs.prefill(si)
         packed, gamma = bl.quantize_weights(to_dev(w))
         m = 512
-        gy = (torch.randn((m, n), device="cuda") * 1e-3).to(torch.bfloat16)
+        g32 = torch.randn((m, n), device="cuda") * 1e-3
         gx = torch.empty((m, k), dtype=torch.float32, device="cuda")
-
-        def bwd():
-            for _ in range(reps):
-                bl.backward_input(gy, packed, gamma, k, grad_x=gx)
-        ms = graph_time(bwd, 10, 2) / reps
-        tflops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
-        # the kernel runs three bf16 MFMAs per product (gradient split in three parts)
-        out[f"backward_input_{name}_M512"] = {
-            "K": k, "N": n, "M": m, "us": round(ms * 1e3, 2), "TFLOP/s": round(tflops, 2),
-            "fp32_equiv_frac": round(tflops / FP32_PEAK_TFLOPS, 4),
-            "bf16_mfma_TFLOP/s": round(3 * tflops, 1),
-            "bf16_mfma_frac": round(3 * tflops / BF16_PEAK_TFLOPS, 4)}
-        log(f"backward input {name}: {ms * 1e3:.1f} us {tflops:.1f} TFLOP/s")
+        for tag, gy, parts in (("", g32.to(torch.bfloat16), 1), ("_fp32grad", g32, 3)):
+            def bwd():
+                for _ in range(reps):
+                    bl.backward_input(gy, packed, gamma, k, grad_x=gx)
+            ms = graph_time(bwd, 10, 2) / reps
+            tflops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+            out[f"backward_input_{name}_M512{tag}"] = {
+                "K": k, "N": n, "M": m, "grad_dtype": "bf16" if parts == 1 else "fp32",
+                "us": round(ms * 1e3, 2), "TFLOP/s": round(tflops, 2),
+                "fp32_equiv_frac": round(tflops / FP32_PEAK_TFLOPS, 4),
+                "bf16_mfma_TFLOP/s": round(parts * tflops, 1),
+                "bf16_mfma_frac": round(parts * tflops / BF16_PEAK_TFLOPS, 4)}
+            log(f"backward input {name}{tag}: {ms * 1e3:.1f} us {tflops:.1f} TFLOP/s")
     return out
 
 

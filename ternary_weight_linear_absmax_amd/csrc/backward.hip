@@ -19,7 +19,8 @@ namespace {
 
 // ---- matrix-core kernel -----------------------------------------------------------
 // The product on v_mfma_f32_32x32x16_bf16: each fp32 gradient is split
-// into three bf16 parts hi + mid + lo (round to nearest at each step; the
+// into three bf16 parts hi + mid + lo (a bf16 gradient is its own hi part,
+// so it needs one product instead of three; round to nearest at each step; the
 // parts carry 8 significant bits each, so for normal values their sum is the
 // gradient exactly), the trits are exact in bf16, and the matrix cores
 // accumulate the three products in fp32.  Block tile 64 (m) x 128 (k), four
@@ -54,6 +55,9 @@ __global__ __launch_bounds__(256 * G) void backward_mfma_kernel(const void *__re
     __shared__ __attribute__((aligned(16))) uint8_t as_all[G][2][3][BM2 * LDAB];
     __shared__ __attribute__((aligned(16))) uint8_t bs_all[G][2][BK2 * LDAB];
     __shared__ __attribute__((aligned(16))) uint32_t traw_all[G][BN2][BK2 / 16];
+    // bf16 gradients are their own first part (the other two are zero), so
+    // one product per fragment gives the same sums
+    constexpr int NPART = DT == DT_BF16 ? 1 : 3;
     const int grp = (int)(threadIdx.x >> 8);
     auto &as = as_all[grp];
     auto &bs = bs_all[grp];
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(256 * G) void backward_mfma_kernel(const void *__re
             part[2][e] = bf16_pair(al, bl2);
         }
 #pragma unroll
-        for (int q = 0; q < 3; ++q)
+        for (int q = 0; q < NPART; ++q)
             *(uint4 *)(&as[buf][q][gr * LDAB + 2 * gc]) =
                 make_uint4(part[q][0], part[q][1], part[q][2], part[q][3]);
         traw[tr][tw] = tv;
@@ -171,7 +175,7 @@ __global__ __launch_bounds__(256 * G) void backward_mfma_kernel(const void *__re
             for (int c = 0; c < 2; ++c)
                 b[c] = *(const bf16x8 *)(&bs[buf][(64 * wk + 32 * c + l32) * LDAB + 32 * s + 16 * h]);
 #pragma unroll
-            for (int q = 0; q < 3; ++q) {
+            for (int q = 0; q < NPART; ++q) {
                 const bf16x8 a =
                     *(const bf16x8 *)(&as[buf][q][(32 * wm + l32) * LDAB + 32 * s + 16 * h]);
 #pragma unroll
