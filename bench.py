@@ -439,20 +439,26 @@ def measure_stack(layers=30, m=64):
     def step():
         stack.x.copy_(x0)
         stack.step()
-    ms = graph_time(step, 20, 3)
     pb = stack.packed_bytes()
     from ternary_weight_linear_absmax_amd import bitlinear as bl
-    # per layer: four quantiser launches and four products, each product with
-    # a finish launch when it splits its k range (a non-empty workspace)
-    per_layer = 4 + sum(1 + (bl.forward_workspace_bytes(m, *st.SHAPES[n]) > 0) for n in st.MATRICES)
-    launches = per_layer * layers + 1
     ops = 2.0 * m * sum(st.SHAPES[n][0] * st.SHAPES[n][1] for n in st.MATRICES) * layers
-    out = {"stack_2B_M64": {
-        "layers": layers, "M": m, "us_per_step": round(ms * 1e3, 1),
-        "tokens_per_s": round(m / (ms * 1e-3), 1), "packed_bytes": pb,
-        "GB/s": round(pb / (ms * 1e-3) / 1e9, 1), "TOPS": round(ops / (ms * 1e-3) / 1e12, 2),
-        "launches_per_step": launches}}
-    log(f"stack {layers} layers M={m}: {ms * 1e3:.1f} us/step, {m / (ms * 1e-3):.0f} tokens/s")
+    out = {}
+    # fused: four product + glue calls per layer, two launches each (every
+    # product here runs on the tiled GEMM, whose split partial sums the glue
+    # kernel finishes); separate calls: four quantiser launches and four
+    # products, each with a finish launch when it splits its k range
+    split = sum(bl.forward_workspace_bytes(m, *st.SHAPES[n]) > 0 for n in st.MATRICES)
+    for fused, name, per_layer in ((True, "stack_2B_M64", 8),
+                                   (False, "stack_2B_M64_separate_calls", 8 + split)):
+        stack.fused = fused
+        ms = graph_time(step, 20, 3)
+        out[name] = {
+            "layers": layers, "M": m, "us_per_step": round(ms * 1e3, 1),
+            "tokens_per_s": round(m / (ms * 1e-3), 1), "packed_bytes": pb,
+            "GB/s": round(pb / (ms * 1e-3) / 1e9, 1), "TOPS": round(ops / (ms * 1e-3) / 1e12, 2),
+            "launches_per_step": per_layer * layers + 1}
+        log(f"{name} {layers} layers M={m}: {ms * 1e3:.1f} us/step, "
+            f"{m / (ms * 1e-3):.0f} tokens/s")
     del stack
     torch.cuda.empty_cache()
     return out

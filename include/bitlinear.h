@@ -285,6 +285,55 @@ int bitlinear_relu2_rmsnorm_quantize(const float *gate_up, int64_t M, int64_t ld
                                      float eps, int8_t *xq, float *scale, int32_t *rowsum,
                                      hipStream_t stream);
 
+/* ---- a BitLinear product followed by the next BitLinear's input glue --------------
+ * [same passages as the glue above, and the BitLinear product of
+ *  bitlinear_forward_ex]
+ *
+ * Same results, bit for bit, as bitlinear_forward_ex(xq, scale, rowsum, M,
+ * packed, BL_PACK2, gamma, N, K, y, ..., BL_PATH_AUTO) into a [M, N] float
+ * y, followed by the glue call named after it on y, with its outputs written
+ * to xq_out [M, K'], scale_out [M] and rowsum_out [M] (K' = the glue's width).
+ * The first input is the product's (xq, scale, rowsum: device, required, as
+ * for bitlinear_forward_ex; the 2-bit layout only).  y itself is not
+ * returned: where the tiled GEMM splits the k range, the glue kernel adds the
+ * split partial products itself, which saves the separate finishing launch.
+ * The outputs may be the same buffers as the inputs xq, scale and rowsum (the
+ * product has read them first); nothing else may overlap.  workspace: device,
+ * 16-byte aligned, at least bitlinear_forward_glue_workspace_bytes(M, N, K)
+ * bytes, any contents; it holds the product's partial sums or its output.
+ * M == 0 is a no-op.  Errors as for bitlinear_forward_ex and the glue calls;
+ * nothing is launched when a check fails. */
+int64_t bitlinear_forward_glue_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* x [M, N] (device, float, updated in place) += y; then the residual glue on
+ * x with K' = N. */
+int bitlinear_forward_residual_rmsnorm_quantize(const int8_t *xq, const float *scale,
+                                                const int32_t *rowsum, int64_t M, int64_t K,
+                                                const uint8_t *packed, const float *gamma,
+                                                int64_t N, float *x, float eps, int8_t *xq_out,
+                                                float *scale_out, int32_t *rowsum_out,
+                                                void *workspace, int64_t workspace_bytes,
+                                                hipStream_t stream);
+
+/* The grouped-query glue on y (qkv = y, ld = N); K' = heads * head_dim. */
+int bitlinear_forward_gqa_rmsnorm_quantize(const int8_t *xq, const float *scale,
+                                           const int32_t *rowsum, int64_t M, int64_t K,
+                                           const uint8_t *packed, const float *gamma, int64_t N,
+                                           int64_t v_col, int64_t heads, int64_t kv_heads,
+                                           int64_t head_dim, float eps, int8_t *xq_out,
+                                           float *scale_out, int32_t *rowsum_out,
+                                           void *workspace, int64_t workspace_bytes,
+                                           hipStream_t stream);
+
+/* The squared-ReLU glue on y (gate_up = y, ld = N >= 2F); K' = F. */
+int bitlinear_forward_relu2_rmsnorm_quantize(const int8_t *xq, const float *scale,
+                                             const int32_t *rowsum, int64_t M, int64_t K,
+                                             const uint8_t *packed, const float *gamma,
+                                             int64_t N, int64_t F, float eps, int8_t *xq_out,
+                                             float *scale_out, int32_t *rowsum_out,
+                                             void *workspace, int64_t workspace_bytes,
+                                             hipStream_t stream);
+
 /* Decode packed weights to int8 trits in {-1, 0, 1} (device, [N, K]). */
 int bitlinear_unpack_weights(const uint8_t *packed, int layout, int64_t N, int64_t K,
                              int8_t *trits, hipStream_t stream);

@@ -70,6 +70,14 @@ def load():
         "bitlinear_relu2_rmsnorm_quantize": (i32, [p, i64, i64, i64, ctypes.c_float, p, p, p, p]),
         "bitlinear_quantize_forward": (i32, [p, i32, i64, i64, p, p, p, p, i32, p, i64, p, p, i64,
                                              i32, p]),
+        "bitlinear_forward_glue_workspace_bytes": (i64, [i64, i64, i64]),
+        "bitlinear_forward_residual_rmsnorm_quantize": (
+            i32, [p, p, p, i64, i64, p, p, i64, p, ctypes.c_float, p, p, p, p, i64, p]),
+        "bitlinear_forward_gqa_rmsnorm_quantize": (
+            i32, [p, p, p, i64, i64, p, p, i64, i64, i64, i64, i64, ctypes.c_float, p, p, p, p,
+                  i64, p]),
+        "bitlinear_forward_relu2_rmsnorm_quantize": (
+            i32, [p, p, p, i64, i64, p, p, i64, i64, ctypes.c_float, p, p, p, p, i64, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -317,6 +325,61 @@ def relu2_rmsnorm_quantize(gate_up: torch.Tensor, f: int, eps: float = 1e-5, xq=
     return xq, scale, rowsum
 
 
+def forward_glue_workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(load().bitlinear_forward_glue_workspace_bytes(m, n, k))
+
+
+def _fused_args(xq, scale, rowsum, n, workspace):
+    m, k = xq.shape
+    need = forward_glue_workspace_bytes(m, n, k)
+    if workspace is None and m > 0:
+        workspace = _zero_workspace(need, xq.device)
+    nbytes = 0 if workspace is None else workspace.numel()
+    return m, k, workspace, nbytes
+
+
+def forward_residual_rmsnorm_quantize(xq, scale, rowsum, packed, gamma, n: int, x: torch.Tensor,
+                                      eps: float = 1e-5, xq_out=None, scale_out=None,
+                                      rowsum_out=None, workspace=None, stream=None):
+    """x += BitLinear(xq) (in place), then RMSNorm + per-token quantisation of
+    x into (xq_out, scale_out, rowsum_out), which may be xq, scale, rowsum."""
+    assert x.dtype == torch.float32 and x.is_contiguous() and tuple(x.shape) == (xq.shape[0], n)
+    m, k, ws, nbytes = _fused_args(xq, scale, rowsum, n, workspace)
+    xq_out, scale_out, rowsum_out = _glue_outputs(m, n, xq.device, xq_out, scale_out, rowsum_out)
+    _check(load().bitlinear_forward_residual_rmsnorm_quantize(
+        _ptr(xq), _ptr(scale), _ptr(rowsum), m, k, _ptr(packed), _ptr(gamma), n, _ptr(x), eps,
+        _ptr(xq_out), _ptr(scale_out), _ptr(rowsum_out), _ptr(ws), nbytes, _stream(stream)),
+        "bitlinear_forward_residual_rmsnorm_quantize")
+    return xq_out, scale_out, rowsum_out
+
+
+def forward_gqa_rmsnorm_quantize(xq, scale, rowsum, packed, gamma, n: int, v_col: int, heads: int,
+                                 kv_heads: int, head_dim: int, eps: float = 1e-5, xq_out=None,
+                                 scale_out=None, rowsum_out=None, workspace=None, stream=None):
+    """QKV = BitLinear(xq) [M, n], then the first-token GQA glue on it."""
+    m, k, ws, nbytes = _fused_args(xq, scale, rowsum, n, workspace)
+    xq_out, scale_out, rowsum_out = _glue_outputs(m, heads * head_dim, xq.device, xq_out,
+                                                  scale_out, rowsum_out)
+    _check(load().bitlinear_forward_gqa_rmsnorm_quantize(
+        _ptr(xq), _ptr(scale), _ptr(rowsum), m, k, _ptr(packed), _ptr(gamma), n, v_col, heads,
+        kv_heads, head_dim, eps, _ptr(xq_out), _ptr(scale_out), _ptr(rowsum_out), _ptr(ws),
+        nbytes, _stream(stream)), "bitlinear_forward_gqa_rmsnorm_quantize")
+    return xq_out, scale_out, rowsum_out
+
+
+def forward_relu2_rmsnorm_quantize(xq, scale, rowsum, packed, gamma, n: int, f: int,
+                                   eps: float = 1e-5, xq_out=None, scale_out=None,
+                                   rowsum_out=None, workspace=None, stream=None):
+    """gate_up = BitLinear(xq) [M, n], then the squared-ReLU glue on it."""
+    m, k, ws, nbytes = _fused_args(xq, scale, rowsum, n, workspace)
+    xq_out, scale_out, rowsum_out = _glue_outputs(m, f, xq.device, xq_out, scale_out, rowsum_out)
+    _check(load().bitlinear_forward_relu2_rmsnorm_quantize(
+        _ptr(xq), _ptr(scale), _ptr(rowsum), m, k, _ptr(packed), _ptr(gamma), n, f, eps,
+        _ptr(xq_out), _ptr(scale_out), _ptr(rowsum_out), _ptr(ws), nbytes, _stream(stream)),
+        "bitlinear_forward_relu2_rmsnorm_quantize")
+    return xq_out, scale_out, rowsum_out
+
+
 def unpack_weights(packed, n: int, k: int, layout: int = BL_PACK2, stream=None):
     lib = load()
     trits = torch.empty((n, k), dtype=torch.int8, device=packed.device)
@@ -338,3 +401,7 @@ bitlinear_relu2_rmsnorm_quantize = relu2_rmsnorm_quantize
 bitlinear_packed_bytes = packed_bytes
 bitlinear_packed_row_bytes = packed_row_bytes
 bitlinear_status_string = status_string
+bitlinear_forward_glue_workspace_bytes = forward_glue_workspace_bytes
+bitlinear_forward_residual_rmsnorm_quantize = forward_residual_rmsnorm_quantize
+bitlinear_forward_gqa_rmsnorm_quantize = forward_gqa_rmsnorm_quantize
+bitlinear_forward_relu2_rmsnorm_quantize = forward_relu2_rmsnorm_quantize

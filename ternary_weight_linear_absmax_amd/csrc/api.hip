@@ -328,6 +328,122 @@ int bitlinear_relu2_rmsnorm_quantize(const float *gate_up, int64_t M, int64_t ld
     return hip_status(bl::launch_glue(bl::GLUE_RELU2, a, M, F, eps, xq, scale, rowsum, stream));
 }
 
+namespace {
+
+// Bytes of the product's own workspace (its split partial sums, whether the
+// product or the glue finishes them), rounded up so that the float output
+// that follows it stays 256-byte aligned.
+int64_t fused_product_ws(int64_t m, int64_t n, int64_t k)
+{
+    int64_t p = bitlinear_forward_workspace_bytes(m, n, k, BL_PACK2);
+    const int64_t part = bl::gemm_partial_workspace_bytes(m, n, k);
+    p = part > p ? part : p;
+    return (p + 255) / 256 * 256;
+}
+
+// BitLinear product of 2-bit weights followed by one of the glue forms.  When
+// the tiled GEMM splits the k range, its int32 slices stay in the workspace
+// and the glue kernel finishes them (no finish launch); otherwise the product
+// writes its float output into the workspace and the glue reads it.
+int forward_glue(int mode, const int8_t *xq, const float *scale, const int32_t *rowsum,
+                 int64_t M, int64_t K, const uint8_t *packed, const float *gamma, int64_t N,
+                 bl::GlueArgs a, int64_t gk, float eps, int8_t *xq_out, float *scale_out,
+                 int32_t *rowsum_out, void *workspace, int64_t workspace_bytes,
+                 hipStream_t stream)
+{
+    if (N < 1 || !good_k(K) || M > 0x7FFFFFFF) return BL_ERR_SHAPE;
+    if (M > 0 && (K > kMaxElems / M || N > kMaxElems / M)) return BL_ERR_SHAPE;
+    if (K > kMaxElems / N) return BL_ERR_SHAPE;
+    const int c = glue_common(M, gk, eps, xq_out, scale_out, rowsum_out);
+    if (c != 1) return c;
+    if (!xq || !scale || !rowsum || !packed || !gamma || !workspace) return BL_ERR_NULL;
+    if (!al16(xq) || !al16(packed) || !al4(scale) || !al4(rowsum) || !al4(gamma) ||
+        !al16(workspace))
+        return BL_ERR_ALIGN;
+    const int64_t pws = fused_product_ws(M, N, K);
+    if (workspace_bytes < pws + 4 * M * N) return BL_ERR_WORKSPACE;
+
+    const int path = choose_path(M, N, K, BL_PACK2);
+    const int splits = path == BL_PATH_MFMA ? bl::gemm_partial_splits(M, N, K) : 0;
+    if (splits > 1) {
+        bl::Out out{scale, gamma, nullptr, nullptr};
+        hipError_t e = bl::launch_gemm_pack2_partials(xq, rowsum, M, packed, N, K, out,
+                                                      (int32_t *)workspace, stream);
+        if (e != hipSuccess) return BL_ERR_HIP;
+        a.part = (const int32_t *)workspace;
+        a.splits = splits;
+        a.pm = M;
+        a.p_rowsum = rowsum;
+        a.p_scale = scale;
+        a.p_gamma = gamma;
+        if (mode == bl::GLUE_RESIDUAL) a.ld = N;
+    } else {
+        float *y = (float *)((uint8_t *)workspace + pws);
+        const int r = run_product(xq, scale, rowsum, M, packed, BL_PACK2, gamma, N, K, y, nullptr,
+                                  workspace, pws, path, stream);
+        if (r != BL_OK) return r;
+        if (mode == bl::GLUE_RESIDUAL) a.add = y;
+        else a.src = y;
+    }
+    return hip_status(bl::launch_glue(mode, a, M, gk, eps, xq_out, scale_out, rowsum_out, stream));
+}
+
+}  // namespace
+
+int64_t bitlinear_forward_glue_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 1 || N < 1 || !good_k(K) || M > 0x7FFFFFFF) return 0;
+    if (K > kMaxElems / M || N > kMaxElems / M || K > kMaxElems / N) return 0;
+    return fused_product_ws(M, N, K) + 4 * M * N;
+}
+
+int bitlinear_forward_residual_rmsnorm_quantize(const int8_t *xq, const float *scale,
+                                                const int32_t *rowsum, int64_t M, int64_t K,
+                                                const uint8_t *packed, const float *gamma,
+                                                int64_t N, float *x, float eps, int8_t *xq_out,
+                                                float *scale_out, int32_t *rowsum_out,
+                                                void *workspace, int64_t workspace_bytes,
+                                                hipStream_t stream)
+{
+    if (M > 0 && !x) return BL_ERR_NULL;
+    if (!al4(x)) return BL_ERR_ALIGN;
+    bl::GlueArgs a{x, nullptr, nullptr, 0, 0, 1, 1};
+    return forward_glue(bl::GLUE_RESIDUAL, xq, scale, rowsum, M, K, packed, gamma, N, a, N, eps,
+                        xq_out, scale_out, rowsum_out, workspace, workspace_bytes, stream);
+}
+
+int bitlinear_forward_gqa_rmsnorm_quantize(const int8_t *xq, const float *scale,
+                                           const int32_t *rowsum, int64_t M, int64_t K,
+                                           const uint8_t *packed, const float *gamma, int64_t N,
+                                           int64_t v_col, int64_t heads, int64_t kv_heads,
+                                           int64_t head_dim, float eps, int8_t *xq_out,
+                                           float *scale_out, int32_t *rowsum_out,
+                                           void *workspace, int64_t workspace_bytes,
+                                           hipStream_t stream)
+{
+    if (heads < 1 || kv_heads < 1 || head_dim < 1 || heads % kv_heads != 0) return BL_ERR_SHAPE;
+    if (heads > bl::GLUE_MAX_K || head_dim > bl::GLUE_MAX_K) return BL_ERR_SHAPE;
+    if (v_col < 0 || N < 1 || v_col + kv_heads * head_dim > N) return BL_ERR_SHAPE;
+    bl::GlueArgs a{nullptr, nullptr, nullptr, N, v_col, heads / kv_heads, head_dim};
+    return forward_glue(bl::GLUE_GQA, xq, scale, rowsum, M, K, packed, gamma, N, a,
+                        heads * head_dim, eps, xq_out, scale_out, rowsum_out, workspace,
+                        workspace_bytes, stream);
+}
+
+int bitlinear_forward_relu2_rmsnorm_quantize(const int8_t *xq, const float *scale,
+                                             const int32_t *rowsum, int64_t M, int64_t K,
+                                             const uint8_t *packed, const float *gamma,
+                                             int64_t N, int64_t F, float eps, int8_t *xq_out,
+                                             float *scale_out, int32_t *rowsum_out,
+                                             void *workspace, int64_t workspace_bytes,
+                                             hipStream_t stream)
+{
+    if (F < 1 || N < 2 * F) return BL_ERR_SHAPE;
+    bl::GlueArgs a{nullptr, nullptr, nullptr, N, F, 1, 1};
+    return forward_glue(bl::GLUE_RELU2, xq, scale, rowsum, M, K, packed, gamma, N, a, F, eps,
+                        xq_out, scale_out, rowsum_out, workspace, workspace_bytes, stream);
+}
+
 int bitlinear_unpack_weights(const uint8_t *packed, int layout, int64_t N, int64_t K,
                              int8_t *trits, hipStream_t stream)
 {

@@ -824,7 +824,7 @@ int64_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k)
 template <int WM, int WN>
 hipError_t launch_gemm_cfg(const int8_t *xq, const int32_t *rowsum, int64_t m,
                            const uint8_t *packed, int64_t n, int64_t k, Out out, int splits,
-                           int32_t *ws, hipStream_t s, int64_t ldy = -1)
+                           int32_t *ws, hipStream_t s, int64_t ldy = -1, bool finish = true)
 {
     constexpr int BM = 64 * WM, BN = 64 * WN;
     const int tiles_m = (int)((m + BM - 1) / BM);
@@ -851,7 +851,7 @@ hipError_t launch_gemm_cfg(const int8_t *xq, const int32_t *rowsum, int64_t m,
                            packed, n, pitch, tiles_m, tiles, per_xcd, splits, stages_per, out, ldy,
                            ws);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || splits == 1) return e;
+    if (e != hipSuccess || splits == 1 || !finish) return e;
     return launch_splitk_finish(ws, rowsum, m, n, splits, out, ldy, s);
 }
 
@@ -890,6 +890,42 @@ hipError_t launch_gemm_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
         }
     }
     return hipSuccess;
+}
+
+// Tiles and k split of a product whose split partial sums the next kernel
+// finishes (no finish launch to pay for).
+static GemmCfg gemm_partial_config(int64_t m, int64_t n, int64_t k)
+{
+    return gemm_config(m, n, k);
+}
+
+int gemm_partial_splits(int64_t m, int64_t n, int64_t k)
+{
+    int64_t mc, nc;
+    gemm_chunks(m, n, k, mc, nc);
+    if (mc < m || nc < n) return 0;
+    const GemmCfg c = gemm_partial_config(m, n, k);
+    return c.splits > 1 ? c.splits : 0;
+}
+
+int64_t gemm_partial_workspace_bytes(int64_t m, int64_t n, int64_t k)
+{
+    const int sp = gemm_partial_splits(m, n, k);
+    return sp > 1 ? 4 * (int64_t)sp * m * n : 0;
+}
+
+hipError_t launch_gemm_pack2_partials(const int8_t *xq, const int32_t *rowsum, int64_t m,
+                                      const uint8_t *packed, int64_t n, int64_t k, Out out,
+                                      int32_t *ws, hipStream_t s)
+{
+    const GemmCfg c = gemm_partial_config(m, n, k);
+    if (c.wm == 2 && c.wn == 2)
+        return launch_gemm_cfg<2, 2>(xq, rowsum, m, packed, n, k, out, c.splits, ws, s, n, false);
+    if (c.wm == 1 && c.wn == 2)
+        return launch_gemm_cfg<1, 2>(xq, rowsum, m, packed, n, k, out, c.splits, ws, s, n, false);
+    if (c.wm == 2 && c.wn == 1)
+        return launch_gemm_cfg<2, 1>(xq, rowsum, m, packed, n, k, out, c.splits, ws, s, n, false);
+    return launch_gemm_cfg<1, 1>(xq, rowsum, m, packed, n, k, out, c.splits, ws, s, n, false);
 }
 
 }  // namespace bl

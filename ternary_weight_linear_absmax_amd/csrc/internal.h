@@ -51,6 +51,16 @@ struct GlueArgs {
     int64_t col;          // gqa: first value column; relu2: offset of "up" from "gate"
     int64_t group;        // gqa: query heads per key-value head
     int64_t head_dim;     // gqa
+    // Product output as split-k partial slices instead of floats (add / src
+    // unused): y[m, c] = (sum over slices of part[(s * pm + m) * ld + c]
+    // - p_rowsum[m]) * (p_gamma[0] / p_scale[m]), the split-k finish's
+    // arithmetic; for the residual form ld = K.
+    const int32_t *part;
+    int splits;
+    int64_t pm;
+    const int32_t *p_rowsum;
+    const float *p_scale;
+    const float *p_gamma;
 };
 hipError_t launch_glue(int mode, const GlueArgs &a, int64_t m, int64_t k, double eps,
                        int8_t *xq, float *scale, int32_t *rowsum, hipStream_t s);
@@ -88,6 +98,17 @@ hipError_t launch_gemm_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
                              const uint8_t *packed, int64_t n, int64_t k, Out out, void *ws,
                              hipStream_t s);
 int64_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
+// The same product with its k range split and the slices left unsummed:
+// ws receives splits int32 [M, N] slices (row stride N), each the slice's sum
+// of xq * (t + 1) without the row-sum term.  gemm_partial_splits gives the
+// split count, or 0 where the product does not run that way (one split, or
+// operands addressed in several blocks); the launch is valid only when it is
+// at least 2.
+int gemm_partial_splits(int64_t m, int64_t n, int64_t k);
+int64_t gemm_partial_workspace_bytes(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_pack2_partials(const int8_t *xq, const int32_t *rowsum, int64_t m,
+                                      const uint8_t *packed, int64_t n, int64_t k, Out out,
+                                      int32_t *ws, hipStream_t s);
 
 // ---- backward (backward.hip) ----
 // grad_x [m, k] fp32 = gamma * grad_y [m, n] (bf16 / fp32) * t [n, k] (2-bit layout).

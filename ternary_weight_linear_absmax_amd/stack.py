@@ -20,6 +20,12 @@ Per layer (x is the float residual stream, [M, 2560]):
     xq = quant(RMSNorm(relu(gate)^2 * up))      bitlinear_relu2_rmsnorm_quantize
     d = BitLinear_down(xq)
     x += d                                      (folded into the next layer's first call)
+
+With `fused` set (the default) every product and the glue after it are one
+call (bitlinear_forward_*_rmsnorm_quantize): where the GEMM splits its k
+range, the glue kernel finishes the split partial sums itself, so the product
+output is never stored and the finishing launch disappears.  The results are
+bit for bit those of the unfused sequence.
 """
 from __future__ import annotations
 
@@ -40,10 +46,10 @@ class DecoderStack:
     """Packed weights of `layers` layers plus the activation buffers of M
     tokens, all resident on the GPU."""
 
-    def __init__(self, layer_weights, layers: int, m: int, device="cuda"):
+    def __init__(self, layer_weights, layers: int, m: int, device="cuda", fused: bool = True):
         """layer_weights(l) -> dict name -> [N, K] bf16/fp32 tensor on the GPU
         (quantised and packed here, then released)."""
-        self.layers, self.m = layers, m
+        self.layers, self.m, self.fused = layers, m, fused
         self.packed, self.gamma = [], []
         for layer in range(layers):
             w = layer_weights(layer)
@@ -75,10 +81,37 @@ class DecoderStack:
         bl.forward(q["xq"], self.scale, self.rowsum, self.packed[layer][name],
                    self.gamma[layer][name], n, k, y=self.y[name])
 
+    def _fused_layer(self, layer: int, note):
+        """One layer as four product + glue calls; expects the quantised
+        attention input in xq / scale / rowsum and leaves the next layer's
+        there (after x += down)."""
+        p, g = self.packed[layer], self.gamma[layer]
+        qh, qf = self._q(HIDDEN), self._q(FFN)
+
+        def args(q, name, n):
+            return (q["xq"], q["scale"], q["rowsum"], p[name], g[name], n)
+
+        def outs(q):
+            return dict(xq_out=q["xq"], scale_out=q["scale"], rowsum_out=q["rowsum"])
+
+        bl.forward_gqa_rmsnorm_quantize(*args(qh, "qkv", QKV), V_COL, HEADS, KV_HEADS, HEAD_DIM,
+                                        EPS, **outs(qh))
+        note("qkv+attn_norm")
+        bl.forward_residual_rmsnorm_quantize(*args(qh, "o", HIDDEN), self.x, EPS, **outs(qh))
+        note("o+norm_ffn")
+        bl.forward_relu2_rmsnorm_quantize(*args(qh, "up_gate", 2 * FFN), FFN, EPS, **outs(qf))
+        note("up_gate+ffn_norm")
+        bl.forward_residual_rmsnorm_quantize(*args(qf, "down", HIDDEN), self.x, EPS, **outs(qh))
+        note("down+norm_attn")
+
     def layer(self, layer: int, trace=None):
         """One decoder layer on the resident buffers.  trace: optional callback
-        trace(op_name) called after every step (for tests)."""
+        trace(op_name) called after every step (for tests).  Fused: the layer
+        starts from the quantised attention input that the previous call left
+        (step() makes the first one) and ends with the next one."""
         note = trace or (lambda op: None)
+        if self.fused:
+            return self._fused_layer(layer, note)
         add = self.y["down"] if layer > 0 else None
         bl.residual_rmsnorm_quantize(self.x, add, EPS, **self._q(HIDDEN))
         note("norm_attn")
@@ -100,7 +133,11 @@ class DecoderStack:
 
     def step(self):
         """All layers on the current residual stream self.x, then the last
-        residual addition; self.x holds the stack's output."""
+        residual addition; self.x holds the stack's output (and xq / scale /
+        rowsum its quantised RMSNorm)."""
+        if self.fused:
+            bl.residual_rmsnorm_quantize(self.x, None, EPS, **self._q(HIDDEN))
         for layer in range(self.layers):
             self.layer(layer)
-        bl.residual_rmsnorm_quantize(self.x, self.y["down"], EPS, **self._q(HIDDEN))
+        if not self.fused:
+            bl.residual_rmsnorm_quantize(self.x, self.y["down"], EPS, **self._q(HIDDEN))

@@ -221,3 +221,42 @@ def test_glue_argument_checks(lib):
     assert h(P, 4, 13823, 6912, 1e-5, P, P, P, None) == -2               # ld < 2F
     assert h(NULL, 4, 13824, 6912, 1e-5, P, P, P, None) == -1
     assert h(P, 0, 13824, 6912, 1e-5, NULL, NULL, NULL, None) == 0
+
+
+def test_fused_product_glue_argument_checks(lib):
+    # workspace: the product's own (256-byte rounded) plus its float output
+    for m, n, k in ((64, 3840, 2560), (64, 13824, 2560), (17, 2560, 6912), (1, 2560, 2560)):
+        own = bl.forward_workspace_bytes(m, n, k)
+        need = bl.forward_glue_workspace_bytes(m, n, k)
+        assert need >= (own + 255) // 256 * 256 + 4 * m * n and need % 4 == 0
+    assert bl.forward_glue_workspace_bytes(0, 64, 64) == 0
+    assert bl.forward_glue_workspace_bytes(4, 64, 0) == 0
+    need = bl.forward_glue_workspace_bytes(4, 64, 64)
+
+    f = lib.bitlinear_forward_residual_rmsnorm_quantize
+
+    def call(xq=P, s=P, r=P, m=4, k=64, pk=P, g=P, n=64, x=P, eps=1e-5, xo=P, so=P, ro=P, ws=P,
+             wsb=need):
+        return f(xq, s, r, m, k, pk, g, n, x, eps, xo, so, ro, ws, wsb, None)
+
+    assert call(x=NULL) == -1
+    assert call(xq=NULL) == -1
+    assert call(g=NULL) == -1
+    assert call(ws=NULL) == -1
+    assert call(xo=NULL) == -1
+    assert call(wsb=need - 1) == -6
+    assert call(k=0) == -2
+    assert call(n=0) == -2
+    assert call(n=8193) == -2                      # glue width past one block
+    assert call(eps=-1.0) == -2
+    assert call(ws=ODD) == -3
+    assert call(pk=ODD) == -3
+    assert call(m=0, xq=NULL, s=NULL, r=NULL, x=NULL, xo=NULL, so=NULL, ro=NULL, ws=NULL) == 0
+    g = lib.bitlinear_forward_gqa_rmsnorm_quantize
+    assert g(P, P, P, 4, 2560, P, P, 3840, 3200, 20, 3, 128, 1e-5, P, P, P, P, 1 << 30,
+             None) == -2                           # 20 % 3 != 0
+    assert g(P, P, P, 4, 2560, P, P, 3800, 3200, 20, 5, 128, 1e-5, P, P, P, P, 1 << 30,
+             None) == -2                           # V past the row
+    h = lib.bitlinear_forward_relu2_rmsnorm_quantize
+    assert h(P, P, P, 4, 2560, P, P, 13823, 6912, 1e-5, P, P, P, P, 1 << 30, None) == -2
+    assert h(P, P, P, 4, 2560, P, P, 13824, 6912, 1e-5, P, P, P, NULL, 1 << 30, None) == -1

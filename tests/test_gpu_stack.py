@@ -43,7 +43,8 @@ def assert_quant_close(got, want):
 def test_stack_layer_against_oracle():
     torch.cuda.synchronize()
     w_np = {layer: np_weights(layer) for layer in range(2)}
-    stack = st.DecoderStack(lambda layer: {k: dev(v) for k, v in w_np[layer].items()}, 2, M)
+    stack = st.DecoderStack(lambda layer: {k: dev(v) for k, v in w_np[layer].items()}, 2, M,
+                            fused=False)
     trits = {}
     for name in st.MATRICES:
         t, g = oracle.quantize_weights(w_np[0][name])
@@ -103,6 +104,7 @@ def test_stack_layer_against_oracle():
 
 
 def test_stack_graph_replay_matches_eager():
+    """The fused stack (product and glue in one call) captured in a HIP graph."""
     gen = torch.Generator(device="cuda")
 
     def weights(layer):
