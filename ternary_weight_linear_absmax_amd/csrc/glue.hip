@@ -118,6 +118,7 @@ __global__ __launch_bounds__(256) void glue_kernel(GlueArgs a, int64_t k, double
 #pragma unroll
                     for (int j = 0; j < EPT; ++j) t[u][q][j] = p[col[q][j]];
             }
+            __builtin_amdgcn_sched_barrier(0);   // every load issued before the first add
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int32_t keep = s0 + u < a.splits ? -1 : 0;   // no branch
@@ -218,7 +219,7 @@ hipError_t launch_mode(const GlueArgs &a, int64_t m, int64_t k, double eps, int8
                            scale, rowsum);                                                      \
         return hipGetLastError();                                                               \
     }
-    GLUE_CASE(4) GLUE_CASE(8) GLUE_CASE(16) GLUE_CASE(32)
+    GLUE_CASE(4) GLUE_CASE(8) GLUE_CASE(12) GLUE_CASE(16) GLUE_CASE(28) GLUE_CASE(32)
 #undef GLUE_CASE
     return hipErrorInvalidValue;
 }

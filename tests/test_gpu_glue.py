@@ -1,0 +1,55 @@
+"""The decoder-block glue (RMSNorm in double precision, then the per-token
+absmax quantiser) against the oracle at row lengths across the kernel's
+per-thread element counts, ragged ones included, for its three input forms.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from ternary_weight_linear_absmax_amd import bitlinear as bl
+
+from gpu_helpers import assert_quant_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+# elements per thread (256 threads a row): 1, 4, 8, 10, 12, 15, 27, 32
+WIDTHS = [1, 100, 1000, 2000, 2560, 3000, 3840, 6912, 8192]
+
+
+def quant(t):
+    return tuple(host(a) for a in t)
+
+
+@pytest.mark.parametrize("k", WIDTHS)
+def test_residual_glue_against_oracle(k):
+    rng = np.random.default_rng(300 + k)
+    m = 5
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    add = (rng.standard_normal((m, k)) * 3).astype(np.float32)
+    xd = dev(x)
+    got = quant(bl.residual_rmsnorm_quantize(xd, dev(add)))
+    x1 = oracle.add_f32(x, add)
+    np.testing.assert_array_equal(host(xd).view(np.uint32), x1.view(np.uint32))
+    assert_quant_close(got, oracle.rmsnorm_quantize(x1))
+    got = quant(bl.residual_rmsnorm_quantize(dev(x)))          # no addition
+    assert_quant_close(got, oracle.rmsnorm_quantize(x))
+
+
+@pytest.mark.parametrize("f", WIDTHS)
+def test_relu2_glue_against_oracle(f):
+    rng = np.random.default_rng(400 + f)
+    m, pad = 3, 7
+    gu = rng.standard_normal((m, 2 * f + pad)).astype(np.float32)
+    got = quant(bl.relu2_rmsnorm_quantize(dev(gu), f))
+    assert_quant_close(got, oracle.rmsnorm_quantize(oracle.relu2_mul(gu[:, :f], gu[:, f:2 * f])))
+
+
+@pytest.mark.parametrize("heads,kv_heads,head_dim", [(1, 1, 1), (4, 2, 25), (20, 5, 128),
+                                                     (32, 8, 128), (6, 3, 500)])
+def test_gqa_glue_against_oracle(heads, kv_heads, head_dim):
+    rng = np.random.default_rng(500 + heads * head_dim)
+    m, v_col = 4, 3 + heads * head_dim
+    qkv = rng.standard_normal((m, v_col + kv_heads * head_dim + 5)).astype(np.float32)
+    got = quant(bl.gqa_rmsnorm_quantize(dev(qkv), v_col, heads, kv_heads, head_dim))
+    v = qkv[:, v_col:v_col + kv_heads * head_dim]
+    assert_quant_close(got, oracle.rmsnorm_quantize(oracle.gqa_expand(v, heads, kv_heads)))

@@ -16,7 +16,7 @@ from ternary_weight_linear_absmax_amd import bitlinear as bl
 from ternary_weight_linear_absmax_amd import inputs
 from ternary_weight_linear_absmax_amd import stack as st
 
-from gpu_helpers import assert_y_close, dev, host
+from gpu_helpers import assert_quant_close, assert_y_close, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -25,19 +25,6 @@ M = 64
 
 def np_weights(layer):
     return inputs.stack_layer_weights(layer)
-
-
-def assert_quant_close(got, want):
-    """xq / scale / rowsum of the glue against the oracle's: codes may differ
-    by one in at most 1 in 10^5 positions (rounding edges), scales by 1e-6."""
-    q, s, r = got
-    q_ref, s_ref, r_ref = want
-    diff = q.astype(np.int32) - q_ref.astype(np.int32)
-    assert np.abs(diff).max() <= 1
-    assert np.count_nonzero(diff) <= max(1, q.size // 100_000), np.count_nonzero(diff)
-    np.testing.assert_allclose(s, s_ref, rtol=1e-6)
-    np.testing.assert_array_equal(r - r_ref, diff.sum(axis=1))
-    assert np.array_equal(r, q.astype(np.int64).sum(axis=1))
 
 
 def test_stack_layer_against_oracle():
