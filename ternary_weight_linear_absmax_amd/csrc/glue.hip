@@ -86,7 +86,9 @@ __global__ __launch_bounds__(256) void glue_kernel(GlueArgs a, int64_t k, double
     if constexpr (PART) {
         // U slices' loads in flight at once (64 registers of loaded values);
         // slices past the last are loaded as slice s0 and masked out of the
-        // sum, so that no load or wait sits behind a branch.  Column offsets fit 32 bits (ld < 2^31).
+        // sum, so that no load or wait sits behind a branch.  Column offsets
+        // fit 32 bits: the GEMM leaves its slices unsummed only for products
+        // it addresses in one block, whose N * pitch is below 2^31.
         constexpr int NSRC = MODE == GLUE_RELU2 ? 2 : 1;
         constexpr int U0 = 64 / (EPT * NSRC);
         constexpr int U = U0 < 1 ? 1 : U0 > 4 ? 4 : U0;
