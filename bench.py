@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=30)
     ap.add_argument("--no-extra", action="store_true", help="skip the 70B / prefill lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-separate-stack", action="store_true",
+                    help="skip the layer stack timed with separate product and glue calls")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy kernel (reference for the "
@@ -300,7 +302,7 @@ def measure_extra(args):
         del c2, c3
         torch.cuda.empty_cache()
     # layer stack: 30 layers of the 2B-class decoder, M = 64 tokens at position 0
-    extra.update(measure_stack())
+    extra.update(measure_stack(separate=not args.no_separate_stack))
     # prefill M=512 (packed weights 6.9 MB: they stay in the Infinity Cache)
     reps = 10
     for si, (name, k, n) in enumerate(inputs.PREFILL_SHAPES):
@@ -414,7 +416,7 @@ def measure_variants():
     return out
 
 
-def measure_stack(layers=30, m=64):
+def measure_stack(layers=30, m=64, separate=True):
     """The 2B-class layer stack (hidden 2560, 20/5 heads of 128, FFN 6912,
     squared ReLU, RMSNorm before every BitLinear), M tokens decoded at
     sequence position 0, one step = all layers, captured in one HIP graph.
@@ -448,8 +450,10 @@ def measure_stack(layers=30, m=64):
     # kernel finishes); separate calls: four quantiser launches and four
     # products, each with a finish launch when it splits its k range
     split = sum(bl.forward_workspace_bytes(m, *st.SHAPES[n]) > 0 for n in st.MATRICES)
-    for fused, name, per_layer in ((True, "stack_2B_M64", 8),
-                                   (False, "stack_2B_M64_separate_calls", 8 + split)):
+    variants = [(True, "stack_2B_M64", 8)]
+    if separate:
+        variants.append((False, "stack_2B_M64_separate_calls", 8 + split))
+    for fused, name, per_layer in variants:
         stack.fused = fused
         ms = graph_time(step, 20, 3)
         out[name] = {
