@@ -301,8 +301,9 @@ int bitlinear_relu2_rmsnorm_quantize(const float *gate_up, int64_t M, int64_t ld
  * product has read them first); nothing else may overlap.  workspace: device,
  * 16-byte aligned, at least bitlinear_forward_glue_workspace_bytes(M, N, K)
  * bytes, any contents; it holds the product's partial sums or its output.
- * M == 0 is a no-op.  Errors as for bitlinear_forward_ex and the glue calls;
- * nothing is launched when a check fails. */
+ * N >= 1 (the glue reads columns of y).  M == 0 is a no-op.  Errors as for
+ * bitlinear_forward_ex and the glue calls; nothing is launched when a check
+ * fails. */
 int64_t bitlinear_forward_glue_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* x [M, N] (device, float, updated in place) += y; then the residual glue on
