@@ -329,7 +329,7 @@ def forward_glue_workspace_bytes(m: int, n: int, k: int) -> int:
     return int(load().bitlinear_forward_glue_workspace_bytes(m, n, k))
 
 
-def _fused_args(xq, scale, rowsum, n, workspace):
+def _fused_args(xq, n, workspace):
     m, k = xq.shape
     need = forward_glue_workspace_bytes(m, n, k)
     if workspace is None and m > 0:
@@ -344,7 +344,7 @@ def forward_residual_rmsnorm_quantize(xq, scale, rowsum, packed, gamma, n: int, 
     """x += BitLinear(xq) (in place), then RMSNorm + per-token quantisation of
     x into (xq_out, scale_out, rowsum_out), which may be xq, scale, rowsum."""
     assert x.dtype == torch.float32 and x.is_contiguous() and tuple(x.shape) == (xq.shape[0], n)
-    m, k, ws, nbytes = _fused_args(xq, scale, rowsum, n, workspace)
+    m, k, ws, nbytes = _fused_args(xq, n, workspace)
     xq_out, scale_out, rowsum_out = _glue_outputs(m, n, xq.device, xq_out, scale_out, rowsum_out)
     _check(load().bitlinear_forward_residual_rmsnorm_quantize(
         _ptr(xq), _ptr(scale), _ptr(rowsum), m, k, _ptr(packed), _ptr(gamma), n, _ptr(x), eps,
@@ -357,7 +357,7 @@ def forward_gqa_rmsnorm_quantize(xq, scale, rowsum, packed, gamma, n: int, v_col
                                  kv_heads: int, head_dim: int, eps: float = 1e-5, xq_out=None,
                                  scale_out=None, rowsum_out=None, workspace=None, stream=None):
     """QKV = BitLinear(xq) [M, n], then the first-token GQA glue on it."""
-    m, k, ws, nbytes = _fused_args(xq, scale, rowsum, n, workspace)
+    m, k, ws, nbytes = _fused_args(xq, n, workspace)
     xq_out, scale_out, rowsum_out = _glue_outputs(m, heads * head_dim, xq.device, xq_out,
                                                   scale_out, rowsum_out)
     _check(load().bitlinear_forward_gqa_rmsnorm_quantize(
@@ -371,7 +371,7 @@ def forward_relu2_rmsnorm_quantize(xq, scale, rowsum, packed, gamma, n: int, f: 
                                    eps: float = 1e-5, xq_out=None, scale_out=None,
                                    rowsum_out=None, workspace=None, stream=None):
     """gate_up = BitLinear(xq) [M, n], then the squared-ReLU glue on it."""
-    m, k, ws, nbytes = _fused_args(xq, scale, rowsum, n, workspace)
+    m, k, ws, nbytes = _fused_args(xq, n, workspace)
     xq_out, scale_out, rowsum_out = _glue_outputs(m, f, xq.device, xq_out, scale_out, rowsum_out)
     _check(load().bitlinear_forward_relu2_rmsnorm_quantize(
         _ptr(xq), _ptr(scale), _ptr(rowsum), m, k, _ptr(packed), _ptr(gamma), n, f, eps,
