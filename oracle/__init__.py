@@ -73,6 +73,8 @@ def _load():
         "orc_quantize_act": (None, [p, i32, i64, i64, p, p, p]),
         "orc_quantize_act_bits": (None, [p, i32, i64, i64, i32, p, p, p]),
         "orc_sign_trits": (None, [p, i32, i64, i64, p]),
+        "orc_group_absmean": (None, [p, i32, i64, i64, i64, p]),
+        "orc_rescale_groups": (None, [p, p, p, i64, i64, i64, p]),
         "orc_backward_input": (None, [p, i32, i64, i64, p, i64, f32, p]),
         "orc_matmul_i32": (None, [p, i64, p, i64, i64, p]),
         "orc_rescale": (None, [p, p, f32, i64, i64, p]),
@@ -162,6 +164,22 @@ def sign_trits(w: np.ndarray) -> np.ndarray:
 def quantize_weights_binary(w: np.ndarray):
     """W -> (binary trits int8 [N,K] in {-1, +1}, beta = mean|W| float32)."""
     return sign_trits(w), absmean_gamma(w)
+
+
+def group_absmean(w: np.ndarray, groups: int) -> np.ndarray:
+    """Group quantisation [LUMEN]: beta[g] = mean |w| over rows
+    g * N/groups .. (g+1) * N/groups - 1 (groups must divide N), float32 [groups]."""
+    w, dt = _as_input(w)
+    n, k = w.shape
+    assert groups >= 1 and n % groups == 0
+    beta = np.empty((groups,), dtype=np.float32)
+    _load().orc_group_absmean(_ptr(w), dt, n, k, groups, _ptr(beta))
+    return beta
+
+
+def quantize_weights_binary_groups(w: np.ndarray, groups: int):
+    """W -> (binary trits int8 [N,K] in {-1, +1}, beta float32 [groups])."""
+    return sign_trits(w), group_absmean(w, groups)
 
 
 def pack2(t: np.ndarray) -> np.ndarray:
@@ -255,6 +273,19 @@ def rescale(acc: np.ndarray, s: np.ndarray, gamma) -> np.ndarray:
     m, n = acc.shape
     y = np.empty((m, n), dtype=np.float64)
     _load().orc_rescale(_ptr(acc), _ptr(s), float(np.float32(gamma)), m, n, _ptr(y))
+    return y
+
+
+def rescale_groups(acc: np.ndarray, s: np.ndarray, beta: np.ndarray) -> np.ndarray:
+    """y[m, n] = acc[m, n] * beta[n // (N / groups)] / s[m] in float64."""
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    beta = np.ascontiguousarray(beta, dtype=np.float32)
+    m, n = acc.shape
+    groups = beta.shape[0]
+    assert n % groups == 0
+    y = np.empty((m, n), dtype=np.float64)
+    _load().orc_rescale_groups(_ptr(acc), _ptr(s), _ptr(beta), groups, m, n, _ptr(y))
     return y
 
 

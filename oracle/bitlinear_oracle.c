@@ -31,15 +31,23 @@
  *   - activation quantisation is symmetric 8-bit: s = 127 / max|x| per token,
  *     q = clamp(rint(x * s), -127, 127), computed in float (the precision of
  *     the GPU kernel, since this decides an integer); an all-zero token gets
- *     s = 1 and q = 0.
+ *     s = 1 and q = 0.  When 127 / max|x| overflows the float range (a token
+ *     whose largest magnitude is below about 3.7e-37), s is the largest
+ *     finite float instead of infinity, so q stays defined (zeros map to 0)
+ *     and acc * gamma / s stays finite.
+ *   - a NaN quotient w / gamma (gamma NaN, or w and gamma both infinite)
+ *     gives the trit 0: the comparison 2|w| > gamma it stands for is false.
  *   - accumulation is exact integer arithmetic; the output is acc * gamma / s,
  *     evaluated here in double precision.
  *   - packed layouts are the ones the library header documents (2-bit codes
  *     t+1 in 32-bit words of 16 trits; base-3 bytes of 5 trits).
  *   - variants: sign binarisation maps w < 0 to -1 and everything else (zero
- *     included) to +1, with the absmean scale of the whole matrix; b-bit
+ *     included) to +1, with the absmean scale of the whole matrix, or one
+ *     absmean scale per group of consecutive weight rows (group quantisation:
+ *     G equal shards of the output features, each scaled on its own); b-bit
  *     activations use Q = 2^(b-1) - 1 in place of 127.
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -163,6 +171,7 @@ void orc_absmean_trits(const void *w, int dtype, int64_t n_rows, int64_t k_cols,
             continue;
         }
         double r = rint(v / (double)gamma);  /* gamma == 0 gives +-inf */
+        if (r != r) r = 0.0;                 /* NaN quotient: 2|w| > gamma is false */
         if (r > 1.0) r = 1.0;
         if (r < -1.0) r = -1.0;
         t[i] = (int8_t)r;
@@ -176,6 +185,20 @@ void orc_sign_trits(const void *w, int dtype, int64_t n_rows, int64_t k_cols, in
 {
     for (int64_t i = 0; i < n_rows * k_cols; ++i)
         t[i] = load_elem(w, dtype, i) < 0.0f ? -1 : 1;
+}
+
+/* Group quantisation [LUMEN: group quantisation and normalisation let the
+ * layer be split over devices with little communication]: the N rows are cut
+ * into `groups` equal, consecutive groups (groups divides N), and group g gets
+ * its own scale beta[g] = mean |w| over its rows, formed exactly as gamma. */
+void orc_group_absmean(const void *w, int dtype, int64_t n_rows, int64_t k_cols, int64_t groups,
+                       float *beta)
+{
+    const int64_t rows = n_rows / groups;
+    const size_t esize = dtype == ORC_BF16 ? 2 : 4;
+    for (int64_t g = 0; g < groups; ++g)
+        beta[g] = orc_absmean_gamma((const char *)w + (size_t)(g * rows * k_cols) * esize, dtype,
+                                    rows, k_cols);
 }
 
 /* ---- 2-bit packing, four trits per byte [ASI, custom-software paragraph] --
@@ -289,6 +312,7 @@ void orc_quantize_act_bits(const void *x, int dtype, int64_t m_rows, int64_t k_c
                 q[m * k_cols + k] = 0;
         } else {
             float s = qmax / amax;
+            if (s > FLT_MAX) s = FLT_MAX;    /* qmax / amax overflowed */
             scale[m] = s;
             for (int64_t k = 0; k < k_cols; ++k) {
                 float r = rintf(load_elem(x, dtype, m * k_cols + k) * s);
@@ -320,6 +344,7 @@ void orc_quantize_act(const void *x, int dtype, int64_t m_rows, int64_t k_cols,
                 q[m * k_cols + k] = 0;
         } else {
             float s = 127.0f / amax;
+            if (s > FLT_MAX) s = FLT_MAX;    /* 127 / amax overflowed */
             scale[m] = s;
             for (int64_t k = 0; k < k_cols; ++k) {
                 float v = load_elem(x, dtype, m * k_cols + k) * s;
@@ -377,6 +402,18 @@ void orc_rescale(const int32_t *acc, const float *scale, float gamma, int64_t m_
         for (int64_t n = 0; n < n_rows; ++n)
             y[m * n_rows + n] =
                 (double)acc[m * n_rows + n] * (double)gamma / (double)scale[m];
+}
+
+/* The same with one weight scale per group of N / groups consecutive output
+ * features: y[m][n] = acc[m][n] * beta[n / (N / groups)] / s[m]. */
+void orc_rescale_groups(const int32_t *acc, const float *scale, const float *beta,
+                        int64_t groups, int64_t m_rows, int64_t n_rows, double *y)
+{
+    const int64_t rows = n_rows / groups;
+    for (int64_t m = 0; m < m_rows; ++m)
+        for (int64_t n = 0; n < n_rows; ++n)
+            y[m * n_rows + n] =
+                (double)acc[m * n_rows + n] * (double)beta[n / rows] / (double)scale[m];
 }
 
 /* ---- 2B-class decoder block glue, used only by the layer-stack workload ----

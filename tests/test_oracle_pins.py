@@ -225,6 +225,14 @@ def test_trit_zero_fraction_gaussian():
     assert abs(float(np.mean(t == 1)) - (1 - p0) / 2) < 5 * sd
 
 
+def test_trits_nan_quotient_gives_zero():
+    """A NaN quotient w / gamma (gamma NaN, or w and gamma both infinite) is
+    the trit 0: the comparison 2|w| > gamma it stands for is false."""
+    w = np.array([[1.0, -2.0, 0.0, np.inf, -np.inf]], np.float32)
+    assert oracle.absmean_trits(w, np.float32(np.nan)).tolist() == [[0, 0, 0, 0, 0]]
+    assert oracle.absmean_trits(w, np.float32(np.inf)).tolist() == [[0, 0, 0, 0, 0]]
+
+
 def test_trits_gamma_zero_underflow_reading():
     # gamma == 0 with a non-zero entry: w/0 is infinite and clips to sign(w)
     w = np.array([[0.0, 1e-45, -1e-45, 0.0]], np.float32)
@@ -481,6 +489,33 @@ def test_rmsnorm_and_relu2():
     np.testing.assert_array_equal(oracle.relu2_mul(g, u), np.array([0.0, 0.0, 0.5, -9.0]))
 
 
+@pytest.mark.parametrize("c,eps", [(1e-3, 1e-5), (3e-3, 1e-5), (0.5, 1e-5), (1e-4, 1e-6)])
+def test_rmsnorm_epsilon_against_decimal(c, eps):
+    """x / sqrt(mean(x^2) + eps) with eps comparable to mean(x^2), against a
+    50-digit decimal evaluation of the definition: an eps outside the square
+    root, added to the sum instead of the mean, or dropped fails here."""
+    import decimal
+    decimal.getcontext().prec = 50
+    rng = np.random.default_rng(int(c * 1e6) + 7)
+    k = 2560
+    x = c * rng.choice([-1.0, 1.0], size=(2, k)) * rng.uniform(0.25, 1.0, size=(2, k))
+    x[1] = c * np.sign(x[1])                     # constant magnitude: h = c / sqrt(c^2 + eps)
+    got = oracle.rmsnorm(x, eps)
+    for m in range(2):
+        ss = sum(decimal.Decimal(float(v)) ** 2 for v in x[m])
+        inv = 1 / (ss / k + decimal.Decimal(eps)).sqrt()
+        want = np.array([float(decimal.Decimal(float(v)) * inv) for v in x[m]])
+        np.testing.assert_allclose(got[m], want, rtol=1e-14, atol=0)
+    h_const = c / math.sqrt(c * c + eps)
+    np.testing.assert_allclose(np.abs(got[1]), h_const, rtol=1e-14)
+    # eps only rescales a token, so the codes equal those of eps = 0 and the
+    # quantiser scale carries the factor: s = 127 sqrt(mean x^2 + eps) / max|x|
+    q, s, _ = oracle.rmsnorm_quantize(x, eps)
+    q0, _, _ = oracle.rmsnorm_quantize(x, 0.0)
+    assert np.abs(q.astype(int) - q0.astype(int)).max() <= 1
+    np.testing.assert_allclose(s[1], 127.0 / h_const, rtol=1e-6)
+
+
 # ---- decoder-block glue of the layer-stack workload ---------------------------------------
 
 def test_add_f32_is_ieee_single_addition():
@@ -533,6 +568,15 @@ def test_act_bits_worked_examples():
     q, s, r = oracle.quantize_act_bits(x, 2)
     assert s[0] == np.float32(1.0) / np.float32(14.0)
     assert q.tolist() == [[1, 0, 0, 0]] and r[0] == 1
+
+
+def test_act_bits_scale_overflow_reading():
+    """4 bits, max|x| = 1e-38: 7 / 1e-38 overflows the float range, so s is
+    FLT_MAX; x s = 3.40 -> 3 and 1e-38 / 2 * s = 1.70 -> 2."""
+    x = np.array([[1e-38, -5e-39, 0.0]], dtype=np.float32)
+    q, s, r = oracle.quantize_act_bits(x, 4)
+    assert s[0] == np.finfo(np.float32).max
+    assert q.tolist() == [[3, -2, 0]] and r[0] == 1
 
 
 def test_act_bits_eight_is_the_pinned_quantiser():
@@ -646,3 +690,55 @@ def test_backward_bf16_gradients_widen_exactly():
     widened = oracle.bf16_to_f32(bits)
     np.testing.assert_array_equal(oracle.backward_input(bits, t, 1.0),
                                   oracle.backward_input(widened, t, 1.0))
+
+
+# ---- group quantisation of the sign-binarised weights ---------------------------------------
+
+def test_group_absmean_worked_example():
+    """Two groups of two rows: rows {[1, -1], [3, 3]} have mean |w| = 2, rows
+    {[0.5, 0.5], [-0.5, 0.25]} have (0.5 + 0.5 + 0.5 + 0.25) / 4 = 0.4375."""
+    w = np.array([[1, -1], [3, 3], [0.5, 0.5], [-0.5, 0.25]], dtype=np.float32)
+    beta = oracle.group_absmean(w, 2)
+    assert beta.tolist() == [2.0, 0.4375]
+    assert oracle.group_absmean(w, 4).tolist() == [1.0, 3.0, 0.5, 0.375]
+    assert oracle.group_absmean(w, 1)[0] == oracle.absmean_gamma(w)
+
+
+@pytest.mark.parametrize("groups", [1, 2, 3, 8])
+def test_group_absmean_matches_fsum_per_group(groups):
+    """beta[g] = fsum(|w| over the group's rows) / count, rounded to float."""
+    w = inputs.normal_bf16(np.random.default_rng(groups), (24, 100), 0.02)
+    wf = inputs.bf16_bits_to_f32(w).astype(np.float64)
+    beta = oracle.group_absmean(w, groups)
+    rows = 24 // groups
+    for g in range(groups):
+        blk = np.abs(wf[g * rows:(g + 1) * rows])
+        assert beta[g] == np.float32(math.fsum(blk.ravel()) / blk.size)
+    # rows permuted inside a group leave every beta unchanged; a row moved to
+    # another group changes both groups' scales
+    perm = w.copy()
+    perm[:rows] = perm[:rows][::-1]
+    np.testing.assert_array_equal(oracle.group_absmean(perm, groups), beta)
+
+
+def test_rescale_groups_against_float_brute_force():
+    """y = (q / s) (beta_g t)^T: the dequantised operands multiplied in
+    float64, each output column scaled by its group's beta."""
+    rng = np.random.default_rng(17)
+    m, n, k, groups = 3, 12, 50, 4
+    w = rng.standard_normal((n, k)).astype(np.float32) * np.float32(0.02)
+    w[4:8] *= np.float32(10.0)                    # groups of very different scale
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    t, beta = oracle.quantize_weights_binary_groups(w, groups)
+    q, s, _ = oracle.quantize_act(x)
+    y = oracle.rescale_groups(oracle.matmul_i32(q, t), s, beta)
+    col_scale = np.repeat(beta.astype(np.float64), n // groups)
+    ref = (q.astype(np.float64) / s.astype(np.float64)[:, None]) @ \
+        (t.astype(np.float64) * col_scale[:, None]).T
+    np.testing.assert_allclose(y, ref, rtol=1e-12)
+    assert beta[1] > 5 * beta[0]
+    # one group is the per-matrix rescale
+    t1, b1 = oracle.quantize_weights_binary_groups(w, 1)
+    acc = oracle.matmul_i32(q, t1)
+    np.testing.assert_array_equal(oracle.rescale_groups(acc, s, b1),
+                                  oracle.rescale(acc, s, oracle.absmean_gamma(w)))
