@@ -53,3 +53,24 @@ def test_gqa_glue_against_oracle(heads, kv_heads, head_dim):
     got = quant(bl.gqa_rmsnorm_quantize(dev(qkv), v_col, heads, kv_heads, head_dim))
     v = qkv[:, v_col:v_col + kv_heads * head_dim]
     assert_quant_close(got, oracle.rmsnorm_quantize(oracle.gqa_expand(v, heads, kv_heads)))
+
+
+@pytest.mark.parametrize("c,eps", [(1e-3, 1e-5), (3e-3, 1e-5), (1e-4, 1e-6)])
+def test_glue_epsilon_comparable_to_mean_square(c, eps):
+    """eps of the order of mean(x^2): it changes the normalised values (and so
+    the quantiser scale), for the three input forms."""
+    rng = np.random.default_rng(600 + int(c * 1e5))
+    m, k = 4, 2560
+    x = (c * rng.standard_normal((m, k))).astype(np.float32)
+    x[1] = np.float32(c) * np.sign(x[1])              # constant magnitude
+    got = quant(bl.residual_rmsnorm_quantize(dev(x), eps=eps))
+    want = oracle.rmsnorm_quantize(x, eps)
+    assert_quant_close(got, want)
+    assert abs(float(want[1][1]) - 127.0 * np.sqrt(c * c + eps) / c) <= 1e-5 * float(want[1][1])
+    gu = np.concatenate([np.abs(x) ** 0.5, x], axis=1).astype(np.float32)
+    got = quant(bl.relu2_rmsnorm_quantize(dev(gu), k, eps=eps))
+    assert_quant_close(got, oracle.rmsnorm_quantize(oracle.relu2_mul(gu[:, :k], gu[:, k:]), eps))
+    qkv = np.concatenate([x, x[:, :640]], axis=1).astype(np.float32)
+    got = quant(bl.gqa_rmsnorm_quantize(dev(qkv), k, 20, 5, 128, eps=eps))
+    want = oracle.rmsnorm_quantize(oracle.gqa_expand(qkv[:, k:k + 640], 20, 5), eps)
+    assert_quant_close(got, want)
