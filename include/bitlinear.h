@@ -79,13 +79,18 @@ typedef enum {
 } bl_layout;
 
 typedef enum {
-    BL_PATH_AUTO = 0,        /* choose by M, K and layout (the default): GEMV for
-                                PACK3 and M <= 2; SKINNY for M <= 32 when it can
-                                run the shape; else GEMV for M <= 4, MFMA above */
+    BL_PATH_AUTO = 0,        /* choose by M, N, K and layout (the default): GEMV
+                                for PACK3 and M <= 2; SKINNY for M <= 32 when it
+                                can run the shape; else GEMV for M <= 4, above
+                                that MFMA_WIDE for M >= 128 and N >= 512 with K
+                                a multiple of 16, MFMA otherwise */
     BL_PATH_GEMV = 1,        /* vector dot-product kernel, tokens in passes of 4 */
-    BL_PATH_MFMA = 2,        /* int8 matrix-core tiled kernel, any M (PACK2 only) */
-    BL_PATH_SKINNY = 3       /* int8 matrix-core weight-streaming kernel for
+    BL_PATH_MFMA = 2,        /* int8 matrix-core kernel with square-ish block
+                                tiles, any M and K (PACK2 only) */
+    BL_PATH_SKINNY = 3,      /* int8 matrix-core weight-streaming kernel for
                                 1 <= M <= 64 and K a multiple of 256 (PACK2 only) */
+    BL_PATH_MFMA_WIDE = 4    /* int8 matrix-core kernel with 64 x 512 block tiles,
+                                any M, K a multiple of 16 (PACK2 only) */
 } bl_path;
 
 #define BITLINEAR_MAX_K (1 << 20)
@@ -151,6 +156,26 @@ int bitlinear_quantize_weights_binary(const void *W, int dtype, int64_t N, int64
                                       uint8_t *packed, float *beta, void *workspace,
                                       int64_t workspace_bytes, hipStream_t stream);
 
+/* ---- weights, 1-bit variant with group quantisation (offline) ----------------
+ * [lumen-it.ai article on the original 1-bit BitNet: group quantisation and
+ *  normalisation, so that the layer splits over devices with little
+ *  communication]
+ *
+ * bitlinear_quantize_weights_binary with one scale per group: the N rows are
+ * cut into `groups` equal groups of consecutive rows (the output features a
+ * device would hold), and group g gets beta[g] = mean |W| over its rows,
+ * computed exactly as gamma.  The packed trits are those of
+ * bitlinear_quantize_weights_binary (the sign does not depend on the scale).
+ * groups   1 <= groups <= N, groups divides N (BL_ERR_SHAPE otherwise).
+ * beta     device, [groups] float, written.
+ * Each group's rows must start 16-byte aligned: (N / groups) * K * element
+ * size a multiple of 16 when groups > 1 (BL_ERR_ALIGN otherwise).  Same
+ * workspace as bitlinear_quantize_weights (the groups reuse it in turn). */
+int bitlinear_quantize_weights_binary_groups(const void *W, int dtype, int64_t N, int64_t K,
+                                             int64_t groups, int layout, uint8_t *packed,
+                                             float *beta, void *workspace,
+                                             int64_t workspace_bytes, hipStream_t stream);
+
 /* ---- activations: per-token absmax to int8 -----------------------------------
  * [cheatsheet.md BitNet b1.58 summary, "What is BitNet b1.58?", activation
  *  bullet; asi.tokyo 2B4T article, 8-bit messages; lumen-it.ai BitNet, absmax]
@@ -186,7 +211,8 @@ int bitlinear_quantize_act_bits(const void *x, int dtype, int64_t M, int64_t K, 
  *         required and must equal sum_k xq[m, k]).
  * packed, gamma      device, as written by bitlinear_quantize_weights.
  * y       device, [M, N] float, written:
- *         y[m, n] = float(acc[m, n]) * (gamma / scale[m]),
+ *         y[m, n] = acc[m, n] * (gamma / scale[m]), the factor gamma / scale[m]
+ *         formed in double precision and the product rounded once to float,
  *         acc[m, n] = sum_k t[n, k] * xq[m, k] computed exactly in int32.
  * workspace  device, >= bitlinear_forward_workspace_bytes(M, N, K, layout).
  */
@@ -201,6 +227,19 @@ int bitlinear_forward_ex(const int8_t *xq, const float *scale, const int32_t *ro
                          int64_t M, const uint8_t *packed, int layout, const float *gamma,
                          int64_t N, int64_t K, float *y, void *workspace,
                          int64_t workspace_bytes, int path, hipStream_t stream);
+
+/* bitlinear_forward_ex with one weight scale per group of N / groups
+ * consecutive output features (bitlinear_quantize_weights_binary_groups):
+ *   y[m, n] = acc[m, n] * (beta[n / (N / groups)] / scale[m]) (the factor in
+ *   double precision, the product rounded once to float).
+ * beta     device, [groups] float; groups divides N (BL_ERR_SHAPE otherwise).
+ * The product writes the exact int32 accumulators into y's memory and a
+ * second kernel rescales them in place (two launches).  Other arguments,
+ * workspace and errors as for bitlinear_forward_ex. */
+int bitlinear_forward_groups(const int8_t *xq, const float *scale, const int32_t *rowsum,
+                             int64_t M, const uint8_t *packed, int layout, const float *beta,
+                             int64_t groups, int64_t N, int64_t K, float *y, void *workspace,
+                             int64_t workspace_bytes, int path, hipStream_t stream);
 
 /* The same kernels without the rescale: acc[m, n] = sum_k t[n, k] * xq[m, k]
  * as int32 (device, [M, N]).  path as in bitlinear_forward_ex. */
@@ -334,6 +373,47 @@ int bitlinear_forward_relu2_rmsnorm_quantize(const int8_t *xq, const float *scal
                                              float *scale_out, int32_t *rowsum_out,
                                              void *workspace, int64_t workspace_bytes,
                                              hipStream_t stream);
+
+/* ---- one token: the next BitLinear's input glue and product in one launch -------
+ * [asi.tokyo 2B4T article, stabiliser paragraph: a norm in front of the
+ *  sub-layers, squared ReLU in the feed-forward block; cheatsheet.md summary,
+ *  "What is BitNet b1.58?": RMSNorm, no bias, activations scaled per token;
+ *  asi.tokyo packing paragraph: the 2-bit product]
+ *
+ * For one token (decode) every block of the 2-bit vector product forms the
+ * token's pre-norm values v itself, applies RMSNorm with unit gain in double
+ * precision (h = v / sqrt(mean v^2 + eps) rounded to float; the sum of squares
+ * is reduced in another order than a sequential loop, as in the glue calls),
+ * quantises h with the arithmetic of bitlinear_quantize_act into an on-chip
+ * int8 copy, and multiplies: no int8 token goes through memory.
+ *
+ * input    BL_NORM_RESIDUAL: src is the float residual stream [K]; with add
+ *          (float [K]) not NULL, v = src + add in float, stored to x_out
+ *          (float [K], required then; it must not overlap src or add: the
+ *          launch's blocks all read src); with add NULL, v = src.
+ *          BL_NORM_GQA: v is the first token's attention output under
+ *          grouped-query attention, v[h * head_dim + d] =
+ *          src[v_col + (h / (heads / kv_heads)) * head_dim + d] (src: the float
+ *          QKV output row), K = heads * head_dim.
+ *          BL_NORM_F64: src is a double [K] (the relu2 output below).
+ * packed, gamma  the 2-bit weights [N, K] and their gamma (BL_PACK2 layout).
+ * relu2 = 0: out is float [N], out[n] = acc[n] * (gamma / s) as in
+ *          bitlinear_forward.
+ * relu2 = 1: packed is a fused up/gate matrix, gate rows [0, F) and up rows
+ *          [F, 2F), N = 2F; out is double [F], out[i] = relu(y_gate)^2 * y_up
+ *          in double, with y_gate = y[i] and y_up = y[F + i] rounded to float
+ *          as the product stores them.
+ * xq, scale, rowsum  optional outputs (may be NULL): the quantised token
+ *          [K], its scale and row sum, as bitlinear_quantize_act writes them.
+ * 1 <= K <= 16384, N >= 1, eps >= 0; float pointers 4-byte aligned, double
+ * pointers 8-byte aligned, packed 16-byte aligned.  One launch. */
+typedef enum { BL_NORM_RESIDUAL = 0, BL_NORM_GQA = 1, BL_NORM_F64 = 2 } bl_norm_input;
+
+int bitlinear_norm_forward(int input, const void *src, const float *add, float *x_out,
+                           int64_t v_col, int64_t heads, int64_t kv_heads, int64_t head_dim,
+                           int64_t K, float eps, const uint8_t *packed, const float *gamma,
+                           int64_t N, int relu2, void *out, int8_t *xq, float *scale,
+                           int32_t *rowsum, hipStream_t stream);
 
 /* Decode packed weights to int8 trits in {-1, 0, 1} (device, [N, K]). */
 int bitlinear_unpack_weights(const uint8_t *packed, int layout, int64_t N, int64_t K,

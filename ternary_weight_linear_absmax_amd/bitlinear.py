@@ -21,7 +21,8 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "bitlinear.h")
 BL_OK = 0
 BL_F32, BL_BF16 = 0, 1
 BL_PACK2, BL_PACK3 = 0, 1
-BL_PATH_AUTO, BL_PATH_GEMV, BL_PATH_MFMA, BL_PATH_SKINNY = 0, 1, 2, 3
+BL_PATH_AUTO, BL_PATH_GEMV, BL_PATH_MFMA, BL_PATH_SKINNY, BL_PATH_MFMA_WIDE = 0, 1, 2, 3, 4
+BL_NORM_RESIDUAL, BL_NORM_GQA, BL_NORM_F64 = 0, 1, 2
 MAX_K = 1 << 20
 
 _lib = None
@@ -59,6 +60,10 @@ def load():
         "bitlinear_quantize_act": (i32, [p, i32, i64, i64, p, p, p, p]),
         "bitlinear_quantize_weights_binary": (i32, [p, i32, i64, i64, i32, p, p, p, i64, p]),
         "bitlinear_quantize_act_bits": (i32, [p, i32, i64, i64, i32, p, p, p, p]),
+        "bitlinear_quantize_weights_binary_groups": (i32, [p, i32, i64, i64, i64, i32, p, p, p,
+                                                           i64, p]),
+        "bitlinear_forward_groups": (i32, [p, p, p, i64, p, i32, p, i64, i64, i64, p, p, i64,
+                                           i32, p]),
         "bitlinear_backward_input": (i32, [p, i32, i64, i64, p, i32, p, i64, p, p]),
         "bitlinear_forward": (i32, [p, p, p, i64, p, i32, p, i64, i64, p, p, i64, p]),
         "bitlinear_forward_ex": (i32, [p, p, p, i64, p, i32, p, i64, i64, p, p, i64, i32, p]),
@@ -71,6 +76,8 @@ def load():
         "bitlinear_quantize_forward": (i32, [p, i32, i64, i64, p, p, p, p, i32, p, i64, p, p, i64,
                                              i32, p]),
         "bitlinear_forward_glue_workspace_bytes": (i64, [i64, i64, i64]),
+        "bitlinear_norm_forward": (i32, [i32, p, p, p, i64, i64, i64, i64, i64, ctypes.c_float, p,
+                                         p, i64, i32, p, p, p, p, p]),
         "bitlinear_forward_residual_rmsnorm_quantize": (
             i32, [p, p, p, i64, i64, p, p, i64, p, ctypes.c_float, p, p, p, p, i64, p]),
         "bitlinear_forward_gqa_rmsnorm_quantize": (
@@ -175,6 +182,47 @@ def quantize_weights(w: torch.Tensor, layout: int = BL_PACK2, stream=None, binar
     _check(getattr(lib, name)(_ptr(w), _dtype_code(w), n, k, layout, _ptr(packed), _ptr(gamma),
                               _ptr(ws), ws.numel(), _stream(stream)), name)
     return packed, gamma
+
+
+def quantize_weights_binary_groups(w: torch.Tensor, groups: int, layout: int = BL_PACK2,
+                                   stream=None, out=None, workspace: torch.Tensor = None):
+    """Sign binariser with one scale per group of N / groups rows:
+    w [N, K] -> (packed uint8 [N, row_bytes], beta float32 [groups])."""
+    lib = load()
+    assert w.dim() == 2 and w.is_contiguous()
+    n, k = w.shape
+    if out is None:
+        packed = torch.empty((n, packed_row_bytes(k, layout)), dtype=torch.uint8, device=w.device)
+        beta = torch.empty((groups,), dtype=torch.float32, device=w.device)
+    else:
+        packed, beta = out
+    ws = workspace
+    if ws is None:
+        ws = torch.empty((max(quantize_weights_workspace_bytes(n, k), 16),), dtype=torch.uint8,
+                         device=w.device)
+    _check(lib.bitlinear_quantize_weights_binary_groups(
+        _ptr(w), _dtype_code(w), n, k, groups, layout, _ptr(packed), _ptr(beta), _ptr(ws),
+        ws.numel(), _stream(stream)), "bitlinear_quantize_weights_binary_groups")
+    return packed, beta
+
+
+def forward_groups(xq, scale, rowsum, packed, beta, n: int, k: int, layout: int = BL_PACK2,
+                   path: int = BL_PATH_AUTO, y=None, workspace=None, stream=None):
+    """y [M, N] float32 = (xq . t^T) * beta[group of n] / scale."""
+    lib = load()
+    m = xq.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
+    ws_bytes = forward_workspace_bytes(m, n, k, layout)
+    if workspace is None and ws_bytes > 0:
+        workspace = _zero_workspace(ws_bytes, xq.device)
+    _check(lib.bitlinear_forward_groups(_ptr(xq), _ptr(scale), _ptr(rowsum), m, _ptr(packed),
+                                        layout, _ptr(beta), beta.numel(), n, k, _ptr(y),
+                                        _ptr(workspace),
+                                        0 if workspace is None else workspace.numel(), path,
+                                        _stream(stream)),
+           "bitlinear_forward_groups")
+    return y
 
 
 def quantize_act(x: torch.Tensor, stream=None, bits: int = 8):
@@ -380,6 +428,27 @@ def forward_relu2_rmsnorm_quantize(xq, scale, rowsum, packed, gamma, n: int, f: 
     return xq_out, scale_out, rowsum_out
 
 
+def norm_forward(src: torch.Tensor, packed, gamma, n: int, input: int = BL_NORM_RESIDUAL,
+                 add=None, x_out=None, v_col: int = 0, heads: int = 1, kv_heads: int = 1,
+                 head_dim: int = 1, k: int = None, eps: float = 1e-5, relu2: bool = False,
+                 out=None, xq=None, scale=None, rowsum=None, stream=None):
+    """One token: the input glue (residual / first-token GQA / double input),
+    RMSNorm and quantisation, then the 2-bit product, in one launch
+    (bitlinear_norm_forward).  Returns out: float [N], or with relu2 double
+    [N/2] = relu(gate)^2 * up."""
+    if k is None:
+        k = heads * head_dim if input == BL_NORM_GQA else src.numel()
+    dev_ = src.device
+    if out is None:
+        out = torch.empty((n // 2,) if relu2 else (n,), dtype=torch.float64 if relu2 else
+                          torch.float32, device=dev_)
+    _check(load().bitlinear_norm_forward(
+        input, _ptr(src), _ptr(add), _ptr(x_out), v_col, heads, kv_heads, head_dim, k, eps,
+        _ptr(packed), _ptr(gamma), n, int(relu2), _ptr(out), _ptr(xq), _ptr(scale), _ptr(rowsum),
+        _stream(stream)), "bitlinear_norm_forward")
+    return out
+
+
 def unpack_weights(packed, n: int, k: int, layout: int = BL_PACK2, stream=None):
     lib = load()
     trits = torch.empty((n, k), dtype=torch.int8, device=packed.device)
@@ -392,6 +461,9 @@ def unpack_weights(packed, n: int, k: int, layout: int = BL_PACK2, stream=None):
 bitlinear_quantize_weights = quantize_weights
 bitlinear_quantize_act = quantize_act
 bitlinear_forward = forward
+bitlinear_quantize_weights_binary_groups = quantize_weights_binary_groups
+bitlinear_forward_groups = forward_groups
+bitlinear_norm_forward = norm_forward
 bitlinear_matmul_i32 = matmul_i32
 bitlinear_unpack_weights = unpack_weights
 bitlinear_quantize_forward = quantize_forward

@@ -50,11 +50,15 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
+// weight loads: non-temporal (1) or cached (0)
+#ifndef GEMM_B_NT
+#define GEMM_B_NT 1
+#endif
+
 constexpr int BK = 128;
 constexpr int LDA = BK + 16;            // padded LDS row (bytes)
 constexpr int NXCD = 8;
 
-__device__ inline uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
 // Global -> register load of this thread's pieces of the [BM x BK] A tile.
 // AL (K a multiple of 16): every load is issued unconditionally from a clamped,
@@ -155,7 +159,7 @@ __device__ __forceinline__ void ld_b(uint4 (&r)[WN], const uint8_t *bbase,
 {
     const uint8_t *p = bbase + (int64_t)(kt < nfull ? kt : nfull - 1) * (BK / 4);
 #pragma unroll
-    for (int s = 0; s < WN; ++s) r[s] = load_nt16(p + boff[s]);
+    for (int s = 0; s < WN; ++s) r[s] = GEMM_B_NT ? load_nt16(p + boff[s]) : load16(p + boff[s]);
 }
 
 template <int BM>
@@ -180,6 +184,7 @@ __device__ __forceinline__ void st_a(uint8_t *lds_buf, const uint4 (&r)[BM / 32]
 #ifndef GEMM_NB
 #define GEMM_NB 4
 #endif
+
 
 // Stages after which every register/LDS ring is back at slot 0.
 constexpr int ring_period(int na, int nb)
@@ -211,20 +216,20 @@ constexpr int ep_tile_bytes() { return BM * (BN + 4) * 4; }
 // Row operands of rows m0 .. m0 + BM - 1 (clamped), by threads 0 .. BM - 1.
 template <int BM>
 __device__ inline void ep_rows(int tid, int64_t m0, int64_t m, const int32_t *rowsum,
-                               const Out &out, int mode, int32_t *ep_rs, float *ep_gs)
+                               const Out &out, int mode, int32_t *ep_rs, double *ep_gs)
 {
     if (tid >= BM || mode == EP_PARTIAL) return;
     int64_t gm = m0 + tid;
     gm = gm < m ? gm : m - 1;
     ep_rs[tid] = rowsum[gm];
-    ep_gs[tid] = mode == EP_Y ? out.gamma[0] / out.scale[gm] : 0.0f;
+    ep_gs[tid] = mode == EP_Y ? epi_gs(out.gamma[0], out.scale[gm]) : 0.0;
 }
 
 // Lane (l32, h) of math wave (wm, wn), register r of acc[a][s]: row
 // 32 WM wm + 32 a + 8 (r / 4) + 4 h + r % 4, column 32 WN wn + 32 s + l32.
 template <int WM, int WN>
 __device__ inline void ep_put(int32_t *tile, const v16i (&acc)[WM][WN], int wm, int wn, int h,
-                              int l32, const int32_t *ep_rs, const float *ep_gs, int mode)
+                              int l32, const int32_t *ep_rs, const double *ep_gs, int mode)
 {
     constexpr int LT = 64 * WN + 4;
 #pragma unroll
@@ -233,12 +238,12 @@ __device__ inline void ep_put(int32_t *tile, const v16i (&acc)[WM][WN], int wm, 
         for (int r = 0; r < 16; ++r) {
             const int row = wm * 32 * WM + 32 * a + 8 * (r / 4) + 4 * h + (r % 4);
             const int32_t rs = mode == EP_PARTIAL ? 0 : ep_rs[row];
-            const float gs = mode == EP_Y ? ep_gs[row] : 0.0f;
+            const double gs = mode == EP_Y ? ep_gs[row] : 0.0;
 #pragma unroll
             for (int s = 0; s < WN; ++s) {
                 const int32_t v = acc[a][s][r] - rs;
                 tile[row * LT + wn * 32 * WN + 32 * s + l32] =
-                    mode == EP_Y ? __float_as_int((float)v * gs) : v;
+                    mode == EP_Y ? __float_as_int(epi_y(v, gs)) : v;
             }
         }
 }
@@ -278,7 +283,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
     constexpr bool LDS_EP = ep_tile_bytes<BM, BN>() <= 2 * BM * LDA;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM * LDA];
     __shared__ int32_t ep_rs[BM];
-    __shared__ float ep_gs[BM];
+    __shared__ double ep_gs[BM];
     const int64_t t = tile_of_block(blockIdx.x, per_xcd);
     if (t >= tiles * splits) return;
     const int64_t tile = t / splits;
@@ -467,13 +472,13 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
 #pragma unroll
     for (int a = 0; a < WM; ++a) {
         int32_t rs[16];
-        float gs[16];
+        double gs[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             int64_t gm = m0 + wm * 32 * WM + 32 * a + 8 * (r / 4) + 4 * h + (r % 4);
             gm = gm < m ? gm : m - 1;
             rs[r] = rowsum[gm];
-            gs[r] = out.acc ? 0.0f : gamma / out.scale[gm];
+            gs[r] = out.acc ? 0.0 : epi_gs(gamma, out.scale[gm]);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -485,7 +490,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
                 if (out.acc)
                     out.acc[gm * ldy + nrow[s]] = v;
                 else
-                    out.y[gm * ldy + nrow[s]] = (float)v * gs[r];
+                    out.y[gm * ldy + nrow[s]] = epi_y(v, gs[r]);
             }
         }
     }
@@ -524,7 +529,7 @@ __global__ __launch_bounds__(512) void gemm3_kernel(const int8_t *__restrict__ x
     constexpr int PB = (BN * 2 + 255) / 256;                      // weight pieces / producer
     __shared__ __attribute__((aligned(16))) uint8_t lds[G3_NS * SS];
     __shared__ int32_t ep_rs[BM];
-    __shared__ float ep_gs[BM];
+    __shared__ double ep_gs[BM];
     static_assert(ep_tile_bytes<BM, BN>() <= G3_NS * SS, "the output tile fits the LDS ring");
     const int64_t t = tile_of_block(blockIdx.x, per_xcd);
     if (t >= tiles * splits) return;
@@ -539,10 +544,20 @@ __global__ __launch_bounds__(512) void gemm3_kernel(const int8_t *__restrict__ x
     const int kt0 = split * stages_per;
     const int kt1 = kt0 + stages_per < nk_total ? kt0 + stages_per : nk_total;
     const int nk = kt1 - kt0;
-    if (nk <= 0) return;
+    const int ep_mode = splits > 1 ? EP_PARTIAL : out.acc ? EP_ACC : EP_Y;
+    if (nk <= 0) {
+        // an empty k slice still stores its partial tile (zeros): the finish
+        // adds every slice, and the workspace has no required contents
+        if (ep_mode == EP_PARTIAL) {
+            int32_t *tl = (int32_t *)lds;
+            for (int e = threadIdx.x; e < BM * (BN + 4); e += 512) tl[e] = 0;
+            __syncthreads();
+            ep_store<BM, BN>(tl, threadIdx.x, 512, m0, n0, m, n, ws + (int64_t)split * m * n, n);
+        }
+        return;
+    }
     constexpr int U3 = G3_NS * R / gcd_int(G3_NS, R);
     constexpr int U = U3 % 2 == 0 ? U3 : 2 * U3;   // ring slots and fragment parity fixed per J
-    const int ep_mode = splits > 1 ? EP_PARTIAL : out.acc ? EP_ACC : EP_Y;
 
     if (producer) {
         const int pt = threadIdx.x - 256;
@@ -584,7 +599,7 @@ __global__ __launch_bounds__(512) void gemm3_kernel(const int8_t *__restrict__ x
             for (int i = 0; i < PB; ++i) {
                 int64_t byte = k0 / 4 + bhalf[i];
                 byte = byte + 16 <= pitch ? byte : pitch - 16;
-                b[i] = load_nt16(packed + boff[i] + byte);
+                b[i] = GEMM_B_NT ? load_nt16(packed + boff[i] + byte) : load16(packed + boff[i] + byte);
             }
         };
         auto lstore = [&](const uint4 (&a)[PA], const uint4 (&b)[PB], int st)
@@ -732,9 +747,9 @@ __global__ __launch_bounds__(256) void splitk_finish4_kernel(const int32_t *__re
         else
             for (int j = 0; j < 4; ++j) d[j] = a[j];
     } else {
-        const float gs = out.gamma[0] / out.scale[gm];
+        const double gs = epi_gs(out.gamma[0], out.scale[gm]);
         float *d = out.y + gm * ldy + gn;
-        const float f[4] = {(float)a[0] * gs, (float)a[1] * gs, (float)a[2] * gs, (float)a[3] * gs};
+        const float f[4] = {epi_y(a[0], gs), epi_y(a[1], gs), epi_y(a[2], gs), epi_y(a[3], gs)};
         if (vec) *(float4 *)d = make_float4(f[0], f[1], f[2], f[3]);
         else
             for (int j = 0; j < 4; ++j) d[j] = f[j];
@@ -759,11 +774,13 @@ hipError_t launch_splitk_finish(const int32_t *ws, const int32_t *rowsum, int64_
     return hipGetLastError();
 }
 
-// Kernel configuration of the GEMM for (M, N, K).
-struct GemmCfg { int wm, wn, splits; };
+// Kernel configuration of the GEMM for (M, N, K): the square-ish tiles of
+// gemm2 / gemm3 (wm x wn blocks of 64), or the wide-tile kernel.
+struct GemmCfg { int wm, wn, splits; bool wide; };
 
-GemmCfg gemm_config(int64_t m, int64_t n, int64_t k)
+GemmCfg gemm_config(int64_t m, int64_t n, int64_t k, int variant = GEMM_TILED)
 {
+    if (variant == GEMM_WIDE) return {0, 0, gemm_wide_splits(m, n, k), true};
     // Chosen from timings of every tile / split combination on the 2B-, 3B-
     // and 70B-class shapes.  M <= 64, or a product with few 64 x 64 tiles:
     // 64 x 64 tiles, the k range split (up to four ways, at least six stages
@@ -780,16 +797,16 @@ GemmCfg gemm_config(int64_t m, int64_t n, int64_t k)
         int64_t sp = t11 < 192 ? 256 / t11 : 1;   // splits: up to 4, >= 6 stages each
         if (sp > 4) sp = 4;
         if (sp > nk / 6) sp = nk / 6;
-        return {1, 1, (int)(sp < 1 ? 1 : sp)};
+        return {1, 1, (int)(sp < 1 ? 1 : sp), false};
     }
     const int64_t t22 = tiles(2, 2);
-    if (t22 >= 192 && t22 <= 256) return {2, 2, 1};
-    if (t22 > 256 && t22 < 512) return {1, 2, 1};
-    if (t22 >= 512) return {2, 2, 1};
+    if (t22 >= 192 && t22 <= 256) return {2, 2, 1, false};
+    if (t22 > 256 && t22 < 512) return {1, 2, 1, false};
+    if (t22 >= 512) return {2, 2, 1, false};
     int64_t sp = 256 / t22;
     if (sp > 8) sp = 8;
     if (sp > nk / 4) sp = nk / 4;
-    return {2, 2, (int)(sp < 1 ? 1 : sp)};
+    return {2, 2, (int)(sp < 1 ? 1 : sp), false};
 }
 
 // Row / column blocks of a product whose operands exceed 32-bit offsets.
@@ -805,8 +822,15 @@ static void gemm_chunks(int64_t m, int64_t n, int64_t k, int64_t &mc, int64_t &n
     if (nc < 1) nc = 1;
 }
 
+// The GEMM variant AUTO takes: the wide tiles for products of at least 128
+// tokens and 512 weight rows with K a multiple of 16.
+int gemm_preferred_variant(int64_t m, int64_t n, int64_t k)
+{
+    return (k % 16 == 0 && m >= 128 && n >= 512) ? GEMM_WIDE : GEMM_TILED;
+}
+
 // One int32 partial tile per split: splits x M x N (largest over the blocks).
-int64_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k)
+int64_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int variant)
 {
     int64_t mc, nc, need = 0;
     gemm_chunks(m, n, k, mc, nc);
@@ -814,7 +838,7 @@ int64_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k)
         for (int64_t n0 = 0; n0 < n; n0 += nc) {
             const int64_t mb = m - m0 < mc ? m - m0 : mc;
             const int64_t nb = n - n0 < nc ? n - n0 : nc;
-            const GemmCfg c = gemm_config(mb, nb, k);
+            const GemmCfg c = gemm_config(mb, nb, k, variant);
             const int64_t b = c.splits > 1 ? 4 * c.splits * mb * nb : 0;
             need = b > need ? b : need;
         }
@@ -857,7 +881,7 @@ hipError_t launch_gemm_cfg(const int8_t *xq, const int32_t *rowsum, int64_t m,
 
 hipError_t launch_gemm_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
                              const uint8_t *packed, int64_t n, int64_t k, Out out, void *ws,
-                             hipStream_t s)
+                             hipStream_t s, int variant)
 {
     // The kernel addresses each operand with 32-bit per-lane offsets: larger
     // operands are processed in blocks of rows of x and of weight rows.
@@ -872,13 +896,15 @@ hipError_t launch_gemm_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
             if (o.scale) o.scale += m0;
             if (o.y) o.y += m0 * n + n0;
             if (o.acc) o.acc += m0 * n + n0;
-            const GemmCfg c = gemm_config(mb, nb, k);
+            const GemmCfg c = gemm_config(mb, nb, k, variant);
             int32_t *w = (int32_t *)ws;
             const int8_t *x = xq + m0 * k;
             const int32_t *rs = rowsum + m0;
             const uint8_t *pk = packed + n0 * pitch;
             hipError_t e;
-            if (c.wm == 2 && c.wn == 2)
+            if (c.wide)
+                e = launch_gemm_wide(x, rs, mb, pk, nb, k, o, c.splits, w, s, n, true);
+            else if (c.wm == 2 && c.wn == 2)
                 e = launch_gemm_cfg<2, 2>(x, rs, mb, pk, nb, k, o, c.splits, w, s, n);
             else if (c.wm == 1 && c.wn == 2)
                 e = launch_gemm_cfg<1, 2>(x, rs, mb, pk, nb, k, o, c.splits, w, s, n);
@@ -894,31 +920,32 @@ hipError_t launch_gemm_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
 
 // Tiles and k split of a product whose split partial sums the next kernel
 // finishes (no finish launch to pay for).
-static GemmCfg gemm_partial_config(int64_t m, int64_t n, int64_t k)
+static GemmCfg gemm_partial_config(int64_t m, int64_t n, int64_t k, int variant)
 {
-    return gemm_config(m, n, k);
+    return gemm_config(m, n, k, variant);
 }
 
-int gemm_partial_splits(int64_t m, int64_t n, int64_t k)
+int gemm_partial_splits(int64_t m, int64_t n, int64_t k, int variant)
 {
     int64_t mc, nc;
     gemm_chunks(m, n, k, mc, nc);
     if (mc < m || nc < n) return 0;
-    const GemmCfg c = gemm_partial_config(m, n, k);
+    const GemmCfg c = gemm_partial_config(m, n, k, variant);
     return c.splits > 1 ? c.splits : 0;
 }
 
-int64_t gemm_partial_workspace_bytes(int64_t m, int64_t n, int64_t k)
+int64_t gemm_partial_workspace_bytes(int64_t m, int64_t n, int64_t k, int variant)
 {
-    const int sp = gemm_partial_splits(m, n, k);
+    const int sp = gemm_partial_splits(m, n, k, variant);
     return sp > 1 ? 4 * (int64_t)sp * m * n : 0;
 }
 
 hipError_t launch_gemm_pack2_partials(const int8_t *xq, const int32_t *rowsum, int64_t m,
                                       const uint8_t *packed, int64_t n, int64_t k, Out out,
-                                      int32_t *ws, hipStream_t s)
+                                      int32_t *ws, hipStream_t s, int variant)
 {
-    const GemmCfg c = gemm_partial_config(m, n, k);
+    const GemmCfg c = gemm_partial_config(m, n, k, variant);
+    if (c.wide) return launch_gemm_wide(xq, rowsum, m, packed, n, k, out, c.splits, ws, s, n, false);
     if (c.wm == 2 && c.wn == 2)
         return launch_gemm_cfg<2, 2>(xq, rowsum, m, packed, n, k, out, c.splits, ws, s, n, false);
     if (c.wm == 1 && c.wn == 2)

@@ -22,8 +22,6 @@
 namespace bl {
 namespace {
 
-__device__ inline uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
-
 // One packed word (16 trits) against the 16 matching activation bytes.
 __device__ inline void dot_word(uint32_t w, uint4 x, int &lo, int &hi)
 {
@@ -38,85 +36,11 @@ __device__ inline void dot_word(uint32_t w, uint4 x, int &lo, int &hi)
     hi = __builtin_amdgcn_sdot4(u3, (int)x.w, hi, false);
 }
 
-// Four values quantised with the activation quantiser's arithmetic
-// (rint(x s) clamped to +-127, as quant1) and packed into the bytes of one
-// word, value a in the lowest byte.
-__device__ inline uint32_t quant4(float a, float b, float c, float d, float s)
-{
-    auto q = [&](float x) __attribute__((always_inline)) {
-        return (uint32_t)(int)__builtin_amdgcn_fmed3f(rintf(x * s), -127.0f, 127.0f);
-    };
-    const uint32_t ab = __builtin_amdgcn_perm(q(b), q(a), 0x0c0c0400u);   // a, b in bytes 0, 1
-    const uint32_t cd = __builtin_amdgcn_perm(q(d), q(c), 0x0c0c0400u);
-    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
-}
-
-// Nibble form of 16 activation bytes for the 4-bit dot products: x = 16 hi + lo
-// with lo = x & 15 (unsigned) and hi = x >> 4 (signed).  Byte j of l02 holds
-// lo(x[j]) | lo(x[8 + j]) << 4, of h02 the two hi nibbles, and l13 / h13 the
-// same for x[4 + j] and x[12 + j]: the nibble order of a packed word masked
-// with 0x33333333 (codes of k = j and 8 + j) or shifted by 2 first (4 + j,
-// 12 + j).
-__device__ inline uint4 nibble_split(uint4 x)
-{
-    uint4 r;
-    r.x = (x.x & 0x0F0F0F0Fu) | ((x.z & 0x0F0F0F0Fu) << 4);          // l02
-    r.y = ((x.x >> 4) & 0x0F0F0F0Fu) | (x.z & 0xF0F0F0F0u);          // h02
-    r.z = (x.y & 0x0F0F0F0Fu) | ((x.w & 0x0F0F0F0Fu) << 4);          // l13
-    r.w = ((x.y >> 4) & 0x0F0F0F0Fu) | (x.w & 0xF0F0F0F0u);          // h13
-    return r;
-}
-
-// One packed word (16 trits) against 16 activation bytes in nibble form:
-// 4-bit dot products of the codes with the signed high nibbles (ah) and the
-// unsigned low nibbles (al); the word's sum is 16 ah + al.  7 ALU operations.
-__device__ inline void dot8_word(uint32_t w, uint4 xs, int &ah, uint32_t &al)
-{
-    const uint32_t c02 = w & 0x33333333u, c13 = (w >> 2) & 0x33333333u;
-    ah = __builtin_amdgcn_sdot8((int)c02, (int)xs.y, ah, false);
-    ah = __builtin_amdgcn_sdot8((int)c13, (int)xs.w, ah, false);
-    al = __builtin_amdgcn_udot8(c02, xs.x, al, false);
-    al = __builtin_amdgcn_udot8(c13, xs.z, al, false);
-}
-
 template <int LG>
 __device__ inline int group_sum(int v)
 {
 #pragma unroll
     for (int off = LG / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
-
-// Sum over the 64 lanes of a wave with DPP row operations; lane 63 holds the
-// result.
-__device__ inline int wave_sum_dpp(int v)
-{
-    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-    v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
-    v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
-    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
-    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
-    return v;
-}
-
-// Maximum of non-negative floats over the wave, same DPP pattern (disabled
-// lanes contribute 0, the identity here); lane 63 holds the result.
-template <int CTRL, int ROWS>
-__device__ inline float max_dpp_step(float v)
-{
-    const int t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false);
-    return fmaxf(v, __int_as_float(t));
-}
-
-__device__ inline float wave_max_dpp(float v)
-{
-    v = max_dpp_step<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
-    v = max_dpp_step<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
-    v = max_dpp_step<0x141, 0xF>(v);   // row_half_mirror
-    v = max_dpp_step<0x140, 0xF>(v);   // row_mirror
-    v = max_dpp_step<0x142, 0xA>(v);   // row_bcast:15
-    v = max_dpp_step<0x143, 0xC>(v);   // row_bcast:31
     return v;
 }
 
@@ -254,10 +178,10 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
     const int nout = wr * RB * MT;
     const int e_rr = threadIdx.x / MT, e_t = threadIdx.x % MT;
     int32_t e_rs = 0;
-    float e_gs = 0.0f;
+    double e_gs = 0.0;
     if (!FUSED && threadIdx.x < nout) {
         e_rs = rowsum[m0 + e_t];
-        if (!out.acc) e_gs = out.gamma[0] / out.scale[m0 + e_t];
+        if (!out.acc) e_gs = epi_gs(out.gamma[0], out.scale[m0 + e_t]);
     }
 
     uint4 xv[MT][CPL][4];
@@ -343,7 +267,7 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
                 const int64_t e0 = 64 * coff[j] + 16 * d;   // K % 16 == 0: pieces are whole
                 xv[0][j][d] = (ok[j] && e0 < k) ? q_lds[e0 / 16] : zero4();
             }
-        if (!out.acc) e_gs = gamma / q_s;
+        if (!out.acc) e_gs = epi_gs(gamma, q_s);
     }
 #pragma unroll
     for (int t = 0; t < MT; ++t)
@@ -391,7 +315,7 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
         if (out.acc)
             out.acc[idx] = acc;
         else
-            out.y[idx] = (float)acc * e_gs;
+            out.y[idx] = epi_y(acc, e_gs);
     }
 }
 
@@ -446,13 +370,13 @@ __global__ __launch_bounds__(256) void gemv3_kernel(const int8_t *__restrict__ x
     if (row >= n) return;
     int acc[MT];
     int32_t e_rs[MT];
-    float e_gs[MT];
+    double e_gs[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         acc[t] = 0;
         // epilogue operands, loaded before the weight stream starts
         e_rs[t] = rowsum[m0 + t];
-        e_gs[t] = out.acc ? 0.0f : out.gamma[0] / out.scale[m0 + t];
+        e_gs[t] = out.acc ? 0.0 : epi_gs(out.gamma[0], out.scale[m0 + t]);
     }
 
     for (int64_t c = lane; c < chunks; c += LG) {
@@ -505,7 +429,7 @@ __global__ __launch_bounds__(256) void gemv3_kernel(const int8_t *__restrict__ x
         if (out.acc)
             out.acc[(m0 + t) * ldy + row] = a;
         else
-            out.y[(m0 + t) * ldy + row] = (float)a * e_gs[t];
+            out.y[(m0 + t) * ldy + row] = epi_y(a, e_gs[t]);
     }
 }
 
@@ -607,10 +531,10 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv3lut_kernel(
 
     const int e_rr = threadIdx.x;
     int32_t e_rs = 0;
-    float e_gs = 0.0f;
+    double e_gs = 0.0;
     if (threadIdx.x < wr * RB) {
         e_rs = rowsum[m0];
-        if (!out.acc) e_gs = out.gamma[0] / out.scale[m0];
+        if (!out.acc) e_gs = epi_gs(out.gamma[0], out.scale[m0]);
     }
 
     // Activations of this lane's chunks (80 each), prearranged; pieces past K
@@ -658,7 +582,7 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv3lut_kernel(
         if (out.acc)
             out.acc[idx] = acc;
         else
-            out.y[idx] = (float)acc * e_gs;
+            out.y[idx] = epi_y(acc, e_gs);
     }
 }
 
@@ -829,6 +753,223 @@ hipError_t launch3(bool al, const int8_t *xq, const int32_t *rowsum, int64_t n, 
     return hipGetLastError();
 }
 
+
+// ---- one token with the decoder block's glue inside (prologue / epilogue) ----
+// Every block forms the token's pre-norm values v itself (NORM_RESIDUAL: the
+// residual stream plus the previous product's output, the sum stored once by
+// block 0; NORM_GQA: the value vectors of the first token's attention,
+// expanded over the query heads; NORM_F64: double values from a squared-ReLU
+// epilogue), applies RMSNorm with unit gain in double precision, rounds to
+// float and quantises with the activation quantiser's arithmetic into an LDS
+// copy of the int8 token; then the 2-bit GEMV of the block's rows runs as in
+// gemv2_kernel.  RELU2: the weight rows are taken as interleaved pairs,
+// logical row 2i = gate row i and 2i + 1 = up row i of the packed up/gate
+// matrix, and the block writes v[i] = relu(y_gate)^2 * y_up in double (y as
+// the product would store it) instead of y.
+template <int PRO, bool RELU2, int CPL, int ST, int EPT>
+__global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv_norm_kernel(
+    NormArgs a, int64_t k, const uint4 *__restrict__ packed, int64_t n, int64_t chunks,
+    int64_t share, Out out, int ks)
+{
+    constexpr int R = GEMV_R, RB = GEMV_R * ST;
+    __shared__ int part[GEMV_KS_MAX][GEMV_KS_MAX * RB];
+    __shared__ double red_d[GEMV_KS_MAX];
+    __shared__ float red_f[GEMV_KS_MAX];
+    __shared__ int red_i[GEMV_KS_MAX];
+    extern __shared__ uint4 q_lds[];   // the int8 token, K bytes (rounded up to 16)
+    const int nthr = (int)blockDim.x, nw = nthr >> 6;
+    const int wr = nw / ks;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kw = wave % ks, rw = wave / ks;
+    const int64_t blk0 = (int64_t)blockIdx.x * wr * RB;
+    const int64_t row0 = blk0 + (int64_t)rw * RB;
+    const int kk = (int)k;
+
+    int64_t coff[CPL];
+    bool ok[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int64_t c = kw * share + lane + 64 * j;
+        ok[j] = (lane + 64 * j < share) && c < chunks;
+        coff[j] = ok[j] ? c : 0;
+    }
+    // logical row -> packed row (RELU2: gate / up pairs)
+    auto phys = [&](int64_t row) __attribute__((always_inline)) {
+        row = row < n ? row : n - 1;
+        return RELU2 ? ((row & 1) ? a.f + (row >> 1) : (row >> 1)) : row;
+    };
+    // weight loads of the first steps go out before the token work
+    constexpr int PF = GEMV_PF < ST ? GEMV_PF : ST;
+    uint4 w[PF + 1][R][CPL];
+    auto load = [&](uint4(&wb)[R][CPL], int s) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t row = phys(row0 + s * R + r);
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) wb[r][j] = load_nt16(packed + row * chunks + coff[j]);
+        }
+    };
+    double v[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int i = threadIdx.x + nthr * j, ic = i < kk ? i : kk - 1;
+        if (PRO == NORM_RESIDUAL) {
+            const float *x = (const float *)a.src;
+            const float xv = a.add ? x[ic] + a.add[ic] : x[ic];
+            if (a.add && blockIdx.x == 0 && i < kk) a.x_out[i] = xv;
+            v[j] = (double)xv;
+        } else if (PRO == NORM_GQA) {
+            const unsigned hd = (unsigned)a.head_dim, head = (unsigned)ic / hd;
+            const unsigned d = (unsigned)ic - head * hd;
+            v[j] = (double)((const float *)a.src)[a.col + (int64_t)(head / (unsigned)a.group) * hd + d];
+        } else {
+            v[j] = ((const double *)a.src)[ic];
+        }
+        if (i >= kk) v[j] = 0.0;
+    }
+#pragma unroll
+    for (int q = 0; q < PF; ++q) load(w[q], q);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // RMSNorm: sum of squares in double over the block
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) ss += v[j] * v[j];
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    if (lane == 0) red_d[wave] = ss;
+    __syncthreads();
+    ss = 0.0;
+    for (int q = 0; q < nw; ++q) ss += red_d[q];
+    const double inv = 1.0 / sqrt(ss / (double)k + a.eps);
+    float h[EPT];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        h[j] = (float)(v[j] * inv);
+        amax = fmaxf(amax, fabsf(h[j]));
+    }
+    amax = wave_max_dpp(amax);
+    if (lane == 63) red_f[wave] = amax;
+    __syncthreads();
+    amax = 0.0f;
+    for (int q = 0; q < nw; ++q) amax = fmaxf(amax, red_f[q]);
+    const float qs = act_scale(amax);
+    int sum = 0;
+    int8_t *ql = (int8_t *)q_lds;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int i = threadIdx.x + nthr * j;
+        if (i >= kk) continue;
+        const int8_t q = quant1(h[j], qs);
+        sum += q;
+        ql[i] = q;
+        if (a.xq && blockIdx.x == 0) a.xq[i] = q;
+    }
+    // zero the pad bytes of the last 16-byte piece
+    if ((int)threadIdx.x < (16 - (kk & 15)) % 16) ql[kk + threadIdx.x] = 0;
+    sum = wave_sum_dpp(sum);
+    if (lane == 63) red_i[wave] = sum;
+    __syncthreads();
+    int e_rs = 0;
+    for (int q = 0; q < nw; ++q) e_rs += red_i[q];
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (a.scale) a.scale[0] = qs;
+        if (a.rowsum) a.rowsum[0] = e_rs;
+    }
+
+    uint4 xv[CPL][4];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const int64_t e0 = 64 * coff[j] + 16 * d;
+            xv[j][d] = (ok[j] && e0 < k) ? nibble_split(q_lds[e0 / 16]) : zero4();
+        }
+
+#pragma unroll
+    for (int s = 0; s < ST; ++s) {
+        if (s + PF < ST) load(w[(s + PF) % (PF + 1)], s + PF);
+        __builtin_amdgcn_sched_barrier(0);
+        const int b = s % (PF + 1);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            int ah = 0;
+            uint32_t al = 0;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                dot8_word(w[b][r][j].x, xv[j][0], ah, al);
+                dot8_word(w[b][r][j].y, xv[j][1], ah, al);
+                dot8_word(w[b][r][j].z, xv[j][2], ah, al);
+                dot8_word(w[b][r][j].w, xv[j][3], ah, al);
+            }
+            const int vsum = wave_sum_dpp(16 * ah + (int)al);
+            if (lane == 63) part[kw][rw * RB + s * R + r] = vsum;
+        }
+    }
+    __syncthreads();
+    const int nout = wr * RB;
+    const double gs = epi_gs(out.gamma[0], qs);
+    const int e_rr = threadIdx.x;
+    if (RELU2) {
+        // thread e_rr < nout / 2 finishes the pair of logical rows 2 e_rr, 2 e_rr + 1
+        if (e_rr < nout / 2 && blk0 + 2 * e_rr + 1 < n) {
+            int sg = 0, su = 0;
+            for (int q = 0; q < ks; ++q) {
+                sg += part[q][2 * e_rr];
+                su += part[q][2 * e_rr + 1];
+            }
+            const float yg = epi_y(sg - e_rs, gs), yu = epi_y(su - e_rs, gs);
+            const double gd = yg > 0.0f ? (double)yg : 0.0;
+            a.v[(blk0 >> 1) + e_rr] = gd * gd * (double)yu;
+        }
+    } else if (e_rr < nout && blk0 + e_rr < n) {
+        int vsum = 0;
+        for (int q = 0; q < ks; ++q) vsum += part[q][e_rr];
+        out.y[blk0 + e_rr] = epi_y(vsum - e_rs, gs);
+    }
+}
+
+template <int PRO, bool RELU2, int CPL, int ST>
+hipError_t launch_norm_ept(const NormArgs &a, int64_t n, int64_t k, const uint8_t *packed,
+                           Out out, const Gemv2Shape &sh, hipStream_t s)
+{
+    const int64_t chunks = pack2_pitch(k) / 16;
+    const int64_t rb = (int64_t)GEMV_R * ST * sh.wr;
+    const dim3 grid((unsigned)((n + rb - 1) / rb)), block((unsigned)(64 * sh.ks * sh.wr));
+    const size_t lds = (size_t)((k + 15) / 16) * 16;
+    const int64_t per = (k + 64 * sh.ks * sh.wr - 1) / (64 * sh.ks * sh.wr);
+#define NORM_CASE(E_)                                                                           \
+    if (per <= E_) {                                                                            \
+        hipLaunchKernelGGL((gemv_norm_kernel<PRO, RELU2, CPL, ST, E_>), grid, block, lds, s, a, \
+                           k, (const uint4 *)packed, n, chunks, sh.share, out, sh.ks);          \
+        return hipGetLastError();                                                               \
+    }
+    NORM_CASE(4) NORM_CASE(8) NORM_CASE(16) NORM_CASE(32)
+#undef NORM_CASE
+    return hipErrorInvalidValue;
+}
+
+template <int PRO, bool RELU2, int CPL>
+hipError_t launch_norm_cpl(const NormArgs &a, int64_t n, int64_t k, const uint8_t *packed,
+                           Out out, const Gemv2Shape &sh, hipStream_t s)
+{
+    switch (sh.st) {
+    case 1: return launch_norm_ept<PRO, RELU2, CPL, 1>(a, n, k, packed, out, sh, s);
+    case 2: return launch_norm_ept<PRO, RELU2, CPL, 2>(a, n, k, packed, out, sh, s);
+    case 4: return launch_norm_ept<PRO, RELU2, CPL, 4>(a, n, k, packed, out, sh, s);
+    default: return launch_norm_ept<PRO, RELU2, CPL, 8>(a, n, k, packed, out, sh, s);
+    }
+}
+
+template <int PRO, bool RELU2>
+hipError_t launch_norm_pro(const NormArgs &a, int64_t n, int64_t k, const uint8_t *packed,
+                           Out out, hipStream_t s)
+{
+    const Gemv2Shape sh = gemv2_fused_shape(n, pack2_pitch(k) / 16);
+    if (sh.cpl == 1) return launch_norm_cpl<PRO, RELU2, 1>(a, n, k, packed, out, sh, s);
+    return launch_norm_cpl<PRO, RELU2, 2>(a, n, k, packed, out, sh, s);
+}
+
 }  // namespace
 
 hipError_t launch_gemv_pack2(const int8_t *xq, const int32_t *rowsum, int64_t m,
@@ -881,9 +1022,18 @@ hipError_t launch_gemv_pack2_fused(const void *x, int dtype, int8_t *xq, float *
     return launch2_fused_cpl<2>(dtype, fq, n, k, packed, out, sh, s);
 }
 
-hipError_t launch_gemv_pack3(const int8_t *xq, const int32_t *rowsum, int64_t m,
-                             const uint8_t *packed, int64_t n, int64_t k, Out out, hipStream_t s)
+int64_t gemv3_workspace_bytes(int64_t m, int64_t n, int64_t k)
 {
+    return gemv3sum_workspace_bytes(m, n, k);
+}
+
+hipError_t launch_gemv_pack3(const int8_t *xq, const int32_t *rowsum, int64_t m,
+                             const uint8_t *packed, int64_t n, int64_t k, Out out, void *ws,
+                             hipStream_t s)
+{
+    // one token on a matrix of many rows: partial-sum tables per group of five
+    if (gemv3sum_slices(m, n, k) > 0)
+        return launch_gemv3sum(xq, rowsum, packed, n, k, out, (int32_t *)ws, s);
     const bool al = (k % 16) == 0;
     const int64_t chunks3 = pack3_pitch(k) / 16;
     if (m == 1 && al && chunks3 <= (int64_t)GEMV_KS_MAX * 128) {
@@ -915,6 +1065,31 @@ hipError_t launch_gemv_pack3(const int8_t *xq, const int32_t *rowsum, int64_t m,
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+}  // namespace bl
+
+namespace bl {
+
+bool gemv_norm_supported(int64_t n, int64_t k)
+{
+    if (n < 1 || k < 1 || k > NORM_MAX_K) return false;
+    const Gemv2Shape sh = gemv2_fused_shape(n, pack2_pitch(k) / 16);
+    return k <= (int64_t)64 * sh.ks * sh.wr * 32;
+}
+
+hipError_t launch_gemv_norm(const NormArgs &a, int64_t n, int64_t k, const uint8_t *packed,
+                            Out out, bool relu2, hipStream_t s)
+{
+    if (!gemv_norm_supported(n, k)) return hipErrorInvalidValue;
+    if (relu2) {
+        if (a.pro == NORM_RESIDUAL) return launch_norm_pro<NORM_RESIDUAL, true>(a, n, k, packed, out, s);
+        if (a.pro == NORM_GQA) return launch_norm_pro<NORM_GQA, true>(a, n, k, packed, out, s);
+        return launch_norm_pro<NORM_F64, true>(a, n, k, packed, out, s);
+    }
+    if (a.pro == NORM_RESIDUAL) return launch_norm_pro<NORM_RESIDUAL, false>(a, n, k, packed, out, s);
+    if (a.pro == NORM_GQA) return launch_norm_pro<NORM_GQA, false>(a, n, k, packed, out, s);
+    return launch_norm_pro<NORM_F64, false>(a, n, k, packed, out, s);
 }
 
 }  // namespace bl

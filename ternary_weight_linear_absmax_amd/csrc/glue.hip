@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void glue_kernel(GlueArgs a, int64_t k, double
         constexpr int U0 = 64 / (EPT * NSRC);
         constexpr int U = U0 < 1 ? 1 : U0 > 4 ? 4 : U0;
         const int32_t prs = a.p_rowsum[m];
-        const float gs = a.p_gamma[0] / a.p_scale[m];
+        const double gs = epi_gs(a.p_gamma[0], a.p_scale[m]);
         const int32_t *row = a.part + m * a.ld;
         const int64_t slice = a.pm * a.ld;
         int col[NSRC][EPT];
@@ -136,10 +136,10 @@ __global__ __launch_bounds__(256) void glue_kernel(GlueArgs a, int64_t k, double
 #pragma clang fp contract(off)
 #pragma unroll
             for (int j = 0; j < EPT; ++j) {
-                const float y0 = (float)(acc[0][j] - prs) * gs;
+                const float y0 = epi_y(acc[0][j] - prs, gs);
                 if (MODE == GLUE_RESIDUAL) f1[j] = y0;
                 else f0[j] = y0;
-                if (NSRC == 2) f1[j] = (float)(acc[NSRC - 1][j] - prs) * gs;
+                if (NSRC == 2) f1[j] = epi_y(acc[NSRC - 1][j] - prs, gs);
             }
         }
     } else {

@@ -90,14 +90,14 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(const int8_t *__restric
     }
     const int8_t *xrow[TG];
     int32_t e_rs[TG];
-    float e_g[TG];
+    double e_g[TG];
 #pragma unroll
     for (int g = 0; g < TG; ++g) {
         const int64_t tok = 16 * g + r < m ? 16 * g + r : m - 1;
         xrow[g] = xq + tok * k + 64 * b;
         // epilogue operands of this lane's tokens, loaded before the stream
         e_rs[g] = rowsum[tok];
-        e_g[g] = out.acc ? 0.0f : out.gamma[0] / out.scale[tok];
+        e_g[g] = out.acc ? 0.0 : epi_gs(out.gamma[0], out.scale[tok]);
     }
 
     // Step c covers chunks CH c .. CH c + CH - 1, so the four k-block lanes of
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(const int8_t *__restric
                 if (out.acc)
                     out.acc[tok * ldy + row0 + q] = v;
                 else
-                    out.y[tok * ldy + row0 + q] = (float)v * e_g[g];
+                    out.y[tok * ldy + row0 + q] = epi_y(v, e_g[g]);
             }
         }
     }
@@ -422,13 +422,13 @@ __global__ __launch_bounds__(256) void skinny2_kernel(const int8_t *__restrict__
             else
                 for (int j = 0; j < 4 && row + j < n; ++j) dst[j] = a[j];
         } else {
-            const float gs = out.gamma[0] / out.scale[tok];
+            const double gs = epi_gs(out.gamma[0], out.scale[tok]);
             float *dst = out.y + tok * ldy + row;
             float4 f;
-            f.x = (float)(v[0] - rs) * gs;
-            f.y = (float)(v[1] - rs) * gs;
-            f.z = (float)(v[2] - rs) * gs;
-            f.w = (float)(v[3] - rs) * gs;
+            f.x = epi_y(v[0] - rs, gs);
+            f.y = epi_y(v[1] - rs, gs);
+            f.z = epi_y(v[2] - rs, gs);
+            f.w = epi_y(v[3] - rs, gs);
             if (vec && row + 3 < n) *(float4 *)dst = f;
             else {
                 const float fa[4] = {f.x, f.y, f.z, f.w};

@@ -26,6 +26,21 @@ call (bitlinear_forward_*_rmsnorm_quantize): where the GEMM splits its k
 range, the glue kernel finishes the split partial sums itself, so the product
 output is never stored and the finishing launch disappears.  The results are
 bit for bit those of the unfused sequence.
+
+With one token (M = 1) and `norm` set, each BitLinear takes its input glue as
+a prologue instead (bitlinear_norm_forward: residual / GQA / double input,
+RMSNorm and quantisation inside the product's blocks) and the up/gate product
+applies relu(gate)^2 * up as its epilogue, so a layer is four launches:
+
+    qkv = BitLinear_qkv(quant(RMSNorm(x += d)))            residual prologue
+    o   = BitLinear_o(quant(RMSNorm(GQA-expand(V))))        GQA prologue
+    v   = relu2(BitLinear_up_gate(quant(RMSNorm(x += o))))  residual prologue, relu2 epilogue
+    d   = BitLinear_down(quant(RMSNorm(v)))                 double-input prologue
+
+The residual stream alternates between two buffers (a launch reads the one
+and writes the sum to the other).  The RMSNorm sums are reduced in another
+order than the glue kernel's, so the result matches the glue sequence up to
+rounding edges of the norm, not bit for bit.
 """
 from __future__ import annotations
 
@@ -46,10 +61,13 @@ class DecoderStack:
     """Packed weights of `layers` layers plus the activation buffers of M
     tokens, all resident on the GPU."""
 
-    def __init__(self, layer_weights, layers: int, m: int, device="cuda", fused: bool = True):
+    def __init__(self, layer_weights, layers: int, m: int, device="cuda", fused: bool = True,
+                 norm: bool = False):
         """layer_weights(l) -> dict name -> [N, K] bf16/fp32 tensor on the GPU
-        (quantised and packed here, then released)."""
-        self.layers, self.m, self.fused = layers, m, fused
+        (quantised and packed here, then released).  norm: one token, glue as
+        the products' prologue (M = 1 only)."""
+        assert not norm or m == 1, "the prologue form takes one token"
+        self.layers, self.m, self.fused, self.norm = layers, m, fused, norm
         self.packed, self.gamma = [], []
         for layer in range(layers):
             w = layer_weights(layer)
@@ -66,6 +84,9 @@ class DecoderStack:
         self.xq = torch.empty((m, FFN), dtype=torch.int8, device=device)
         self.scale = torch.empty((m,), **f32)
         self.rowsum = torch.empty((m,), dtype=torch.int32, device=device)
+        if norm:
+            self.x_alt = torch.zeros((m, HIDDEN), **f32)
+            self.v64 = torch.empty((FFN,), dtype=torch.float64, device=device)
 
     def packed_bytes(self) -> int:
         return sum(p.numel() for layer in self.packed for p in layer.values())
@@ -131,10 +152,37 @@ class DecoderStack:
         self._linear(layer, "down", FFN)
         note("down")
 
+    def _norm_step(self):
+        """One token, four launches per layer (prologue / epilogue forms)."""
+        cur, alt = self.x, self.x_alt
+        add = None
+        for layer in range(self.layers):
+            p, g = self.packed[layer], self.gamma[layer]
+            if add is None:
+                bl.norm_forward(cur, p["qkv"], g["qkv"], QKV, out=self.y["qkv"])
+            else:
+                bl.norm_forward(cur, p["qkv"], g["qkv"], QKV, add=add, x_out=alt,
+                                out=self.y["qkv"])
+                cur, alt = alt, cur
+            bl.norm_forward(self.y["qkv"], p["o"], g["o"], HIDDEN, bl.BL_NORM_GQA, v_col=V_COL,
+                            heads=HEADS, kv_heads=KV_HEADS, head_dim=HEAD_DIM, out=self.y["o"])
+            bl.norm_forward(cur, p["up_gate"], g["up_gate"], 2 * FFN, add=self.y["o"], x_out=alt,
+                            relu2=True, out=self.v64)
+            cur, alt = alt, cur
+            bl.norm_forward(self.v64, p["down"], g["down"], HIDDEN, bl.BL_NORM_F64,
+                            out=self.y["down"])
+            add = self.y["down"]
+        # last residual addition (and the quantised RMSNorm of the output)
+        bl.residual_rmsnorm_quantize(cur, add, EPS, **self._q(HIDDEN))
+        if cur.data_ptr() != self.x.data_ptr():
+            self.x.copy_(cur)
+
     def step(self):
         """All layers on the current residual stream self.x, then the last
         residual addition; self.x holds the stack's output (and xq / scale /
         rowsum its quantised RMSNorm)."""
+        if self.norm:
+            return self._norm_step()
         if self.fused:
             bl.residual_rmsnorm_quantize(self.x, None, EPS, **self._q(HIDDEN))
         for layer in range(self.layers):

@@ -26,6 +26,26 @@ def test_every_header_function_is_exported(lib):
         assert hasattr(lib, name), name
 
 
+def test_ceilings_library_exports_its_header():
+    """The benchmark's measured-ceiling kernels (a library of their own)."""
+    import re
+    path = os.path.join(os.path.dirname(bl.LIB_PATH), "libbitlinear_ceilings.so")
+    if not os.path.exists(path):
+        build_lib.build()
+    clib = ctypes.CDLL(path)
+    header = os.path.join(os.path.dirname(bl.HEADER), "bitlinear_ceilings.h")
+    names = sorted(set(re.findall(r"\b(blc_\w+)\s*\(", open(header).read())))
+    assert len(names) == 4
+    for name in names:
+        assert hasattr(clib, name), name
+    clib.blc_mfma_i8_ops.restype = ctypes.c_int64
+    assert clib.blc_mfma_i8_ops(10, 3) == 3 * 4 * 8 * 10 * 65536
+    clib.blc_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    assert clib.blc_read_stream(P, 15, 1, P, None) == -1        # not whole 16-byte vectors
+    assert clib.blc_read_stream(ODD, 64, 1, P, None) == -1      # misaligned
+
+
 def test_size_queries_match_the_layout_definitions(lib):
     for k in (1, 15, 16, 64, 65, 256, 2560, 6912, 8192, 28672):
         assert bl.packed_row_bytes(k, bl.BL_PACK2) == oracle.pack2_pitch(k)
@@ -38,8 +58,9 @@ def test_size_queries_match_the_layout_definitions(lib):
     assert bl.quantize_weights_workspace_bytes(28672, 8192) == 128 * 2048
     assert bl.quantize_weights_workspace_bytes(0, 64) == 0
     assert bl.forward_workspace_bytes(512, 8640, 3200) >= 0
-    # skinny path with its k range split four ways: 4 * 4 * M * N bytes
-    assert bl.forward_workspace_bytes(16, 8192, 28672) == 4 * 4 * 16 * 8192
+    # the largest need over the paths a caller may force: at least the skinny
+    # path's k range split four ways (4 * 4 * M * N bytes)
+    assert bl.forward_workspace_bytes(16, 8192, 28672) >= 4 * 4 * 16 * 8192
     # a split-k shape: one int32 [M, N] partial tile per split
     ws = bl.forward_workspace_bytes(64, 128, 4096)
     assert ws > 0 and ws % (4 * 64 * 128) == 0
@@ -50,7 +71,9 @@ def test_path_selection(lib):
     assert bl.forward_path(16, 28672, 8192) == bl.BL_PATH_SKINNY
     assert bl.forward_path(16, 8640, 3200) == bl.BL_PATH_MFMA     # K % 256 != 0
     assert bl.forward_path(64, 3840, 2560) == bl.BL_PATH_MFMA
-    assert bl.forward_path(512, 8640, 3200) == bl.BL_PATH_MFMA
+    assert bl.forward_path(512, 8640, 3200) == bl.BL_PATH_MFMA_WIDE
+    assert bl.forward_path(512, 8640, 3208) == bl.BL_PATH_MFMA      # K % 16 != 0
+    assert bl.forward_path(128, 28672, 8192) == bl.BL_PATH_MFMA_WIDE
     assert bl.forward_path(1, 28672, 8192, bl.BL_PACK3) == bl.BL_PATH_GEMV
 
 
@@ -158,6 +181,9 @@ def test_forward_argument_checks(lib):
     assert call(lay=bl.BL_PACK3, path=bl.BL_PATH_MFMA) == -8
     assert call(lay=bl.BL_PACK3, path=bl.BL_PATH_SKINNY) == -8
     assert call(path=bl.BL_PATH_SKINNY) == -8              # K = 64 is not a multiple of 256
+    assert call(k=72, path=bl.BL_PATH_MFMA_WIDE) == -8      # K % 16 != 0
+    assert call(lay=bl.BL_PACK3, path=bl.BL_PATH_MFMA_WIDE) == -8
+    assert call(path=5) == -8
     assert call(m=65, k=256, path=bl.BL_PATH_SKINNY) == -8  # more than 64 tokens
     assert call(k=0) == -2
     assert call(m=-1) == -2
@@ -260,3 +286,27 @@ def test_fused_product_glue_argument_checks(lib):
     h = lib.bitlinear_forward_relu2_rmsnorm_quantize
     assert h(P, P, P, 4, 2560, P, P, 13823, 6912, 1e-5, P, P, P, P, 1 << 30, None) == -2
     assert h(P, P, P, 4, 2560, P, P, 13824, 6912, 1e-5, P, P, P, NULL, 1 << 30, None) == -1
+
+
+def test_group_argument_checks(lib):
+    fq = lib.bitlinear_quantize_weights_binary_groups
+
+    def q(W=P, dt=bl.BL_BF16, n=8, k=64, groups=2, lay=0, pk=P, beta=P, ws=P, wsb=1 << 20):
+        return fq(W, dt, n, k, groups, lay, pk, beta, ws, wsb, None)
+
+    assert q(groups=0) == -2 and q(groups=3) == -2 and q(groups=9) == -2
+    assert q(W=NULL) == -1 and q(beta=NULL) == -1
+    assert q(dt=5) == -4 and q(lay=4) == -5
+    assert q(beta=ODD) == -3
+    assert q(n=2, k=4, groups=2) == -3                      # second group starts 8 bytes in
+    assert q(wsb=0) == -6
+    ff = lib.bitlinear_forward_groups
+
+    def fwd(m=4, n=8, groups=2, beta=P, y=P, lay=0, path=0):
+        return ff(P, P, P, m, P, lay, beta, groups, n, 64, y, NULL, 0, path, None)
+
+    assert fwd(groups=0) == -2 and fwd(groups=3) == -2
+    assert fwd(beta=NULL) == -1 and fwd(y=NULL) == -1
+    assert fwd(beta=ODD) == -3
+    assert fwd(lay=9) == -5
+    assert fwd(m=0) == 0 and fwd(n=0, groups=1) == 0

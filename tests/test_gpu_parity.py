@@ -13,7 +13,7 @@ import oracle
 from ternary_weight_linear_absmax_amd import bitlinear as bl
 from ternary_weight_linear_absmax_amd import inputs
 
-from gpu_helpers import assert_y_close, dev, host, oracle_weights
+from gpu_helpers import assert_y_close, dev, host, oracle_matmul_rows, oracle_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -40,6 +40,8 @@ def run_case(w: np.ndarray, x: np.ndarray, layout: int, paths=(bl.BL_PATH_AUTO,)
     for path in paths:
         if path == bl.BL_PATH_SKINNY and not skinny_ok(m, k):
             continue
+        if path == bl.BL_PATH_MFMA_WIDE and k % 16 != 0:
+            continue
         acc = bl.matmul_i32(xq, rowsum, packed, n, k, layout, path=path)
         np.testing.assert_array_equal(host(acc), acc_ref, err_msg=f"path {path}")
         y = bl.forward(xq, scale, rowsum, packed, gamma, n, k, layout, path=path)
@@ -52,7 +54,8 @@ def skinny_ok(m, k):
 
 def all_paths(layout):
     if layout == bl.BL_PACK2:
-        return (bl.BL_PATH_AUTO, bl.BL_PATH_GEMV, bl.BL_PATH_MFMA, bl.BL_PATH_SKINNY)
+        return (bl.BL_PATH_AUTO, bl.BL_PATH_GEMV, bl.BL_PATH_MFMA, bl.BL_PATH_SKINNY,
+                bl.BL_PATH_MFMA_WIDE)
     return (bl.BL_PATH_AUTO, bl.BL_PATH_GEMV)
 
 
@@ -88,7 +91,7 @@ def test_skinny_shapes(m, n, k):
     """Weight-streaming matrix-core path: ragged N and M, every row-block /
     wave split and token-group count."""
     w, x = inputs.random_case(20_000 + m * 7 + n * 13 + k, m, n, k, bf16=True)
-    run_case(w, x, bl.BL_PACK2, (bl.BL_PATH_SKINNY, bl.BL_PATH_MFMA))
+    run_case(w, x, bl.BL_PACK2, (bl.BL_PATH_SKINNY, bl.BL_PATH_MFMA, bl.BL_PATH_MFMA_WIDE))
     if m <= 16:
         assert bl.forward_path(m, n, k) == (bl.BL_PATH_GEMV if m <= 2 else bl.BL_PATH_SKINNY)
 
@@ -117,6 +120,21 @@ def test_base3_one_token_shapes(n, k):
     chunks of 80 trits that run past K, one and two chunks per lane."""
     w, x = inputs.random_case(50_000 + n + k, 1, n, k, bf16=True)
     run_case(w, x, bl.BL_PACK3, (bl.BL_PATH_AUTO,))
+
+
+@pytest.mark.parametrize("n,k", [(4096, 16), (4100, 1296), (6001, 6400), (4097, 12801),
+                                 (8192, 1280), (5000, 2561)])
+def test_base3_partial_sum_tables(n, k):
+    """Base-3 GEMV for one token on matrices of many rows: per-group tables
+    of partial sums, the k range in slices of 256 packed bytes (one slice, a
+    short last slice, K not a multiple of 16 or of 5), slices added by the
+    split-k finish."""
+    w, x = inputs.random_case(51_000 + n + k, 1, n, k, bf16=True)
+    x[0, :7] = 0
+    run_case(w, x, bl.BL_PACK3, (bl.BL_PATH_AUTO,))
+    assert bl.forward_workspace_bytes(1, n, k, bl.BL_PACK3) == (
+        4 * n * ((bl.packed_row_bytes(k, bl.BL_PACK3) + 255) // 256)
+        if bl.packed_row_bytes(k, bl.BL_PACK3) > 256 else 0)
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
@@ -164,7 +182,7 @@ def test_repeated_calls_are_bit_identical():
     packed, gamma = bl.quantize_weights(dev(w))
     xq, scale, rowsum = bl.quantize_act(dev(x))
     n, k = w.shape
-    for path in (bl.BL_PATH_GEMV, bl.BL_PATH_MFMA, bl.BL_PATH_SKINNY):
+    for path in (bl.BL_PATH_GEMV, bl.BL_PATH_MFMA, bl.BL_PATH_SKINNY, bl.BL_PATH_MFMA_WIDE):
         ys = [host(bl.forward(xq, scale, rowsum, packed, gamma, n, k, path=path)) for _ in range(3)]
         assert all(np.array_equal(ys[0].view(np.uint32), v.view(np.uint32)) for v in ys[1:])
 
@@ -183,12 +201,13 @@ def test_decode_shapes_m1_base3(shape):
     run_case(w, x, bl.BL_PACK3)
 
 
-# ---- prefill shapes of the 3B-class model, M = 512 (sampled tokens) ------------------------
+# ---- prefill shapes of the 3B-class model, M = 512 (every output) ---------------------------
 
 @pytest.mark.parametrize("shape", range(len(inputs.PREFILL_SHAPES)))
-def test_prefill_shapes_m512_sampled(shape):
+def test_prefill_shapes_m512_all_rows(shape):
     _, w, x = inputs.prefill(shape)
     n, k = w.shape
+    print(f"prefill shape {shape}: M=512 N={n} K={k}", flush=True)
     t, g, packed_ref = oracle_weights(w, bl.BL_PACK2)
     q_ref, s_ref, r_ref = oracle.quantize_act(x)
     packed, gamma = bl.quantize_weights(dev(w))
@@ -200,12 +219,9 @@ def test_prefill_shapes_m512_sampled(shape):
     np.testing.assert_array_equal(host(rowsum), r_ref)
     acc = host(bl.matmul_i32(xq, rowsum, packed, n, k))
     y = host(bl.forward(xq, scale, rowsum, packed, gamma, n, k))
-    rng = np.random.default_rng(99)
-    rows = np.sort(rng.choice(512, size=12, replace=False))
-    rows[0], rows[-1] = 0, 511
-    acc_ref = oracle.matmul_i32(q_ref[rows], t)
-    np.testing.assert_array_equal(acc[rows], acc_ref)
-    assert_y_close(y[rows], oracle.rescale(acc_ref, s_ref[rows], g), acc_ref)
+    acc_ref = oracle_matmul_rows(q_ref, t)
+    np.testing.assert_array_equal(acc, acc_ref)
+    assert_y_close(y, oracle.rescale(acc_ref, s_ref, g), acc_ref)
     # the zero fraction the generator produces (30% forced near zero)
     zero_frac = float(np.mean(t == 0))
     assert 0.40 < zero_frac < 0.50
@@ -228,13 +244,130 @@ def test_tiled_gemm_block_shapes(m, n, k):
     packed, gamma = bl.quantize_weights(dev(w))
     np.testing.assert_array_equal(host(packed), packed_ref)
     xq, scale, rowsum = bl.quantize_act(dev(x))
-    assert bl.forward_path(m, n, k) == bl.BL_PATH_MFMA
-    acc = host(bl.matmul_i32(xq, rowsum, packed, n, k))
-    y = host(bl.forward(xq, scale, rowsum, packed, gamma, n, k))
+    assert bl.forward_path(m, n, k) in (bl.BL_PATH_MFMA, bl.BL_PATH_MFMA_WIDE)
     rows = np.array(sorted(r for r in {0, 1, 63, 64, 127, 128, m // 2, m - 2, m - 1} if r < m))
     acc_ref = oracle.matmul_i32(q_ref[rows], t)
-    np.testing.assert_array_equal(acc[rows], acc_ref)
-    assert_y_close(y[rows], oracle.rescale(acc_ref, s_ref[rows], g), acc_ref)
+    for path in (bl.BL_PATH_MFMA, bl.BL_PATH_MFMA_WIDE):
+        acc = host(bl.matmul_i32(xq, rowsum, packed, n, k, path=path))
+        y = host(bl.forward(xq, scale, rowsum, packed, gamma, n, k, path=path))
+        np.testing.assert_array_equal(acc[rows], acc_ref, err_msg=f"path {path}")
+        assert_y_close(y[rows], oracle.rescale(acc_ref, s_ref[rows], g), acc_ref)
+
+
+@pytest.mark.parametrize("m,n,k,cfg", [
+    (256, 12288, 256, "128 x 128 tiles, one round of the CUs"),
+    (256, 16640, 256, "64 x 128 tiles"),
+    (256, 6144, 1024, "128 x 128 tiles, k range split in two"),
+    (300, 12400, 272, "128 x 128 tiles, ragged M, N and K"),
+])
+def test_tiled_gemm_configs_every_output(m, n, k, cfg):
+    """Every output of each tile configuration of the tiled GEMM (every
+    accumulator register row of every tile), against the oracle."""
+    w, x = inputs.random_case(71_000 + m + n + k, m, n, k, bf16=True)
+    t, g, _ = oracle_weights(w, bl.BL_PACK2)
+    q_ref, s_ref, _ = oracle.quantize_act(x)
+    packed, gamma = bl.quantize_weights(dev(w))
+    xq, scale, rowsum = bl.quantize_act(dev(x))
+    acc_ref = oracle_matmul_rows(q_ref, t)
+    for path in (bl.BL_PATH_MFMA, bl.BL_PATH_MFMA_WIDE):
+        acc = host(bl.matmul_i32(xq, rowsum, packed, n, k, path=path))
+        np.testing.assert_array_equal(acc, acc_ref, err_msg=f"{cfg}, path {path}")
+        y = host(bl.forward(xq, scale, rowsum, packed, gamma, n, k, path=path))
+        assert_y_close(y, oracle.rescale(acc_ref, s_ref, g), acc_ref)
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (300, 1100, 272),      # three stages (below the unrolled loop), ragged everything
+    (130, 5000, 2000),     # k range split in two, sixteen stages
+    (64, 513, 4096),       # two tiles, k range split four ways, one valid column
+    (200, 700, 16),        # one 16-value stage
+    (150, 777, 512),       # rows of an odd number of floats (element-wise stores)
+    (1, 600, 640), (33, 2049, 1040), (512, 8640, 3200),
+])
+def test_wide_gemm_every_output(m, n, k):
+    """The wide-tile GEMM (64 x 512 block tiles) on every output: partial
+    token, column and k tiles, split k slices, stage counts inside and outside
+    the unrolled loop."""
+    w, x = inputs.random_case(74_000 + m + n + k, m, n, k, bf16=True)
+    t, g, _ = oracle_weights(w, bl.BL_PACK2)
+    q_ref, s_ref, _ = oracle.quantize_act(x)
+    packed, gamma = bl.quantize_weights(dev(w))
+    xq, scale, rowsum = bl.quantize_act(dev(x))
+    acc_ref = oracle_matmul_rows(q_ref, t)
+    acc = host(bl.matmul_i32(xq, rowsum, packed, n, k, path=bl.BL_PATH_MFMA_WIDE))
+    np.testing.assert_array_equal(acc, acc_ref)
+    y = host(bl.forward(xq, scale, rowsum, packed, gamma, n, k, path=bl.BL_PATH_MFMA_WIDE))
+    assert_y_close(y, oracle.rescale(acc_ref, s_ref, g), acc_ref)
+
+
+def test_tiled_gemm_operands_beyond_32_bit_offsets():
+    """M * K >= 2^31 bytes of activations: the GEMM runs in blocks of rows
+    whose per-lane offsets fit 32 bits.  Activations drawn on the GPU (4 GB of
+    bf16) and quantised there; rows around the block boundary and a sample of
+    others are checked against the oracle on the int8 rows the GPU produced
+    (whose quantisation is itself pinned elsewhere)."""
+    m, n, k = (1 << 20) + 300, 72, 2048
+    assert m * k >= 1 << 31
+    w, _ = inputs.random_case(72_000, 1, n, k, bf16=True)
+    t, g, _ = oracle_weights(w, bl.BL_PACK2)
+    packed, gamma = bl.quantize_weights(dev(w))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(72_001)
+    x = torch.randn((m, k), generator=gen, device="cuda", dtype=torch.bfloat16)
+    xq, scale, rowsum = bl.quantize_act(x)
+    del x
+    boundary = ((1 << 31) - 1) // k // 128 * 128          # first row of the second block
+    rows = np.unique(np.concatenate([
+        np.arange(0, 130), np.arange(boundary - 200, boundary + 200), np.arange(m - 130, m),
+        np.random.default_rng(5).choice(m, size=400, replace=False)]))
+    ridx = torch.from_numpy(rows).cuda()
+    q_rows = host(xq[ridx])
+    acc_ref = oracle.matmul_i32(q_rows, t)
+    np.testing.assert_array_equal(host(rowsum[ridx]), q_rows.astype(np.int64).sum(axis=1))
+    for path in (bl.BL_PATH_MFMA, bl.BL_PATH_MFMA_WIDE):
+        print(f"beyond 32-bit offsets: path {path}", flush=True)
+        y = bl.forward(xq, scale, rowsum, packed, gamma, n, k, path=path)
+        acc = bl.matmul_i32(xq, rowsum, packed, n, k, path=path)
+        np.testing.assert_array_equal(host(acc[ridx]), acc_ref)
+        assert_y_close(host(y[ridx]), oracle.rescale(acc_ref, host(scale[ridx]), g), acc_ref)
+        del y, acc
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_scale_overflow_tokens(bf16):
+    """Tokens whose max |x| is below 127 / FLT_MAX: s is the largest finite
+    float (not infinity), zeros stay 0, y stays finite; quantiser, b-bit
+    quantiser and the one-token fused GEMV against the oracle."""
+    m, n, k = 3, 200, 512
+    w, x = inputs.random_case(73_000 + int(bf16), m, n, k, bf16=False)
+    x = x * np.float32(1e-38)
+    x[:, ::7] = 0.0
+    x[1, 5] = np.float32(3e-37)
+    x[2] = x[2] * np.float32(1e-2)                 # subnormal magnitudes (bf16 too)
+    x[2, 3] = np.float32(2e-40)
+    if bf16:
+        x = inputs.f32_to_bf16_bits(x)
+    t, g, _ = oracle_weights(w, bl.BL_PACK2)
+    q_ref, s_ref, r_ref = oracle.quantize_act(x)
+    assert np.all(s_ref == np.finfo(np.float32).max)
+    packed, gamma = bl.quantize_weights(dev(w))
+    xd = dev(x)
+    xq, scale, rowsum = bl.quantize_act(xd)
+    np.testing.assert_array_equal(host(xq), q_ref)
+    np.testing.assert_array_equal(host(scale), s_ref)
+    np.testing.assert_array_equal(host(rowsum), r_ref)
+    acc_ref = oracle.matmul_i32(q_ref, t)
+    y = host(bl.forward(xq, scale, rowsum, packed, gamma, n, k))
+    assert np.isfinite(y).all()
+    assert_y_close(y, oracle.rescale(acc_ref, s_ref, g), acc_ref)
+    q4, s4, r4 = oracle.quantize_act_bits(x, 4)
+    got = bl.quantize_act(xd, bits=4)
+    for a, b in zip(got, (q4, s4, r4)):
+        np.testing.assert_array_equal(host(a), b)
+    y1, xq1, s1, r1 = bl.quantize_forward(dev(x[:1]), packed, gamma, n)
+    np.testing.assert_array_equal(host(xq1), q_ref[:1])
+    np.testing.assert_array_equal(host(s1), s_ref[:1])
+    assert_y_close(host(y1), oracle.rescale(acc_ref[:1], s_ref[:1], g), acc_ref[:1])
 
 
 # ---- 70B-class layer (single GPU), M in {1, 16, 128}; base-3 at M = 1 -------------------------
@@ -256,13 +389,14 @@ def test_xl_layer(shape):
     q_ref, s_ref, r_ref = oracle.quantize_act(x)
     xq, scale, rowsum = bl.quantize_act(dev(x))
     np.testing.assert_array_equal(host(xq), q_ref)
+    acc_all = oracle_matmul_rows(q_ref, t)        # every row of every M below
     for m in inputs.XL_MS:
+        print(f"xl shape {shape}: M={m}", flush=True)
         acc = host(bl.matmul_i32(xq[:m], rowsum[:m], packed, n, k))
-        rows = np.arange(m) if m <= 16 else np.array([0, 1, 37, 64, 100, 127])
-        acc_ref = oracle.matmul_i32(q_ref[rows], t)
-        np.testing.assert_array_equal(acc[rows], acc_ref, err_msg=f"M={m}")
+        acc_ref = acc_all[:m]
+        np.testing.assert_array_equal(acc, acc_ref, err_msg=f"M={m}")
         y = host(bl.forward(xq[:m], scale[:m], rowsum[:m], packed, gamma, n, k))
-        assert_y_close(y[rows], oracle.rescale(acc_ref, s_ref[rows], g), acc_ref)
+        assert_y_close(y, oracle.rescale(acc_ref, s_ref[:m], g), acc_ref)
         if m == 1:
             acc3 = host(bl.matmul_i32(xq[:1], rowsum[:1], packed3, n, k, bl.BL_PACK3))
             np.testing.assert_array_equal(acc3, acc)      # base-3 == 2-bit, bit for bit

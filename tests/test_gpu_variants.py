@@ -7,6 +7,7 @@ accumulators; fp32 outputs within 1e-5 relative (exact zeros where acc = 0).
 """
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from ternary_weight_linear_absmax_amd import bitlinear as bl
@@ -16,7 +17,8 @@ from gpu_helpers import assert_y_close, dev, host
 
 pytestmark = pytest.mark.gpu
 
-PATHS2 = (bl.BL_PATH_AUTO, bl.BL_PATH_GEMV, bl.BL_PATH_MFMA, bl.BL_PATH_SKINNY)
+PATHS2 = (bl.BL_PATH_AUTO, bl.BL_PATH_GEMV, bl.BL_PATH_MFMA, bl.BL_PATH_SKINNY,
+          bl.BL_PATH_MFMA_WIDE)
 
 
 def _products(xq, scale, rowsum, packed, gamma, n, k, layout, q_ref, s_ref, t, g, m):
@@ -25,6 +27,8 @@ def _products(xq, scale, rowsum, packed, gamma, n, k, layout, q_ref, s_ref, t, g
     paths = PATHS2 if layout == bl.BL_PACK2 else (bl.BL_PATH_AUTO,)
     for path in paths:
         if path == bl.BL_PATH_SKINNY and not (m <= 64 and k % 256 == 0):
+            continue
+        if path == bl.BL_PATH_MFMA_WIDE and k % 16 != 0:
             continue
         acc = host(bl.matmul_i32(xq, rowsum, packed, n, k, layout, path=path))
         np.testing.assert_array_equal(acc, acc_ref, err_msg=f"path {path}")
@@ -82,3 +86,42 @@ def test_binary_weights_with_four_bit_activations():
     packed, gamma = bl.quantize_weights(dev(w), binary=True)
     xq, scale, rowsum = bl.quantize_act(dev(x), bits=4)
     _products(xq, scale, rowsum, packed, gamma, n, k, bl.BL_PACK2, q_ref, s_ref, t, beta, m)
+
+
+# ---- group quantisation of the sign-binarised weights ---------------------------------
+
+@pytest.mark.parametrize("layout", [bl.BL_PACK2, bl.BL_PACK3])
+@pytest.mark.parametrize("m,n,k,groups", [(1, 300, 2560, 4), (8, 1000, 512, 8), (64, 200, 384, 2),
+                                          (4, 128, 64, 128), (40, 2560, 1024, 1),
+                                          (16, 12352, 1024, 16), (130, 640, 2048, 5)])
+def test_binary_weight_groups_all_paths(layout, m, n, k, groups):
+    """beta_g bit-exact per group, packed bytes and int32 accumulators exact on
+    every path, y within 1e-5 of the oracle's per-group rescale."""
+    w, x = inputs.random_case(63_000 + m + n + k + groups, m, n, k, bf16=True)
+    wf = inputs.bf16_bits_to_f32(w)
+    wf[: n // groups] *= np.float32(8.0)                  # groups of different scale
+    w = inputs.f32_to_bf16_bits(wf)
+    t, beta_ref = oracle.quantize_weights_binary_groups(w, groups)
+    packed_ref = oracle.pack2(t) if layout == bl.BL_PACK2 else oracle.pack3(t)
+    packed, beta = bl.quantize_weights_binary_groups(dev(w), groups, layout)
+    np.testing.assert_array_equal(host(beta), beta_ref)
+    np.testing.assert_array_equal(host(packed), packed_ref)
+    q_ref, s_ref, _ = oracle.quantize_act(x)
+    xq, scale, rowsum = bl.quantize_act(dev(x))
+    acc_ref = oracle.matmul_i32(q_ref, t)
+    y_ref = oracle.rescale_groups(acc_ref, s_ref, beta_ref)
+    paths = PATHS2 if layout == bl.BL_PACK2 else (bl.BL_PATH_AUTO,)
+    for path in paths:
+        if path == bl.BL_PATH_SKINNY and not (m <= 64 and k % 256 == 0):
+            continue
+        if path == bl.BL_PATH_MFMA_WIDE and k % 16 != 0:
+            continue
+        y = host(bl.forward_groups(xq, scale, rowsum, packed, beta, n, k, layout, path=path))
+        assert_y_close(y, y_ref, acc_ref)
+
+
+def test_binary_weight_groups_argument_checks():
+    w = torch.zeros((12, 64), dtype=torch.bfloat16, device="cuda")
+    for groups in (0, 5, 13):
+        with pytest.raises(bl.BitLinearError):
+            bl.quantize_weights_binary_groups(w, groups)
