@@ -49,6 +49,10 @@ def parse():
     ap.add_argument("--no-separate-stack", action="store_true",
                     help="skip the layer stack timed with separate product and glue calls")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--only", default="",
+                    help="comma-separated sections to run instead of the whole line (for "
+                         "profiling): decode, xl, stack, prefill, variants, backward, ceilings, "
+                         "cpu")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy kernel (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -132,25 +136,27 @@ def decode_workload(layers):
     return mats
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark measures one GPU only; run with --gpus 1 "
-                          "(sharding over several GPUs is described, not implemented)"}))
-        sys.exit(2)
+def sections(args):
+    """Sections to run: the whole line by default, or the --only list."""
+    every = ["decode", "ceilings", "xl", "stack", "prefill", "variants", "backward", "cpu"]
+    if not args.only:
+        out = list(every)
+        if args.no_extra:
+            out = [x for x in out if x in ("decode", "cpu")]
+        if args.no_cpu:
+            out.remove("cpu")
+        return out
+    want = [x.strip() for x in args.only.split(",") if x.strip()]
+    bad = [x for x in want if x not in every]
+    if bad:
+        raise SystemExit(f"unknown section(s) {bad}; choose from {every}")
+    return want
 
-    import torch
+
+def measure_decode(args):
+    """Headline: the decode step (one bitlinear_quantize_forward launch per
+    matrix and layer), graph-replayed; returns the line's core fields."""
     from ternary_weight_linear_absmax_amd import bitlinear as bl
-    from ternary_weight_linear_absmax_amd import inputs
-
-    if args.calibrate_copy:
-        calibrate_copy()
-        return
-    bl.load()
-    dev_name = torch.cuda.get_device_name(0)
-    log(f"device {dev_name}")
-
-    # ---------------- headline: decode M=1, 30 layers -----------------------
     mats = decode_workload(args.layers)
     step_bytes = sum(m["bytes"] for m in mats) * args.layers
     log(f"decode workload ready: {step_bytes / 1e6:.1f} MB packed per step")
@@ -181,7 +187,8 @@ def main():
                 "kernel": "gemv2_kernel<1,CPL,ST,true,bf16> (decode, M=1, activation "
                           "quantisation inside); per-launch time = graph replay / launches",
                 "avg_launch_us": round(us_per_launch, 3),
-                "algorithmic_bytes_per_launch": int(bytes_per_launch)}
+                "algorithmic_bytes_per_launch": int(bytes_per_launch),
+                "per_matrix_bytes": {m["name"]: m["bytes"] for m in mats}}
 
     # the same GEMV on pre-quantised activations, timed alone over the same rotation
     def gemv_only():
@@ -193,26 +200,62 @@ def main():
     roofline["prequantised_gemv_us_per_launch"] = round(ms_gemv * 1e3 / launches, 3)
     log(f"decode per launch: {us_per_launch:.2f} us with quantisation, "
         f"{ms_gemv * 1e3 / launches:.2f} us GEMV alone")
+    return dict(value=value, ms_step=ms_step, ms_step_eager=ms_step_eager, step_bytes=step_bytes,
+                roofline=roofline, launches=launches)
 
-    # ---------------- extra: 70B-class layer and prefill ------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU only; run with --gpus 1 "
+                          "(sharding over several GPUs is described, not implemented)"}))
+        sys.exit(2)
+
+    import torch
+    from ternary_weight_linear_absmax_amd import bitlinear as bl
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    bl.load()
+    dev_name = torch.cuda.get_device_name(0)
+    log(f"device {dev_name}")
+    todo = sections(args)
+    log(f"sections: {', '.join(todo)}")
+
+    dec = measure_decode(args) if "decode" in todo else None
     extra = {}
-    if not args.no_extra:
-        extra = measure_extra(args)
-
-    # ---------------- CPU oracle baseline ----------------------------------------
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(args.cpu_seconds)
+    ceil = measure_ceilings(args) if "ceilings" in todo else None
+    if ceil:
+        extra["ceilings"] = ceil
+    if "xl" in todo:
+        extra.update(measure_xl(args))
+    if "stack" in todo:
+        extra.update(measure_stack(separate=not args.no_separate_stack))
+    roofline_prefill = None
+    if "prefill" in todo:
+        pre, roofline_prefill = measure_prefill(ceil)
+        extra.update(pre)
+    if "variants" in todo:
+        extra.update(measure_variants())
+    if "backward" in todo:
+        extra.update(measure_backward())
+    cpu = cpu_baseline(args.cpu_seconds) if "cpu" in todo else None
+    if dec and ceil:
+        dec["roofline"]["frac_of_measured_read_ceiling"] = round(
+            dec["roofline"]["achieved"] / ceil["hbm_read_stream_GB/s"], 4)
+        floor = ceil["decode_plain_read_us_per_launch"]
+        dec["roofline"]["plain_read_same_launches_us"] = floor
 
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(dec["value"], 2) if dec else None,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "ms_per_step_eager_launch": round(ms_step_eager, 4),
+        "ms_per_step": round(dec["ms_step"], 4) if dec else None,
+        "ms_per_step_eager_launch": round(dec["ms_step_eager"], 4) if dec else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -225,22 +268,138 @@ def main():
                         "the step captured in a HIP graph" % args.layers,
             "M": 1,
             "layers": args.layers,
-            "packed_bytes_per_step": step_bytes,
-            "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+            "packed_bytes_per_step": dec["step_bytes"] if dec else None,
+            "hbm_frac": round(dec["value"] / HBM_PEAK_GBS, 4) if dec else None,
             "device": dev_name,
+            "sections": todo,
         },
-        "roofline": roofline,
+        "roofline": dec["roofline"] if dec else None,
+        "roofline_prefill": roofline_prefill,
         "cpu_baseline": cpu,
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
 
 
-def measure_extra(args):
-    """The other workloads, each timed as one captured graph of launches:
-    the 70B-class layer (rotating 10 copies of each matrix, 587 MB, so the
-    weights stream from HBM) at M = 1, 16, 128 and in base-3 at M = 1; the
-    3B-class prefill GEMMs at M = 512."""
+CEILINGS_LIB = os.path.join(ROOT, "ternary_weight_linear_absmax_amd", "libbitlinear_ceilings.so")
+
+
+def _ceilings_lib():
+    import ctypes
+    if not os.path.exists(CEILINGS_LIB):
+        raise RuntimeError(f"{CEILINGS_LIB} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(CEILINGS_LIB)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.blc_read_stream.argtypes = [p, i64, i32, p, p]
+    lib.blc_read_stream.restype = i32
+    lib.blc_mfma_i8_ops.argtypes = [i32, i32]
+    lib.blc_mfma_i8_ops.restype = i64
+    lib.blc_mfma_i8_loop.argtypes = [i32, i32, p, p]
+    lib.blc_mfma_i8_loop.restype = i32
+    lib.blc_empty.argtypes = [p]
+    lib.blc_empty.restype = i32
+    return lib
+
+
+def measure_ceilings(args):
+    """Measured ceilings of this device (libbitlinear_ceilings.so): a plain
+    HBM read stream (1 GiB of 16-byte non-temporal loads), the same plain read
+    over the decode step's launches (each decode matrix's byte count, from 30
+    distinct addresses, graph-replayed like the decode step) and over the
+    70B-class matrix size, an empty kernel per graph node, and an int8
+    matrix-core loop with no memory traffic."""
+    import ctypes
+    import torch
+    from ternary_weight_linear_absmax_amd import inputs
+    from ternary_weight_linear_absmax_amd import bitlinear as bl
+    lib = _ceilings_lib()
+    sink = torch.zeros((4,), dtype=torch.int32, device="cuda")
+    sp = ctypes.c_void_p(sink.data_ptr())
+
+    def st():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def chk(rc):
+        if rc != 0:
+            raise RuntimeError(f"ceiling kernel failed ({rc})")
+    out = {}
+    gib = 1 << 30
+    buf = torch.empty((gib,), dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    bp = buf.data_ptr()
+    best = 0.0
+    for blocks in (1024, 2048, 4096, 8192):
+        ms = graph_time(lambda: chk(lib.blc_read_stream(ctypes.c_void_p(bp), gib, blocks, sp,
+                                                        st())), 10, 2)
+        gbs = gib / (ms * 1e-3) / 1e9
+        out[f"read_stream_1GiB_{blocks}_blocks_GB/s"] = round(gbs, 1)
+        best = max(best, gbs)
+    out["hbm_read_stream_GB/s"] = round(best, 1)
+    out["hbm_read_stream_frac_of_peak"] = round(best / HBM_PEAK_GBS, 4)
+    log(f"ceiling: HBM read stream {best:.0f} GB/s")
+
+    # the decode step's launch pattern with a plain read in place of each GEMV
+    sizes = [bl.packed_bytes(n, k) for (_, k, n) in inputs.DECODE_SHAPES]
+    layers = args.layers
+    offs = []
+    off = 0
+    for _ in range(layers):
+        for b in sizes:
+            offs.append((off, b))
+            off += (b + 4095) // 4096 * 4096
+    assert off <= gib
+
+    def plain_step():
+        for o, b in offs:
+            chk(lib.blc_read_stream(ctypes.c_void_p(bp + o), b, 1024, sp, st()))
+    ms = graph_time(plain_step, 20, 3)
+    out["decode_plain_read_us_per_launch"] = round(ms * 1e3 / len(offs), 3)
+    out["decode_plain_read_GB/s"] = round(sum(sizes) * layers / (ms * 1e-3) / 1e9, 1)
+    log(f"ceiling: plain read of the decode step {ms * 1e3:.1f} us "
+        f"({ms * 1e3 / len(offs):.2f} us per launch)")
+    for i, (name, k, n) in enumerate(inputs.DECODE_SHAPES):
+        def one():
+            for layer in range(layers):
+                o, b = offs[layer * len(sizes) + i]
+                chk(lib.blc_read_stream(ctypes.c_void_p(bp + o), b, 1024, sp, st()))
+        ms = graph_time(one, 20, 3)
+        out[f"decode_plain_read_{name}_us"] = round(ms * 1e3 / layers, 3)
+    xl_bytes = bl.packed_bytes(28672, 8192)
+    copies = gib // ((xl_bytes + 4095) // 4096 * 4096)
+    copies = min(copies, 10)
+    stride = (xl_bytes + 4095) // 4096 * 4096
+    for blocks in (2048, 4096):
+        def xl_read():
+            for c in range(copies):
+                chk(lib.blc_read_stream(ctypes.c_void_p(bp + c * stride), xl_bytes, blocks, sp,
+                                        st()))
+        ms = graph_time(xl_read, 20, 3) / copies
+        out[f"xl_plain_read_{blocks}_blocks_us"] = round(ms * 1e3, 2)
+    out["xl_plain_read_us"] = min(out["xl_plain_read_2048_blocks_us"],
+                                  out["xl_plain_read_4096_blocks_us"])
+    del buf
+    torch.cuda.empty_cache()
+
+    def empties():
+        for _ in range(120):
+            chk(lib.blc_empty(st()))
+    ms = graph_time(empties, 20, 3)
+    out["empty_kernel_graph_node_us"] = round(ms * 1e3 / 120, 3)
+    log(f"ceiling: empty kernel {ms * 1e3 / 120:.2f} us per graph node")
+
+    iters, blocks = 2000, 1024
+    ms = graph_time(lambda: chk(lib.blc_mfma_i8_loop(iters, blocks, sp, st())), 5, 1)
+    tops = lib.blc_mfma_i8_ops(iters, blocks) / (ms * 1e-3) / 1e12
+    out["mfma_i8_loop_TOPS"] = round(tops, 1)
+    out["mfma_i8_loop_frac_of_peak"] = round(tops / I8_PEAK_TOPS, 4)
+    log(f"ceiling: int8 matrix-core loop {tops:.0f} TOPS")
+    return out
+
+
+def measure_xl(args):
+    """The 70B-class layer (rotating 10 copies of each matrix, 587 MB, so the
+    weights stream from HBM) at M = 1, 16, 128 and in base-3 at M = 1, plus
+    the weight quantiser on the same matrices."""
     import torch
     from ternary_weight_linear_absmax_amd import bitlinear as bl
     from ternary_weight_linear_absmax_amd import inputs
@@ -301,10 +460,21 @@ def measure_extra(args):
                 log(f"xl {name} M=1 pack3: {ms3 * 1e3:.1f} us {gbs3:.0f} GB/s")
         del c2, c3
         torch.cuda.empty_cache()
-    # layer stack: 30 layers of the 2B-class decoder, M = 64 tokens at position 0
-    extra.update(measure_stack(separate=not args.no_separate_stack))
-    # prefill M=512 (packed weights 6.9 MB: they stay in the Infinity Cache)
+    return extra
+
+
+def measure_prefill(ceil):
+    """The 3B-class prefill products at M = 512 (packed weights 6.9 MB: they
+    stay in the Infinity Cache), the product alone and with the activation
+    quantiser; the int8 library GEMM (torch._int_mm, unpacked int8 weights)
+    on the same shapes for context.  Returns (entries, roofline object of the
+    slower shape's product)."""
+    import torch
+    from ternary_weight_linear_absmax_amd import bitlinear as bl
+    from ternary_weight_linear_absmax_amd import inputs
+    extra = {}
     reps = 10
+    worst = None
     for si, (name, k, n) in enumerate(inputs.PREFILL_SHAPES):
         _, w, x = inputs.prefill(si)
         packed, gamma = bl.quantize_weights(to_dev(w))
@@ -324,15 +494,36 @@ def measure_extra(args):
                 bl.quantize_act(xd)
                 bl.forward(xq, scale, rowsum, packed, gamma, n, k, y=y)
         ms_full = graph_time(full, 20, 3) / reps
-        extra[f"prefill_{name}_M512"] = {
-            "K": k, "N": n, "M": m, "us": round(ms * 1e3, 2), "TOPS": round(tops, 2),
-            "i8_frac": round(tops / I8_PEAK_TOPS, 4),
-            "us_with_act_quant": round(ms_full * 1e3, 2),
-            "TOPS_with_act_quant": round(2.0 * m * n * k / (ms_full * 1e-3) / 1e12, 2)}
+        ent = {"K": k, "N": n, "M": m, "us": round(ms * 1e3, 2), "TOPS": round(tops, 2),
+               "i8_frac": round(tops / I8_PEAK_TOPS, 4),
+               "us_with_act_quant": round(ms_full * 1e3, 2),
+               "TOPS_with_act_quant": round(2.0 * m * n * k / (ms_full * 1e-3) / 1e12, 2),
+               "splits_workspace_bytes": bl.forward_workspace_bytes(m, n, k)}
+        if ceil:
+            ent["frac_of_measured_mfma_ceiling"] = round(tops / ceil["mfma_i8_loop_TOPS"], 4)
+        # context: the int8 library GEMM on unpacked int8 operands
+        try:
+            a8 = xq
+            b8 = bl.unpack_weights(packed, n, k).t()     # [K, N] view of the trits
+            b8c = b8.contiguous()
+            ms_lib = time_loop(lambda: torch._int_mm(a8, b8c), 20, 3)
+            ent["library_int8_gemm_us"] = round(ms_lib * 1e3, 2)
+        except Exception as e:                             # library path missing on this build
+            ent["library_int8_gemm_us"] = f"unavailable: {type(e).__name__}"
+        extra[f"prefill_{name}_M512"] = ent
         log(f"prefill {name}: {ms * 1e3:.1f} us {tops:.1f} TOPS")
-    extra.update(measure_variants())
-    extra.update(measure_backward())
-    return extra
+        if worst is None or ms > worst[0]:
+            worst = (ms, name, m, n, k, tops)
+    ms, name, m, n, k, tops = worst
+    roof = {"bound": "mfma", "achieved": round(tops, 1), "peak": I8_PEAK_TOPS, "unit": "TOP/s",
+            "frac": round(tops / I8_PEAK_TOPS, 4), "traffic": None,
+            "kernel": f"tiled int8 GEMM, prefill {name} M={m} N={n} K={k} (the slower of the "
+                      f"two 3B-class shapes; per-launch time = graph replay / launches, "
+                      f"including a split-k finish where the shape splits)",
+            "avg_launch_us": round(ms * 1e3, 3), "algorithmic_ops_per_launch": 2 * m * n * k}
+    if ceil:
+        roof["frac_of_measured_mfma_ceiling"] = round(tops / ceil["mfma_i8_loop_TOPS"], 4)
+    return extra, roof
 
 
 def measure_backward():
@@ -515,12 +706,45 @@ def measured_traffic():
         return None
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _split_rows(fn, rows, threads):
+    """fn(r0, r1) over row ranges on `threads` host threads (the oracle's
+    ctypes calls release the GIL)."""
+    import concurrent.futures
+    bounds = np.linspace(0, rows, threads + 1).astype(int)
+    with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+        return list(ex.map(lambda i: fn(bounds[i], bounds[i + 1]), range(threads)))
+
+
 def cpu_baseline(seconds):
-    """The oracle, untuned, on this host: the decode workload's per-matrix chain
-    (absmax quantisation, exact int32 product, rescale) at M = 1, repeated over
-    the four shapes until `seconds` have passed."""
+    """The oracle, untuned, on this host.  Headline value: the decode
+    workload's per-matrix chain (absmax quantisation, exact int32 product,
+    rescale) at M = 1 on one thread, repeated over the four shapes until
+    `seconds` have passed.  Also: the same chain with the weight rows split
+    over all host threads (a row split of the oracle's own calls), one pass of
+    the 3B-class prefill at M = 512 and of the 70B-class layer at M = 128 on
+    all threads, and the prefill on one thread over a bounded sample of rows."""
     import oracle
     from ternary_weight_linear_absmax_amd import inputs
+    threads = _cpu_threads()
     prepared = []
     for i in range(len(inputs.DECODE_SHAPES)):
         _, w, x = inputs.decode(i, m=1)
@@ -536,10 +760,67 @@ def cpu_baseline(seconds):
             done_bytes += nbytes
         passes += 1
     el = time.perf_counter() - t0
-    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{passes} passes over the 4 decode matrices (one layer, M=1) in "
-                      f"{el:.1f} s; single-threaded scalar C"}
+    out = {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+           "kind": "oracle", "cpu_model": _cpu_model(), "host_threads_available": threads,
+           "sample": f"{passes} passes over the 4 decode matrices (one layer, M=1) in "
+                     f"{el:.1f} s; single-threaded scalar C"}
+    log(f"cpu oracle decode, 1 thread: {out['value']} GB/s")
+
+    # decode chain with the weight rows split over all threads
+    done_bytes, passes = 0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds / 2:
+        for x, t, g, nbytes in prepared:
+            q, s, r = oracle.quantize_act(x)
+            parts = _split_rows(lambda a, b: oracle.matmul_i32(q, t[a:b]), t.shape[0], threads)
+            oracle.rescale(np.concatenate(parts, axis=1), s, g)
+            done_bytes += nbytes
+        passes += 1
+    el = time.perf_counter() - t0
+    out["all_cores"] = {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s",
+                        "cores": threads,
+                        "sample": f"{passes} passes over the 4 decode matrices, weight rows "
+                                  f"split over {threads} threads, in {el:.1f} s"}
+    log(f"cpu oracle decode, {threads} threads: {out['all_cores']['value']} GB/s")
+
+    # prefill M=512 (one pass per shape on all threads; one thread on 32 rows)
+    for si, (name, k, n) in enumerate(inputs.PREFILL_SHAPES):
+        _, w, x = inputs.prefill(si)
+        t, g = oracle.quantize_weights(w)
+        m = x.shape[0]
+        t0 = time.perf_counter()
+        q, s, r = oracle.quantize_act(x)
+        parts = _split_rows(lambda a, b: oracle.matmul_i32(q[a:b], t), m, threads)
+        oracle.rescale(np.concatenate(parts, axis=0), s, g)
+        el = time.perf_counter() - t0
+        sub = 32
+        t1 = time.perf_counter()
+        q1, s1, _ = oracle.quantize_act(x[:sub])
+        oracle.rescale(oracle.matmul_i32(q1, t), s1, g)
+        el1 = time.perf_counter() - t1
+        out[f"prefill_{name}_M512"] = {
+            "TOPS": round(2.0 * m * n * k / el / 1e12, 5), "seconds": round(el, 2),
+            "cores": threads,
+            "one_thread_TOPS": round(2.0 * sub * n * k / el1 / 1e12, 5),
+            "one_thread_sample": f"{sub} of {m} tokens in {el1:.2f} s"}
+        log(f"cpu oracle prefill {name}: {el:.1f} s on {threads} threads")
+    # 70B-class layer, M = 128 (one pass per shape on all threads)
+    for si, (name, k, n) in enumerate(inputs.XL_SHAPES):
+        _, w, x = inputs.xl(si, m=128)
+        t, g = oracle.quantize_weights(w)
+        del w
+        m = x.shape[0]
+        t0 = time.perf_counter()
+        q, s, r = oracle.quantize_act(x)
+        parts = _split_rows(lambda a, b: oracle.matmul_i32(q[a:b], t), m, threads)
+        oracle.rescale(np.concatenate(parts, axis=0), s, g)
+        el = time.perf_counter() - t0
+        out[f"xl_{name}_M128"] = {"TOPS": round(2.0 * m * n * k / el / 1e12, 5),
+                                  "GB/s_packed": round(n * oracle.pack2_pitch(k) / el / 1e9, 4),
+                                  "seconds": round(el, 2), "cores": threads}
+        log(f"cpu oracle xl {name} M=128: {el:.1f} s on {threads} threads")
+        del t
+    return out
 
 
 if __name__ == "__main__":
