@@ -31,7 +31,9 @@
  *     launch (the buffers of an empty product may be NULL); K must be in
  *     [1, BITLINEAR_MAX_K].  Other size and layout checks come first.
  *   - Every call is stateless and re-entrant; calls on different streams may
- *     overlap if their buffers do not.
+ *     overlap if their buffers do not.  The one exception is
+ *     bitlinear_forward_noalloc, whose calls on one GPU share a static
+ *     scratch array.
  */
 #ifndef BITLINEAR_H
 #define BITLINEAR_H
@@ -53,7 +55,8 @@ typedef enum {
     BL_ERR_LAYOUT = -5,      /* unknown bl_layout */
     BL_ERR_WORKSPACE = -6,   /* workspace smaller than the size query returned */
     BL_ERR_HIP = -7,         /* a HIP launch or runtime call failed */
-    BL_ERR_PATH = -8         /* the requested kernel path cannot run this shape */
+    BL_ERR_PATH = -8,        /* the requested kernel path cannot run this shape */
+    BL_ERR_SCRATCH = -9      /* the allocation-free call needs more scratch than it has */
 } bl_status;
 
 typedef enum {
@@ -247,6 +250,26 @@ int bitlinear_matmul_i32(const int8_t *xq, const int32_t *rowsum, int64_t M,
                          const uint8_t *packed, int layout, int64_t N, int64_t K,
                          int32_t *acc, void *workspace, int64_t workspace_bytes, int path,
                          hipStream_t stream);
+
+/* ---- forward without any allocation ------------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, results and errors as bitlinear_forward_ex without the
+ * workspace: the split-k partial sums go to a static scratch array of
+ * BITLINEAR_NOALLOC_SCRATCH_BYTES in the library, one per GPU, which the GPU
+ * holds until the process ends.  The call allocates and frees nothing.
+ * Returns BL_ERR_SCRATCH, and launches nothing, when the shape needs more
+ * scratch than that (bitlinear_forward_workspace_bytes tells how much a shape
+ * needs on its path).  The scratch needs no initial contents and keeps the
+ * last call's partial sums; calls that overlap on one GPU (other streams,
+ * other host threads) share it and race, so serialise them.  The first call
+ * on a device looks up the array's device address (hipGetSymbolAddress). */
+#define BITLINEAR_NOALLOC_SCRATCH_BYTES ((size_t)14 << 20)
+
+int bitlinear_forward_noalloc(const int8_t *xq, const float *scale, const int32_t *rowsum,
+                              int64_t M, const uint8_t *packed, int layout, const float *gamma,
+                              int64_t N, int64_t K, float *y, int path, hipStream_t stream);
 
 /* ---- backward through BitLinear: input gradient -------------------------------
  * [lumen-it.ai BitNet article, training paragraph: straight-through estimators

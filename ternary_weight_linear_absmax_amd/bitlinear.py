@@ -67,6 +67,7 @@ def load():
         "bitlinear_backward_input": (i32, [p, i32, i64, i64, p, i32, p, i64, p, p]),
         "bitlinear_forward": (i32, [p, p, p, i64, p, i32, p, i64, i64, p, p, i64, p]),
         "bitlinear_forward_ex": (i32, [p, p, p, i64, p, i32, p, i64, i64, p, p, i64, i32, p]),
+        "bitlinear_forward_noalloc": (i32, [p, p, p, i64, p, i32, p, i64, i64, p, i32, p]),
         "bitlinear_matmul_i32": (i32, [p, p, i64, p, i32, i64, i64, p, p, i64, i32, p]),
         "bitlinear_unpack_weights": (i32, [p, i32, i64, i64, p, p]),
         "bitlinear_residual_rmsnorm_quantize": (i32, [p, p, i64, i64, ctypes.c_float, p, p, p, p]),
@@ -276,6 +277,24 @@ def forward(xq, scale, rowsum, packed, gamma, n: int, k: int, layout: int = BL_P
     return y
 
 
+NOALLOC_SCRATCH_BYTES = 14 << 20
+
+
+def forward_noalloc(xq, scale, rowsum, packed, gamma, n: int, k: int, layout: int = BL_PACK2,
+                    path: int = BL_PATH_AUTO, y=None, stream=None):
+    """bitlinear_forward_noalloc: the forward with the library's static scratch
+    instead of a workspace (y must be passed in to allocate nothing here)."""
+    lib = load()
+    m = xq.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
+    _check(lib.bitlinear_forward_noalloc(_ptr(xq), _ptr(scale), _ptr(rowsum), m, _ptr(packed),
+                                         layout, _ptr(gamma), n, k, _ptr(y), path,
+                                         _stream(stream)),
+           "bitlinear_forward_noalloc")
+    return y
+
+
 def matmul_i32(xq, rowsum, packed, n: int, k: int, layout: int = BL_PACK2,
                path: int = BL_PATH_AUTO, acc=None, workspace=None, stream=None):
     """acc [M, N] int32 = xq . t^T exactly."""
@@ -461,6 +480,7 @@ def unpack_weights(packed, n: int, k: int, layout: int = BL_PACK2, stream=None):
 bitlinear_quantize_weights = quantize_weights
 bitlinear_quantize_act = quantize_act
 bitlinear_forward = forward
+bitlinear_forward_noalloc = forward_noalloc
 bitlinear_quantize_weights_binary_groups = quantize_weights_binary_groups
 bitlinear_forward_groups = forward_groups
 bitlinear_norm_forward = norm_forward

@@ -1,5 +1,7 @@
 // C ABI of libbitlinear: host-side argument checks, kernel-path dispatch and
 // launches.  Nothing here allocates, frees or synchronises.
+#include <mutex>
+
 #include "../../include/bitlinear.h"
 #include "internal.h"
 
@@ -151,6 +153,9 @@ const char *bitlinear_status_string(int status)
     case BL_ERR_WORKSPACE: return "workspace smaller than the size query returned";
     case BL_ERR_HIP: return "a HIP launch or runtime call failed";
     case BL_ERR_PATH: return "the requested kernel path cannot run this shape or layout";
+    case BL_ERR_SCRATCH:
+        return "the product needs more scratch than the library's static buffer holds "
+               "(BITLINEAR_NOALLOC_SCRATCH_BYTES); call bitlinear_forward_ex with a workspace";
     default: return "unknown status";
     }
 }
@@ -270,6 +275,64 @@ int bitlinear_forward_ex(const int8_t *xq, const float *scale, const int32_t *ro
 {
     return run_product(xq, scale, rowsum, M, packed, layout, gamma, N, K, y, nullptr, workspace,
                        workspace_bytes, path, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of the allocation-free forward: one array per GPU, held for the
+// life of the process.  Host code never passes the array's name to a kernel
+// (in host code it is a stand-in, not a device address): the device address
+// is looked up once per device, with that device current, and kept.
+__device__ __attribute__((aligned(256))) uint8_t scratch[BITLINEAR_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of the current device's scratch array.
+hipError_t scratch_address(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    *out = g_scratch_ptr[dev];
+    return g_scratch_err[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int bitlinear_forward_noalloc(const int8_t *xq, const float *scale, const int32_t *rowsum,
+                              int64_t M, const uint8_t *packed, int layout, const float *gamma,
+                              int64_t N, int64_t K, float *y, int path, hipStream_t stream)
+{
+    // shape, layout and path checks first (no HIP call for a rejected call)
+    if (!good_layout(layout)) return BL_ERR_LAYOUT;
+    if (!known_path(path)) return BL_ERR_PATH;
+    if (M < 0 || N < 0 || !good_k(K)) return BL_ERR_SHAPE;
+    if ((M > 0 && K > kMaxElems / M) || (N > 0 && K > kMaxElems / N) ||
+        (M > 0 && N > kMaxElems / M))
+        return BL_ERR_SHAPE;
+    const int p = path == BL_PATH_AUTO ? choose_path(M, N, K, layout) : path;
+    if (M > 0 && N > 0 && path_runs(p, M, N, K, layout) &&
+        workspace_need(p, M, N, K, layout) > (int64_t)BITLINEAR_NOALLOC_SCRATCH_BYTES)
+        return BL_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (M > 0 && N > 0 && workspace_need(p, M, N, K, layout) > 0 &&
+        scratch_address(&ws) != hipSuccess)
+        return BL_ERR_HIP;
+    return run_product(xq, scale, rowsum, M, packed, layout, gamma, N, K, y, nullptr, ws,
+                       ws ? (int64_t)BITLINEAR_NOALLOC_SCRATCH_BYTES : 0, path, stream);
 }
 
 int bitlinear_forward_groups(const int8_t *xq, const float *scale, const int32_t *rowsum,

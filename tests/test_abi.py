@@ -78,7 +78,7 @@ def test_path_selection(lib):
 
 
 def test_status_strings(lib):
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         assert bl.status_string(code) and bl.status_string(code) != "unknown status"
     assert bl.status_string(-99) == "unknown status"
 
@@ -286,6 +286,25 @@ def test_fused_product_glue_argument_checks(lib):
     h = lib.bitlinear_forward_relu2_rmsnorm_quantize
     assert h(P, P, P, 4, 2560, P, P, 13823, 6912, 1e-5, P, P, P, P, 1 << 30, None) == -2
     assert h(P, P, P, 4, 2560, P, P, 13824, 6912, 1e-5, P, P, P, NULL, 1 << 30, None) == -1
+
+
+def test_noalloc_forward_argument_checks(lib):
+    """The allocation-free forward validates like bitlinear_forward_ex and
+    rejects products whose split-k partial sums exceed its static scratch,
+    all before any HIP call."""
+    f = lib.bitlinear_forward_noalloc
+
+    def call(xq=P, s=P, r=P, m=4, pk=P, lay=0, g=P, n=8, k=64, y=P, path=0):
+        return f(xq, s, r, m, pk, lay, g, n, k, y, path, None)
+
+    assert call(lay=7) == -5
+    assert call(path=9) == -8
+    assert call(k=0) == -2 and call(m=-1) == -2
+    assert call(m=0) == 0 and call(n=0) == 0
+    # 512 x 2048 x 8192 splits its k range four ways: 16 MiB of partial sums
+    assert bl.forward_workspace_bytes(512, 2048, 8192) > bl.NOALLOC_SCRATCH_BYTES
+    assert call(m=512, n=2048, k=8192) == -9
+    assert "scratch" in bl.status_string(-9)
 
 
 def test_group_argument_checks(lib):
