@@ -52,7 +52,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 
 // weight loads: non-temporal (1) or cached (0)
 #ifndef GEMM_B_NT
-#define GEMM_B_NT 1
+#define GEMM_B_NT 0
 #endif
 
 constexpr int BK = 128;

@@ -23,7 +23,8 @@
 // block tile is 64 tokens x 512 weight rows and the block's activation tile
 // (64 x 128 bytes per stage) is loaded from memory once and read from LDS by
 // all four waves.  The packed weights never touch LDS: each lane loads its 16
-// bytes per stage into a register ring NB stages ahead.  Activations go
+// bytes per stage into a register ring NB stages ahead, through the caches
+// (each weight tile is read again by the other token tiles).  Activations go
 // through a two-slot register ring into a double-buffered LDS tile (one
 // barrier per stage); the next stage's fragments are read from LDS while the
 // current stage's MFMAs run.
@@ -52,9 +53,12 @@ constexpr int WLDA = WBK + 16;        // padded LDS row of the activation tile (
 #define WIDE_NB 4
 #endif
 #ifndef WIDE_B_NT
-#define WIDE_B_NT 1
+#define WIDE_B_NT 0
 #endif
-constexpr int WNA = 2;                // activation register ring (stages)
+#ifndef WIDE_NA
+#define WIDE_NA 2
+#endif
+constexpr int WNA = WIDE_NA;          // activation register ring (stages)
 constexpr int WNB = WIDE_NB;          // weight register ring (stages)
 constexpr int WNXCD = 8;
 // WWN 32-column blocks per wave: the block tile is 64 x 128 WWN

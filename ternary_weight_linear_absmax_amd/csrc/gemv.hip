@@ -1031,12 +1031,37 @@ hipError_t launch_gemv_pack3(const int8_t *xq, const int32_t *rowsum, int64_t m,
                              const uint8_t *packed, int64_t n, int64_t k, Out out, void *ws,
                              hipStream_t s)
 {
-    // one token on a matrix of many rows: partial-sum tables per group of five
+    // one token: the digit table where it runs (K a multiple of 16; measured
+    // faster than the partial-sum tables on the 70B-class matrices), else the
+    // partial-sum tables on matrices of many rows
+    if (gemv3lut_supported(m, k)) return launch_gemv3lut(xq, rowsum, packed, n, k, out, s);
     if (gemv3sum_slices(m, n, k) > 0)
         return launch_gemv3sum(xq, rowsum, packed, n, k, out, (int32_t *)ws, s);
     const bool al = (k % 16) == 0;
+    for (int64_t m0 = 0; m0 < m; m0 += 4) {
+        const int64_t mt = (m - m0) < 4 ? (m - m0) : 4;
+        hipError_t e;
+        switch (mt) {
+        case 1: e = launch3<1>(al, xq, rowsum, n, k, packed, out, m0, s); break;
+        case 2: e = launch3<2>(al, xq, rowsum, n, k, packed, out, m0, s); break;
+        case 3: e = launch3<3>(al, xq, rowsum, n, k, packed, out, m0, s); break;
+        default: e = launch3<4>(al, xq, rowsum, n, k, packed, out, m0, s); break;
+        }
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+bool gemv3lut_supported(int64_t m, int64_t k)
+{
+    return m == 1 && (k % 16) == 0 && pack3_pitch(k) / 16 <= (int64_t)GEMV_KS_MAX * 128;
+}
+
+hipError_t launch_gemv3lut(const int8_t *xq, const int32_t *rowsum, const uint8_t *packed,
+                           int64_t n, int64_t k, Out out, hipStream_t s)
+{
     const int64_t chunks3 = pack3_pitch(k) / 16;
-    if (m == 1 && al && chunks3 <= (int64_t)GEMV_KS_MAX * 128) {
+    {
         // one token: table decode, shaped like the 2-bit kernel
         const Gemv2Shape sh = gemv2_shape(n, chunks3, 1);
         const int64_t rb = (int64_t)GEMV_R * sh.st * sh.wr;
@@ -1053,18 +1078,6 @@ hipError_t launch_gemv_pack3(const int8_t *xq, const int32_t *rowsum, int64_t m,
 #undef G3_CASE
         return hipErrorInvalidValue;
     }
-    for (int64_t m0 = 0; m0 < m; m0 += 4) {
-        const int64_t mt = (m - m0) < 4 ? (m - m0) : 4;
-        hipError_t e;
-        switch (mt) {
-        case 1: e = launch3<1>(al, xq, rowsum, n, k, packed, out, m0, s); break;
-        case 2: e = launch3<2>(al, xq, rowsum, n, k, packed, out, m0, s); break;
-        case 3: e = launch3<3>(al, xq, rowsum, n, k, packed, out, m0, s); break;
-        default: e = launch3<4>(al, xq, rowsum, n, k, packed, out, m0, s); break;
-        }
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
 }
 
 }  // namespace bl

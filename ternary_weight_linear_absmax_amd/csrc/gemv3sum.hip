@@ -153,7 +153,7 @@ __global__ __launch_bounds__(64 * S3_WAVES) void gemv3sum_kernel(const int8_t *_
 // Slices of the k range (0: the shape does not take this kernel).
 int gemv3sum_slices(int64_t m, int64_t n, int64_t k)
 {
-    if (m != 1) return 0;
+    if (m != 1 || gemv3lut_supported(m, k)) return 0;
     const int64_t pitch = pack3_pitch(k);
     // the tables pay off once every block streams several hundred rows
     if (n < 4096) return 0;

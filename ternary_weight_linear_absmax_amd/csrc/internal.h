@@ -107,6 +107,10 @@ int64_t gemv3_workspace_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemv_pack3(const int8_t *xq, const int32_t *rowsum, int64_t m,
                              const uint8_t *packed, int64_t n, int64_t k, Out out, void *ws,
                              hipStream_t s);
+// one token, digit table (K a multiple of 16)
+bool gemv3lut_supported(int64_t m, int64_t k);
+hipError_t launch_gemv3lut(const int8_t *xq, const int32_t *rowsum, const uint8_t *packed,
+                           int64_t n, int64_t k, Out out, hipStream_t s);
 // one token, partial-sum tables (gemv3sum.hip); 0 slices: not this shape
 int gemv3sum_slices(int64_t m, int64_t n, int64_t k);
 int64_t gemv3sum_workspace_bytes(int64_t m, int64_t n, int64_t k);

@@ -122,13 +122,12 @@ def test_base3_one_token_shapes(n, k):
     run_case(w, x, bl.BL_PACK3, (bl.BL_PATH_AUTO,))
 
 
-@pytest.mark.parametrize("n,k", [(4096, 16), (4100, 1296), (6001, 6400), (4097, 12801),
-                                 (8192, 1280), (5000, 2561)])
+@pytest.mark.parametrize("n,k", [(4097, 12801), (5000, 2561), (4100, 1283), (6001, 6401)])
 def test_base3_partial_sum_tables(n, k):
-    """Base-3 GEMV for one token on matrices of many rows: per-group tables
-    of partial sums, the k range in slices of 256 packed bytes (one slice, a
-    short last slice, K not a multiple of 16 or of 5), slices added by the
-    split-k finish."""
+    """Base-3 GEMV for one token on matrices of many rows with K not a
+    multiple of 16: per-group tables of partial sums, the k range in slices
+    of 256 packed bytes (a short last slice, K not a multiple of 5), slices
+    added by the split-k finish."""
     w, x = inputs.random_case(51_000 + n + k, 1, n, k, bf16=True)
     x[0, :7] = 0
     run_case(w, x, bl.BL_PACK3, (bl.BL_PATH_AUTO,))
