@@ -515,7 +515,7 @@ constexpr int LDB = 48;   // LDS row of a packed weight tile (32 bytes + pad)
 constexpr int G3_NS = 3;
 
 template <int WM, int WN, int R>
-__global__ __launch_bounds__(512) void gemm3_kernel(const int8_t *__restrict__ xq,
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void gemm3_kernel(const int8_t *__restrict__ xq,
                                                     const int32_t *__restrict__ rowsum,
                                                     int64_t m, int64_t k,
                                                     const uint8_t *__restrict__ packed, int64_t n,
@@ -613,18 +613,21 @@ __global__ __launch_bounds__(512) void gemm3_kernel(const int8_t *__restrict__ x
             for (int i = 0; i < PB; ++i)
                 if (bon[i]) *(uint4 *)(slot + blds[i]) = b[i];
         };
-        // prologue: stages 0 and 1 straight into LDS, stages 2 .. 2+R-1 in flight
+        // prologue: stages 0 and 1 straight into LDS, stages 2 .. 2+R-1 in
+        // flight (each stage's registers are written to LDS before the next
+        // loads are issued, which bounds the registers held at once)
         {
             uint4 a0[PA], b0[PB], a1[PA], b1[PB];
             gload(a0, b0, 0);
             gload(a1, b1, 1);
-#pragma unroll
-            for (int r = 0; r < R; ++r) gload(ra[(2 + r) % R], rb[(2 + r) % R], 2 + r);
             // row operands of the epilogue (visible after the first barrier),
             // read while the stage loads are in flight
             ep_rows<BM>(pt, m0, m, rowsum, out, ep_mode, ep_rs, ep_gs);
             lstore(a0, b0, 0);
+            gload(ra[2 % R], rb[2 % R], 2);
             if (nk > 1) lstore(a1, b1, 1);
+#pragma unroll
+            for (int r = 1; r < R; ++r) gload(ra[(2 + r) % R], rb[(2 + r) % R], 2 + r);
         }
         __syncthreads();
         auto iter = [&](auto jc, int j) __attribute__((always_inline)) {
@@ -652,52 +655,62 @@ __global__ __launch_bounds__(512) void gemm3_kernel(const int8_t *__restrict__ x
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][s][r] = 0;
 
-    struct Frag { v4i a[4][WM]; uint4 b[WN]; };
-    auto read_frag = [&](Frag &f, int st) __attribute__((always_inline)) {
-        const uint8_t *slot = lds + (st % G3_NS) * SS;
+    // Fragments stream two k pieces ahead of the MFMAs: while the MFMAs of
+    // piece p of stage j run, piece p + 2 is read from LDS (pieces 0 and 1 of
+    // stage j + 1 during pieces 2 and 3, with the stage's weight words).
+    // Keeping four pieces of A and two stages of weight words live holds the
+    // wave to 128 registers, so two blocks share a CU and one block's MFMAs
+    // fill the other's waits.  The last stage also reads a next stage that
+    // does not exist: those reads stay inside the LDS ring and their values
+    // are never used.
+    auto read_a = [&](v4i (&a)[WM], const uint8_t *slot, int p) __attribute__((always_inline)) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-#pragma unroll
-            for (int a = 0; a < WM; ++a) {
-                const int row = wm * 32 * WM + 32 * a + l32;
-                const uint4 v = load16(slot + row * LDA + 64 * h + 16 * p);
-                f.a[p][a] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-            }
+        for (int i = 0; i < WM; ++i) {
+            const int row = wm * 32 * WM + 32 * i + l32;
+            const uint4 v = load16(slot + row * LDA + 64 * h + 16 * p);
+            a[i] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+        }
+    };
+    auto read_b = [&](uint4 (&b)[WN], const uint8_t *slot) __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < WN; ++s)
-            f.b[s] = load16(slot + SA + (wn * 32 * WN + 32 * s + l32) * LDB + 16 * h);
+            b[s] = load16(slot + SA + (wn * 32 * WN + 32 * s + l32) * LDB + 16 * h);
     };
-    auto mma = [&](const Frag &f) __attribute__((always_inline)) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
+    v4i af[4][WM];
+    uint4 bw[WN], bn[WN];
+    __syncthreads();          // stages 0 and 1 are in LDS
+    read_a(af[0], lds, 0);
+    read_a(af[1], lds, 1);
+    read_b(bw, lds);
+    int cur = 0;              // ring slot of stage j
+    for (int j = 0; j < nk; ++j) {
+        const int nxt = cur == G3_NS - 1 ? 0 : cur + 1;
+        const uint8_t *slot = lds + cur * SS, *nslot = lds + nxt * SS;
+        static_for<4>([&](auto pc) __attribute__((always_inline)) {
+            constexpr int P = decltype(pc)::value;
             v4i bf[WN];
 #pragma unroll
-            for (int s = 0; s < WN; ++s) bf[s] = unpack_word(word_of(f.b[s], p));
+            for (int s = 0; s < WN; ++s) bf[s] = unpack_word(word_of(bw[s], P));
+            if (P < 2) {
+                read_a(af[P + 2], slot, P + 2);
+            } else {
+                read_a(af[P - 2], nslot, P - 2);
+                if (P == 2) read_b(bn, nslot);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int a = 0; a < WM; ++a)
 #pragma unroll
                 for (int s = 0; s < WN; ++s)
-                    acc[a][s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[p][a], bf[s], acc[a][s],
-                                                                      0, 0, 0);
-        }
-    };
-    Frag fr[2];
-    __syncthreads();          // stages 0 and 1 are in LDS
-    read_frag(fr[0], 0);
-    auto iter = [&](auto jc, int j) __attribute__((always_inline)) {
-        constexpr int C = decltype(jc)::value & 1;
-        if (j + 1 < nk) read_frag(fr[C ^ 1], j + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mma(fr[C]);
-        __builtin_amdgcn_sched_barrier(0);
+                    acc[a][s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[P][a], bf[s],
+                                                                      acc[a][s], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+#pragma unroll
+        for (int s = 0; s < WN; ++s) bw[s] = bn[s];
+        cur = nxt;
         __syncthreads();
-    };
-    const int nu = nk - nk % U;
-    for (int j = 0; j < nu; j += U)
-        static_for<U>([&](auto jc) __attribute__((always_inline)) { iter(jc, j + jc); });
-    static_for<U - 1>([&](auto jc) __attribute__((always_inline)) {
-        if (nu + jc < nk) iter(jc, nu + jc);
-    });
+    }
 
     // Epilogue: the accumulators into the output tile in the ring (every
     // wave is past its last ring access after the final barrier of the loop)
@@ -787,7 +800,8 @@ GemmCfg gemm_config(int64_t m, int64_t n, int64_t k, int variant = GEMM_TILED)
     // each) when there are few of them.
     // Larger: 128 x 128 tiles when they fill one round of the 256 CUs or many;
     // 64 x 128 tiles when 128 x 128 ones would spill a few tiles into a second
-    // round; 128 x 128 tiles with the k range split when they are too few.
+    // round, or when 128 x 128 ones are too few and 64 x 128 ones still fill
+    // most of the chip; else 128 x 128 tiles with the k range split.
     const int64_t nk = (k + BK - 1) / BK;
     auto tiles = [&](int wm, int wn) {
         return ((m + 64 * wm - 1) / (64 * wm)) * ((n + 64 * wn - 1) / (64 * wn));
@@ -803,6 +817,9 @@ GemmCfg gemm_config(int64_t m, int64_t n, int64_t k, int variant = GEMM_TILED)
     if (t22 >= 192 && t22 <= 256) return {2, 2, 1, false};
     if (t22 > 256 && t22 < 512) return {1, 2, 1, false};
     if (t22 >= 512) return {2, 2, 1, false};
+    // 64 x 128 tiles that fill most of the chip beat 128 x 128 tiles with the
+    // k range split (no partial sums to write, read back and add)
+    if (tiles(1, 2) >= 192) return {1, 2, 1, false};
     int64_t sp = 256 / t22;
     if (sp > 8) sp = 8;
     if (sp > nk / 4) sp = nk / 4;
@@ -822,11 +839,12 @@ static void gemm_chunks(int64_t m, int64_t n, int64_t k, int64_t &mc, int64_t &n
     if (nc < 1) nc = 1;
 }
 
-// The GEMM variant AUTO takes: the wide tiles for products of at least 128
-// tokens and 512 weight rows with K a multiple of 16.
-int gemm_preferred_variant(int64_t m, int64_t n, int64_t k)
+// The GEMM variant AUTO takes: the tiled kernel.  Timed against the wide
+// tiles on the 3B-class M=512 and 70B-class M=128 products, it is as fast or
+// faster on every one (the wide kernel stays available by explicit path).
+int gemm_preferred_variant(int64_t, int64_t, int64_t)
 {
-    return (k % 16 == 0 && m >= 128 && n >= 512) ? GEMM_WIDE : GEMM_TILED;
+    return GEMM_TILED;
 }
 
 // One int32 partial tile per split: splits x M x N (largest over the blocks).

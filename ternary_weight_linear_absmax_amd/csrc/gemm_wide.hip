@@ -84,14 +84,15 @@ __device__ inline uint32_t word_p(const uint4 &v, int p)
 
 constexpr int lcm_int(int a, int b) { return a / gcd_int(a, b) * b; }
 
-template <int WWN>
-__global__ __launch_bounds__(256) void gemm_wide_kernel(
+template <int WWN, int KG>
+__global__ __launch_bounds__(256 * KG) void gemm_wide_kernel(
     const int8_t *__restrict__ xq, const int32_t *__restrict__ rowsum, int64_t m, int64_t k,
     const uint8_t *__restrict__ packed, int64_t n, int64_t pitch, int tiles_m, int64_t units,
     int64_t per_xcd, int splits, int stages_per, Out out, int64_t ldy, int32_t *__restrict__ ws)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][WBM * WLDA];
+    static_assert(KG == 1 || (KG == 2 && WWN == 2), "two k-groups with 64-column waves");
     constexpr int WBN = wbn<WWN>(), WEPL = wepl<WWN>();
+    __shared__ __attribute__((aligned(16))) uint8_t a_lds[KG][2][WBM * WLDA];
     __shared__ __attribute__((aligned(16))) int32_t e_lds[4][32 * WEPL];
     // blocks b, b + 8, ... run on one XCD: give each XCD a contiguous range of
     // units (the splits of a tile, then the token tiles of a weight-row
@@ -102,6 +103,7 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(
     const int64_t tile = u / splits;
     const int split = (int)(u % splits);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int kg = wave >> 2, wc = wave & 3, tg = tid & 255;   // k-group, column wave, thread in group
     const int h = lane >> 5, l32 = lane & 31;
     const int tm = (int)(tile % tiles_m);
     const int64_t tn = tile / tiles_m;
@@ -111,6 +113,15 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(
     int nk = nk_total - kt0;
     nk = nk < stages_per ? nk : stages_per;
     nk = nk > 0 ? nk : 0;
+    // the k-groups take consecutive halves of the slice's stages; both run
+    // nloop stages (one barrier each), stages past a group's own range are
+    // written as zeros
+    const int nloop = (nk + KG - 1) / KG;
+    const int g0 = kt0 + kg * nloop;                       // first stage of this group
+    int nk_g = nk - kg * nloop;
+    nk_g = nk_g < nloop ? nk_g : nloop;
+    nk_g = nk_g > 0 ? nk_g : 0;
+    const int64_t k_end = (int64_t)(g0 + nk_g) * WBK < k ? (int64_t)(g0 + nk_g) * WBK : k;
     const int ep_mode = splits > 1 ? WEP_PARTIAL : out.acc ? WEP_ACC : WEP_Y;
 
     v16i acc[2][WWN];
@@ -121,15 +132,14 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][s][r] = 0;
 
-    if (nk > 0) {
-        // per-lane byte offsets, fixed for the whole k loop (rows clamped into
-        // the matrices: clamped rows feed outputs that are never stored); a
-        // stage adds a uniform offset, clamped to the last stage of the slice
+    if (nloop > 0) {
+        // per-lane row bases, fixed for the whole k loop (rows clamped into
+        // the matrices: clamped rows feed outputs that are never stored)
         uint32_t aoff[2];
         int acol[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int e = tid + 256 * i;
+            const int e = tg + 256 * i;
             int64_t gm = m0 + (e >> 3);
             gm = gm < m ? gm : m - 1;
             acol[i] = (e & 7) * 16;
@@ -138,46 +148,42 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(
         uint32_t boff[WWN];
 #pragma unroll
         for (int s = 0; s < WWN; ++s) {
-            int64_t row = n0 + wave * 32 * WWN + 32 * s + l32;
+            int64_t row = n0 + wc * 32 * WWN + 32 * s + l32;
             row = row < n ? row : n - 1;
-            boff[s] = (uint32_t)(row * pitch + 16 * h);
+            boff[s] = (uint32_t)(row * pitch);
         }
-        const int8_t *abase = xq + (int64_t)kt0 * WBK;
-        const uint8_t *bbase = packed + (int64_t)kt0 * (WBK / 4);
-        const int64_t k_left = k - (int64_t)kt0 * WBK;   // k values from the slice start
+        const int last = nk_g > 0 ? nk_g - 1 : 0;
 
-        // Stage j of the slice (clamped to the last one; loads past it are
-        // never used).  Activation pieces past K read a clamped address and
-        // are zeroed when written to LDS; weight bytes past the row pitch read
-        // a clamped address and meet those zero activations.
+        // Stage j of the group (clamped to its last one).  Loads use in-row
+        // offsets clamped into the row, so every address is valid; activation
+        // pieces past the group's range or past K are zeroed when written to
+        // LDS, and the weight bytes they meet then contribute nothing.
         auto ld_a = [&](uint4 (&r)[2], int j) __attribute__((always_inline)) {
-            const int jj = j < nk ? j : nk - 1;
+            const int jj = j < last ? j : last;
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                int64_t kk = (int64_t)jj * WBK;
-                if (kk + acol[i] + 16 > k_left) kk = k_left - 16 - acol[i];   // in-row clamp
-                r[i] = load16(abase + aoff[i] + kk);
+                int64_t o = (int64_t)(g0 + jj) * WBK;
+                if (o > k - 16 - acol[i]) o = k - 16 - acol[i];
+                if (o < -acol[i]) o = -acol[i];
+                r[i] = load16(xq + aoff[i] + o);
             }
         };
         auto st_a = [&](uint8_t *buf, const uint4 (&r)[2], int j) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int e = tid + 256 * i;
+                const int e = tg + 256 * i;
                 uint4 v = r[i];
-                if ((int64_t)j * WBK + acol[i] >= k_left) v = make_uint4(0u, 0u, 0u, 0u);
+                if ((int64_t)(g0 + j) * WBK + acol[i] >= k_end) v = make_uint4(0u, 0u, 0u, 0u);
                 *(uint4 *)(buf + (e >> 3) * WLDA + (e & 7) * 16) = v;
             }
         };
-        // last stage offset at which this lane's 16 bytes still lie inside the
-        // row (a lane half whose bytes start past the pitch covers k >= K)
-        const int64_t b_lim = pitch - 16 - (int64_t)kt0 * (WBK / 4) - 16 * h;
         auto ld_b = [&](uint4 (&r)[WWN], int j) __attribute__((always_inline)) {
-            const int jj = j < nk ? j : nk - 1;
-            int64_t byte = (int64_t)jj * (WBK / 4);
-            byte = byte < b_lim ? byte : b_lim;
+            const int jj = j < last ? j : last;
+            int64_t byte = (int64_t)(g0 + jj) * (WBK / 4) + 16 * h;
+            byte = byte < pitch - 16 ? byte : pitch - 16;
 #pragma unroll
             for (int s = 0; s < WWN; ++s)
-                r[s] = WIDE_B_NT ? load_nt16(bbase + boff[s] + byte) : load16(bbase + boff[s] + byte);
+                r[s] = WIDE_B_NT ? load_nt16(packed + boff[s] + byte) : load16(packed + boff[s] + byte);
         };
         // this wave's A fragments of one stage: 4 k steps x 2 row blocks
         auto read_frags = [&](v4i (&af)[4][2], const uint8_t *buf) __attribute__((always_inline)) {
@@ -203,6 +209,7 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(
             }
         };
 
+        uint8_t(&abuf)[2][WBM * WLDA] = a_lds[kg];
         uint4 areg[WNA][2];
         uint4 breg[WNB][WWN];
         v4i af[2][4][2];
@@ -210,12 +217,12 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(
         for (int j = 0; j < WNB - 1; ++j) ld_b(breg[j], j);
         ld_a(areg[0], 0);
         ld_a(areg[1], 1);
-        st_a(a_lds[0], areg[0], 0);
-        st_a(a_lds[1], areg[1], 1);
+        st_a(abuf[0], areg[0], 0);
+        st_a(abuf[1], areg[1], 1);
 #pragma unroll
         for (int j = 0; j < WNA; ++j) ld_a(areg[j], 2 + j);
         __syncthreads();
-        read_frags(af[0], a_lds[0]);
+        read_frags(af[0], abuf[0]);
         __syncthreads();   // buffer 0 is rewritten in stage 0
 
         // Stage j: issue the weight loads of stage j + NB - 1, read the next
@@ -228,30 +235,54 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(
             constexpr int J = decltype(jc)::value;
             constexpr int C = J & 1;
             ld_b(breg[(J + WNB - 1) % WNB], j + WNB - 1);
-            read_frags(af[C ^ 1], a_lds[C ^ 1]);
+            read_frags(af[C ^ 1], abuf[C ^ 1]);
             __builtin_amdgcn_sched_barrier(0);
             mma(af[C], breg[J % WNB]);
             __builtin_amdgcn_sched_barrier(0);
-            if (j + 2 < nk) st_a(a_lds[C], areg[J % WNA], j + 2);
+            if (j + 2 < nloop) st_a(abuf[C], areg[J % WNA], j + 2);
             ld_a(areg[J % WNA], j + 2 + WNA);
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
         };
         constexpr int U = lcm_int(lcm_int(2, WNA), WNB);
-        const int nu = nk - nk % U;
+        const int nu = nloop - nloop % U;
         for (int j = 0; j < nu; j += U)
             static_for<U>([&](auto jc) __attribute__((always_inline)) { stage(jc, j + jc); });
         static_for<U - 1>([&](auto jc) __attribute__((always_inline)) {
-            if (nu + jc < nk) stage(jc, nu + jc);
+            if (nu + jc < nloop) stage(jc, nu + jc);
         });
+    }
+    if constexpr (KG == 2) {
+        // the second k-group's sums join the first's through LDS, one 32-row
+        // block at a time (the activation buffers are free after the loop)
+        int32_t *red = (int32_t *)&a_lds[0][0][0] + wc * (WWN * 16 * 64);
+        static_assert(4 * WWN * 16 * 64 * 4 <= KG * 2 * WBM * WLDA, "reduction fits");
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            __syncthreads();
+            if (kg == 1) {
+#pragma unroll
+                for (int s = 0; s < WWN; ++s)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) red[(s * 16 + r) * 64 + lane] = acc[a][s][r];
+            }
+            __syncthreads();
+            if (kg == 0) {
+#pragma unroll
+                for (int s = 0; s < WWN; ++s)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[a][s][r] += red[(s * 16 + r) * 64 + lane];
+            }
+        }
+        if (kg == 1) return;
     }
 
     // Epilogue through this wave's LDS area, 32 rows at a time: the
     // accumulators go in as written by the MFMA (register r of lane (l32, h)
     // is row 8(r/4) + 4h + r%4, column 32 s + l32), then every lane reads 4
     // consecutive columns of one row and stores 16 bytes.
-    int32_t *el = e_lds[wave];
-    const int64_t col0 = n0 + wave * 32 * WWN;
+    int32_t *el = e_lds[wc];
+    const int64_t col0 = n0 + wc * 32 * WWN;
     int32_t *dst = ep_mode == WEP_PARTIAL ? ws + (int64_t)split * m * n
                    : ep_mode == WEP_ACC   ? out.acc
                                           : (int32_t *)out.y;
@@ -326,12 +357,14 @@ GemmWide gemm_wide_config(int64_t m, int64_t n, int64_t k)
         // no empty slice: every slice starts before the end of the k range
         while (sp > 1 && (sp - 1) * ((nk + sp - 1) / sp) >= nk) --sp;
     }
-    return {wn, (int)sp};
+    // two k-groups per block (eight waves) only where the k range is split:
+    // timed faster there, slower on unsplit products
+    return {wn, (int)sp, (wn == 2 && sp > 1) ? 2 : 1};
 }
 
 int gemm_wide_splits(int64_t m, int64_t n, int64_t k) { return gemm_wide_config(m, n, k).splits; }
 
-template <int WWN>
+template <int WWN, int KG>
 static hipError_t launch_wide_wn(const int8_t *xq, const int32_t *rowsum, int64_t m,
                                  const uint8_t *packed, int64_t n, int64_t k, Out out, int splits,
                                  int32_t *ws, hipStream_t s, int64_t ldy)
@@ -341,7 +374,7 @@ static hipError_t launch_wide_wn(const int8_t *xq, const int32_t *rowsum, int64_
     const int64_t nk = (k + WBK - 1) / WBK;
     const int stages_per = (int)((nk + splits - 1) / splits);
     const int64_t per_xcd = (units + WNXCD - 1) / WNXCD;
-    hipLaunchKernelGGL((gemm_wide_kernel<WWN>), dim3((unsigned)(per_xcd * WNXCD)), dim3(256), 0, s,
+    hipLaunchKernelGGL((gemm_wide_kernel<WWN, KG>), dim3((unsigned)(per_xcd * WNXCD)), dim3(256 * KG), 0, s,
                        xq, rowsum, m, k, packed, n, pack2_pitch(k), tiles_m, units, per_xcd,
                        splits, stages_per, out, ldy, ws);
     return hipGetLastError();
@@ -351,9 +384,9 @@ hipError_t launch_gemm_wide_cfg(const int8_t *xq, const int32_t *rowsum, int64_t
                                 const uint8_t *packed, int64_t n, int64_t k, Out out,
                                 GemmWide c, int32_t *ws, hipStream_t s, int64_t ldy, bool finish)
 {
-    hipError_t e = c.wn == 4
-        ? launch_wide_wn<4>(xq, rowsum, m, packed, n, k, out, c.splits, ws, s, ldy)
-        : launch_wide_wn<2>(xq, rowsum, m, packed, n, k, out, c.splits, ws, s, ldy);
+    hipError_t e = c.wn == 4 ? launch_wide_wn<4, 1>(xq, rowsum, m, packed, n, k, out, c.splits, ws, s, ldy)
+                   : c.kg == 2 ? launch_wide_wn<2, 2>(xq, rowsum, m, packed, n, k, out, c.splits, ws, s, ldy)
+                               : launch_wide_wn<2, 1>(xq, rowsum, m, packed, n, k, out, c.splits, ws, s, ldy);
     if (e != hipSuccess || c.splits == 1 || !finish) return e;
     return launch_splitk_finish(ws, rowsum, m, n, c.splits, out, ldy, s);
 }

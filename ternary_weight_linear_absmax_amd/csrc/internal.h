@@ -141,7 +141,7 @@ int64_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int variant = GEMM
 // wide-tile kernel (gemm_wide.hip): columns per wave (32-column blocks, 2 or
 // 4) and k split for a shape, and one launch (plus the split-k finish when
 // finish is set and it splits)
-struct GemmWide { int wn, splits; };
+struct GemmWide { int wn, splits, kg; };   // kg: k-groups per block (2: eight waves)
 GemmWide gemm_wide_config(int64_t m, int64_t n, int64_t k);
 int gemm_wide_splits(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_wide_cfg(const int8_t *xq, const int32_t *rowsum, int64_t m,

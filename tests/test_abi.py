@@ -71,9 +71,9 @@ def test_path_selection(lib):
     assert bl.forward_path(16, 28672, 8192) == bl.BL_PATH_SKINNY
     assert bl.forward_path(16, 8640, 3200) == bl.BL_PATH_MFMA     # K % 256 != 0
     assert bl.forward_path(64, 3840, 2560) == bl.BL_PATH_MFMA
-    assert bl.forward_path(512, 8640, 3200) == bl.BL_PATH_MFMA_WIDE
+    assert bl.forward_path(512, 8640, 3200) == bl.BL_PATH_MFMA
     assert bl.forward_path(512, 8640, 3208) == bl.BL_PATH_MFMA      # K % 16 != 0
-    assert bl.forward_path(128, 28672, 8192) == bl.BL_PATH_MFMA_WIDE
+    assert bl.forward_path(128, 28672, 8192) == bl.BL_PATH_MFMA     # wide tiles by request only
     assert bl.forward_path(1, 28672, 8192, bl.BL_PACK3) == bl.BL_PATH_GEMV
 
 
