@@ -53,6 +53,9 @@ def parse():
                     help="comma-separated sections to run instead of the whole line (for "
                          "profiling): decode, xl, stack, prefill, variants, backward, ceilings, "
                          "cpu")
+    ap.add_argument("--graph-only", action="store_true",
+                    help="time only the graph replays (no eager or GEMV-alone runs), so that "
+                         "a kernel trace of the run holds graph-replayed dispatches only")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy kernel (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -170,10 +173,10 @@ def measure_decode(args):
 
     # one step = one replay of the captured step (120 launches at 30 layers)
     ms_step = graph_time(step, args.steps, args.warmup)
-    ms_step_eager = time_loop(step, max(2, args.steps // 10), 1)
+    ms_step_eager = None if args.graph_only else time_loop(step, max(2, args.steps // 10), 1)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    log(f"decode step {ms_step * 1e3:.1f} us (eager launches: {ms_step_eager * 1e3:.1f} us)"
-        f" -> {value:.1f} GB/s")
+    eager = "" if ms_step_eager is None else f" (eager launches: {ms_step_eager * 1e3:.1f} us)"
+    log(f"decode step {ms_step * 1e3:.1f} us{eager} -> {value:.1f} GB/s")
 
     # dominant kernel: the step is one launch per matrix (one-token quantisation
     # fused into the 2-bit GEMV), so its per-launch time is the step's
@@ -189,6 +192,10 @@ def measure_decode(args):
                 "avg_launch_us": round(us_per_launch, 3),
                 "algorithmic_bytes_per_launch": int(bytes_per_launch),
                 "per_matrix_bytes": {m["name"]: m["bytes"] for m in mats}}
+
+    if args.graph_only:
+        return dict(value=value, ms_step=ms_step, ms_step_eager=None, step_bytes=step_bytes,
+                    roofline=roofline, launches=launches)
 
     # the same GEMV on pre-quantised activations, timed alone over the same rotation
     def gemv_only():
@@ -255,7 +262,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(dec["ms_step"], 4) if dec else None,
-        "ms_per_step_eager_launch": round(dec["ms_step_eager"], 4) if dec else None,
+        "ms_per_step_eager_launch": (round(dec["ms_step_eager"], 4)
+                                     if dec and dec["ms_step_eager"] is not None else None),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -655,6 +663,28 @@ def measure_stack(layers=30, m=64, separate=True):
         log(f"{name} {layers} layers M={m}: {ms * 1e3:.1f} us/step, "
             f"{m / (ms * 1e-3):.0f} tokens/s")
     del stack
+    torch.cuda.empty_cache()
+
+    # one token through the same layers with the glue as the products'
+    # prologue / epilogue (RMSNorm + quantisation inside the GEMV, relu^2 * up
+    # in the up/gate epilogue): four launches per layer
+    stack1 = st.DecoderStack(weights, layers, 1, norm=True)
+    gen.manual_seed(4998)
+    x1 = torch.randn((1, st.HIDDEN), device="cuda", generator=gen)
+
+    def step1():
+        stack1.x.copy_(x1)
+        stack1.step()
+    ms = graph_time(step1, 20, 3)
+    pb1 = stack1.packed_bytes()
+    out["stack_2B_M1_norm_prologue"] = {
+        "layers": layers, "M": 1, "us_per_step": round(ms * 1e3, 1),
+        "tokens_per_s": round(1 / (ms * 1e-3), 1), "packed_bytes": pb1,
+        "GB/s": round(pb1 / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(pb1 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "launches_per_step": 4 * layers + 3}   # + input copy, last residual, output copy
+    log(f"stack_2B_M1_norm_prologue {layers} layers M=1: {ms * 1e3:.1f} us/step")
+    del stack1
     torch.cuda.empty_cache()
     return out
 
