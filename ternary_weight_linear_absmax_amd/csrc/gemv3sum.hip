@@ -170,8 +170,10 @@ hipError_t launch_gemv3sum(const int8_t *xq, const int32_t *rowsum, const uint8_
                            int64_t n, int64_t k, Out out, int32_t *ws, hipStream_t s)
 {
     const int slices = gemv3sum_slices(1, n, k);
-    // about one block per CU in total (the tables take most of the LDS)
-    int64_t rgroups = (256 + slices - 1) / slices;
+    // at most one block per CU in total (the tables take most of the LDS, so
+    // a block more than the CUs would run in a second round on its own)
+    int64_t rgroups = 256 / slices;
+    rgroups = rgroups < 1 ? 1 : rgroups;
     int64_t rows_per = (n + rgroups - 1) / rgroups;
     rows_per = (rows_per + 15) / 16 * 16;
     rgroups = (n + rows_per - 1) / rows_per;
