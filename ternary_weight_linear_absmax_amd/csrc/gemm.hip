@@ -506,22 +506,22 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
 // Iteration j (one block barrier each):
 //   producers: write stage j + 2 from registers to LDS slot (j + 2) % 3, then
 //              issue the global loads of stage j + 2 + R;
-//   math:      read the fragments of stage j + 1 from slot (j + 1) % 3 and run
-//              the MFMAs of stage j from registers.
+//   math:      run the MFMAs of stage j piece by piece (four pieces of 32 k),
+//              reading each piece's A fragments two pieces ahead: pieces 2
+//              and 3 of stage j, then pieces 0 and 1 and the weight words of
+//              stage j + 1 from slot (j + 1) % 3.
 // A slot is rewritten two iterations after its stage was read, so one barrier
 // per iteration orders every access.  Activation pieces past K are zero;
-// weight bytes past the row are clamped (they meet zero activations).
+// weight bytes past the row are clamped (they meet zero activations).  At
+// 122 VGPRs (four waves per SIMD) two 128 x 128 blocks share a CU.
 constexpr int LDB = 48;   // LDS row of a packed weight tile (32 bytes + pad)
 constexpr int G3_NS = 3;
 
 template <int WM, int WN, int R>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void gemm3_kernel(const int8_t *__restrict__ xq,
-                                                    const int32_t *__restrict__ rowsum,
-                                                    int64_t m, int64_t k,
-                                                    const uint8_t *__restrict__ packed, int64_t n,
-                                                    int64_t pitch, int tiles_m, int64_t tiles,
-                                                    int64_t per_xcd, int splits, int stages_per,
-                                                    Out out, int64_t ldy, int32_t *__restrict__ ws)
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void gemm3_kernel(
+    const int8_t *__restrict__ xq, const int32_t *__restrict__ rowsum, int64_t m, int64_t k,
+    const uint8_t *__restrict__ packed, int64_t n, int64_t pitch, int tiles_m, int64_t tiles,
+    int64_t per_xcd, int splits, int stages_per, Out out, int64_t ldy, int32_t *__restrict__ ws)
 {
     constexpr int BM = 64 * WM, BN = 64 * WN;
     constexpr int SA = BM * LDA, SB = BN * LDB, SS = SA + SB;     // bytes per stage slot
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
         return;
     }
     constexpr int U3 = G3_NS * R / gcd_int(G3_NS, R);
-    constexpr int U = U3 % 2 == 0 ? U3 : 2 * U3;   // ring slots and fragment parity fixed per J
+    constexpr int U = U3 % 2 == 0 ? U3 : 2 * U3;   // producer ring slots fixed per J
 
     if (producer) {
         const int pt = threadIdx.x - 256;
