@@ -24,14 +24,16 @@ inline bool known_path(int p)
 }
 
 // M = 1, 2: the vector kernel reads each weight word once per pass of up to
-// four tokens and is the fastest; 3..32 tokens: the weight-streaming
-// matrix-core kernel (one pass over the weights for all tokens; measured
-// faster than the tiled GEMM up to 32 tokens); more: a tiled GEMM, the wide
-// tiles for large products.
+// four tokens and is the fastest; 3..16 tokens: the weight-streaming
+// matrix-core kernel (one pass over the weights for all tokens), measured
+// faster than the tiled GEMM on every 2B- and 70B-class matrix; 17..32 tokens
+// (a second group of 16 token slots): still faster on matrices of up to 8192
+// rows, slower on the 13824- and 28672-row ones; more: a tiled GEMM.
 int choose_path(int64_t m, int64_t n, int64_t k, int layout)
 {
     if (layout == BL_PACK3 || m <= 2) return BL_PATH_GEMV;
-    if (m <= 32 && bl::skinny_supported(m, n, k)) return BL_PATH_SKINNY;
+    if ((m <= 16 || (m <= 32 && n <= 8192)) && bl::skinny_supported(m, n, k))
+        return BL_PATH_SKINNY;
     if (m <= 4) return BL_PATH_GEMV;
     return bl::gemm_preferred_variant(m, n, k) == bl::GEMM_WIDE ? BL_PATH_MFMA_WIDE : BL_PATH_MFMA;
 }

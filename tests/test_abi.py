@@ -69,6 +69,9 @@ def test_size_queries_match_the_layout_definitions(lib):
 def test_path_selection(lib):
     assert bl.forward_path(1, 28672, 8192) == bl.BL_PATH_GEMV
     assert bl.forward_path(16, 28672, 8192) == bl.BL_PATH_SKINNY
+    assert bl.forward_path(24, 3840, 2560) == bl.BL_PATH_SKINNY     # <= 8192 rows
+    assert bl.forward_path(24, 13824, 2560) == bl.BL_PATH_MFMA      # more rows: tiled
+    assert bl.forward_path(33, 3840, 2560) == bl.BL_PATH_MFMA
     assert bl.forward_path(16, 8640, 3200) == bl.BL_PATH_MFMA     # K % 256 != 0
     assert bl.forward_path(64, 3840, 2560) == bl.BL_PATH_MFMA
     assert bl.forward_path(512, 8640, 3200) == bl.BL_PATH_MFMA
