@@ -776,8 +776,7 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv_norm_kernel(
 {
     constexpr int R = GEMV_R, RB = GEMV_R * ST;
     __shared__ int part[GEMV_KS_MAX][GEMV_KS_MAX * RB];
-    __shared__ double red_d[GEMV_KS_MAX];
-    __shared__ float red_f[GEMV_KS_MAX];
+    __shared__ double red_d[GEMV_KS_MAX], red_vm[GEMV_KS_MAX];
     __shared__ int red_i[GEMV_KS_MAX];
     extern __shared__ uint4 q_lds[];   // the int8 token, K bytes (rounded up to 16)
     const int nthr = (int)blockDim.x, nw = nthr >> 6;
@@ -834,28 +833,20 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv_norm_kernel(
     for (int q = 0; q < PF; ++q) load(w[q], q);
     __builtin_amdgcn_sched_barrier(0);
 
-    // RMSNorm: sum of squares in double over the block
-    double ss = 0.0;
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) ss += v[j] * v[j];
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-    if (lane == 0) red_d[wave] = ss;
-    __syncthreads();
-    ss = 0.0;
-    for (int q = 0; q < nw; ++q) ss += red_d[q];
-    const double inv = 1.0 / sqrt(ss / (double)k + a.eps);
-    float h[EPT];
-    float amax = 0.0f;
+    // RMSNorm: sum of squares in double over the block, with max |v| in the
+    // same reduction (the quantiser's max |h| follows from it exactly)
+    double ss = 0.0, vm = 0.0;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-        h[j] = (float)(v[j] * inv);
-        amax = fmaxf(amax, fabsf(h[j]));
+        ss += v[j] * v[j];
+        vm = fmax(vm, fabs(v[j]));
     }
-    amax = wave_max_dpp(amax);
-    if (lane == 63) red_f[wave] = amax;
-    __syncthreads();
-    amax = 0.0f;
-    for (int q = 0; q < nw; ++q) amax = fmaxf(amax, red_f[q]);
+    block_ss_vmax(ss, vm, red_d, red_vm, nw);
+    const double inv = 1.0 / sqrt(ss / (double)k + a.eps);
+    float h[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) h[j] = (float)(v[j] * inv);
+    const float amax = vm > 0.0 ? (float)(vm * inv) : 0.0f;
     const float qs = act_scale(amax);
     int sum = 0;
     int8_t *ql = (int8_t *)q_lds;

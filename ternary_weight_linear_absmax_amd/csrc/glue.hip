@@ -23,27 +23,10 @@
 namespace bl {
 namespace {
 
-__device__ inline float block_max(float v, float *red)
-{
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    return v;
-}
-
-__device__ inline double block_sum_d(double v, double *red)
-{
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    return (red[0] + red[1]) + (red[2] + red[3]);
-}
-
 __device__ inline int block_sum_i(int v, int *red)
 {
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    v = wave_sum_dpp(v);
+    if ((threadIdx.x & 63) == 63) red[threadIdx.x >> 6] = v;
     __syncthreads();
     return (red[0] + red[1]) + (red[2] + red[3]);
 }
@@ -71,8 +54,7 @@ __global__ __launch_bounds__(256) void glue_kernel(GlueArgs a, int64_t k, double
                                                    float *__restrict__ scale,
                                                    int32_t *__restrict__ rowsum)
 {
-    __shared__ double red_d[4];
-    __shared__ float red_f[4];
+    __shared__ double red_d[4], red_vm[4];
     __shared__ int red_i[4];
     const int tid = threadIdx.x;
     const int64_t m = blockIdx.x;
@@ -163,7 +145,7 @@ __global__ __launch_bounds__(256) void glue_kernel(GlueArgs a, int64_t k, double
     const bool has_add = PART || a.add;
 
     double v[EPT];
-    double ss = 0.0;
+    double ss = 0.0, vm = 0.0;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
         const int i = tid + 256 * j;
@@ -179,18 +161,16 @@ __global__ __launch_bounds__(256) void glue_kernel(GlueArgs a, int64_t k, double
         }
         if (i >= kk) v[j] = 0.0;
         ss += v[j] * v[j];
+        vm = fmax(vm, fabs(v[j]));
     }
-    ss = block_sum_d(ss, red_d);
+    block_ss_vmax(ss, vm, red_d, red_vm, 4);
     const double inv = 1.0 / sqrt(ss / (double)k + eps);
 
     float h[EPT];
-    float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        h[j] = (float)(v[j] * inv);
-        amax = fmaxf(amax, fabsf(h[j]));
-    }
-    amax = block_max(amax, red_f);
+    for (int j = 0; j < EPT; ++j) h[j] = (float)(v[j] * inv);
+    // max |h| from max |v| (see block_ss_vmax); an all-zero row gives 0
+    const float amax = vm > 0.0 ? (float)(vm * inv) : 0.0f;
     const float s = act_scale(amax);
 
     int sum = 0;

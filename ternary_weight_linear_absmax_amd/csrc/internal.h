@@ -300,6 +300,60 @@ __device__ inline float wave_max_dpp(float v)
 }
 
 
+// The same patterns on doubles (two 32-bit DPP moves per step; disabled lanes
+// contribute 0.0): the sum, and the maximum of non-negative values, over the
+// wave, in lane 63.
+template <int CTRL, int ROWS>
+__device__ inline double dpp_d(double v)
+{
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROWS, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROWS, 0xF, false);
+    return __hiloint2double(hi, lo);
+}
+
+__device__ inline double wave_sum_dpp_d(double v)
+{
+    v += dpp_d<0xB1, 0xF>(v);
+    v += dpp_d<0x4E, 0xF>(v);
+    v += dpp_d<0x141, 0xF>(v);
+    v += dpp_d<0x140, 0xF>(v);
+    v += dpp_d<0x142, 0xA>(v);
+    v += dpp_d<0x143, 0xC>(v);
+    return v;
+}
+
+__device__ inline double wave_max_dpp_d(double v)
+{
+    v = fmax(v, dpp_d<0xB1, 0xF>(v));
+    v = fmax(v, dpp_d<0x4E, 0xF>(v));
+    v = fmax(v, dpp_d<0x141, 0xF>(v));
+    v = fmax(v, dpp_d<0x140, 0xF>(v));
+    v = fmax(v, dpp_d<0x142, 0xA>(v));
+    v = fmax(v, dpp_d<0x143, 0xC>(v));
+    return v;
+}
+
+// RMSNorm's two reductions in one pass: the sum of squares of v and max |v|
+// over the block (nw waves; red_ss and red_vm hold one entry per wave).  The
+// quantiser's max |h| with h = (float)(v * inv) is then (float)(max|v| * inv)
+// exactly, since v -> (float)(|v| * inv) is non-decreasing for inv > 0.
+__device__ inline void block_ss_vmax(double &ss, double &vm, double *red_ss, double *red_vm,
+                                     int nw)
+{
+    ss = wave_sum_dpp_d(ss);
+    vm = wave_max_dpp_d(vm);
+    if ((threadIdx.x & 63) == 63) {
+        red_ss[threadIdx.x >> 6] = ss;
+        red_vm[threadIdx.x >> 6] = vm;
+    }
+    __syncthreads();
+    ss = 0.0;
+    vm = 0.0;
+    for (int q = 0; q < nw; ++q) {
+        ss += red_ss[q];
+        vm = fmax(vm, red_vm[q]);
+    }
+}
 
 template <class F, int... I>
 __device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)

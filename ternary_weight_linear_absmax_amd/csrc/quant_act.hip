@@ -19,18 +19,6 @@
 namespace bl {
 namespace {
 
-__device__ inline float wave_max(float v)
-{
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
-}
-
-__device__ inline int wave_sum(int v)
-{
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
-
 
 // Vector path: 16-byte loads (8 bf16 or 4 fp32); requires K to be a multiple
 // of the vector width so that every row stays 16-byte aligned.
@@ -71,8 +59,8 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void *__restrict__
             amax = fmaxf(amax, fabsf(f));
         }
     }
-    amax = wave_max(amax);
-    if (lane == 0) red_f[wave] = amax;
+    amax = wave_max_dpp(amax);
+    if (lane == 63) red_f[wave] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
     const float s = act_scale_q(amax, qmax);
@@ -113,8 +101,8 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void *__restrict__
             qrow[i] = a;
         }
     }
-    sum = wave_sum(sum);
-    if (lane == 0) red_i[wave] = sum;
+    sum = wave_sum_dpp(sum);
+    if (lane == 63) red_i[wave] = sum;
     __syncthreads();
     if (tid == 0) {
         scale[m] = s;
@@ -161,8 +149,8 @@ __global__ __launch_bounds__(256) void quant_act_reg_kernel(const void *__restri
                 amax = fmaxf(amax, fabsf(__uint_as_float(w[e])));
         }
     }
-    amax = wave_max(amax);
-    if (lane == 0) red_f[wave] = amax;
+    amax = wave_max_dpp(amax);
+    if (lane == 63) red_f[wave] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
     const float s = act_scale_q(amax, qmax);
@@ -194,8 +182,8 @@ __global__ __launch_bounds__(256) void quant_act_reg_kernel(const void *__restri
             ((uint32_t *)qrow)[i] = out;
         }
     }
-    sum = wave_sum(sum);
-    if (lane == 0) red_i[wave] = sum;
+    sum = wave_sum_dpp(sum);
+    if (lane == 63) red_i[wave] = sum;
     __syncthreads();
     if (tid == 0) {
         scale[m] = s;
