@@ -16,7 +16,7 @@
 // the slice's packed bytes of its rows: a wave takes four rows at once, 16
 // lanes per row, 16 bytes per lane, so an instruction reads four contiguous
 // 256-byte runs (eight waves per block, two per SIMD, share the tables).
-// Each lane adds its 16 table entries, the row's 16 lanes are
+// Each lane adds its 16 table entries, the row's 16 lanes (one DPP row) are
 // summed, and the slice's partial sum of the row goes to its own slice of the
 // workspace; the split-k finish adds the slices in order, subtracts the row
 // sum and rescales.  One slice (K <= 1280) writes the outputs directly.
@@ -118,9 +118,12 @@ __global__ __launch_bounds__(64 * S3_WAVES) void gemv3sum_kernel(const int8_t *_
             acc += tbase[i * S3_STRIDE + byte];
         }
         acc = chunk_ok ? acc : 0;
-        // sum over the 16 lanes of the row
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
+        // sum over the 16 lanes of the row (a DPP row: pairs, quads, half
+        // rows, rows; every lane of the row ends with the sum)
+        acc += __builtin_amdgcn_update_dpp(0, acc, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+        acc += __builtin_amdgcn_update_dpp(0, acc, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+        acc += __builtin_amdgcn_update_dpp(0, acc, 0x141, 0xF, 0xF, false);   // row_half_mirror
+        acc += __builtin_amdgcn_update_dpp(0, acc, 0x140, 0xF, 0xF, false);   // row_mirror
         const int64_t row = r0 + 4 * (wave + S3_WAVES * j) + sub;
         if (c == 0 && row < r1) {
             if (part) {
