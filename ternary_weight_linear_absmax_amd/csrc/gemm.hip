@@ -691,7 +691,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
             v4i bf[WN];
 #pragma unroll
             for (int s = 0; s < WN; ++s) bf[s] = unpack_word(word_of(bw[s], P));
-            if (P < 2) {
+            if constexpr (P < 2) {
                 read_a(af[P + 2], slot, P + 2);
             } else {
                 read_a(af[P - 2], nslot, P - 2);
