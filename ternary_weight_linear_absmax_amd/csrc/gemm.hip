@@ -28,7 +28,10 @@
 // the loop every address is a per-lane offset fixed at the start plus a
 // uniform stage offset, so the stage costs no address arithmetic.  Blocks are
 // numbered so that consecutive tiles (which share weight columns) land on the
-// same XCD and its L2.
+// same XCD and its L2.  Tiles with two weight-column blocks per wave (WN >= 2)
+// run the warp-specialised variant further down instead: producer waves move
+// both operands of each stage straight from global memory into an LDS ring
+// (gfx950 direct loads), and the math waves read both from LDS.
 //
 // Split-K (S > 1 slices of the k range) stores each slice's int32 partial
 // tile into its own slice of a workspace [S][M][N] (plain stores, no
@@ -178,8 +181,8 @@ __device__ __forceinline__ void st_a(uint8_t *lds_buf, const uint4 (&r)[BM / 32]
 #ifndef GEMM_SPECIALISED
 #define GEMM_SPECIALISED 1
 #endif
-#ifndef GEMM3_R
-#define GEMM3_R 3
+#ifndef GEMM3_NS
+#define GEMM3_NS 4
 #endif
 #ifndef GEMM_NB
 #define GEMM_NB 4
@@ -498,39 +501,71 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
 
 // ---- warp-specialised variant ------------------------------------------------
 // Eight waves: four math waves (the 2 x 2 arrangement above) and four
-// producer waves.  With one math wave per SIMD, a wave that issues the stage's
-// global loads stalls its own MFMAs while the loads are accepted; here the
-// producers own every global load, and the math waves read both operands from
-// LDS.  LDS holds a ring of NS = 3 stages (activations [BM][LDA] and packed
-// weights [BN][LDB]); producers keep R stages of loads in flight in registers.
+// producer waves.  The producers move every stage from global memory straight
+// into LDS with gfx950's direct loads (global_load_lds_dwordx4: each
+// instruction writes 64 x 16 bytes, lane i at byte 16 i of a 1 KB block), so
+// no stage passes through registers and no ds_write competes with the math
+// waves' fragment reads (measured: LDS reads next to direct loads run at
+// their full rate, next to ds_write_b128 at about 60% of it).  LDS holds a
+// ring of NS stages, each activations [BM][128] and packed weights [BN][32]
+// without padding; the 16-byte chunks of a row are permuted (activations:
+// chunk c of row r at c ^ g3_fa(r); weights: half h at h ^ g3_fb(r)) so that
+// a fragment read of 16 consecutive rows touches 16 distinct 16-byte bank
+// groups, which is what the padding did before.
 // Iteration j (one block barrier each):
-//   producers: write stage j + 2 from registers to LDS slot (j + 2) % 3, then
-//              issue the global loads of stage j + 2 + R;
+//   producers: issue stage j + NS - 1 into the slot of stage j - 1 (read for
+//              the last time in iteration j - 1), then wait until stage j + 2
+//              has landed (NS - 3 stages stay in flight across the barrier);
 //   math:      run the MFMAs of stage j piece by piece (four pieces of 32 k),
 //              reading each piece's A fragments two pieces ahead: pieces 2
 //              and 3 of stage j, then pieces 0 and 1 and the weight words of
-//              stage j + 1 from slot (j + 1) % 3.
-// A slot is rewritten two iterations after its stage was read, so one barrier
-// per iteration orders every access.  Activation pieces past K are zero;
-// weight bytes past the row are clamped (they meet zero activations).  At
-// 122 VGPRs (four waves per SIMD) two 128 x 128 blocks share a CU.
-constexpr int LDB = 48;   // LDS row of a packed weight tile (32 bytes + pad)
-constexpr int G3_NS = 3;
+//              stage j + 1.
+// Producers wait on their own load counter and pass the barrier without a
+// memory fence: a fence there would drain every load in flight.  Loads of a
+// stage that ends past K are clamped into their rows; the activation chunks
+// past K are then zeroed in LDS (weights past K meet zero activations).
+constexpr int G3_LB = BK / 4;   // bytes of one packed weight row per stage
 
-template <int WM, int WN, int R>
+__device__ inline int g3_fa(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ inline int g3_fb(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+
+// s_waitcnt operand: at most v vector-memory operations outstanding, the
+// other counters left free.
+constexpr unsigned g3_vmcnt(int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr unsigned G3_LGKM0 = 15 | (3 << 14) | (7 << 4);   // lgkmcnt(0) only
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ inline void g3_dma16(const void *src, uint8_t *dst)
+{
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)dst, 16, 0, 0);
+}
+
+// Block barrier of the producer waves: no fence, so direct loads stay in
+// flight; the compiler may not move memory accesses across it.
+__device__ inline void g3_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int WM, int WN, int NS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void gemm3_kernel(
     const int8_t *__restrict__ xq, const int32_t *__restrict__ rowsum, int64_t m, int64_t k,
     const uint8_t *__restrict__ packed, int64_t n, int64_t pitch, int tiles_m, int64_t tiles,
     int64_t per_xcd, int splits, int stages_per, Out out, int64_t ldy, int32_t *__restrict__ ws)
 {
+    static_assert(WN >= 2 && NS >= 4, "weight tiles of whole 1 KB transfers, two stages in flight");
     constexpr int BM = 64 * WM, BN = 64 * WN;
-    constexpr int SA = BM * LDA, SB = BN * LDB, SS = SA + SB;     // bytes per stage slot
-    constexpr int PA = BM / 32;                                   // activation pieces / producer
-    constexpr int PB = (BN * 2 + 255) / 256;                      // weight pieces / producer
-    __shared__ __attribute__((aligned(16))) uint8_t lds[G3_NS * SS];
+    constexpr int SA = BM * BK, SB = BN * G3_LB, SS = SA + SB;    // bytes per stage slot
+    constexpr int PA = BM / 32;          // 1 KB activation transfers per producer wave and stage
+    constexpr int PB = BN / 128;         // 1 KB weight transfers per producer wave and stage
+    constexpr int PT = PA + PB;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NS * SS];
     __shared__ int32_t ep_rs[BM];
     __shared__ double ep_gs[BM];
-    static_assert(ep_tile_bytes<BM, BN>() <= G3_NS * SS, "the output tile fits the LDS ring");
+    static_assert(ep_tile_bytes<BM, BN>() <= NS * SS, "the output tile fits the LDS ring");
     const int64_t t = tile_of_block(blockIdx.x, per_xcd);
     if (t >= tiles * splits) return;
     const int64_t tile = t / splits;
@@ -556,93 +591,88 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
         }
         return;
     }
-    constexpr int U3 = G3_NS * R / gcd_int(G3_NS, R);
-    constexpr int U = U3 % 2 == 0 ? U3 : 2 * U3;   // producer ring slots fixed per J
 
     if (producer) {
-        const int pt = threadIdx.x - 256;
-        // per-thread sources, fixed for the loop (rows clamped into the matrices)
-        uint32_t aoff[PA], alds[PA];
-        int acol[PA];
+        const int pw = wave - 4;
+        // Per-lane sources, fixed for the loop: transfer q of this wave fills
+        // LDS bytes [1024 qi, 1024 qi + 1024) of the slot's activation (or
+        // weight) part, qi = pw * PA + q (or pw * PB + q); lane i writes the
+        // chunk at byte 16 i of it.  Rows are clamped into the matrices.
+        uint32_t aoff[PA], boff[PB];
+        int acol[PA], bhalf[PB];
 #pragma unroll
-        for (int i = 0; i < PA; ++i) {
-            const int e = pt + 256 * i;
-            int64_t gm = m0 + (e >> 3);
+        for (int q = 0; q < PA; ++q) {
+            const int r = 8 * (pw * PA + q) + (lane >> 3);
+            const int c = (lane & 7) ^ g3_fa(r);
+            int64_t gm = m0 + r;
             gm = gm < m ? gm : m - 1;
-            acol[i] = (e & 7) * 16;
-            aoff[i] = (uint32_t)(gm * k + acol[i]);
-            alds[i] = (uint32_t)((e >> 3) * LDA + acol[i]);
+            acol[q] = 16 * c;
+            aoff[q] = (uint32_t)(gm * k + 16 * c);
         }
-        uint32_t boff[PB], blds[PB];
-        int bhalf[PB];
-        bool bon[PB];
 #pragma unroll
-        for (int i = 0; i < PB; ++i) {
-            const int e = pt + 256 * i;
-            bon[i] = e < BN * 2;
-            int64_t row = n0 + (e >> 1);
+        for (int q = 0; q < PB; ++q) {
+            const int r = 32 * (pw * PB + q) + (lane >> 1);
+            const int hh = (lane & 1) ^ g3_fb(r);
+            int64_t row = n0 + r;
             row = row < n ? row : n - 1;
-            bhalf[i] = 16 * (e & 1);
-            boff[i] = (uint32_t)(row * pitch);
-            blds[i] = (uint32_t)(SA + (e >> 1) * LDB + 16 * (e & 1));
+            bhalf[q] = 16 * hh;
+            boff[q] = (uint32_t)(row * pitch + 16 * hh);
         }
-        uint4 ra[R][PA], rb[R][PB];
-        auto gload = [&](uint4 (&a)[PA], uint4 (&b)[PB], int st) __attribute__((always_inline)) {
-            const int sc = st < nk ? st : nk - 1;
-            const int64_t k0 = (int64_t)(kt0 + sc) * BK;
+        const int full_end = (int)(k / BK) - kt0;   // stages [0, full_end) lie inside K
+        auto issue = [&](int st) __attribute__((always_inline)) {
+            uint8_t *slot = lds + (st % NS) * SS;
+            const int64_t k0 = (int64_t)(kt0 + st) * BK;
+            if (st < full_end) {
+                const int8_t *ab = xq + k0;
+                const uint8_t *bb = packed + k0 / 4;
 #pragma unroll
-            for (int i = 0; i < PA; ++i) {
-                const int64_t kk = k0 + acol[i] < k ? k0 : k - 16 - acol[i];
-                a[i] = load16(xq + aoff[i] + kk);
+                for (int q = 0; q < PA; ++q) g3_dma16(ab + aoff[q], slot + 1024 * (pw * PA + q));
+#pragma unroll
+                for (int q = 0; q < PB; ++q) g3_dma16(bb + boff[q], slot + SA + 1024 * (pw * PB + q));
+                return;
             }
 #pragma unroll
-            for (int i = 0; i < PB; ++i) {
-                int64_t byte = k0 / 4 + bhalf[i];
-                byte = byte + 16 <= pitch ? byte : pitch - 16;
-                b[i] = GEMM_B_NT ? load_nt16(packed + boff[i] + byte) : load16(packed + boff[i] + byte);
+            for (int q = 0; q < PA; ++q) {
+                const int64_t kk = k0 + acol[q] < k ? k0 : k - 16 - acol[q];
+                g3_dma16(xq + aoff[q] + kk, slot + 1024 * (pw * PA + q));
+            }
+#pragma unroll
+            for (int q = 0; q < PB; ++q) {
+                int64_t byte = k0 / 4;
+                byte = byte + bhalf[q] + 16 <= pitch ? byte : pitch - 16 - bhalf[q];
+                g3_dma16(packed + boff[q] + byte, slot + SA + 1024 * (pw * PB + q));
             }
         };
-        auto lstore = [&](const uint4 (&a)[PA], const uint4 (&b)[PB], int st)
-            __attribute__((always_inline)) {
-            uint8_t *slot = lds + (st % G3_NS) * SS;
+        // Activation chunks past K of the stage st (once its loads have landed).
+        auto zero_tail = [&](int st) __attribute__((always_inline)) {
+            if (st < full_end || st >= nk) return;
+            uint8_t *slot = lds + (st % NS) * SS;
             const int64_t k0 = (int64_t)(kt0 + st) * BK;
 #pragma unroll
-            for (int i = 0; i < PA; ++i)
-                *(uint4 *)(slot + alds[i]) = (k0 + acol[i] < k) ? a[i] : zero4();
-#pragma unroll
-            for (int i = 0; i < PB; ++i)
-                if (bon[i]) *(uint4 *)(slot + blds[i]) = b[i];
+            for (int q = 0; q < PA; ++q)
+                if (k0 + acol[q] >= k) *(uint4 *)(slot + 1024 * (pw * PA + q) + 16 * lane) = zero4();
         };
-        // prologue: stages 0 and 1 straight into LDS, stages 2 .. 2+R-1 in
-        // flight (each stage's registers are written to LDS before the next
-        // loads are issued, which bounds the registers held at once)
-        {
-            uint4 a0[PA], b0[PB], a1[PA], b1[PB];
-            gload(a0, b0, 0);
-            gload(a1, b1, 1);
-            // row operands of the epilogue (visible after the first barrier),
-            // read while the stage loads are in flight
-            ep_rows<BM>(pt, m0, m, rowsum, out, ep_mode, ep_rs, ep_gs);
-            lstore(a0, b0, 0);
-            gload(ra[2 % R], rb[2 % R], 2);
-            if (nk > 1) lstore(a1, b1, 1);
-#pragma unroll
-            for (int r = 1; r < R; ++r) gload(ra[(2 + r) % R], rb[(2 + r) % R], 2 + r);
-        }
-        __syncthreads();
-        auto iter = [&](auto jc, int j) __attribute__((always_inline)) {
-            constexpr int J = decltype(jc)::value;
-            constexpr int RS = (J + 2) % R;
-            if (j + 2 < nk) lstore(ra[RS], rb[RS], j + 2);
-            gload(ra[RS], rb[RS], j + 2 + R);
-            __syncthreads();
-        };
-        const int nu = nk - nk % U;
-        for (int j = 0; j < nu; j += U)
-            static_for<U>([&](auto jc) __attribute__((always_inline)) { iter(jc, j + jc); });
-        static_for<U - 1>([&](auto jc) __attribute__((always_inline)) {
-            if (nu + jc < nk) iter(jc, nu + jc);
+        // prologue: stages 0 .. NS - 2 in flight; stages 0 and 1 landed
+        static_for<NS - 1>([&](auto sc) __attribute__((always_inline)) {
+            if (decltype(sc)::value < nk) issue(decltype(sc)::value);
         });
+        if (nk >= NS - 1) __builtin_amdgcn_s_waitcnt(g3_vmcnt((NS - 3) * PT));
+        else __builtin_amdgcn_s_waitcnt(g3_vmcnt(0));
+        zero_tail(0);
+        zero_tail(1);
+        __builtin_amdgcn_s_waitcnt(G3_LGKM0);
+        g3_barrier();
+        for (int j = 0; j < nk; ++j) {
+            if (j + NS - 1 < nk) {
+                issue(j + NS - 1);
+                __builtin_amdgcn_s_waitcnt(g3_vmcnt((NS - 3) * PT));
+            } else {
+                __builtin_amdgcn_s_waitcnt(g3_vmcnt(0));
+                zero_tail(j + 2);
+                __builtin_amdgcn_s_waitcnt(G3_LGKM0);
+            }
+            g3_barrier();
+        }
     } else {
     // ---- math waves ----
     const int wm = wave & 1, wn = wave >> 1;
@@ -655,26 +685,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][s][r] = 0;
 
+    // row operands of the epilogue, visible after the first barrier
+    ep_rows<BM>(threadIdx.x, m0, m, rowsum, out, ep_mode, ep_rs, ep_gs);
     // Fragments stream two k pieces ahead of the MFMAs: while the MFMAs of
     // piece p of stage j run, piece p + 2 is read from LDS (pieces 0 and 1 of
     // stage j + 1 during pieces 2 and 3, with the stage's weight words).
-    // Keeping four pieces of A and two stages of weight words live holds the
-    // wave to 128 registers, so two blocks share a CU and one block's MFMAs
-    // fill the other's waits.  The last stage also reads a next stage that
+    // Four pieces of A and two stages of weight words are live: 77 registers
+    // with 64 x 128 tiles, so with the 49 KB ring three blocks share a CU and
+    // fill each other's waits.  The last stage also reads a next stage that
     // does not exist: those reads stay inside the LDS ring and their values
     // are never used.
     auto read_a = [&](v4i (&a)[WM], const uint8_t *slot, int p) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < WM; ++i) {
             const int row = wm * 32 * WM + 32 * i + l32;
-            const uint4 v = load16(slot + row * LDA + 64 * h + 16 * p);
+            const uint4 v = load16(slot + row * BK + 16 * ((4 * h + p) ^ g3_fa(row)));
             a[i] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
         }
     };
     auto read_b = [&](uint4 (&b)[WN], const uint8_t *slot) __attribute__((always_inline)) {
 #pragma unroll
-        for (int s = 0; s < WN; ++s)
-            b[s] = load16(slot + SA + (wn * 32 * WN + 32 * s + l32) * LDB + 16 * h);
+        for (int s = 0; s < WN; ++s) {
+            const int row = wn * 32 * WN + 32 * s + l32;
+            b[s] = load16(slot + SA + row * G3_LB + 16 * (h ^ g3_fb(row)));
+        }
     };
     v4i af[4][WM];
     uint4 bw[WN], bn[WN];
@@ -684,7 +718,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
     read_b(bw, lds);
     int cur = 0;              // ring slot of stage j
     for (int j = 0; j < nk; ++j) {
-        const int nxt = cur == G3_NS - 1 ? 0 : cur + 1;
+        const int nxt = cur == NS - 1 ? 0 : cur + 1;
         const uint8_t *slot = lds + cur * SS, *nslot = lds + nxt * SS;
         static_for<4>([&](auto pc) __attribute__((always_inline)) {
             constexpr int P = decltype(pc)::value;
@@ -798,10 +832,11 @@ GemmCfg gemm_config(int64_t m, int64_t n, int64_t k, int variant = GEMM_TILED)
     // and 70B-class shapes.  M <= 64, or a product with few 64 x 64 tiles:
     // 64 x 64 tiles, the k range split (up to four ways, at least six stages
     // each) when there are few of them.
-    // Larger: 128 x 128 tiles when they fill one round of the 256 CUs or many;
-    // 64 x 128 tiles when 128 x 128 ones would spill a few tiles into a second
-    // round, or when 128 x 128 ones are too few and 64 x 128 ones still fill
-    // most of the chip; else 128 x 128 tiles with the k range split.
+    // Larger: 128 x 128 tiles (one block per CU, its LDS ring takes half the
+    // CU's LDS) when they fill one round of the 256 CUs; 64 x 128 tiles (three
+    // blocks per CU) when there are more, or when 128 x 128 ones are too few
+    // and 64 x 128 ones still fill most of the chip; else 128 x 128 tiles with
+    // the k range split.
     const int64_t nk = (k + BK - 1) / BK;
     auto tiles = [&](int wm, int wn) {
         return ((m + 64 * wm - 1) / (64 * wm)) * ((n + 64 * wn - 1) / (64 * wn));
@@ -815,8 +850,7 @@ GemmCfg gemm_config(int64_t m, int64_t n, int64_t k, int variant = GEMM_TILED)
     }
     const int64_t t22 = tiles(2, 2);
     if (t22 >= 192 && t22 <= 256) return {2, 2, 1, false};
-    if (t22 > 256 && t22 < 512) return {1, 2, 1, false};
-    if (t22 >= 512) return {2, 2, 1, false};
+    if (t22 > 256) return {1, 2, 1, false};
     // 64 x 128 tiles that fill most of the chip beat 128 x 128 tiles with the
     // k range split (no partial sums to write, read back and add)
     if (tiles(1, 2) >= 192) return {1, 2, 1, false};
@@ -880,10 +914,17 @@ hipError_t launch_gemm_cfg(const int8_t *xq, const int32_t *rowsum, int64_t m,
     if (ldy < 0) ldy = n;
     // the producer/consumer kernel pays off once a block has two weight-column
     // blocks per wave (WN >= 2); narrower tiles keep the single-role kernel
-    if (k % 16 == 0 && GEMM_SPECIALISED && WN >= 2)
-        hipLaunchKernelGGL((gemm3_kernel<WM, WN, GEMM3_R>), grid, dim3(512), 0, s, xq, rowsum, m,
-                           k, packed, n, pitch, tiles_m, tiles, per_xcd, splits, stages_per, out,
-                           ldy, ws);
+    bool specialised = false;
+    if constexpr (WN >= 2) {
+        if (k % 16 == 0 && GEMM_SPECIALISED) {
+            hipLaunchKernelGGL((gemm3_kernel<WM, WN, GEMM3_NS>), grid, dim3(512), 0, s, xq, rowsum,
+                               m, k, packed, n, pitch, tiles_m, tiles, per_xcd, splits, stages_per,
+                               out, ldy, ws);
+            specialised = true;
+        }
+    }
+    if (specialised)
+        ;
     else if (k % 16 == 0)
         hipLaunchKernelGGL((gemm2_kernel<WM, WN, true>), grid, block, 0, s, xq, rowsum, m, k,
                            packed, n, pitch, tiles_m, tiles, per_xcd, splits, stages_per, out, ldy,
