@@ -306,6 +306,8 @@ def _ceilings_lib():
     lib.blc_mfma_i8_loop.restype = i32
     lib.blc_empty.argtypes = [p]
     lib.blc_empty.restype = i32
+    lib.blc_lds_mix.argtypes = [i32, i32, i32, i32, p, i64, p, p]
+    lib.blc_lds_mix.restype = i32
     return lib
 
 
@@ -401,6 +403,46 @@ def measure_ceilings(args):
     out["mfma_i8_loop_TOPS"] = round(tops, 1)
     out["mfma_i8_loop_frac_of_peak"] = round(tops / I8_PEAK_TOPS, 4)
     log(f"ceiling: int8 matrix-core loop {tops:.0f} TOPS")
+    out.update(measure_lds_mix(lib, chk, st, sp))
+    return out
+
+
+def measure_lds_mix(lib, chk, st, sp):
+    """LDS traffic in the tiled GEMM's patterns, two 512-thread blocks per CU
+    (blc_lds_mix): the fragment reads of four waves alone, 16-byte LDS writes
+    of the other four waves alone (as ds_write_b128, or as direct
+    global-to-LDS loads from an 8 MiB window), and both together.  Run
+    together, the reads and writes overlap fully when the time is the longer
+    of the two alone and not at all when it is their sum; `overlap` is
+    (alone_r + alone_w - together) / min(alone_r, alone_w)."""
+    import ctypes
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 2 * cus
+    window = 8 << 20
+    src = torch.ones((window,), dtype=torch.uint8, device="cuda")
+    srcp = ctypes.c_void_p(src.data_ptr())
+    it_r = 2000
+    out = {}
+
+    def t(mode, ir, iw):
+        return graph_time(lambda: chk(lib.blc_lds_mix(mode, ir, iw, blocks, srcp, window, sp,
+                                                      st())), 5, 1) * 1e3
+    read_us = t(0, it_r, 0)
+    per_cu_read = 2 * it_r * 16384 / (read_us * 1e-6) / 1e9
+    out["lds_read_alone_us"] = round(read_us, 1)
+    out["lds_read_GB/s_per_CU"] = round(per_cu_read, 1)
+    for name, mode, it_w in (("ds_write_b128", 1, 4000), ("direct_load", 2, 2400)):
+        w_us = t(mode, 0, it_w)
+        both_us = t(mode, it_r, it_w)
+        ov = (read_us + w_us - both_us) / min(read_us, w_us)
+        out[f"lds_{name}_alone_us"] = round(w_us, 1)
+        out[f"lds_{name}_GB/s_per_CU"] = round(2 * it_w * 4096 / (w_us * 1e-6) / 1e9, 1)
+        out[f"lds_read_with_{name}_us"] = round(both_us, 1)
+        out[f"lds_read_with_{name}_overlap"] = round(ov, 3)
+        log(f"ceiling: LDS fragment reads {read_us:.0f} us alone, {name} {w_us:.0f} us alone, "
+            f"{both_us:.0f} us together (overlap {ov:.2f})")
+    del src
     return out
 
 

@@ -36,6 +36,19 @@ int blc_mfma_i8_loop(int iters, int blocks, int32_t *sink, hipStream_t stream);
 /* One block of one wave that does nothing: the cost of a launch. */
 int blc_empty(hipStream_t stream);
 
+/* LDS traffic in the tiled GEMM's patterns, `blocks` blocks of 512 threads.
+ * Waves 0-3 run `it_r` steps of four 16-byte LDS reads per lane (rows of a
+ * padded 144-byte-pitch tile, the fragment pattern: 4 KB per wave and step);
+ * waves 4-7 run `it_w` 16-byte LDS writes per lane: mode 0 none, mode 1
+ * ds_write_b128 stores (8 lanes per 128-byte row of the same layout), mode 2
+ * direct global-to-LDS loads (1 KB of LDS per wave and step) from the first
+ * `window` bytes of `src` (16-byte aligned, at least 1 MiB, a multiple of
+ * 16; unused otherwise).  Timing a mode against the readers alone and the
+ * writers alone shows how much the two kinds of LDS write slow the reads.
+ * `sink` as above. */
+int blc_lds_mix(int mode, int it_r, int it_w, int blocks, const void *src, int64_t window,
+                uint32_t *sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -181,9 +181,22 @@ __device__ __forceinline__ void st_a(uint8_t *lds_buf, const uint4 (&r)[BM / 32]
 #ifndef GEMM_SPECIALISED
 #define GEMM_SPECIALISED 1
 #endif
-#ifndef GEMM3_NS
-#define GEMM3_NS 4
+// Stages in the LDS ring of the warp-specialised kernel: four for 64 x 128
+// tiles (a 49 KB ring, three blocks per CU), six for 128 x 128 tiles (one
+// block per CU either way; the deeper ring keeps three stages of loads in
+// flight, which pays when the weights stream from HBM).  Timed with ten
+// rotating weight copies: 64 x 128 with six stages 28.3 against 24.9 us on
+// 512 x 8640 x 3200; 128 x 128 with four stages 39.8 against 38.7 us on
+// 128 x 28672 x 8192.
+template <int WM, int WN>
+constexpr int gemm3_ring()
+{
+#ifdef GEMM3_NS
+    return GEMM3_NS;
+#else
+    return WM == 1 ? 4 : 6;
 #endif
+}
 #ifndef GEMM_NB
 #define GEMM_NB 4
 #endif
@@ -832,8 +845,8 @@ GemmCfg gemm_config(int64_t m, int64_t n, int64_t k, int variant = GEMM_TILED)
     // and 70B-class shapes.  M <= 64, or a product with few 64 x 64 tiles:
     // 64 x 64 tiles, the k range split (up to four ways, at least six stages
     // each) when there are few of them.
-    // Larger: 128 x 128 tiles (one block per CU, its LDS ring takes half the
-    // CU's LDS) when they fill one round of the 256 CUs; 64 x 128 tiles (three
+    // Larger: 128 x 128 tiles (one block per CU, its six-stage LDS ring takes
+    // 120 KB) when they fill one round of the 256 CUs; 64 x 128 tiles (three
     // blocks per CU) when there are more, or when 128 x 128 ones are too few
     // and 64 x 128 ones still fill most of the chip; else 128 x 128 tiles with
     // the k range split.
@@ -917,9 +930,9 @@ hipError_t launch_gemm_cfg(const int8_t *xq, const int32_t *rowsum, int64_t m,
     bool specialised = false;
     if constexpr (WN >= 2) {
         if (k % 16 == 0 && GEMM_SPECIALISED) {
-            hipLaunchKernelGGL((gemm3_kernel<WM, WN, GEMM3_NS>), grid, dim3(512), 0, s, xq, rowsum,
-                               m, k, packed, n, pitch, tiles_m, tiles, per_xcd, splits, stages_per,
-                               out, ldy, ws);
+            hipLaunchKernelGGL((gemm3_kernel<WM, WN, gemm3_ring<WM, WN>()>), grid, dim3(512), 0,
+                               s, xq, rowsum, m, k, packed, n, pitch, tiles_m, tiles, per_xcd,
+                               splits, stages_per, out, ldy, ws);
             specialised = true;
         }
     }

@@ -35,7 +35,7 @@ def test_ceilings_library_exports_its_header():
     clib = ctypes.CDLL(path)
     header = os.path.join(os.path.dirname(bl.HEADER), "bitlinear_ceilings.h")
     names = sorted(set(re.findall(r"\b(blc_\w+)\s*\(", open(header).read())))
-    assert len(names) == 4
+    assert len(names) == 5
     for name in names:
         assert hasattr(clib, name), name
     clib.blc_mfma_i8_ops.restype = ctypes.c_int64
@@ -44,6 +44,12 @@ def test_ceilings_library_exports_its_header():
                                      ctypes.c_void_p, ctypes.c_void_p]
     assert clib.blc_read_stream(P, 15, 1, P, None) == -1        # not whole 16-byte vectors
     assert clib.blc_read_stream(ODD, 64, 1, P, None) == -1      # misaligned
+    clib.blc_lds_mix.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_int64,
+                                                      ctypes.c_void_p, ctypes.c_void_p]
+    assert clib.blc_lds_mix(3, 1, 1, 1, P, 1 << 20, P, None) == -1   # no such mode
+    assert clib.blc_lds_mix(2, 1, 1, 1, None, 1 << 20, P, None) == -1  # direct loads, no source
+    assert clib.blc_lds_mix(2, 1, 1, 1, P, 4096, P, None) == -1      # window under 1 MiB
+    assert clib.blc_lds_mix(0, 1, 1, 1, P, 0, None, None) == -1      # no sink
 
 
 def test_size_queries_match_the_layout_definitions(lib):
