@@ -756,7 +756,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
 #pragma unroll
         for (int s = 0; s < WN; ++s) bw[s] = bn[s];
         cur = nxt;
-        __syncthreads();
+        // No fence: the fragment reads still in flight here are of stage
+        // j + 1, whose slot is refilled only after three more barriers, and
+        // every read of stage j has been consumed by this stage's MFMAs; so
+        // their latency overlaps the barrier instead of preceding it.
+        g3_barrier();
     }
 
     // Epilogue: the accumulators into the output tile in the ring (every
