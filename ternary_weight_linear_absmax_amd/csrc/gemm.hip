@@ -703,7 +703,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
     // Fragments stream two k pieces ahead of the MFMAs: while the MFMAs of
     // piece p of stage j run, piece p + 2 is read from LDS (pieces 0 and 1 of
     // stage j + 1 during pieces 2 and 3, with the stage's weight words).
-    // Four pieces of A and two stages of weight words are live: 77 registers
+    // The weight operands are unpacked one piece ahead, interleaved with the
+    // MFMAs (timed: 128 x 128 tiles 8-11% faster than unpacking a piece
+    // before its MFMAs behind scheduling barriers, 64 x 128 tiles 1-3%).
+    // Four pieces of A and two stages of weight words are live: 76 registers
     // with 64 x 128 tiles, so with the 49 KB ring three blocks share a CU and
     // fill each other's waits.  The last stage also reads a next stage that
     // does not exist: those reads stay inside the LDS ring and their values
@@ -729,29 +732,41 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
     read_a(af[0], lds, 0);
     read_a(af[1], lds, 1);
     read_b(bw, lds);
+    v4i bfc[WN];              // unpacked weights of the current piece
+#pragma unroll
+    for (int s = 0; s < WN; ++s) bfc[s] = unpack_word(word_of(bw[s], 0));
     int cur = 0;              // ring slot of stage j
     for (int j = 0; j < nk; ++j) {
         const int nxt = cur == NS - 1 ? 0 : cur + 1;
         const uint8_t *slot = lds + cur * SS, *nslot = lds + nxt * SS;
         static_for<4>([&](auto pc) __attribute__((always_inline)) {
             constexpr int P = decltype(pc)::value;
-            v4i bf[WN];
-#pragma unroll
-            for (int s = 0; s < WN; ++s) bf[s] = unpack_word(word_of(bw[s], P));
             if constexpr (P < 2) {
                 read_a(af[P + 2], slot, P + 2);
             } else {
                 read_a(af[P - 2], nslot, P - 2);
                 if (P == 2) read_b(bn, nslot);
             }
-            __builtin_amdgcn_sched_barrier(0);
+            // This piece's MFMAs on the weights unpacked during the previous
+            // piece, each followed by the unpack (7 VALU) of one weight
+            // operand of the next piece (piece 0 of stage j + 1 after piece 3).
+            v4i bfn[WN];
 #pragma unroll
-            for (int a = 0; a < WM; ++a)
+            for (int s = 0; s < WN; ++s) {
 #pragma unroll
-                for (int s = 0; s < WN; ++s)
-                    acc[a][s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[P][a], bf[s],
+                for (int a = 0; a < WM; ++a)
+                    acc[a][s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[P][a], bfc[s],
                                                                       acc[a][s], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
+                if constexpr (P < 3) bfn[s] = unpack_word(word_of(bw[s], P + 1));
+                else bfn[s] = unpack_word(word_of(bn[s], 0));
+            }
+#pragma unroll
+            for (int s = 0; s < WN; ++s) {
+                __builtin_amdgcn_sched_group_barrier(0x008, WM, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);    // VALU
+            }
+#pragma unroll
+            for (int s = 0; s < WN; ++s) bfc[s] = bfn[s];
         });
 #pragma unroll
         for (int s = 0; s < WN; ++s) bw[s] = bn[s];
