@@ -45,6 +45,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "dma.h"
 #include "internal.h"
 
 namespace bl {
@@ -542,27 +543,6 @@ constexpr int G3_LB = BK / 4;   // bytes of one packed weight row per stage
 __device__ inline int g3_fa(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ inline int g3_fb(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 
-// s_waitcnt operand: at most v vector-memory operations outstanding, the
-// other counters left free.
-constexpr unsigned g3_vmcnt(int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4) | (15 << 8); }
-constexpr unsigned G3_LGKM0 = 15 | (3 << 14) | (7 << 4);   // lgkmcnt(0) only
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ inline void g3_dma16(const void *src, uint8_t *dst)
-{
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)dst, 16, 0, 0);
-}
-
-// Block barrier of the producer waves: no fence, so direct loads stay in
-// flight; the compiler may not move memory accesses across it.
-__device__ inline void g3_barrier()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 template <int WM, int WN, int NS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void gemm3_kernel(
     const int8_t *__restrict__ xq, const int32_t *__restrict__ rowsum, int64_t m, int64_t k,
@@ -639,21 +619,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
                 const int8_t *ab = xq + k0;
                 const uint8_t *bb = packed + k0 / 4;
 #pragma unroll
-                for (int q = 0; q < PA; ++q) g3_dma16(ab + aoff[q], slot + 1024 * (pw * PA + q));
+                for (int q = 0; q < PA; ++q) dl_load16(ab + aoff[q], slot + 1024 * (pw * PA + q));
 #pragma unroll
-                for (int q = 0; q < PB; ++q) g3_dma16(bb + boff[q], slot + SA + 1024 * (pw * PB + q));
+                for (int q = 0; q < PB; ++q) dl_load16(bb + boff[q], slot + SA + 1024 * (pw * PB + q));
                 return;
             }
 #pragma unroll
             for (int q = 0; q < PA; ++q) {
                 const int64_t kk = k0 + acol[q] < k ? k0 : k - 16 - acol[q];
-                g3_dma16(xq + aoff[q] + kk, slot + 1024 * (pw * PA + q));
+                dl_load16(xq + aoff[q] + kk, slot + 1024 * (pw * PA + q));
             }
 #pragma unroll
             for (int q = 0; q < PB; ++q) {
                 int64_t byte = k0 / 4;
                 byte = byte + bhalf[q] + 16 <= pitch ? byte : pitch - 16 - bhalf[q];
-                g3_dma16(packed + boff[q] + byte, slot + SA + 1024 * (pw * PB + q));
+                dl_load16(packed + boff[q] + byte, slot + SA + 1024 * (pw * PB + q));
             }
         };
         // Activation chunks past K of the stage st (once its loads have landed).
@@ -669,22 +649,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
         static_for<NS - 1>([&](auto sc) __attribute__((always_inline)) {
             if (decltype(sc)::value < nk) issue(decltype(sc)::value);
         });
-        if (nk >= NS - 1) __builtin_amdgcn_s_waitcnt(g3_vmcnt((NS - 3) * PT));
-        else __builtin_amdgcn_s_waitcnt(g3_vmcnt(0));
+        if (nk >= NS - 1) __builtin_amdgcn_s_waitcnt(dl_vmcnt((NS - 3) * PT));
+        else __builtin_amdgcn_s_waitcnt(dl_vmcnt(0));
         zero_tail(0);
         zero_tail(1);
-        __builtin_amdgcn_s_waitcnt(G3_LGKM0);
-        g3_barrier();
+        __builtin_amdgcn_s_waitcnt(DL_LGKM0);
+        dl_barrier();
         for (int j = 0; j < nk; ++j) {
             if (j + NS - 1 < nk) {
                 issue(j + NS - 1);
-                __builtin_amdgcn_s_waitcnt(g3_vmcnt((NS - 3) * PT));
+                __builtin_amdgcn_s_waitcnt(dl_vmcnt((NS - 3) * PT));
             } else {
-                __builtin_amdgcn_s_waitcnt(g3_vmcnt(0));
+                __builtin_amdgcn_s_waitcnt(dl_vmcnt(0));
                 zero_tail(j + 2);
-                __builtin_amdgcn_s_waitcnt(G3_LGKM0);
+                __builtin_amdgcn_s_waitcnt(DL_LGKM0);
             }
-            g3_barrier();
+            dl_barrier();
         }
     } else {
     // ---- math waves ----
@@ -775,7 +755,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
         // j + 1, whose slot is refilled only after three more barriers, and
         // every read of stage j has been consumed by this stage's MFMAs; so
         // their latency overlaps the barrier instead of preceding it.
-        g3_barrier();
+        dl_barrier();
     }
 
     // Epilogue: the accumulators into the output tile in the ring (every

@@ -27,6 +27,7 @@
 // round-robin; each wave keeps RB accumulators (RB row blocks share one
 // activation fragment) and prefetches the next chunk while computing the
 // current one.  The waves' partial sums meet in LDS at the end.
+#include "dma.h"
 #include "internal.h"
 
 namespace bl {
@@ -238,192 +239,148 @@ bool skinny_supported(int64_t m, int64_t n, int64_t k)
 }
 
 
-// ---- shared-activation variant ------------------------------------------------
-// Block: 4 waves on BN = 64 RB weight rows and all M (<= 16 TG) tokens, over
-// all k stages of 256; used when the row blocks alone fill the CUs.  Per
-// stage the block copies the
-// activations [16 TG tokens][256 bytes] into an LDS ring with contiguous
-// 16-byte loads (each wave instruction reads whole token rows); each wave
-// streams the packed bytes of its RB row blocks of 16 rows straight from HBM
-// into registers, several stages ahead, and reads every token's activation
-// fragments from LDS.  Same k mapping as above: lane (r, b), word u of its 16
-// packed bytes <-> activation bytes 64 b + 16 u .. +15 of the stage.
-// gridDim.y > 1 splits the stages over blocks: each split stores its raw code
-// sums into its own slice of a partial buffer, which a finish kernel adds in
-// split order (device-scope atomics with a last-block finish instead measured
-// several times slower: the atomics dominate).
 namespace {
 
-constexpr int SK2_LDA = 256 + 16;   // LDS row of one token's stage (bytes)
-constexpr int SK2_NS = 3;           // LDS ring
-constexpr int SK2_DA = 2;   // activation stages in flight ahead (registers; deeper: slower)
-constexpr int SK2_PW = 4;   // weight stages in flight ahead (registers; deeper: slower)
+// ---- shared-activation variant -------------------------------------------------
+// Block: 64 weight rows and all M (<= 16) tokens, over all k stages of 256;
+// used when the row blocks fill the CUs.  Four producer waves move both
+// operands of each stage straight into an LDS ring of NS stages (direct
+// loads, 8 KB per stage), so that NS - 2 stages of weights are in flight per
+// block without holding them in registers; four math waves read both from
+// LDS, each on 16 of the rows.  (Its predecessor streamed the weights into
+// registers, four stages ahead, and copied the activations through
+// registers into a padded LDS ring: 20.0 / 22.3 us on the 70B-class
+// matrices at M = 16, against 17.1 / 19.3 us.)
+// Ring layout without padding, 16-byte chunks permuted so that the 16 lanes
+// of one row group read distinct bank groups: weights [64 rows][64 bytes],
+// chunk b of row r at b ^ ((r >> 2) & 3); activations [16 tokens][256
+// bytes], chunk c of token t at c ^ t.  Stage j + 1 is published at the
+// barrier that ends stage j (producers wait on their own load counter; no
+// fence on either side: a math wave's reads of stage j are consumed by its
+// MFMAs before it reaches the barrier).  Same k mapping as above: lane (r,
+// b), word u of its 16 packed bytes <-> activation bytes 64 b + 16 u .. +15
+// of the stage; K % 256 = 0.  gridDim.y > 1 splits the stages over blocks:
+// each split stores its raw code sums into its own slice of a partial
+// buffer, which a finish kernel adds in split order (device-scope atomics
+// with a last-block finish instead measured several times slower: the
+// atomics dominate).
+// Ring depth: six stages (48 KB, four stages of weights in flight per block);
+// timed on the 70B-class matrices at M = 16 with rotating weights: four
+// stages 18.8 us, six 17.1, eight 17.4, nine 17.7 (K = 8192).
+constexpr int SK3_NS = 6;
 
-template <int TG, int RB>
-__global__ __launch_bounds__(256) void skinny2_kernel(const int8_t *__restrict__ xq,
+template <int NS>
+__global__ __launch_bounds__(512) void skinny3_kernel(const int8_t *__restrict__ xq,
                                                       const int32_t *__restrict__ rowsum,
                                                       int64_t m, int64_t k,
                                                       const uint8_t *__restrict__ packed,
                                                       int64_t n, int64_t pitch, Out out,
                                                       int64_t ldy, int32_t *__restrict__ part)
 {
-    constexpr int MT = 16 * TG, BN = 64 * RB;
-    constexpr int SLOT = MT * SK2_LDA;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[SK2_NS * SLOT];
+    static_assert(NS >= 3, "two stages in flight");
+    constexpr int MT = 16, BN = 64;
+    constexpr int SW = BN * (SK_CHUNK / 4), SX = MT * SK_CHUNK, SS = SW + SX;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NS * SS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r = lane & 15, b = lane >> 4;
     const int64_t n0 = (int64_t)blockIdx.x * BN;
-    // split y of gridDim.y takes stages [s0, s1) of the k range (>= 1 each)
     const int ns_all = (int)(k / SK_CHUNK);
     const int s0 = (int)((int64_t)blockIdx.y * ns_all / gridDim.y);
     const int s1 = (int)((int64_t)(blockIdx.y + 1) * ns_all / gridDim.y);
     const int ns = s1 - s0;
+    v4i acc = v4i{0, 0, 0, 0};
+    const int r = lane & 15, b = lane >> 4;
 
-    // activation pieces of this thread: piece p = tid + 256 i of the stage,
-    // token p / 16, bytes 16 (p % 16) .. +15 (tokens past M clamped: they
-    // only feed outputs that are never stored)
-    const int8_t *asrc[TG];
-    uint32_t adst[TG];
-#pragma unroll
-    for (int i = 0; i < TG; ++i) {
-        const int p = tid + 256 * i;
-        int64_t tok = p >> 4;
-        tok = tok < m ? tok : m - 1;
-        asrc[i] = xq + tok * k + (int64_t)s0 * SK_CHUNK + 16 * (p & 15);
-        adst[i] = (uint32_t)((p >> 4) * SK2_LDA + 16 * (p & 15));
-    }
-    // weight rows of this lane (clamped into the matrix)
-    const uint8_t *wsrc[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        int64_t row = n0 + 16 * (wave * RB + rb) + r;
+    if (wave >= 4) {
+        // producer wave pw fills weight rows 16 pw .. 16 pw + 15 and tokens
+        // 4 pw .. 4 pw + 3 of every stage (1 KB each); rows and tokens past
+        // the matrices are clamped (they feed outputs that are never stored)
+        const int pw = wave - 4;
+        const int wr = 16 * pw + (lane >> 2);
+        int64_t row = n0 + wr;
         row = row < n ? row : n - 1;
-        wsrc[rb] = packed + row * pitch + (int64_t)s0 * (SK_CHUNK / 4) + 16 * b;
-    }
-
-    auto aload = [&](uint4 (&a)[TG], int st) __attribute__((always_inline)) {
-        const int sc = st < ns ? st : ns - 1;
-        const int64_t k0 = (int64_t)sc * SK_CHUNK;
-#pragma unroll
-        for (int i = 0; i < TG; ++i) a[i] = load16(asrc[i] + k0);
-    };
-    auto astore = [&](const uint4 (&a)[TG], int st) __attribute__((always_inline)) {
-        uint8_t *slot = lds + (st % SK2_NS) * SLOT;
-#pragma unroll
-        for (int i = 0; i < TG; ++i) *(uint4 *)(slot + adst[i]) = a[i];
-    };
-    auto wload = [&](uint4 (&w)[RB], int st) __attribute__((always_inline)) {
-        const int sc = st < ns ? st : ns - 1;
-        const int64_t off = (int64_t)sc * (SK_CHUNK / 4);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) w[rb] = load_nt16(wsrc[rb] + off);
-    };
-
-    v4i acc[RB][TG];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int g = 0; g < TG; ++g) acc[rb][g] = v4i{0, 0, 0, 0};
-
-    // prologue: stage 0 into LDS; activations of stages 1 .. DA and weights
-    // of stages 0 .. PW-1 in flight
-    uint4 ra[SK2_DA][TG], rw[SK2_PW][RB];
-    {
-        uint4 a0[TG];
-        aload(a0, 0);
-#pragma unroll
-        for (int d = 0; d < SK2_DA; ++d) aload(ra[d], 1 + d);
-#pragma unroll
-        for (int q = 0; q < SK2_PW; ++q) wload(rw[q], q);
-        astore(a0, 0);
-    }
-    __syncthreads();
-
-    // Iteration j: store the activations of stage j+1 (loaded DA iterations
-    // ago) into slot (j+1) % 3, issue the loads of stage j+1+DA (activations)
-    // and j+PW (weights), then the MFMAs of stage j from slot j % 3; one
-    // barrier.  Slot (j+1) % 3 was last read in iteration j-2.
-    constexpr int UR = SK2_DA * SK2_PW / gcd_int(SK2_DA, SK2_PW);
-    constexpr int U = UR * SK2_NS / gcd_int(UR, SK2_NS);
-    auto iter = [&](auto jc, int j) __attribute__((always_inline)) {
-        constexpr int J = decltype(jc)::value;
-        constexpr int AS = J % SK2_DA, WS = J % SK2_PW;
-        if (j + 1 < ns) astore(ra[AS], j + 1);
-        aload(ra[AS], j + 1 + SK2_DA);
-        uint4 wcur[RB];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) wcur[rb] = rw[WS][rb];
-        wload(rw[WS], j + SK2_PW);
-        __builtin_amdgcn_sched_barrier(0);
-        const uint8_t *slot = lds + (J % SK2_NS) * SLOT;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            v4i xb[TG];
-#pragma unroll
-            for (int g = 0; g < TG; ++g) {
-                const uint4 v = load16(slot + (16 * g + r) * SK2_LDA + 64 * b + 16 * u);
-                xb[g] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+        const uint8_t *wsrc = packed + row * pitch + (int64_t)s0 * (SK_CHUNK / 4) +
+                              16 * ((lane & 3) ^ ((wr >> 2) & 3));
+        const int xt = 4 * pw + (lane >> 4);
+        int64_t tok = xt;
+        tok = tok < m ? tok : m - 1;
+        const int8_t *xsrc = xq + tok * k + (int64_t)s0 * SK_CHUNK + 16 * ((lane & 15) ^ xt);
+        auto issue = [&](int st) __attribute__((always_inline)) {
+            uint8_t *slot = lds + (st % NS) * SS;
+            dl_load16(wsrc + (int64_t)st * (SK_CHUNK / 4), slot + 1024 * pw);
+            dl_load16(xsrc + (int64_t)st * SK_CHUNK, slot + SW + 1024 * pw);
+        };
+        static_for<NS - 1>([&](auto sc) __attribute__((always_inline)) {
+            if (decltype(sc)::value < ns) issue(decltype(sc)::value);
+        });
+        if (ns >= NS - 1) __builtin_amdgcn_s_waitcnt(dl_vmcnt((NS - 2) * 2));
+        else __builtin_amdgcn_s_waitcnt(dl_vmcnt(0));
+        dl_barrier();
+        for (int j = 0; j < ns; ++j) {
+            if (j + NS - 1 < ns) {
+                issue(j + NS - 1);
+                __builtin_amdgcn_s_waitcnt(dl_vmcnt((NS - 2) * 2));   // stage j + 1 landed
+            } else {
+                __builtin_amdgcn_s_waitcnt(dl_vmcnt(0));
             }
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                const v4i a = unpack_word16(word_at(wcur[rb], u));
-#pragma unroll
-                for (int g = 0; g < TG; ++g)
-                    acc[rb][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, xb[g], acc[rb][g], 0, 0, 0);
-            }
+            dl_barrier();
         }
-        __syncthreads();
-    };
-    const int nu = ns - ns % U;
-    for (int j = 0; j < nu; j += U)
-        static_for<U>([&](auto jc) __attribute__((always_inline)) { iter(jc, j + jc); });
-    static_for<U - 1>([&](auto jc) __attribute__((always_inline)) {
-        if (nu + jc < ns) iter(jc, nu + jc);
-    });
+    } else {
+        // math wave: weight rows 16 wave + r (A operand), tokens r (B)
+        const int wr = 16 * wave + r;
+        const int woff = wr * (SK_CHUNK / 4) + 16 * (b ^ ((wr >> 2) & 3));
+        dl_barrier();
+        for (int j = 0; j < ns; ++j) {
+            const uint8_t *slot = lds + (j % NS) * SS;
+            const uint4 wv = load16(slot + woff);
+            v4i xb[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint4 v = load16(slot + SW + r * SK_CHUNK + 16 * ((4 * b + u) ^ r));
+                xb[u] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack_word16(word_at(wv, u)), xb[u],
+                                                            acc, 0, 0, 0);
+            dl_barrier();
+        }
+    }
+    __syncthreads();   // every load has landed and every read is done
 
-    // Epilogue: lane (r, b) holds rows 16 (wave RB + rb) + 4 b + q of token
-    // 16 g + r.  The block's [MT tokens][BN rows] tile is transposed through
-    // LDS (the ring is free after the last barrier) so that every thread then
-    // writes four consecutive rows of one token: stores are contiguous along
-    // the output rows.  Split k range: the raw code sums go to this split's
-    // slice of the partial buffer, the finish kernel adds the slices in order.
-    static_assert(MT * (BN + 4) * 4 <= SK2_NS * SLOT, "epilogue tile fits the ring");
+    // Epilogue (math lanes hold D[4 b + q][r] = weight row 16 wave + 4 b + q,
+    // token r): the [16 tokens][64 rows] tile transposed through LDS, then
+    // four consecutive rows of one token per thread, as in the
+    // shared-activation kernel.
     int32_t *tile = (int32_t *)lds;   // [MT][BN + 4]
-#pragma unroll
-    for (int g = 0; g < TG; ++g)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-            *(v4i *)(tile + (16 * g + r) * (BN + 4) + 16 * (wave * RB + rb) + 4 * b) = acc[rb][g];
+    if (wave < 4) *(v4i *)(tile + r * (BN + 4) + 16 * wave + 4 * b) = acc;
     __syncthreads();
-    // 16-byte stores where rows of four stay 16-byte aligned (the partial
-    // buffer always is)
     const uintptr_t base = part ? 0 : out.acc ? (uintptr_t)out.acc : (uintptr_t)out.y;
     const bool vec = (n % 4) == 0 && (part || ((ldy % 4) == 0 && (base & 15) == 0));
-    for (int e = tid; e < MT * (BN / 4); e += 256) {
-        const int tok = e / (BN / 4), c4 = 4 * (e % (BN / 4));
-        if (tok >= m) continue;
+    for (int e = tid; e < MT * (BN / 4); e += 512) {
+        const int t = e / (BN / 4), c4 = 4 * (e % (BN / 4));
+        if (t >= m) continue;
         const int64_t row = n0 + c4;
         if (row >= n) continue;
-        const v4i v = *(const v4i *)(tile + tok * (BN + 4) + c4);
+        const v4i v = *(const v4i *)(tile + t * (BN + 4) + c4);
         if (part) {
-            int32_t *dst = part + ((int64_t)blockIdx.y * m + tok) * n + row;
+            int32_t *dst = part + ((int64_t)blockIdx.y * m + t) * n + row;
             if (vec && row + 3 < n) {
                 *(v4i *)dst = v;
             } else {
-                for (int j = 0; j < 4 && row + j < n; ++j) dst[j] = v[j];
+                for (int q = 0; q < 4 && row + q < n; ++q) dst[q] = v[q];
             }
             continue;
         }
-        const int32_t rs = rowsum[tok];
+        const int32_t rs = rowsum[t];
         if (out.acc) {
-            int32_t *dst = out.acc + tok * ldy + row;
+            int32_t *dst = out.acc + t * ldy + row;
             const v4i a = v - rs;
             if (vec && row + 3 < n) *(v4i *)dst = a;
             else
-                for (int j = 0; j < 4 && row + j < n; ++j) dst[j] = a[j];
+                for (int q = 0; q < 4 && row + q < n; ++q) dst[q] = a[q];
         } else {
-            const double gs = epi_gs(out.gamma[0], out.scale[tok]);
-            float *dst = out.y + tok * ldy + row;
+            const double gs = epi_gs(out.gamma[0], out.scale[t]);
+            float *dst = out.y + t * ldy + row;
             float4 f;
             f.x = epi_y(v[0] - rs, gs);
             f.y = epi_y(v[1] - rs, gs);
@@ -432,7 +389,7 @@ __global__ __launch_bounds__(256) void skinny2_kernel(const int8_t *__restrict__
             if (vec && row + 3 < n) *(float4 *)dst = f;
             else {
                 const float fa[4] = {f.x, f.y, f.z, f.w};
-                for (int j = 0; j < 4 && row + j < n; ++j) dst[j] = fa[j];
+                for (int q = 0; q < 4 && row + q < n; ++q) dst[q] = fa[q];
             }
         }
     }
@@ -442,12 +399,12 @@ __global__ __launch_bounds__(256) void skinny2_kernel(const int8_t *__restrict__
 
 namespace {
 
-template <int TG>
-hipError_t launch_sk2(const int8_t *xq, const int32_t *rowsum, int64_t m, const uint8_t *packed,
-                      int64_t n, int64_t k, Out out, int splits, int32_t *part, hipStream_t s)
+hipError_t launch_shared(const int8_t *xq, const int32_t *rowsum, int64_t m,
+                         const uint8_t *packed, int64_t n, int64_t k, Out out, int splits,
+                         int32_t *part, hipStream_t s)
 {
-    hipLaunchKernelGGL((skinny2_kernel<TG, 1>), dim3((unsigned)((n + 63) / 64), (unsigned)splits),
-                       dim3(256), 0, s, xq, rowsum, m, k, packed, n, pack2_pitch(k), out,
+    hipLaunchKernelGGL((skinny3_kernel<SK3_NS>), dim3((unsigned)((n + 63) / 64), (unsigned)splits),
+                       dim3(512), 0, s, xq, rowsum, m, k, packed, n, pack2_pitch(k), out,
                        (int64_t)n, splits > 1 ? part : (int32_t *)nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
@@ -461,15 +418,14 @@ int skinny_splits(int64_t m, int64_t n, int64_t k)
     if (m > 16 || k % SK_CHUNK != 0) return 0;   // 0: the per-wave kernel
     // Measured on the 2B- and 70B-class shapes at M = 16: with >= 192 blocks of
     // 64 rows the unsplit kernel is fastest; with 96..191 blocks and long rows
-    // (>= 32 stages of 256 k) splitting k up to about 512 blocks pays for the
-    // extra finish launch (70B-class K = 28672, N = 8192: 26.1 -> 22.3 us);
+    // (>= 32 stages of 256 k) the k range split in two (about one block per
+    // CU) pays for the extra finish launch (70B-class K = 28672, N = 8192 with
+    // the direct-load kernel: 19.3 us split two ways, 22.6 three, 19.9 four);
     // smaller matrices run faster on the per-wave kernel.
     const int64_t blocks = (n + 63) / 64, stages = k / SK_CHUNK;
     if (blocks >= 192) return 1;
     if (blocks < 96 || stages < 32) return 0;
-    int64_t sp = (512 + blocks - 1) / blocks;
-    if (sp > stages / 8) sp = stages / 8;
-    return (int)sp;
+    return 2;
 }
 
 int64_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k)
@@ -488,7 +444,7 @@ hipError_t launch_skinny_pack2(const int8_t *xq, const int32_t *rowsum, int64_t 
     // flight; otherwise the per-wave kernel, which splits k over the waves of
     // a block
     const int sp = skinny_splits(m, n, k);
-    if (sp >= 1) return launch_sk2<1>(xq, rowsum, m, packed, n, k, out, sp, (int32_t *)ws, s);
+    if (sp >= 1) return launch_shared(xq, rowsum, m, packed, n, k, out, sp, (int32_t *)ws, s);
     if (m <= 16) return launch_tg<1>(xq, rowsum, m, packed, n, k, out, s);
     if (m <= 32) return launch_tg<2>(xq, rowsum, m, packed, n, k, out, s);
     return launch_tg<4>(xq, rowsum, m, packed, n, k, out, s);

@@ -20,7 +20,7 @@ CASES = [  # (m, n, k, path); the first case goes through bitlinear_quantize_for
     (8, 1000, 512, bl.BL_PATH_SKINNY),
     (64, 128, 4096, bl.BL_PATH_MFMA),     # few tiles: k range split, workspace used
     (40, 700, 384, bl.BL_PATH_MFMA),
-    (13, 6150, 8192, bl.BL_PATH_SKINNY),  # 97 row blocks: k split four ways, workspace used
+    (13, 6150, 8192, bl.BL_PATH_SKINNY),  # 97 row blocks: k split two ways, workspace used
     (130, 5000, 2000, bl.BL_PATH_MFMA_WIDE),  # wide tiles, k split in two, workspace used
 ]
 

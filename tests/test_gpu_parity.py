@@ -83,7 +83,7 @@ def test_ragged_shapes_bf16(layout, m, n, k):
     # up to 16 tokens on at least 192 blocks of 64 rows: activations shared
     # through LDS, ragged last row block and token slots
     (13, 12300, 512), (16, 13824, 2560), (1, 12289, 256), (5, 12352, 1024),
-    # 96..191 row blocks with long rows: the k range split over blocks (4 and 6
+    # 96..191 row blocks with long rows: the k range split over blocks (two
     # splits), partial sums added by the finish kernel; ragged and aligned N
     (13, 6150, 8192), (16, 6144, 12288),
 ])
