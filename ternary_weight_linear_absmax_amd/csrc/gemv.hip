@@ -73,6 +73,20 @@ __device__ inline void load_x64(const int8_t *__restrict__ xrow, int64_t k, int6
     }
 }
 
+// A 4-byte load that always takes the vector memory path (a raw buffer load
+// of a 4-byte range; a uniform address would otherwise become a scalar load).
+// Vector loads return in issue order, so one issued just ahead of a kernel's
+// weight loads has arrived by the time the first weights have; a scalar load
+// in flight instead holds up every later kernel-argument load (whose wait
+// drains the scalar counter to zero), and one left to the compiler tends to
+// sink to its first use in the epilogue, adding a memory latency there.
+__device__ inline uint32_t vload_u32(const void *p)
+{
+    // 0x00020000: the gfx9 raw-buffer descriptor word (untyped 32-bit data)
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)p, 0, 4, 0x00020000);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, 0);
+}
+
 // ---- 2-bit layout ------------------------------------------------------------
 // A block is KS waves.  It owns RB = R * ST consecutive weight rows; wave w
 // takes the w-th share of every row's 16-byte chunks, and lane l of the wave
@@ -159,6 +173,38 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
         __builtin_amdgcn_sched_barrier(0);
     }
 
+    // Activations read straight from global memory (neither fused nor staged
+    // in LDS): every lane's activation loads and the epilogue operands go out
+    // before the weights, with no branch or use between them (the operands'
+    // loads read the row sums in place of gamma and s for an int32 output),
+    // so that nothing waits for one of them before the weight loads are out.
+    uint4 xv[MT][CPL][4];
+    int32_t g_rs = 0;
+    float g_g = 0.0f, g_sc = 1.0f;
+    if constexpr (!FUSED && !XLDS) {
+        const int g_t = threadIdx.x % MT;
+        const float *gp = out.acc ? (const float *)rowsum : out.gamma;
+        const float *sp = out.acc ? (const float *)rowsum + m0 : out.scale + m0;
+        g_rs = rowsum[m0 + g_t];
+        g_g = __uint_as_float(vload_u32(gp));
+        g_sc = sp[g_t];
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                if constexpr (AL) {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const int64_t e0 = 64 * coff[j] + 16 * d;
+                        xv[t][j][d] = load16(xq + (m0 + t) * k + (e0 < k ? e0 : 0));
+                    }
+                } else {
+                    load_x64<AL>(xq + (m0 + t) * k, k, coff[j], xv[t][j]);
+                }
+            }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
     // weight ring: GEMV_PF steps of loads in flight ahead of the arithmetic
     constexpr int PF = GEMV_PF < ST ? GEMV_PF : ST;
     uint4 w[PF + 1][R][CPL];
@@ -182,12 +228,15 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
     const int e_rr = threadIdx.x / MT, e_t = threadIdx.x % MT;
     int32_t e_rs = 0;
     double e_gs = 0.0;
-    if (!FUSED && threadIdx.x < nout) {
+    if (XLDS && threadIdx.x < nout) {
         e_rs = rowsum[m0 + e_t];
         if (!out.acc) e_gs = epi_gs(out.gamma[0], out.scale[m0 + e_t]);
     }
+    if constexpr (!FUSED && !XLDS) {
+        e_rs = g_rs;
+        if (!out.acc) e_gs = epi_gs(g_g, g_sc);
+    }
 
-    uint4 xv[MT][CPL][4];
     float q_s = 0.0f;
     if constexpr (XLDS) {
         const int nvec = (int)(k / 16);
@@ -208,12 +257,10 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv2_kernel(
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-                load_x64<AL>(xq + (m0 + t) * k, k, coff[j], xv[t][j]);
-                if (!ok[j])
+            for (int j = 0; j < CPL; ++j)
 #pragma unroll
-                    for (int d = 0; d < 4; ++d) xv[t][j][d] = zero4();
-            }
+                for (int d = 0; d < 4; ++d)
+                    if (!ok[j] || (AL && 64 * coff[j] + 16 * d >= k)) xv[t][j][d] = zero4();
     } else {
         const int nvec = (int)(k / QE), nthr = (int)blockDim.x;
         const float gamma = out.gamma[0];
@@ -800,7 +847,6 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv_norm_kernel(
         row = row < n ? row : n - 1;
         return RELU2 ? ((row & 1) ? a.f + (row >> 1) : (row >> 1)) : row;
     };
-    // weight loads of the first steps go out before the token work
     constexpr int PF = GEMV_PF < ST ? GEMV_PF : ST;
     uint4 w[PF + 1][R][CPL];
     auto load = [&](uint4(&wb)[R][CPL], int s) {
@@ -811,27 +857,51 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv_norm_kernel(
             for (int j = 0; j < CPL; ++j) wb[r][j] = load_nt16(packed + row * chunks + coff[j]);
         }
     };
+    // The token's loads go out first, then the first steps' weight loads, and
+    // only then is anything computed from the token (an addition or a
+    // conversion before the weight loads would wait for the token first);
+    // block 0's copy of the new residual is stored after all loads are issued.
     double v[EPT];
+    float xo[EPT], ad[EPT];
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
         const int i = threadIdx.x + nthr * j, ic = i < kk ? i : kk - 1;
         if (PRO == NORM_RESIDUAL) {
-            const float *x = (const float *)a.src;
-            const float xv = a.add ? x[ic] + a.add[ic] : x[ic];
-            if (a.add && blockIdx.x == 0 && i < kk) a.x_out[i] = xv;
-            v[j] = (double)xv;
+            xo[j] = ((const float *)a.src)[ic];
         } else if (PRO == NORM_GQA) {
             const unsigned hd = (unsigned)a.head_dim, head = (unsigned)ic / hd;
             const unsigned d = (unsigned)ic - head * hd;
-            v[j] = (double)((const float *)a.src)[a.col + (int64_t)(head / (unsigned)a.group) * hd + d];
+            xo[j] = ((const float *)a.src)[a.col + (int64_t)(head / (unsigned)a.group) * hd + d];
         } else {
             v[j] = ((const double *)a.src)[ic];
         }
-        if (i >= kk) v[j] = 0.0;
     }
+    if (PRO == NORM_RESIDUAL && a.add)
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const int i = threadIdx.x + nthr * j;
+            ad[j] = a.add[i < kk ? i : kk - 1];
+        }
+    // gamma goes out after the token, before the weights (a vector load):
+    // read in the epilogue, its latency would follow the block's last barrier
+    const float gamma = __uint_as_float(vload_u32(out.gamma));
 #pragma unroll
     for (int q = 0; q < PF; ++q) load(w[q], q);
     __builtin_amdgcn_sched_barrier(0);
+    if (PRO == NORM_RESIDUAL && a.add)
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) xo[j] += ad[j];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        if (PRO != NORM_F64) v[j] = (double)xo[j];
+        if ((int)threadIdx.x + nthr * j >= kk) v[j] = 0.0;
+    }
+    if (PRO == NORM_RESIDUAL && a.add && blockIdx.x == 0)
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const int i = threadIdx.x + nthr * j;
+            if (i < kk) a.x_out[i] = xo[j];
+        }
 
     // RMSNorm: sum of squares in double over the block, with max |v| in the
     // same reduction (the quantiser's max |h| follows from it exactly)
@@ -879,6 +949,9 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv_norm_kernel(
             const int64_t e0 = 64 * coff[j] + 16 * d;
             xv[j][d] = (ok[j] && e0 < k) ? nibble_split(q_lds[e0 / 16]) : zero4();
         }
+    // gamma / s, formed here: gamma (a vector load issued before the weights)
+    // has arrived by the time the first weights have
+    const double gs = epi_gs(gamma, qs);
 
 #pragma unroll
     for (int s = 0; s < ST; ++s) {
@@ -902,7 +975,6 @@ __global__ __launch_bounds__(GEMV_KS_MAX * 64) void gemv_norm_kernel(
     }
     __syncthreads();
     const int nout = wr * RB;
-    const double gs = epi_gs(out.gamma[0], qs);
     const int e_rr = threadIdx.x;
     if (RELU2) {
         // thread e_rr < nout / 2 finishes the pair of logical rows 2 e_rr, 2 e_rr + 1
