@@ -159,6 +159,7 @@ def sections(args):
 def measure_decode(args):
     """Headline: the decode step (one bitlinear_quantize_forward launch per
     matrix and layer), graph-replayed; returns the line's core fields."""
+    import torch
     from ternary_weight_linear_absmax_amd import bitlinear as bl
     mats = decode_workload(args.layers)
     step_bytes = sum(m["bytes"] for m in mats) * args.layers
@@ -207,8 +208,31 @@ def measure_decode(args):
     roofline["prequantised_gemv_us_per_launch"] = round(ms_gemv * 1e3 / launches, 3)
     log(f"decode per launch: {us_per_launch:.2f} us with quantisation, "
         f"{ms_gemv * 1e3 / launches:.2f} us GEMV alone")
+
+    # a few tokens at once (M = 2 and 4, pre-quantised, the path AUTO takes:
+    # the GEMV on these matrices), the same 30-layer rotation
+    multi = {}
+    for mt in (2, 4):
+        g = torch.Generator(device="cuda").manual_seed(90 + mt)
+        for m in mats:
+            xm = torch.randn((mt, m["k"]), device="cuda", generator=g).to(torch.bfloat16)
+            m["xqM"], m["scM"], m["rsM"] = bl.quantize_act(xm)
+            m["yM"] = torch.empty((mt, m["n"]), dtype=torch.float32, device="cuda")
+
+        def few_tokens():
+            for layer in range(args.layers):
+                for m in mats:
+                    bl.forward(m["xqM"], m["scM"], m["rsM"], m["copies"][layer], m["gamma"],
+                               m["n"], m["k"], y=m["yM"])
+        ms_m = graph_time(few_tokens, args.steps, args.warmup)
+        multi[f"decode_M{mt}"] = {
+            "us_per_step": round(ms_m * 1e3, 1),
+            "GB/s": round(step_bytes / (ms_m * 1e-3) / 1e9, 1),
+            "hbm_frac": round(step_bytes / (ms_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "paths": sorted({bl.forward_path(mt, m["n"], m["k"]) for m in mats})}
+        log(f"decode M={mt}: {ms_m * 1e3:.1f} us per step")
     return dict(value=value, ms_step=ms_step, ms_step_eager=ms_step_eager, step_bytes=step_bytes,
-                roofline=roofline, launches=launches)
+                roofline=roofline, launches=launches, multi=multi)
 
 
 def main():
@@ -231,7 +255,7 @@ def main():
     log(f"sections: {', '.join(todo)}")
 
     dec = measure_decode(args) if "decode" in todo else None
-    extra = {}
+    extra = dict(dec.get("multi", {})) if dec else {}
     ceil = measure_ceilings(args) if "ceilings" in todo else None
     if ceil:
         extra["ceilings"] = ceil
