@@ -266,6 +266,10 @@ __device__ inline void ep_put(int32_t *tile, const v16i (&acc)[WM][WN], int wm, 
 }
 
 // Stores the tile to dst[(row) * ld + col] for rows m0.. < m, columns n0.. < n.
+// The 16-byte stores are non-temporal: the tile is not read again by this
+// kernel, and streaming it out keeps the last tiles' stores from piling up in
+// the cache at the end of the launch (512 x 8640 x 3200: 24.3 -> 23.3 us,
+// 128 x 28672 x 8192: 35.9 -> 35.1 us in paired graph-replay timing).
 template <int BM, int BN>
 __device__ inline void ep_store(const int32_t *tile, int tid, int nthreads, int64_t m0,
                                 int64_t n0, int64_t m, int64_t n, int32_t *dst, int64_t ld)
@@ -279,7 +283,7 @@ __device__ inline void ep_store(const int32_t *tile, int tid, int nthreads, int6
         const v4i v = *(const v4i *)(tile + row * LT + c);
         int32_t *d = dst + gm * ld + gn;
         if (vec && gn + 3 < n) {
-            *(v4i *)d = v;
+            __builtin_nontemporal_store(v, (v4i *)d);
         } else {
             for (int j = 0; j < 4 && gn + j < n; ++j) d[j] = v[j];
         }

@@ -242,12 +242,18 @@ bool skinny_supported(int64_t m, int64_t n, int64_t k)
 namespace {
 
 // ---- shared-activation variant -------------------------------------------------
-// Block: 64 weight rows and all M (<= 16) tokens, over all k stages of 256;
+// Block: 64 RB weight rows and all M (<= 16) tokens, over all k stages of 256;
 // used when the row blocks fill the CUs.  Four producer waves move both
 // operands of each stage straight into an LDS ring of NS stages (direct
-// loads, 8 KB per stage), so that NS - 2 stages of weights are in flight per
-// block without holding them in registers; four math waves read both from
-// LDS, each on 16 of the rows.  (Its predecessor streamed the weights into
+// loads, 16 RB KB of weights and 4 KB of activations per stage), so that
+// NS - 2 stages of weights are in flight per block without holding them in
+// registers; four math waves read both from LDS, each on 16 RB of the rows
+// (one activation fragment feeds RB MFMAs).  RB = 2 on the 70B-class
+// matrices: each activation stage then serves twice the weight bytes, and
+// the 72 KB ring still lets two blocks share a CU (M = 16, rotating weights,
+// paired timing: 19.0 -> 17.7 us with K = 8192, 21.8 -> 20.0 us with K = 28672
+// split four ways instead of two; rings of 10 or 12 stages, one block per
+// CU, 18.9 / 21.1 and 19.4 / 21.8 us; eight splits 21.8 us).  (Its predecessor streamed the weights into
 // registers, four stages ahead, and copied the activations through
 // registers into a padded LDS ring: 20.0 / 22.3 us on the 70B-class
 // matrices at M = 16, against 17.1 / 19.3 us.)
@@ -264,12 +270,13 @@ namespace {
 // buffer, which a finish kernel adds in split order (device-scope atomics
 // with a last-block finish instead measured several times slower: the
 // atomics dominate).
-// Ring depth: six stages (48 KB, four stages of weights in flight per block);
-// timed on the 70B-class matrices at M = 16 with rotating weights: four
-// stages 18.8 us, six 17.1, eight 17.4, nine 17.7 (K = 8192).
+// Ring depth: six stages (48 KB with RB = 1, four stages of weights in flight
+// per block); timed on the 70B-class matrices at M = 16 with rotating
+// weights and RB = 1: four stages 18.8 us, six 17.1, eight 17.4, nine 17.7
+// (K = 8192).
 constexpr int SK3_NS = 6;
 
-template <int NS>
+template <int NS, int RB>
 __global__ __launch_bounds__(512) void skinny3_kernel(const int8_t *__restrict__ xq,
                                                       const int32_t *__restrict__ rowsum,
                                                       int64_t m, int64_t k,
@@ -278,8 +285,9 @@ __global__ __launch_bounds__(512) void skinny3_kernel(const int8_t *__restrict__
                                                       int64_t ldy, int32_t *__restrict__ part)
 {
     static_assert(NS >= 3, "two stages in flight");
-    constexpr int MT = 16, BN = 64;
+    constexpr int MT = 16, BN = 64 * RB;
     constexpr int SW = BN * (SK_CHUNK / 4), SX = MT * SK_CHUNK, SS = SW + SX;
+    constexpr int PT = RB + 1;    // direct loads per producer wave and stage
     __shared__ __attribute__((aligned(16))) uint8_t lds[NS * SS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t n0 = (int64_t)blockIdx.x * BN;
@@ -287,51 +295,66 @@ __global__ __launch_bounds__(512) void skinny3_kernel(const int8_t *__restrict__
     const int s0 = (int)((int64_t)blockIdx.y * ns_all / gridDim.y);
     const int s1 = (int)((int64_t)(blockIdx.y + 1) * ns_all / gridDim.y);
     const int ns = s1 - s0;
-    v4i acc = v4i{0, 0, 0, 0};
+    v4i acc[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) acc[i] = v4i{0, 0, 0, 0};
     const int r = lane & 15, b = lane >> 4;
 
     if (wave >= 4) {
-        // producer wave pw fills weight rows 16 pw .. 16 pw + 15 and tokens
-        // 4 pw .. 4 pw + 3 of every stage (1 KB each); rows and tokens past
-        // the matrices are clamped (they feed outputs that are never stored)
+        // producer wave pw fills weight rows 16 (pw RB + q) .. + 15 (q < RB)
+        // and tokens 4 pw .. 4 pw + 3 of every stage (1 KB each); rows and
+        // tokens past the matrices are clamped (they feed outputs that are
+        // never stored)
         const int pw = wave - 4;
-        const int wr = 16 * pw + (lane >> 2);
-        int64_t row = n0 + wr;
-        row = row < n ? row : n - 1;
-        const uint8_t *wsrc = packed + row * pitch + (int64_t)s0 * (SK_CHUNK / 4) +
-                              16 * ((lane & 3) ^ ((wr >> 2) & 3));
+        const uint8_t *wsrc[RB];
+#pragma unroll
+        for (int q = 0; q < RB; ++q) {
+            const int wr = 16 * (pw * RB + q) + (lane >> 2);
+            int64_t row = n0 + wr;
+            row = row < n ? row : n - 1;
+            wsrc[q] = packed + row * pitch + (int64_t)s0 * (SK_CHUNK / 4) +
+                      16 * ((lane & 3) ^ ((wr >> 2) & 3));
+        }
         const int xt = 4 * pw + (lane >> 4);
         int64_t tok = xt;
         tok = tok < m ? tok : m - 1;
         const int8_t *xsrc = xq + tok * k + (int64_t)s0 * SK_CHUNK + 16 * ((lane & 15) ^ xt);
         auto issue = [&](int st) __attribute__((always_inline)) {
             uint8_t *slot = lds + (st % NS) * SS;
-            dl_load16(wsrc + (int64_t)st * (SK_CHUNK / 4), slot + 1024 * pw);
+#pragma unroll
+            for (int q = 0; q < RB; ++q)
+                dl_load16(wsrc[q] + (int64_t)st * (SK_CHUNK / 4), slot + 1024 * (pw * RB + q));
             dl_load16(xsrc + (int64_t)st * SK_CHUNK, slot + SW + 1024 * pw);
         };
         static_for<NS - 1>([&](auto sc) __attribute__((always_inline)) {
             if (decltype(sc)::value < ns) issue(decltype(sc)::value);
         });
-        if (ns >= NS - 1) __builtin_amdgcn_s_waitcnt(dl_vmcnt((NS - 2) * 2));
+        if (ns >= NS - 1) __builtin_amdgcn_s_waitcnt(dl_vmcnt((NS - 2) * PT));
         else __builtin_amdgcn_s_waitcnt(dl_vmcnt(0));
         dl_barrier();
         for (int j = 0; j < ns; ++j) {
             if (j + NS - 1 < ns) {
                 issue(j + NS - 1);
-                __builtin_amdgcn_s_waitcnt(dl_vmcnt((NS - 2) * 2));   // stage j + 1 landed
+                __builtin_amdgcn_s_waitcnt(dl_vmcnt((NS - 2) * PT));   // stage j + 1 landed
             } else {
                 __builtin_amdgcn_s_waitcnt(dl_vmcnt(0));
             }
             dl_barrier();
         }
     } else {
-        // math wave: weight rows 16 wave + r (A operand), tokens r (B)
-        const int wr = 16 * wave + r;
-        const int woff = wr * (SK_CHUNK / 4) + 16 * (b ^ ((wr >> 2) & 3));
+        // math wave: weight rows 16 (RB wave + i) + r (A operands), tokens r (B)
+        int woff[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const int wr = 16 * (RB * wave + i) + r;
+            woff[i] = wr * (SK_CHUNK / 4) + 16 * (b ^ ((wr >> 2) & 3));
+        }
         dl_barrier();
         for (int j = 0; j < ns; ++j) {
             const uint8_t *slot = lds + (j % NS) * SS;
-            const uint4 wv = load16(slot + woff);
+            uint4 wv[RB];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) wv[i] = load16(slot + woff[i]);
             v4i xb[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -340,19 +363,24 @@ __global__ __launch_bounds__(512) void skinny3_kernel(const int8_t *__restrict__
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack_word16(word_at(wv, u)), xb[u],
-                                                            acc, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < RB; ++i)
+                    acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack_word16(word_at(wv[i], u)),
+                                                                   xb[u], acc[i], 0, 0, 0);
             dl_barrier();
         }
     }
     __syncthreads();   // every load has landed and every read is done
 
-    // Epilogue (math lanes hold D[4 b + q][r] = weight row 16 wave + 4 b + q,
-    // token r): the [16 tokens][64 rows] tile transposed through LDS, then
-    // four consecutive rows of one token per thread, as in the
-    // shared-activation kernel.
+    // Epilogue (math lanes hold D[4 b + q][r] of row tile i = weight row
+    // 16 (RB wave + i) + 4 b + q, token r): the [16 tokens][BN rows] tile
+    // transposed through LDS, then four consecutive rows of one token per
+    // thread, as in the shared-activation kernel.
     int32_t *tile = (int32_t *)lds;   // [MT][BN + 4]
-    if (wave < 4) *(v4i *)(tile + r * (BN + 4) + 16 * wave + 4 * b) = acc;
+    if (wave < 4)
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+            *(v4i *)(tile + r * (BN + 4) + 16 * (RB * wave + i) + 4 * b) = acc[i];
     __syncthreads();
     const uintptr_t base = part ? 0 : out.acc ? (uintptr_t)out.acc : (uintptr_t)out.y;
     const bool vec = (n % 4) == 0 && (part || ((ldy % 4) == 0 && (base & 15) == 0));
@@ -399,13 +427,28 @@ __global__ __launch_bounds__(512) void skinny3_kernel(const int8_t *__restrict__
 
 namespace {
 
+// 128-row blocks (RB = 2) for matrices with at least 160 of them, or at least
+// 32 with rows of at least 64 stages (split over blocks); K of at least 16
+// stages.  The 2B-class matrices keep 64-row blocks.
+bool wide_rows(int64_t n, int64_t k)
+{
+    const int64_t b128 = (n + 127) / 128, stages = k / SK_CHUNK;
+    return stages >= 16 && (b128 >= 160 || (b128 >= 32 && stages >= 64));
+}
+
 hipError_t launch_shared(const int8_t *xq, const int32_t *rowsum, int64_t m,
                          const uint8_t *packed, int64_t n, int64_t k, Out out, int splits,
                          int32_t *part, hipStream_t s)
 {
-    hipLaunchKernelGGL((skinny3_kernel<SK3_NS>), dim3((unsigned)((n + 63) / 64), (unsigned)splits),
-                       dim3(512), 0, s, xq, rowsum, m, k, packed, n, pack2_pitch(k), out,
-                       (int64_t)n, splits > 1 ? part : (int32_t *)nullptr);
+    int32_t *pp = splits > 1 ? part : (int32_t *)nullptr;
+    if (wide_rows(n, k))
+        hipLaunchKernelGGL((skinny3_kernel<SK3_NS, 2>),
+                           dim3((unsigned)((n + 127) / 128), (unsigned)splits), dim3(512), 0, s,
+                           xq, rowsum, m, k, packed, n, pack2_pitch(k), out, (int64_t)n, pp);
+    else
+        hipLaunchKernelGGL((skinny3_kernel<SK3_NS, 1>),
+                           dim3((unsigned)((n + 63) / 64), (unsigned)splits), dim3(512), 0, s,
+                           xq, rowsum, m, k, packed, n, pack2_pitch(k), out, (int64_t)n, pp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     return launch_splitk_finish(part, rowsum, m, n, splits, out, n, s);
@@ -416,6 +459,15 @@ hipError_t launch_shared(const int8_t *xq, const int32_t *rowsum, int64_t m,
 int skinny_splits(int64_t m, int64_t n, int64_t k)
 {
     if (m > 16 || k % SK_CHUNK != 0) return 0;   // 0: the per-wave kernel
+    if (wide_rows(n, k)) {
+        // about one 128-row block per CU, at least eight stages per split
+        // (70B-class: K = 8192 unsplit, K = 28672 four ways)
+        const int64_t b128 = (n + 127) / 128, stages = k / SK_CHUNK;
+        int sp = (int)(256 / b128);
+        sp = sp < 1 ? 1 : sp;
+        while (sp > 1 && stages / sp < 8) --sp;
+        return sp;
+    }
     // Measured on the 2B- and 70B-class shapes at M = 16: with >= 192 blocks of
     // 64 rows the unsplit kernel is fastest; with 96..191 blocks and long rows
     // (>= 32 stages of 256 k) the k range split in two (about one block per

@@ -86,6 +86,9 @@ def test_ragged_shapes_bf16(layout, m, n, k):
     # 96..191 row blocks with long rows: the k range split over blocks (two
     # splits), partial sums added by the finish kernel; ragged and aligned N
     (13, 6150, 8192), (16, 6144, 12288),
+    # 128-row blocks: >= 160 of them unsplit (ragged last block), and 34 of
+    # them with 64 stages split seven ways
+    (13, 20483, 4096), (16, 4229, 16384),
 ])
 def test_skinny_shapes(m, n, k):
     """Weight-streaming matrix-core path: ragged N and M, every row-block /
