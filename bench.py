@@ -916,7 +916,51 @@ def cpu_baseline(seconds):
                                   "seconds": round(el, 2), "cores": threads}
         log(f"cpu oracle xl {name} M=128: {el:.1f} s on {threads} threads")
         del t
+    out.update(_cpu_stack(threads))
     return out
+
+
+def _cpu_stack(threads, layers=2):
+    """The oracle's 2B-class decoder layer at M = 64 (the layer-stack
+    workload: RMSNorm + quantiser before every product, first-token GQA
+    expansion, relu(gate)^2 * up, residual adds), every product's weight
+    rows split over all threads; `layers` distinct layers timed, tokens/s
+    extrapolated to the 30-layer step.  Weights are quantised before the
+    timed region, as on the GPU."""
+    import oracle
+    from ternary_weight_linear_absmax_amd import inputs
+    from ternary_weight_linear_absmax_amd import stack as st
+    prepared = []
+    for layer in range(layers):
+        wl = inputs.stack_layer_weights(layer)
+        prepared.append({name: oracle.quantize_weights(wl[name]) for name in st.MATRICES})
+    x = oracle.bf16_to_f32(inputs.stack_input())
+    m = x.shape[0]
+
+    def product(qsr, tg):
+        q, s, _ = qsr
+        t, g = tg
+        parts = _split_rows(lambda a, b: oracle.matmul_i32(q, t[a:b]), t.shape[0], threads)
+        return oracle.rescale(np.concatenate(parts, axis=1), s, g).astype(np.float32)
+
+    t0 = time.perf_counter()
+    for lw in prepared:
+        qkv = product(oracle.rmsnorm_quantize(x), lw["qkv"])
+        v = qkv[:, st.V_COL:]
+        o = product(oracle.rmsnorm_quantize(oracle.gqa_expand(v, st.HEADS, st.KV_HEADS)), lw["o"])
+        x = oracle.add_f32(x, o)
+        gu = product(oracle.rmsnorm_quantize(x), lw["up_gate"])
+        d = product(oracle.rmsnorm_quantize(oracle.relu2_mul(gu[:, :st.FFN], gu[:, st.FFN:])),
+                    lw["down"])
+        x = oracle.add_f32(x, d)
+    el = time.perf_counter() - t0
+    per_layer = el / layers
+    res = {"stack_2B_M64": {
+        "tokens_per_s": round(m / (30 * per_layer), 2), "seconds_per_layer": round(per_layer, 3),
+        "cores": threads,
+        "sample": f"{layers} of the 30 layers at M = {m} in {el:.2f} s, extrapolated to 30"}}
+    log(f"cpu oracle stack M={m}: {per_layer:.2f} s per layer on {threads} threads")
+    return res
 
 
 if __name__ == "__main__":
