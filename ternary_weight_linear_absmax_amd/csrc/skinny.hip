@@ -242,41 +242,52 @@ bool skinny_supported(int64_t m, int64_t n, int64_t k)
 namespace {
 
 // ---- shared-activation variant -------------------------------------------------
-// Block: 64 RB weight rows and all M (<= 16) tokens, over all k stages of 256;
+// Block: 64 RB weight rows and all M (<= 16) tokens, over all k stages of KS;
 // used when the row blocks fill the CUs.  Four producer waves move both
 // operands of each stage straight into an LDS ring of NS stages (direct
-// loads, 16 RB KB of weights and 4 KB of activations per stage), so that
-// NS - 2 stages of weights are in flight per block without holding them in
-// registers; four math waves read both from LDS, each on 16 RB of the rows
-// (one activation fragment feeds RB MFMAs).  RB = 2 on the 70B-class
-// matrices: each activation stage then serves twice the weight bytes, and
-// the 72 KB ring still lets two blocks share a CU (M = 16, rotating weights,
-// paired timing: 19.0 -> 17.7 us with K = 8192, 21.8 -> 20.0 us with K = 28672
-// split four ways instead of two; rings of 10 or 12 stages, one block per
-// CU, 18.9 / 21.1 and 19.4 / 21.8 us; eight splits 21.8 us).  (Its predecessor streamed the weights into
-// registers, four stages ahead, and copied the activations through
-// registers into a padded LDS ring: 20.0 / 22.3 us on the 70B-class
-// matrices at M = 16, against 17.1 / 19.3 us.)
-// Ring layout without padding, 16-byte chunks permuted so that the 16 lanes
-// of one row group read distinct bank groups: weights [64 rows][64 bytes],
-// chunk b of row r at b ^ ((r >> 2) & 3); activations [16 tokens][256
+// loads: RB KS / 16 bytes of weights and 16 KS of activations per stage),
+// so that NS - 2 stages of weights are in flight per block without holding
+// them in registers; four math waves read both from LDS, each on 16 RB of
+// the rows (one activation fragment feeds RB MFMAs).  (A predecessor
+// streamed the weights into registers, four stages ahead, and copied the
+// activations through registers into a padded LDS ring: 20.0 / 22.3 us on
+// the 70B-class matrices at M = 16, against 17.1 / 19.3 us.)
+// RB = 1, KS = 256 (48 KB in six stages) on the 2B-class matrices.
+// RB = 2 on the 70B-class matrices: each activation stage then serves twice
+// the weight bytes (M = 16, rotating weights, paired timing: 19.0 -> 17.7 us
+// with K = 8192, 21.8 -> 20.0 us with K = 28672 split four ways instead of
+// two; rings of 10 or 12 stages 18.9 / 21.1 and 19.4 / 21.8 us; eight splits
+// 21.8 us); and there KS = 512 in a four-stage ring (96 KB: half the
+// barriers per k) runs 15.9 -> 13.9 us and 18.8 -> 16.9 us (five or six
+// stages 14.3-15.0 / 17.3-17.8 us, three 14.2 / 17.0; KS = 1024 in three
+// stages 14.7 / 18.7 us).
+// Ring layout without padding, 16-byte chunks permuted so that a fragment
+// read of consecutive rows hits distinct bank groups: weights [BN rows][KS/4
+// bytes], chunk c of row r at c ^ wswz(r); activations [16 tokens][KS
 // bytes], chunk c of token t at c ^ t.  Stage j + 1 is published at the
 // barrier that ends stage j (producers wait on their own load counter; no
 // fence on either side: a math wave's reads of stage j are consumed by its
-// MFMAs before it reaches the barrier).  Same k mapping as above: lane (r,
-// b), word u of its 16 packed bytes <-> activation bytes 64 b + 16 u .. +15
-// of the stage; K % 256 = 0.  gridDim.y > 1 splits the stages over blocks:
-// each split stores its raw code sums into its own slice of a partial
-// buffer, which a finish kernel adds in split order (device-scope atomics
-// with a last-block finish instead measured several times slower: the
-// atomics dominate).
-// Ring depth: six stages (48 KB with RB = 1, four stages of weights in flight
-// per block); timed on the 70B-class matrices at M = 16 with rotating
-// weights and RB = 1: four stages 18.8 us, six 17.1, eight 17.4, nine 17.7
-// (K = 8192).
+// MFMAs before it reaches the barrier).  k mapping: lane (r, b) takes the
+// stage's k range [KS/4 b, KS/4 (b + 1)); word u of its packed bytes <->
+// activation bytes KS/4 b + 16 u .. +15 of the stage; K % KS = 0.
+// gridDim.y > 1 splits the stages over blocks: each split stores its raw
+// code sums into its own slice of a partial buffer, which a finish kernel
+// adds in split order (device-scope atomics with a last-block finish instead
+// measured several times slower: the atomics dominate).
+// Ring depth with KS = 256: six stages (48 KB with RB = 1, four stages of
+// weights in flight per block); timed on the 70B-class matrices at M = 16
+// with rotating weights and RB = 1: four stages 18.8 us, six 17.1, eight
+// 17.4, nine 17.7 (K = 8192).
 constexpr int SK3_NS = 6;
 
-template <int NS, int RB>
+// LDS position of a weight row's 16-byte chunks: chunk c of row r at
+// c ^ wswz(r), so that eight consecutive rows' chunks of one fragment read
+// fall in distinct bank groups (rows of 64 bytes: four rows share a bank
+// group pattern, hence r >> 2; rows of 128 bytes and more: r itself)
+template <int KS>
+__device__ inline int wswz(int r) { return KS == 256 ? (r >> 2) & 3 : r & 7; }
+
+template <int NS, int RB, int KS = 256>
 __global__ __launch_bounds__(512) void skinny3_kernel(const int8_t *__restrict__ xq,
                                                       const int32_t *__restrict__ rowsum,
                                                       int64_t m, int64_t k,
@@ -286,12 +297,15 @@ __global__ __launch_bounds__(512) void skinny3_kernel(const int8_t *__restrict__
 {
     static_assert(NS >= 3, "two stages in flight");
     constexpr int MT = 16, BN = 64 * RB;
-    constexpr int SW = BN * (SK_CHUNK / 4), SX = MT * SK_CHUNK, SS = SW + SX;
-    constexpr int PT = RB + 1;    // direct loads per producer wave and stage
+    constexpr int SW = BN * (KS / 4), SX = MT * KS, SS = SW + SX;
+    constexpr int CW = KS / 64;             // 16-byte chunks of a weight row per stage
+    constexpr int WT = SW / 1024 / 4;       // weight transfers per producer wave
+    constexpr int XT = SX / 1024 / 4;       // activation transfers per producer wave
+    constexpr int PT = WT + XT;             // direct loads per producer wave and stage
     __shared__ __attribute__((aligned(16))) uint8_t lds[NS * SS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t n0 = (int64_t)blockIdx.x * BN;
-    const int ns_all = (int)(k / SK_CHUNK);
+    const int ns_all = (int)(k / KS);
     const int s0 = (int)((int64_t)blockIdx.y * ns_all / gridDim.y);
     const int s1 = (int)((int64_t)(blockIdx.y + 1) * ns_all / gridDim.y);
     const int ns = s1 - s0;
@@ -306,25 +320,31 @@ __global__ __launch_bounds__(512) void skinny3_kernel(const int8_t *__restrict__
         // tokens past the matrices are clamped (they feed outputs that are
         // never stored)
         const int pw = wave - 4;
-        const uint8_t *wsrc[RB];
+        const uint8_t *wsrc[WT];
 #pragma unroll
-        for (int q = 0; q < RB; ++q) {
-            const int wr = 16 * (pw * RB + q) + (lane >> 2);
+        for (int q = 0; q < WT; ++q) {
+            const int wr = (1024 / (KS / 4)) * (pw * WT + q) + lane / CW;
             int64_t row = n0 + wr;
             row = row < n ? row : n - 1;
-            wsrc[q] = packed + row * pitch + (int64_t)s0 * (SK_CHUNK / 4) +
-                      16 * ((lane & 3) ^ ((wr >> 2) & 3));
+            wsrc[q] = packed + row * pitch + (int64_t)s0 * (KS / 4) +
+                      16 * ((lane % CW) ^ wswz<KS>(wr));
         }
-        const int xt = 4 * pw + (lane >> 4);
-        int64_t tok = xt;
-        tok = tok < m ? tok : m - 1;
-        const int8_t *xsrc = xq + tok * k + (int64_t)s0 * SK_CHUNK + 16 * ((lane & 15) ^ xt);
+        const int8_t *xsrc[XT];
+#pragma unroll
+        for (int q = 0; q < XT; ++q) {
+            const int xt = (1024 / KS) * (pw * XT + q) + lane / (KS / 16);
+            int64_t tok = xt;
+            tok = tok < m ? tok : m - 1;
+            xsrc[q] = xq + tok * k + (int64_t)s0 * KS + 16 * ((lane % (KS / 16)) ^ xt);
+        }
         auto issue = [&](int st) __attribute__((always_inline)) {
             uint8_t *slot = lds + (st % NS) * SS;
 #pragma unroll
-            for (int q = 0; q < RB; ++q)
-                dl_load16(wsrc[q] + (int64_t)st * (SK_CHUNK / 4), slot + 1024 * (pw * RB + q));
-            dl_load16(xsrc + (int64_t)st * SK_CHUNK, slot + SW + 1024 * pw);
+            for (int q = 0; q < WT; ++q)
+                dl_load16(wsrc[q] + (int64_t)st * (KS / 4), slot + 1024 * (pw * WT + q));
+#pragma unroll
+            for (int q = 0; q < XT; ++q)
+                dl_load16(xsrc[q] + (int64_t)st * KS, slot + SW + 1024 * (pw * XT + q));
         };
         static_for<NS - 1>([&](auto sc) __attribute__((always_inline)) {
             if (decltype(sc)::value < ns) issue(decltype(sc)::value);
@@ -343,30 +363,37 @@ __global__ __launch_bounds__(512) void skinny3_kernel(const int8_t *__restrict__
         }
     } else {
         // math wave: weight rows 16 (RB wave + i) + r (A operands), tokens r (B)
-        int woff[RB];
+        // lane (r, b) takes the stage's k range [KS/4 b, KS/4 (b + 1)): packed
+        // chunks CW/4 b .. of its weight rows, activation chunks of token r
+        constexpr int CL = CW / 4;          // weight chunks per lane and stage
+        int woff[RB][CL];
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
             const int wr = 16 * (RB * wave + i) + r;
-            woff[i] = wr * (SK_CHUNK / 4) + 16 * (b ^ ((wr >> 2) & 3));
+#pragma unroll
+            for (int c = 0; c < CL; ++c)
+                woff[i][c] = wr * (KS / 4) + 16 * ((CL * b + c) ^ wswz<KS>(wr));
         }
         dl_barrier();
         for (int j = 0; j < ns; ++j) {
             const uint8_t *slot = lds + (j % NS) * SS;
-            uint4 wv[RB];
+            uint4 wv[RB][CL];
 #pragma unroll
-            for (int i = 0; i < RB; ++i) wv[i] = load16(slot + woff[i]);
-            v4i xb[4];
+            for (int i = 0; i < RB; ++i)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint4 v = load16(slot + SW + r * SK_CHUNK + 16 * ((4 * b + u) ^ r));
+                for (int c = 0; c < CL; ++c) wv[i][c] = load16(slot + woff[i][c]);
+            v4i xb[4 * CL];
+#pragma unroll
+            for (int u = 0; u < 4 * CL; ++u) {
+                const uint4 v = load16(slot + SW + r * KS + 16 * ((4 * CL * b + u) ^ r));
                 xb[u] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < 4 * CL; ++u)
 #pragma unroll
                 for (int i = 0; i < RB; ++i)
-                    acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack_word16(word_at(wv[i], u)),
-                                                                   xb[u], acc[i], 0, 0, 0);
+                    acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                        unpack_word16(word_at(wv[i][u / 4], u % 4)), xb[u], acc[i], 0, 0, 0);
             dl_barrier();
         }
     }
@@ -442,9 +469,14 @@ hipError_t launch_shared(const int8_t *xq, const int32_t *rowsum, int64_t m,
 {
     int32_t *pp = splits > 1 ? part : (int32_t *)nullptr;
     if (wide_rows(n, k))
-        hipLaunchKernelGGL((skinny3_kernel<SK3_NS, 2>),
-                           dim3((unsigned)((n + 127) / 128), (unsigned)splits), dim3(512), 0, s,
-                           xq, rowsum, m, k, packed, n, pack2_pitch(k), out, (int64_t)n, pp);
+        if (k % 512 == 0)
+            hipLaunchKernelGGL((skinny3_kernel<4, 2, 512>),
+                               dim3((unsigned)((n + 127) / 128), (unsigned)splits), dim3(512), 0,
+                               s, xq, rowsum, m, k, packed, n, pack2_pitch(k), out, (int64_t)n, pp);
+        else
+            hipLaunchKernelGGL((skinny3_kernel<SK3_NS, 2, 256>),
+                               dim3((unsigned)((n + 127) / 128), (unsigned)splits), dim3(512), 0,
+                               s, xq, rowsum, m, k, packed, n, pack2_pitch(k), out, (int64_t)n, pp);
     else
         hipLaunchKernelGGL((skinny3_kernel<SK3_NS, 1>),
                            dim3((unsigned)((n + 63) / 64), (unsigned)splits), dim3(512), 0, s,
@@ -460,9 +492,10 @@ int skinny_splits(int64_t m, int64_t n, int64_t k)
 {
     if (m > 16 || k % SK_CHUNK != 0) return 0;   // 0: the per-wave kernel
     if (wide_rows(n, k)) {
-        // about one 128-row block per CU, at least eight stages per split
-        // (70B-class: K = 8192 unsplit, K = 28672 four ways)
-        const int64_t b128 = (n + 127) / 128, stages = k / SK_CHUNK;
+        // about one 128-row block per CU, at least eight stages (of 512 k,
+        // or 256 when K % 512 != 0) per split (70B-class: K = 8192 unsplit,
+        // K = 28672 four ways)
+        const int64_t b128 = (n + 127) / 128, stages = k / (k % 512 == 0 ? 512 : 256);
         int sp = (int)(256 / b128);
         sp = sp < 1 ? 1 : sp;
         while (sp > 1 && stages / sp < 8) --sp;

@@ -86,9 +86,10 @@ def test_ragged_shapes_bf16(layout, m, n, k):
     # 96..191 row blocks with long rows: the k range split over blocks (two
     # splits), partial sums added by the finish kernel; ragged and aligned N
     (13, 6150, 8192), (16, 6144, 12288),
-    # 128-row blocks: >= 160 of them unsplit (ragged last block), and 34 of
-    # them with 64 stages split seven ways
-    (13, 20483, 4096), (16, 4229, 16384),
+    # 128-row blocks: >= 160 of them unsplit (ragged last block), 34 of them
+    # with 32 stages of 512 k split four ways, and stages of 256 k where
+    # K % 512 != 0
+    (13, 20483, 4096), (16, 4229, 16384), (16, 20480, 4352),
 ])
 def test_skinny_shapes(m, n, k):
     """Weight-streaming matrix-core path: ragged N and M, every row-block /
