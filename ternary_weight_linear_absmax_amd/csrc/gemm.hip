@@ -525,29 +525,34 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
 // no stage passes through registers and no ds_write competes with the math
 // waves' fragment reads (measured: LDS reads next to direct loads run at
 // their full rate, next to ds_write_b128 at about 60% of it).  LDS holds a
-// ring of NS stages, each activations [BM][128] and packed weights [BN][32]
+// ring of NS stages of BKT k (128, or 256 where the tiles fit one round of
+// the CUs), each activations [BM][BKT] and packed weights [BN][BKT/4]
 // without padding; the 16-byte chunks of a row are permuted (activations:
-// chunk c of row r at c ^ g3_fa(r); weights: half h at h ^ g3_fb(r)) so that
-// a fragment read of 16 consecutive rows touches 16 distinct 16-byte bank
+// chunk c of row r at c ^ g3_fa(r); weights: chunk c at c ^ g3_fb(r)) so
+// that a fragment read of consecutive rows touches distinct 16-byte bank
 // groups, which is what the padding did before.
 // Iteration j (one block barrier each):
 //   producers: issue stage j + NS - 1 into the slot of stage j - 1 (read for
 //              the last time in iteration j - 1), then wait until stage j + 2
 //              has landed (NS - 3 stages stay in flight across the barrier);
-//   math:      run the MFMAs of stage j piece by piece (four pieces of 32 k),
-//              reading each piece's A fragments two pieces ahead: pieces 2
-//              and 3 of stage j, then pieces 0 and 1 and the weight words of
+//   math:      run the MFMAs of stage j piece by piece (BKT / 32 pieces of
+//              32 k), reading each piece's A fragments two pieces ahead: the
+//              last two pieces read pieces 0 and 1 and the weight words of
 //              stage j + 1.
 // Producers wait on their own load counter and pass the barrier without a
 // memory fence: a fence there would drain every load in flight.  Loads of a
 // stage that ends past K are clamped into their rows; the activation chunks
 // past K are then zeroed in LDS (weights past K meet zero activations).
-constexpr int G3_LB = BK / 4;   // bytes of one packed weight row per stage
-
 __device__ inline int g3_fa(int r) { return (r ^ (r >> 3)) & 7; }
-__device__ inline int g3_fb(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+// weight chunk permutation: rows of 32 bytes (BKT = 128, two chunks) or of
+// 64 bytes (BKT = 256, four chunks)
+template <int BKT>
+__device__ inline int g3_fb(int r)
+{
+    return BKT == 128 ? ((r >> 2) ^ (r >> 3)) & 1 : (r >> 1) & 3;
+}
 
-template <int WM, int WN, int NS>
+template <int WM, int WN, int NS, int BKT = BK>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void gemm3_kernel(
     const int8_t *__restrict__ xq, const int32_t *__restrict__ rowsum, int64_t m, int64_t k,
     const uint8_t *__restrict__ packed, int64_t n, int64_t pitch, int tiles_m, int64_t tiles,
@@ -555,10 +560,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
 {
     static_assert(WN >= 2 && NS >= 4, "weight tiles of whole 1 KB transfers, two stages in flight");
     constexpr int BM = 64 * WM, BN = 64 * WN;
-    constexpr int SA = BM * BK, SB = BN * G3_LB, SS = SA + SB;    // bytes per stage slot
-    constexpr int PA = BM / 32;          // 1 KB activation transfers per producer wave and stage
-    constexpr int PB = BN / 128;         // 1 KB weight transfers per producer wave and stage
+    constexpr int LB = BKT / 4;          // bytes of one packed weight row per stage
+    constexpr int SA = BM * BKT, SB = BN * LB, SS = SA + SB;    // bytes per stage slot
+    constexpr int PA = SA / 4096;        // 1 KB activation transfers per producer wave and stage
+    constexpr int PB = SB / 4096;        // 1 KB weight transfers per producer wave and stage
     constexpr int PT = PA + PB;
+    constexpr int NP = BKT / 32;         // 32-k pieces per stage
+    constexpr int CB = BKT / 128;        // 16-byte weight chunks per lane and stage
     __shared__ __attribute__((aligned(16))) uint8_t lds[NS * SS];
     __shared__ int32_t ep_rs[BM];
     __shared__ double ep_gs[BM];
@@ -572,7 +580,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
     const int tm = (int)(tile % tiles_m);
     const int64_t tn = tile / tiles_m;
     const int64_t m0 = (int64_t)tm * BM, n0 = tn * BN;
-    const int nk_total = (int)((k + BK - 1) / BK);
+    const int nk_total = (int)((k + BKT - 1) / BKT);
     const int kt0 = split * stages_per;
     const int kt1 = kt0 + stages_per < nk_total ? kt0 + stages_per : nk_total;
     const int nk = kt1 - kt0;
@@ -599,8 +607,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
         int acol[PA], bhalf[PB];
 #pragma unroll
         for (int q = 0; q < PA; ++q) {
-            const int r = 8 * (pw * PA + q) + (lane >> 3);
-            const int c = (lane & 7) ^ g3_fa(r);
+            const int r = (1024 / BKT) * (pw * PA + q) + lane / (BKT / 16);
+            const int c = (lane % (BKT / 16)) ^ g3_fa(r);
             int64_t gm = m0 + r;
             gm = gm < m ? gm : m - 1;
             acol[q] = 16 * c;
@@ -608,17 +616,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
         }
 #pragma unroll
         for (int q = 0; q < PB; ++q) {
-            const int r = 32 * (pw * PB + q) + (lane >> 1);
-            const int hh = (lane & 1) ^ g3_fb(r);
+            const int r = (1024 / LB) * (pw * PB + q) + lane / (LB / 16);
+            const int hh = (lane % (LB / 16)) ^ g3_fb<BKT>(r);
             int64_t row = n0 + r;
             row = row < n ? row : n - 1;
             bhalf[q] = 16 * hh;
             boff[q] = (uint32_t)(row * pitch + 16 * hh);
         }
-        const int full_end = (int)(k / BK) - kt0;   // stages [0, full_end) lie inside K
+        const int full_end = (int)(k / BKT) - kt0;   // stages [0, full_end) lie inside K
         auto issue = [&](int st) __attribute__((always_inline)) {
             uint8_t *slot = lds + (st % NS) * SS;
-            const int64_t k0 = (int64_t)(kt0 + st) * BK;
+            const int64_t k0 = (int64_t)(kt0 + st) * BKT;
             if (st < full_end) {
                 const int8_t *ab = xq + k0;
                 const uint8_t *bb = packed + k0 / 4;
@@ -644,7 +652,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
         auto zero_tail = [&](int st) __attribute__((always_inline)) {
             if (st < full_end || st >= nk) return;
             uint8_t *slot = lds + (st % NS) * SS;
-            const int64_t k0 = (int64_t)(kt0 + st) * BK;
+            const int64_t k0 = (int64_t)(kt0 + st) * BKT;
 #pragma unroll
             for (int q = 0; q < PA; ++q)
                 if (k0 + acol[q] >= k) *(uint4 *)(slot + 1024 * (pw * PA + q) + 16 * lane) = zero4();
@@ -695,41 +703,46 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
     // fill each other's waits.  The last stage also reads a next stage that
     // does not exist: those reads stay inside the LDS ring and their values
     // are never used.
+    // lane half h takes the stage's k range [BKT/2 h, BKT/2 (h + 1)): piece p
+    // is activation chunk NP h + p, and word p % 4 of weight chunk CB h + p / 4
+    // (64 trits per chunk)
     auto read_a = [&](v4i (&a)[WM], const uint8_t *slot, int p) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < WM; ++i) {
             const int row = wm * 32 * WM + 32 * i + l32;
-            const uint4 v = load16(slot + row * BK + 16 * ((4 * h + p) ^ g3_fa(row)));
+            const uint4 v = load16(slot + row * BKT + 16 * ((NP * h + p) ^ g3_fa(row)));
             a[i] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
         }
     };
-    auto read_b = [&](uint4 (&b)[WN], const uint8_t *slot) __attribute__((always_inline)) {
+    auto read_b = [&](uint4 (&b)[WN][CB], const uint8_t *slot) __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < WN; ++s) {
             const int row = wn * 32 * WN + 32 * s + l32;
-            b[s] = load16(slot + SA + row * G3_LB + 16 * (h ^ g3_fb(row)));
+#pragma unroll
+            for (int c = 0; c < CB; ++c)
+                b[s][c] = load16(slot + SA + row * LB + 16 * ((CB * h + c) ^ g3_fb<BKT>(row)));
         }
     };
     v4i af[4][WM];
-    uint4 bw[WN], bn[WN];
+    uint4 bw[WN][CB], bn[WN][CB];
     __syncthreads();          // stages 0 and 1 are in LDS
     read_a(af[0], lds, 0);
     read_a(af[1], lds, 1);
     read_b(bw, lds);
     v4i bfc[WN];              // unpacked weights of the current piece
 #pragma unroll
-    for (int s = 0; s < WN; ++s) bfc[s] = unpack_word(word_of(bw[s], 0));
+    for (int s = 0; s < WN; ++s) bfc[s] = unpack_word(word_of(bw[s][0], 0));
     int cur = 0;              // ring slot of stage j
     for (int j = 0; j < nk; ++j) {
         const int nxt = cur == NS - 1 ? 0 : cur + 1;
         const uint8_t *slot = lds + cur * SS, *nslot = lds + nxt * SS;
-        static_for<4>([&](auto pc) __attribute__((always_inline)) {
+        static_for<NP>([&](auto pc) __attribute__((always_inline)) {
             constexpr int P = decltype(pc)::value;
-            if constexpr (P < 2) {
-                read_a(af[P + 2], slot, P + 2);
+            if constexpr (P < NP - 2) {
+                read_a(af[(P + 2) % 4], slot, P + 2);
             } else {
-                read_a(af[P - 2], nslot, P - 2);
-                if (P == 2) read_b(bn, nslot);
+                read_a(af[(P + 2) % 4], nslot, P + 2 - NP);
+                if (P == NP - 2) read_b(bn, nslot);
             }
             // This piece's MFMAs on the weights unpacked during the previous
             // piece, each followed by the unpack (7 VALU) of one weight
@@ -739,10 +752,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
             for (int s = 0; s < WN; ++s) {
 #pragma unroll
                 for (int a = 0; a < WM; ++a)
-                    acc[a][s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[P][a], bfc[s],
+                    acc[a][s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[P % 4][a], bfc[s],
                                                                       acc[a][s], 0, 0, 0);
-                if constexpr (P < 3) bfn[s] = unpack_word(word_of(bw[s], P + 1));
-                else bfn[s] = unpack_word(word_of(bn[s], 0));
+                if constexpr (P < NP - 1)
+                    bfn[s] = unpack_word(word_of(bw[s][(P + 1) / 4], (P + 1) % 4));
+                else
+                    bfn[s] = unpack_word(word_of(bn[s][0], 0));
             }
 #pragma unroll
             for (int s = 0; s < WN; ++s) {
@@ -753,7 +768,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
             for (int s = 0; s < WN; ++s) bfc[s] = bfn[s];
         });
 #pragma unroll
-        for (int s = 0; s < WN; ++s) bw[s] = bn[s];
+        for (int s = 0; s < WN; ++s)
+#pragma unroll
+            for (int c = 0; c < CB; ++c) bw[s][c] = bn[s][c];
         cur = nxt;
         // No fence: the fragment reads still in flight here are of stage
         // j + 1, whose slot is refilled only after three more barriers, and
@@ -950,9 +967,27 @@ hipError_t launch_gemm_cfg(const int8_t *xq, const int32_t *rowsum, int64_t m,
     bool specialised = false;
     if constexpr (WN >= 2) {
         if (k % 16 == 0 && GEMM_SPECIALISED) {
-            hipLaunchKernelGGL((gemm3_kernel<WM, WN, gemm3_ring<WM, WN>()>), grid, dim3(512), 0,
-                               s, xq, rowsum, m, k, packed, n, pitch, tiles_m, tiles, per_xcd,
-                               splits, stages_per, out, ldy, ws);
+            bool deep = false;
+            if constexpr (WM == 1 && WN == 2) {
+                if (units <= 256) {
+                    // 64 x 128 tiles that fit one round of the CUs (one block
+                    // each): stages of 256 k in a four-stage ring (96 KB).
+                    // 512 x 3200 x 8640, 200 tiles: 25.3 -> 21.0 us (paired,
+                    // steady state); three stages 32.6 us; 128 x 128 tiles with
+                    // 256-k stages in three (the most that fit) 45.6 against
+                    // 35.2 us on 128 x 28672 x 8192.
+                    const int64_t nk2 = (k + 255) / 256;
+                    const int sp2 = (int)((nk2 + splits - 1) / splits);
+                    hipLaunchKernelGGL((gemm3_kernel<WM, WN, 4, 256>), grid, dim3(512), 0, s, xq,
+                                       rowsum, m, k, packed, n, pitch, tiles_m, tiles, per_xcd,
+                                       splits, sp2, out, ldy, ws);
+                    deep = true;
+                }
+            }
+            if (!deep)
+                hipLaunchKernelGGL((gemm3_kernel<WM, WN, gemm3_ring<WM, WN>()>), grid, dim3(512),
+                                   0, s, xq, rowsum, m, k, packed, n, pitch, tiles_m, tiles,
+                                   per_xcd, splits, stages_per, out, ldy, ws);
             specialised = true;
         }
     }

@@ -262,6 +262,8 @@ def test_tiled_gemm_block_shapes(m, n, k):
     (256, 16640, 256, "64 x 128 tiles"),
     (256, 6144, 1024, "128 x 128 tiles, k range split in two"),
     (300, 12400, 272, "128 x 128 tiles, ragged M, N and K"),
+    (500, 3100, 8688, "64 x 128 tiles in one round, stages of 256 k, ragged, partial last stage"),
+    (384, 4000, 2000, "64 x 128 tiles in one round, stages of 256 k, K % 256 = 208"),
 ])
 def test_tiled_gemm_configs_every_output(m, n, k, cfg):
     """Every output of each tile configuration of the tiled GEMM (every
