@@ -252,7 +252,10 @@ namespace {
 // streamed the weights into registers, four stages ahead, and copied the
 // activations through registers into a padded LDS ring: 20.0 / 22.3 us on
 // the 70B-class matrices at M = 16, against 17.1 / 19.3 us.)
-// RB = 1, KS = 256 (48 KB in six stages) on the 2B-class matrices.
+// RB = 1 on the 2B-class matrices: KS = 512 in four stages (64 KB, two
+// blocks per CU) where K % 512 = 0 (up/gate, K = 2560, at M = 4 / 8 / 16:
+// 5.43 / 5.53 / 5.58 -> 5.12 / 5.23 / 5.31 us; six such stages 5.37-5.69 us),
+// else KS = 256 in six stages (48 KB).
 // RB = 2 on the 70B-class matrices: each activation stage then serves twice
 // the weight bytes (M = 16, rotating weights, paired timing: 19.0 -> 17.7 us
 // with K = 8192, 21.8 -> 20.0 us with K = 28672 split four ways instead of
@@ -477,6 +480,10 @@ hipError_t launch_shared(const int8_t *xq, const int32_t *rowsum, int64_t m,
             hipLaunchKernelGGL((skinny3_kernel<SK3_NS, 2, 256>),
                                dim3((unsigned)((n + 127) / 128), (unsigned)splits), dim3(512), 0,
                                s, xq, rowsum, m, k, packed, n, pack2_pitch(k), out, (int64_t)n, pp);
+    else if (k % 512 == 0)
+        hipLaunchKernelGGL((skinny3_kernel<4, 1, 512>),
+                           dim3((unsigned)((n + 63) / 64), (unsigned)splits), dim3(512), 0, s,
+                           xq, rowsum, m, k, packed, n, pack2_pitch(k), out, (int64_t)n, pp);
     else
         hipLaunchKernelGGL((skinny3_kernel<SK3_NS, 1>),
                            dim3((unsigned)((n + 63) / 64), (unsigned)splits), dim3(512), 0, s,

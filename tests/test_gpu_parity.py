@@ -90,6 +90,8 @@ def test_ragged_shapes_bf16(layout, m, n, k):
     # with 32 stages of 512 k split four ways, and stages of 256 k where
     # K % 512 != 0
     (13, 20483, 4096), (16, 4229, 16384), (16, 20480, 4352),
+    # 64-row blocks with stages of 512 k (K % 512 = 0), ragged N and M
+    (5, 12300, 1536), (13, 12352, 1024),
 ])
 def test_skinny_shapes(m, n, k):
     """Weight-streaming matrix-core path: ragged N and M, every row-block /
