@@ -567,10 +567,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
     constexpr int PT = PA + PB;
     constexpr int NP = BKT / 32;         // 32-k pieces per stage
     constexpr int CB = BKT / 128;        // 16-byte weight chunks per lane and stage
-    __shared__ __attribute__((aligned(16))) uint8_t lds[NS * SS];
-    __shared__ int32_t ep_rs[BM];
-    __shared__ double ep_gs[BM];
-    static_assert(ep_tile_bytes<BM, BN>() <= NS * SS, "the output tile fits the LDS ring");
+    // EPL: the ring takes all of the LDS, so the epilogue's row operands are
+    // held in the producers' registers during the k loop and written behind
+    // the output tile in the drained ring afterwards
+    constexpr bool EPL = NS * SS + BM * 12 > 163840;
+    constexpr int EPO = EPL ? ep_tile_bytes<BM, BN>() : NS * SS;   // row operands' offset
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NS * SS + (EPL ? 0 : BM * 12)];
+    int32_t *const ep_rs = (int32_t *)(lds + EPO);
+    double *const ep_gs = (double *)(lds + EPO + BM * 4);
+    static_assert(ep_tile_bytes<BM, BN>() + (EPL ? BM * 12 : 0) <= NS * SS,
+                  "the output tile (and, with EPL, the row operands) fits the LDS ring");
     const int64_t t = tile_of_block(blockIdx.x, per_xcd);
     if (t >= tiles * splits) return;
     const int64_t tile = t / splits;
@@ -599,6 +605,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
 
     if (producer) {
         const int pw = wave - 4;
+        int32_t epl_rs = 0;
+        double epl_gs = 0.0;
+        if constexpr (EPL) {
+            // this thread's row operands of the epilogue, loaded now
+            const int pt = threadIdx.x - 256;
+            if (pt < BM && ep_mode != EP_PARTIAL) {
+                int64_t gm = m0 + pt;
+                gm = gm < m ? gm : m - 1;
+                epl_rs = rowsum[gm];
+                epl_gs = ep_mode == EP_Y ? epi_gs(out.gamma[0], out.scale[gm]) : 0.0;
+            }
+        }
         // Per-lane sources, fixed for the loop: transfer q of this wave fills
         // LDS bytes [1024 qi, 1024 qi + 1024) of the slot's activation (or
         // weight) part, qi = pw * PA + q (or pw * PB + q); lane i writes the
@@ -678,6 +696,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
             }
             dl_barrier();
         }
+        if constexpr (EPL) {
+            // the ring is drained (every stage landed and consumed): the row
+            // operands go behind the output tile's place, then one barrier
+            // publishes them to the math waves
+            const int pt = threadIdx.x - 256;
+            if (pt < BM) {
+                ep_rs[pt] = epl_rs;
+                ep_gs[pt] = epl_gs;
+            }
+            __syncthreads();
+        }
     } else {
     // ---- math waves ----
     const int wm = wave & 1, wn = wave >> 1;
@@ -691,7 +720,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
             for (int r = 0; r < 16; ++r) acc[a][s][r] = 0;
 
     // row operands of the epilogue, visible after the first barrier
-    ep_rows<BM>(threadIdx.x, m0, m, rowsum, out, ep_mode, ep_rs, ep_gs);
+    if constexpr (!EPL) ep_rows<BM>(threadIdx.x, m0, m, rowsum, out, ep_mode, ep_rs, ep_gs);
     // Fragments stream two k pieces ahead of the MFMAs: while the MFMAs of
     // piece p of stage j run, piece p + 2 is read from LDS (pieces 0 and 1 of
     // stage j + 1 during pieces 2 and 3, with the stage's weight words).
@@ -781,6 +810,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
 
     // Epilogue: the accumulators into the output tile in the ring (every
     // wave is past its last ring access after the final barrier of the loop)
+    if constexpr (EPL) __syncthreads();   // the producers' row operands
     ep_put<WM, WN>((int32_t *)lds, acc, wm, wn, h, l32, ep_rs, ep_gs, ep_mode);
     }
     // all waves store the tile
@@ -968,14 +998,16 @@ hipError_t launch_gemm_cfg(const int8_t *xq, const int32_t *rowsum, int64_t m,
     if constexpr (WN >= 2) {
         if (k % 16 == 0 && GEMM_SPECIALISED) {
             bool deep = false;
-            if constexpr (WM == 1 && WN == 2) {
+            if constexpr (WN == 2) {
                 if (units <= 256) {
-                    // 64 x 128 tiles that fit one round of the CUs (one block
-                    // each): stages of 256 k in a four-stage ring (96 KB).
-                    // 512 x 3200 x 8640, 200 tiles: 25.3 -> 21.0 us (paired,
-                    // steady state); three stages 32.6 us; 128 x 128 tiles with
-                    // 256-k stages in three (the most that fit) 45.6 against
-                    // 35.2 us on 128 x 28672 x 8192.
+                    // tiles that fit one round of the CUs (one block each):
+                    // stages of 256 k in a four-stage ring (64 x 128 tiles:
+                    // 96 KB; 128 x 128 tiles: all 160 KB, the epilogue's row
+                    // operands held by the producers).  Paired steady-state
+                    // timing: 512 x 3200 x 8640 (200 tiles) 25.3 -> 21.0 us
+                    // (three stages 32.6 us); 128 x 28672 x 8192 35.6 -> 34.6
+                    // us, 128 x 8192 x 28672 41.7 -> 40.0 us (three 256-k
+                    // stages 45.6 / 48.5 us).
                     const int64_t nk2 = (k + 255) / 256;
                     const int sp2 = (int)((nk2 + splits - 1) / splits);
                     hipLaunchKernelGGL((gemm3_kernel<WM, WN, 4, 256>), grid, dim3(512), 0, s, xq,
