@@ -543,13 +543,19 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const int8_t *__restrict__ x
 // memory fence: a fence there would drain every load in flight.  Loads of a
 // stage that ends past K are clamped into their rows; the activation chunks
 // past K are then zeroed in LDS (weights past K meet zero activations).
-__device__ inline int g3_fa(int r) { return (r ^ (r >> 3)) & 7; }
-// weight chunk permutation: rows of 32 bytes (BKT = 128, two chunks) or of
-// 64 bytes (BKT = 256, four chunks)
+// Chunk permutations: a fragment read of 16 consecutive rows (one lane half)
+// must touch 16 distinct 16-byte groups of a 256-byte bank window.
+// Activation rows of 128 bytes (BKT = 128) pair up in one window, so the
+// permutation separates the eight rows of each parity; rows of 256 bytes
+// (BKT = 256) each span the window, so it separates all sixteen.
+template <int BKT>
+__device__ inline int g3_fa(int r) { return BKT == 128 ? (r ^ (r >> 3)) & 7 : r & 15; }
+// weight rows of 32 bytes (BKT = 128, two chunks; eight rows per window) or
+// of 64 bytes (BKT = 256, four chunks; four rows per window)
 template <int BKT>
 __device__ inline int g3_fb(int r)
 {
-    return BKT == 128 ? ((r >> 2) ^ (r >> 3)) & 1 : (r >> 1) & 3;
+    return BKT == 128 ? ((r >> 2) ^ (r >> 3)) & 1 : (r >> 2) & 3;
 }
 
 template <int WM, int WN, int NS, int BKT = BK>
@@ -626,7 +632,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
 #pragma unroll
         for (int q = 0; q < PA; ++q) {
             const int r = (1024 / BKT) * (pw * PA + q) + lane / (BKT / 16);
-            const int c = (lane % (BKT / 16)) ^ g3_fa(r);
+            const int c = (lane % (BKT / 16)) ^ g3_fa<BKT>(r);
             int64_t gm = m0 + r;
             gm = gm < m ? gm : m - 1;
             acol[q] = 16 * c;
@@ -739,7 +745,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
 #pragma unroll
         for (int i = 0; i < WM; ++i) {
             const int row = wm * 32 * WM + 32 * i + l32;
-            const uint4 v = load16(slot + row * BKT + 16 * ((NP * h + p) ^ g3_fa(row)));
+            const uint4 v = load16(slot + row * BKT + 16 * ((NP * h + p) ^ g3_fa<BKT>(row)));
             a[i] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
         }
     };
