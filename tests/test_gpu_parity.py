@@ -267,6 +267,8 @@ def test_tiled_gemm_block_shapes(m, n, k):
     (500, 3100, 8688, "64 x 128 tiles in one round, stages of 256 k, ragged, partial last stage"),
     (384, 4000, 2000, "64 x 128 tiles in one round, stages of 256 k, K % 256 = 208"),
     (200, 4000, 8240, "128 x 128 tiles, stages of 256 k, k split four ways, ragged"),
+    (130, 6000, 16, "128 x 128 tiles, one 16-value stage of the 256-k kernel"),
+    (100, 12300, 272, "64 x 128 tiles, a whole and a 16-value stage of 256 k"),
 ])
 def test_tiled_gemm_configs_every_output(m, n, k, cfg):
     """Every output of each tile configuration of the tiled GEMM (every
