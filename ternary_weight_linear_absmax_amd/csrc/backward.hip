@@ -34,6 +34,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BM2 = 64, BK2 = 128, BN2 = 32;
 constexpr int LDAB = BN2 * 2 + 16;   // bytes per LDS row of 32 bf16 (+16 pad)
+constexpr int TRS = BN2 + 4;         // words per LDS row of raw packed words [word][n]
 
 __device__ inline uint32_t bf16_pair(__bf16 a, __bf16 b)
 {
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(256 * G) void backward_mfma_kernel(const void *__re
     // serial chain of stages per block)
     __shared__ __attribute__((aligned(16))) uint8_t as_all[G][2][3][BM2 * LDAB];
     __shared__ __attribute__((aligned(16))) uint8_t bs_all[G][2][BK2 * LDAB];
-    __shared__ __attribute__((aligned(16))) uint32_t traw_all[G][BN2][BK2 / 16];
+    __shared__ __attribute__((aligned(16))) uint32_t traw_all[G][BK2 / 16][TRS];
     // bf16 gradients are their own first part (the other two are zero), so
     // one product per fragment gives the same sums
     constexpr int NPART = DT == DT_BF16 ? 1 : 3;
@@ -133,25 +134,34 @@ __global__ __launch_bounds__(256 * G) void backward_mfma_kernel(const void *__re
         for (int q = 0; q < NPART; ++q)
             *(uint4 *)(&as[buf][q][gr * LDAB + 2 * gc]) =
                 make_uint4(part[q][0], part[q][1], part[q][2], part[q][3]);
-        traw[tr][tw] = tv;
+        traw[tw][tr] = tv;
     };
-    // trits of the stage into bs[buf][k][n]: thread -> k = tid % 128, n half
-    // tid / 128 (16 n): 16 codes gathered from the raw words, two 16-byte writes
+    // trits of the stage into bs[buf][k][n]: thread -> n octet tid % 4 and k
+    // pair tid / 4; the octet's eight raw words come in two 16-byte LDS reads
+    // ([word][n] layout), and each pair of codes (n even, n odd) becomes a
+    // pair of bf16 trits with one byte permute: code c selects the bytes of
+    // -1 (0xBF80), 0 or +1 (0x3F80) from a table held in two constants
     auto unpack = [&](int buf) __attribute__((always_inline)) {
-        const int kk = tid & 127, nh = tid >> 7;
-        const int g = kk >> 4, i = (kk & 15) >> 2, j = kk & 3;
-        const int sh = 8 * j + 2 * i;
-        uint32_t v[8];
+        const int o = tid & 3, kp = tid >> 2;
+        const int g = kp >> 3, q = (2 * kp) & 15;   // word, first k within it (even)
+        // k q of a word sits at bits 8 (q % 4) + 2 (q / 4); k q + 1 one byte up
+        const int sh = 8 * (q & 3) + 2 * (q >> 2);
+        const uint4 wa = *(const uint4 *)&traw[g][8 * o];
+        const uint4 wb = *(const uint4 *)&traw[g][8 * o + 4];
+        const uint32_t w[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+        uint32_t v0[4], v1[4];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int n0r = 16 * nh + 2 * q;
-            const float t0 = (float)(int)((traw[n0r][g] >> sh) & 3u) - 1.0f;
-            const float t1 = (float)(int)((traw[n0r + 1][g] >> sh) & 3u) - 1.0f;
-            v[q] = bf16_pair((__bf16)t0, (__bf16)t1);
+        for (int e = 0; e < 4; ++e) {
+            // selector bytes (c0 + 4, c0, c1 + 4, c1): low byte then high byte
+            // of each bf16, table bytes 0..3 = BF 00 3F 00, 4..7 = 80 00 80 00
+            const uint32_t x0 = ((w[2 * e] >> sh) & 3u) | (((w[2 * e + 1] >> sh) & 3u) << 16);
+            const uint32_t x1 =
+                ((w[2 * e] >> (sh + 8)) & 3u) | (((w[2 * e + 1] >> (sh + 8)) & 3u) << 16);
+            v0[e] = __builtin_amdgcn_perm(0x00800080u, 0x003F00BFu, x0 * 0x101u + 0x00040004u);
+            v1[e] = __builtin_amdgcn_perm(0x00800080u, 0x003F00BFu, x1 * 0x101u + 0x00040004u);
         }
-        uint4 *dst = (uint4 *)(&bs[buf][kk * LDAB + 32 * nh]);
-        dst[0] = make_uint4(v[0], v[1], v[2], v[3]);
-        dst[1] = make_uint4(v[4], v[5], v[6], v[7]);
+        *(uint4 *)(&bs[buf][(2 * kp) * LDAB + 16 * o]) = make_uint4(v0[0], v0[1], v0[2], v0[3]);
+        *(uint4 *)(&bs[buf][(2 * kp + 1) * LDAB + 16 * o]) = make_uint4(v1[0], v1[1], v1[2], v1[3]);
     };
 
     f32x16 acc[2];
